@@ -1,0 +1,242 @@
+/*
+ * frt.h — C ABI of the MI355X (gfx950) FP8 norm-quantize producers and the
+ * packed sibling-projection FP8 GEMM.
+ *
+ * The operations follow the flashrt-structures 0.2.0 wheel pages:
+ *   - impls/adarms_stack/fp8_chain.py: the fused gated-residual AdaRMS
+ *     producer that feeds the merged QKV and gate/up GEMMs, and the stack's
+ *     fp32 tail that prints its arithmetic;
+ *   - impls/modnorm_qkv_chain/fp8_ptok_table.py: the per-token-table
+ *     no-affine adaptive LayerNorm producer;
+ *   - impls/qkv_pack/fp8_static.py: `_pack_weights` (one joint per-tensor
+ *     scale over the concatenated siblings) and `PackedLinear._run` (the
+ *     packed FP8 GEMM with optional bias whose columns are handed out per
+ *     sibling).
+ *
+ * Conventions shared by every entry point
+ *   - All pointers are DEVICE pointers unless marked [host].
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call is
+ *     asynchronous and stream-ordered; no call synchronises the host.
+ *   - The caller owns every buffer. No call allocates or frees memory, and
+ *     the library keeps no state between calls (except the thread-local
+ *     error string).
+ *   - bf16 tensors are passed as uint16_t bit patterns, FP8 as uint8_t
+ *     e4m3fn codes (OCP FP8: bias 7, max 448, 0x7F/0xFF NaN, no infinity).
+ *   - Leading dimensions (`ld_*`) are in ELEMENTS of the tensor's own type.
+ *   - Row counts are logical: any M not above the caller's buffer rows is
+ *     legal and only M rows are read or written (the pages' row *capacity*
+ *     contract). M = 0 is a no-op returning FRT_OK.
+ *   - Device-resident scalars (act_scale, w_scale) are never read on the
+ *     host.
+ *   - Return value: FRT_OK, or a negative status with a reason available
+ *     from frt_last_error() ("refused: ..."). FRT_E_INVALID = a violated
+ *     contract (bad pointer, size, stride, alignment or aliasing);
+ *     FRT_E_UNSUPPORTED = legal but outside what the kernels implement;
+ *     FRT_E_HIP = a HIP launch error. Validation happens before any launch,
+ *     so a refused call has not touched any buffer.
+ */
+#ifndef FRT_H_
+#define FRT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FRT_OK 0
+#define FRT_E_INVALID (-1)
+#define FRT_E_UNSUPPORTED (-2)
+#define FRT_E_HIP (-3)
+
+/* Largest number of column splits (siblings) one packed call can serve. */
+#define FRT_MAX_SPLITS 16
+
+/* Reason for the last non-OK status on this thread ("" if none). */
+const char* frt_last_error(void);
+
+/* ABI version of this header (bumped on any signature change). */
+int frt_abi_version(void);
+
+/*
+ * frt_ada_norm_quant_fp8 — gated residual + AdaRMS + static per-tensor FP8.
+ *
+ * Source: fp8_chain.py, `_band_elements` (the producer call with the
+ * residual, the delta x, the previous site's gate, a ones norm weight, one
+ * style row, the site's activation scale, eps, `out=` FP8 and `gate_out=`)
+ * and `_make_run` / the stack tail for the arithmetic. Per row m < M and
+ * column d < D:
+ *   h        = fl32(residual[m,d] + gate[m,d] * x[m,d])     (single rounding)
+ *   residual_out[m,d] = bf16_rne(h)
+ *   r_m      = 1 / sqrt(sum_d h^2 / D + eps)
+ *   y        = (h * r_m * weight[d]) * (1 + scale[d]) + shift[d]
+ *   out_fp8  = e4m3_rne(clamp(fl32(y / act_scale), -448, 448))
+ *   gate_out[m,d] = gate_chunk[d]
+ * where the modulation row is mod[m', 0:D] = scale, mod[m', D:2D] = shift,
+ * mod[m', 2D:3D] = gate_chunk (m' = m, or 0 when ld_mod = 0). y is kept in
+ * fp32 and is not rounded to bf16 before the quantiser.
+ *
+ *   M, D          rows; hidden size. D in [512, 16384], even.
+ *   residual      bf16 [M, ld_res]. Required.
+ *   x             bf16 [M, ld_x] delta; NULL => h = residual.
+ *   gate          bf16 previous-site gate; ld_gate = 0 => one row [D]
+ *                 broadcast to every row, else [M, ld_gate]. NULL => zero
+ *                 gate (h = residual, layer 0 of a chain).
+ *   weight        bf16 [D] norm weight; NULL => ones.
+ *   mod           bf16 [*, ld_mod] rows of 3D = [scale | shift | gate];
+ *                 ld_mod = 0 => one row broadcast. Required.
+ *   act_scale     fp32 [1] static scale (> 0). Required iff out_fp8.
+ *   eps           added to the mean square.
+ *   residual_out  bf16 [M, ld_rout]; may be exactly `residual` with the same
+ *                 ld (in-place update). Any other overlap with an input is
+ *                 refused. NULL => not written.
+ *   out_fp8       e4m3fn [M, ld_out]; NULL => not written.
+ *   gate_out      bf16 [M, ld_gout]; NULL => not written.
+ *   y_f32         fp32 [M, ld_y] pre-quantisation y (diagnostic); NULL =>
+ *                 not written.
+ *   amax_out      fp32 [1]: atomically raised to max |y| over the call
+ *                 (calibration); the caller initialises it. NULL => off.
+ * Alignment: every pointer 16-byte aligned and every ld a multiple of 8
+ * (16 for out_fp8) with D % 8 == 0 takes the vector path; otherwise 4-byte
+ * alignment is required (FRT_E_INVALID if not).
+ */
+int frt_ada_norm_quant_fp8(void* stream, int64_t M, int64_t D,
+                           const uint16_t* residual, int64_t ld_res,
+                           const uint16_t* x, int64_t ld_x,
+                           const uint16_t* gate, int64_t ld_gate,
+                           const uint16_t* weight,
+                           const uint16_t* mod, int64_t ld_mod,
+                           const float* act_scale, float eps,
+                           uint16_t* residual_out, int64_t ld_rout,
+                           uint8_t* out_fp8, int64_t ld_out,
+                           uint16_t* gate_out, int64_t ld_gout,
+                           float* y_f32, int64_t ld_y,
+                           float* amax_out);
+
+/*
+ * frt_ptok_table_norm_quant_fp8 — per-token-table no-affine adaptive
+ * LayerNorm + static per-tensor FP8.
+ *
+ * Source: fp8_ptok_table.py, module docstring (table add + chunk selection
+ * + no-affine LayerNorm + modulation + static FP8 quantize in one pass,
+ * never materialising the six chunks), `PerTokenModChainBlock.forward` (the
+ * producer call with x2d, the bf16 temb, the fp32 table, the site scale,
+ * the shift and scale chunk indices, eps), `_ATTN_CHUNKS` / `_FFN_CHUNKS`
+ * (chunk roles shift, scale, gate) and `SUPPORT` (6 chunks, D in
+ * [512, 16384], even). Per row r < R, column d < D:
+ *   shift = fl32(table[shift_idx, d] + temb[r, shift_idx, d])
+ *   scale = fl32(table[scale_idx, d] + temb[r, scale_idx, d])
+ *   mu    = mean_d x[r, d];  var = mean_d (x[r, d] - mu)^2   (biased)
+ *   y     = (x - mu) / sqrt(var + eps) * (1 + scale) + shift
+ *   out_fp8 = e4m3_rne(clamp(fl32(y / act_scale), -448, 448))
+ *
+ *   R, D          rows (= B*M tokens); hidden size. D in [512, 16384], even.
+ *   C             chunks per temb row; must be 6.
+ *   x             bf16 [R, ld_x].
+ *   temb          bf16 [R, C, D] with row stride ld_temb (>= C*D) elements;
+ *                 row r pairs with x row r. Only the two selected chunks
+ *                 are read.
+ *   table         fp32 [C, D] contiguous.
+ *   act_scale     fp32 [1] (> 0). Required iff out_fp8.
+ *   shift_idx, scale_idx   chunk indices in [0, C).
+ *   out_fp8, y_f32, amax_out   as in frt_ada_norm_quant_fp8.
+ * Alignment as in frt_ada_norm_quant_fp8 (table 16-byte aligned for the
+ * vector path).
+ */
+int frt_ptok_table_norm_quant_fp8(void* stream, int64_t R, int64_t D, int C,
+                                  const uint16_t* x, int64_t ld_x,
+                                  const uint16_t* temb, int64_t ld_temb,
+                                  const float* table,
+                                  const float* act_scale,
+                                  int shift_idx, int scale_idx, float eps,
+                                  uint8_t* out_fp8, int64_t ld_out,
+                                  float* y_f32, int64_t ld_y,
+                                  float* amax_out);
+
+/*
+ * frt_pack_weights_fp8 — pack sibling projections into one FP8 matrix with
+ * one joint per-tensor scale.
+ *
+ * Source: qkv_pack/fp8_static.py `_pack_weights` (also `_q8` in
+ * fp8_ptok_table.py). With W = concat_i W_i along the output axis:
+ *   w_scale = max(fl32(max|W| / 448), 1e-8)
+ *   W8      = e4m3_rne(clamp(fl32(W / w_scale), -448, 448))  (true division)
+ *   bias_cat = concat_i (b_i, or zeros for a sibling without bias)
+ * The result is bit-exact to that definition.
+ *
+ *   n_sib         number of siblings, 1 .. FRT_MAX_SPLITS.
+ *   N_i   [host]  int64 [n_sib] output widths (each >= 1).
+ *   K             shared input width, >= 1.
+ *   W_i   [host]  array of n_sib device pointers to bf16 [N_i, K]
+ *                 (checkpoint layout, K contiguous, rows packed).
+ *   b_i   [host]  array of n_sib device pointers to bf16 [N_i] or NULL
+ *                 entries; the array itself NULL => no biases.
+ *   W8            e4m3fn [sum N_i, K] output, rows packed.
+ *   w_scale       fp32 [1] output. Used as the amax accumulator while the
+ *                 call runs; holds the scale when the stream reaches the
+ *                 call's end.
+ *   bias_cat      bf16 [sum N_i] output, or NULL => not written.
+ * Non-finite weights make w_scale and the codes NaN, as the definition does.
+ */
+int frt_pack_weights_fp8(void* stream, int n_sib, const int64_t* N_i,
+                         int64_t K, const uint16_t* const* W_i,
+                         const uint16_t* const* b_i, uint8_t* W8,
+                         float* w_scale, uint16_t* bias_cat);
+
+/*
+ * Workspace bytes frt_packed_gemm_fp8_split needs for this shape (0 when
+ * the chosen kernel needs none). The workspace must be zero-filled once
+ * before its first use; every call leaves it zero-filled again.
+ */
+size_t frt_packed_gemm_fp8_workspace_size(int64_t M, int64_t N_total,
+                                          int64_t K);
+
+/*
+ * frt_packed_gemm_fp8_split — packed FP8 GEMM with dequant, bias and
+ * column-split epilogue.
+ *
+ * Source: qkv_pack/fp8_static.py `PackedLinear._run` (fp8_gemm_bf16 /
+ * fp8_linear_bias_bf16 with act_scale and w_scale into the [M, sum N_i]
+ * output; sibling i takes columns [off_i, off_i + N_i)) and fp8_chain.py
+ * `_quantize` (alpha = act_scale * w_scale folded into one factor). For
+ * m < M, n < N_total:
+ *   acc[m, n] = sum_k dec(x8[m, k]) * dec(W8[n, k])      (fp32 accumulate)
+ *   v         = fl32(alpha * acc[m, n]) + bias_cat[n],  alpha = fl32(as*ws)
+ *   out_s[m, n - off_s] = bf16_rne(v)   (or v itself for out_dtype 1)
+ * with s the split holding column n (off_s = split_n[0] + ... + split_n[s-1]).
+ * The bias is added once, before the single output rounding.
+ *
+ *   M             rows (logical; 0 => no-op).
+ *   K             reduction size: 512 <= K <= 16384 and K % 16 == 0.
+ *   x8            e4m3fn [M, ld_x] (K contiguous); ld_x >= K, ld_x % 16 == 0,
+ *                 16-byte aligned.
+ *   W8            e4m3fn [N_total, K] packed rows (ld = K), 16-byte aligned.
+ *   act_scale, w_scale   fp32 [1] each.
+ *   bias_cat      bf16 [N_total] or NULL (no bias).
+ *   n_split       1 .. FRT_MAX_SPLITS.
+ *   split_n [host] int64 [n_split], each >= 1, summing to N_total.
+ *   out     [host] n_split device pointers; split s is [M, split_n[s]] with
+ *                 row stride ld_out[s] >= split_n[s] (elements). One pointer
+ *                 may cover several adjacent columns runs by merging them
+ *                 into one split. Output regions must not overlap each
+ *                 other or the inputs. 4-byte aligned (bf16: ld even).
+ *   ld_out  [host] int64 [n_split].
+ *   out_dtype     0 = bf16, 1 = fp32 (parity / diagnostics).
+ *   workspace, ws_bytes   see frt_packed_gemm_fp8_workspace_size; NULL/0
+ *                 allowed when the size is 0.
+ */
+int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K,
+                              const uint8_t* x8, int64_t ld_x,
+                              const uint8_t* W8, int64_t N_total,
+                              const float* act_scale, const float* w_scale,
+                              const uint16_t* bias_cat, int n_split,
+                              const int64_t* split_n, void* const* out,
+                              const int64_t* ld_out, int out_dtype,
+                              void* workspace, size_t ws_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FRT_H_ */

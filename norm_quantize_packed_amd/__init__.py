@@ -1,0 +1,293 @@
+"""MI355X (gfx950) FP8 norm-quantize producers and packed sibling GEMM.
+
+Thin ctypes binding over ``libfrt.so`` (built in-tree from ``csrc/`` by
+``norm_quantize_packed_amd._build``). The Python functions carry the C ABI's
+names and do argument marshalling only: torch tensors supply device
+pointers, strides and the current HIP stream; every step of the computation
+runs in the library's HIP kernels. There is no CPU fallback: if the library
+is missing or fails to load, every call raises.
+
+Tensor conventions: bf16 operands are ``torch.bfloat16`` (or 16-bit integer
+views of bf16 bits), FP8 operands ``torch.float8_e4m3fn`` or ``torch.uint8``
+code views, scales ``torch.float32`` device tensors of one element. Matrices
+must be contiguous along their last dimension; the row stride is taken from
+``stride(0)``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "FrtError", "load_library", "library_path",
+    "frt_ada_norm_quant_fp8", "frt_ptok_table_norm_quant_fp8",
+    "frt_pack_weights_fp8", "frt_packed_gemm_fp8_workspace_size",
+    "frt_packed_gemm_fp8_split", "frt_last_error", "frt_abi_version",
+    "FRT_OK", "FRT_E_INVALID", "FRT_E_UNSUPPORTED", "FRT_E_HIP",
+]
+
+FRT_OK, FRT_E_INVALID, FRT_E_UNSUPPORTED, FRT_E_HIP = 0, -1, -2, -3
+FRT_MAX_SPLITS = 16
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB: Optional[ctypes.CDLL] = None
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+_SIGNATURES = {
+    "frt_last_error": (ctypes.c_char_p, []),
+    "frt_abi_version": (_i32, []),
+    "frt_ada_norm_quant_fp8": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _f32,
+        _p, _i64, _p, _i64, _p, _i64, _p, _i64, _p]),
+    "frt_ptok_table_norm_quant_fp8": (_i32, [
+        _p, _i64, _i64, _i32, _p, _i64, _p, _i64, _p, _p, _i32, _i32, _f32,
+        _p, _i64, _p, _i64, _p]),
+    "frt_pack_weights_fp8": (_i32, [
+        _p, _i32, ctypes.POINTER(_i64), _i64, ctypes.POINTER(_p),
+        ctypes.POINTER(_p), _p, _p, _p]),
+    "frt_packed_gemm_fp8_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "frt_packed_gemm_fp8_split": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i32,
+        ctypes.POINTER(_i64), ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32,
+        _p, _sz]),
+}
+
+
+class FrtError(RuntimeError):
+    """A refused or failed library call (status code + reason)."""
+
+    def __init__(self, status: int, reason: str):
+        super().__init__(f"frt status {status}: {reason}")
+        self.status = status
+        self.reason = reason
+
+
+def library_path() -> str:
+    return os.environ.get("FRT_LIBRARY", os.path.join(_HERE, "libfrt.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libfrt.so (once). Raises if it is missing: there is no
+    fallback path."""
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"frt: HIP library not built ({path} missing); run "
+                "`python -m norm_quantize_packed_amd._build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def frt_last_error() -> str:
+    return load_library().frt_last_error().decode()
+
+
+def frt_abi_version() -> int:
+    return load_library().frt_abi_version()
+
+
+def _check(status: int):
+    if status != FRT_OK:
+        raise FrtError(status, frt_last_error())
+
+
+# ------------------------------------------------------------ marshalling
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _ld(t, rows_dim: int = 0) -> int:
+    if t is None:
+        return 0
+    if t.dim() < 2:
+        return 0
+    if t.stride(-1) != 1:
+        raise ValueError("frt: tensors must be contiguous along the last dim")
+    return int(t.stride(rows_dim))
+
+
+def _bf16_like(t, name):
+    if t is None:
+        return
+    import torch
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"frt: {name} must be bfloat16 (or 16-bit bits), "
+                        f"got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"frt: {name} must be a device tensor")
+
+
+def _u8_like(t, name):
+    if t is None:
+        return
+    import torch
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.int8):
+        raise TypeError(f"frt: {name} must be e4m3fn codes, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"frt: {name} must be a device tensor")
+
+
+def _f32_like(t, name):
+    if t is None:
+        return
+    import torch
+    if t.dtype != torch.float32:
+        raise TypeError(f"frt: {name} must be float32, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"frt: {name} must be a device tensor")
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+# ------------------------------------------------------------ entry points
+
+def frt_ada_norm_quant_fp8(residual, mod, act_scale=None, *, x=None,
+                           gate=None, weight=None, eps: float = 1e-6,
+                           residual_out=None, out_fp8=None, gate_out=None,
+                           y_f32=None, amax_out=None, M: Optional[int] = None,
+                           stream=None) -> None:
+    """Gated residual + AdaRMS + static FP8 (see include/frt.h).
+
+    ``gate`` 1-D => one broadcast row; ``mod`` with one row (or 1-D) =>
+    broadcast. ``M`` defaults to ``residual.shape[0]``."""
+    for t, n in ((residual, "residual"), (mod, "mod"), (x, "x"),
+                 (gate, "gate"), (weight, "weight"),
+                 (residual_out, "residual_out"), (gate_out, "gate_out")):
+        _bf16_like(t, n)
+    _u8_like(out_fp8, "out_fp8")
+    for t, n in ((act_scale, "act_scale"), (y_f32, "y_f32"),
+                 (amax_out, "amax_out")):
+        _f32_like(t, n)
+    Mv = residual.shape[0] if M is None else int(M)
+    D = residual.shape[-1]
+    ld_mod = 0 if (mod.dim() == 1 or mod.shape[0] == 1) else _ld(mod)
+    ld_gate = 0 if (gate is None or gate.dim() == 1 or gate.shape[0] == 1) \
+        else _ld(gate)
+    lib = load_library()
+    _check(lib.frt_ada_norm_quant_fp8(
+        _stream(stream), Mv, D, _ptr(residual), _ld(residual), _ptr(x),
+        _ld(x), _ptr(gate), ld_gate, _ptr(weight), _ptr(mod), ld_mod,
+        _ptr(act_scale), float(eps), _ptr(residual_out), _ld(residual_out),
+        _ptr(out_fp8), _ld(out_fp8), _ptr(gate_out), _ld(gate_out),
+        _ptr(y_f32), _ld(y_f32), _ptr(amax_out)))
+
+
+def frt_ptok_table_norm_quant_fp8(x, temb, table, act_scale, shift_idx: int,
+                                  scale_idx: int, *, eps: float = 1e-6,
+                                  out_fp8=None, y_f32=None, amax_out=None,
+                                  R: Optional[int] = None,
+                                  stream=None) -> None:
+    """Per-token-table no-affine adaptive LayerNorm + static FP8.
+
+    ``temb`` is ``[R, C, D]`` (or ``[R, C*D]``), ``table`` ``[C, D]``."""
+    _bf16_like(x, "x")
+    _bf16_like(temb, "temb")
+    _u8_like(out_fp8, "out_fp8")
+    for t, n in ((table, "table"), (act_scale, "act_scale"),
+                 (y_f32, "y_f32"), (amax_out, "amax_out")):
+        _f32_like(t, n)
+    Rv = x.shape[0] if R is None else int(R)
+    D = x.shape[-1]
+    C = table.shape[0]
+    if temb.stride(-1) != 1:
+        raise ValueError("frt: temb must be contiguous along D")
+    if not table.is_contiguous():
+        raise ValueError("frt: table must be contiguous")
+    lib = load_library()
+    _check(lib.frt_ptok_table_norm_quant_fp8(
+        _stream(stream), Rv, D, C, _ptr(x), _ld(x), _ptr(temb),
+        int(temb.stride(0)), _ptr(table), _ptr(act_scale), int(shift_idx),
+        int(scale_idx), float(eps), _ptr(out_fp8), _ld(out_fp8),
+        _ptr(y_f32), _ld(y_f32), _ptr(amax_out)))
+
+
+def frt_pack_weights_fp8(weights: Sequence, biases: Optional[Sequence],
+                         W8, w_scale, bias_cat=None, *, stream=None) -> None:
+    """Joint-scale FP8 packing of sibling ``[N_i, K]`` bf16 weights."""
+    n = len(weights)
+    K = weights[0].shape[1]
+    for i, w in enumerate(weights):
+        _bf16_like(w, f"W_{i}")
+        if not w.is_contiguous():
+            raise ValueError("frt: sibling weights must be contiguous")
+    _u8_like(W8, "W8")
+    _f32_like(w_scale, "w_scale")
+    _bf16_like(bias_cat, "bias_cat")
+    Ns = (_i64 * n)(*[int(w.shape[0]) for w in weights])
+    Ws = (_p * n)(*[_ptr(w) for w in weights])
+    if biases is None:
+        Bs = None
+    else:
+        for i, b in enumerate(biases):
+            _bf16_like(b, f"b_{i}")
+        Bs = (_p * n)(*[_ptr(b) for b in biases])
+    lib = load_library()
+    _check(lib.frt_pack_weights_fp8(_stream(stream), n, Ns, K, Ws, Bs,
+                                    _ptr(W8), _ptr(w_scale), _ptr(bias_cat)))
+
+
+def frt_packed_gemm_fp8_workspace_size(M: int, N_total: int, K: int) -> int:
+    return int(load_library().frt_packed_gemm_fp8_workspace_size(M, N_total, K))
+
+
+def frt_packed_gemm_fp8_split(x8, W8, act_scale, w_scale, outs: Sequence,
+                              split_n: Sequence[int], bias_cat=None, *,
+                              M: Optional[int] = None, workspace=None,
+                              stream=None) -> None:
+    """Packed FP8 GEMM + dequant + bias, each split written to ``outs[s]``
+    (bf16 or float32 tensors ``[>= M, split_n[s]]``, any row stride)."""
+    import torch
+    _u8_like(x8, "x8")
+    _u8_like(W8, "W8")
+    _f32_like(act_scale, "act_scale")
+    _f32_like(w_scale, "w_scale")
+    _bf16_like(bias_cat, "bias_cat")
+    n = len(split_n)
+    if len(outs) != n:
+        raise ValueError("frt: one output per split")
+    dts = {o.dtype for o in outs}
+    if dts == {torch.float32}:
+        out_dtype = 1
+    elif dts <= {torch.bfloat16, torch.int16, torch.uint16}:
+        out_dtype = 0
+    else:
+        raise TypeError(f"frt: outputs must all be bf16 or all float32: {dts}")
+    for o in outs:
+        if not o.is_cuda:
+            raise ValueError("frt: outputs must be device tensors")
+    Mv = x8.shape[0] if M is None else int(M)
+    K = x8.shape[1]
+    N = W8.shape[0]
+    ws_need = frt_packed_gemm_fp8_workspace_size(Mv, N, K)
+    ws_ptr, ws_bytes = 0, 0
+    if ws_need:
+        if workspace is None:
+            raise ValueError(f"frt: this shape needs a {ws_need}-byte workspace")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    lib = load_library()
+    _check(lib.frt_packed_gemm_fp8_split(
+        _stream(stream), Mv, K, _ptr(x8), _ld(x8), _ptr(W8), N,
+        _ptr(act_scale), _ptr(w_scale), _ptr(bias_cat), n,
+        (_i64 * n)(*[int(s) for s in split_n]),
+        (_p * n)(*[_ptr(o) for o in outs]),
+        (_i64 * n)(*[_ld(o) for o in outs]), out_dtype, ws_ptr, ws_bytes))

@@ -1,0 +1,320 @@
+// C ABI of the frt library: argument validation, refusal reasons, dispatch.
+//
+// Every check runs on the host before any launch, so a refused call leaves
+// all buffers untouched. The contracts follow the pages' own refusals
+// (flashrt-structures 0.2.0): the per-token-table producer's SUPPORT
+// envelope (6 chunks, D in [512, 16384], even) in
+// impls/modnorm_qkv_chain/fp8_ptok_table.py `bind_block_seam`; the
+// projection envelope (K in [512, 16384]) of impls/linear_proj/
+// fp8_static.py; the row-capacity contract and the aliasing checks of
+// impls/qkv_pack/fp8_static.py (`PackedLinear`, `alias_stash`).
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "frt_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int refuse(int code, const char* fmt, ...) {
+  char msg[448];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(msg, sizeof msg, fmt, ap);
+  va_end(ap);
+  snprintf(g_err, sizeof g_err, "refused: %s", msg);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return FRT_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return refuse(FRT_E_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// [lo, hi) byte range covered by a [rows, cols] matrix with row stride ld
+struct Range {
+  uintptr_t lo, hi;
+};
+Range span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
+  if (p == nullptr || rows <= 0) return Range{0, 0};
+  const uintptr_t lo = (uintptr_t)p;
+  return Range{lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * esize)};
+}
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.lo && b.hi > b.lo; }
+
+// Do two [rows, cols] matrices with row stride ld (elements of esize bytes)
+// share an element? Exact when both use the same stride (columns of one
+// buffer handed to different splits, rows interleaved); otherwise the
+// conservative byte-span test.
+bool overlap_mat(const void* p, int64_t rp, int64_t cp, const void* q, int64_t rq, int64_t cq,
+                 int64_t ld, int64_t esize) {
+  if (p == nullptr || q == nullptr || rp <= 0 || rq <= 0) return false;
+  const int64_t db = (int64_t)((intptr_t)q - (intptr_t)p);
+  if (db % esize != 0 || cp > ld || cq > ld)
+    return overlap(span(p, rp, cp, ld, esize), span(q, rq, cq, ld, esize));
+  const int64_t d = db / esize;  // q = p + d elements
+  int64_t qd = d / ld, r = d % ld;
+  if (r < 0) { r += ld; qd -= 1; }
+  // element (i, c1) of p equals (j, c2) of q iff (i - j) * ld + (c1 - c2) = d
+  const bool same_row = r < cp && qd > -rq && qd < rp;            // i - j = qd
+  const bool next_row = (ld - r) < cq && qd + 1 > -rq && qd + 1 < rp;  // i - j = qd + 1
+  return same_row || next_row;
+}
+
+constexpr int64_t kDMin = 512, kDMax = 16384;
+
+}  // namespace
+
+extern "C" {
+
+const char* frt_last_error(void) { return g_err; }
+
+int frt_abi_version(void) { return 1; }
+
+int frt_ada_norm_quant_fp8(void* stream, int64_t M, int64_t D, const uint16_t* residual,
+                           int64_t ld_res, const uint16_t* x, int64_t ld_x, const uint16_t* gate,
+                           int64_t ld_gate, const uint16_t* weight, const uint16_t* mod,
+                           int64_t ld_mod, const float* act_scale, float eps,
+                           uint16_t* residual_out, int64_t ld_rout, uint8_t* out_fp8,
+                           int64_t ld_out, uint16_t* gate_out, int64_t ld_gout, float* y_f32,
+                           int64_t ld_y, float* amax_out) {
+  if (M < 0) return refuse(FRT_E_INVALID, "ada_norm: M=%lld < 0", (long long)M);
+  if (D < kDMin || D > kDMax || D % 2)
+    return refuse(FRT_E_INVALID, "ada_norm: D=%lld outside [512, 16384] or odd", (long long)D);
+  if (M > (int64_t)0x7fffffff) return refuse(FRT_E_UNSUPPORTED, "ada_norm: M too large");
+  if (residual == nullptr || mod == nullptr)
+    return refuse(FRT_E_INVALID, "ada_norm: residual and mod are required");
+  if (ld_res < D) return refuse(FRT_E_INVALID, "ada_norm: ld_res < D");
+  if (x != nullptr && ld_x < D) return refuse(FRT_E_INVALID, "ada_norm: ld_x < D");
+  if (gate != nullptr && ld_gate != 0 && ld_gate < D)
+    return refuse(FRT_E_INVALID, "ada_norm: ld_gate must be 0 (broadcast) or >= D");
+  if (ld_mod != 0 && ld_mod < 3 * D)
+    return refuse(FRT_E_INVALID, "ada_norm: ld_mod must be 0 (broadcast) or >= 3*D");
+  if (out_fp8 != nullptr && act_scale == nullptr)
+    return refuse(FRT_E_INVALID, "ada_norm: out_fp8 needs act_scale");
+  if (residual_out != nullptr && ld_rout < D) return refuse(FRT_E_INVALID, "ada_norm: ld_rout < D");
+  if (out_fp8 != nullptr && ld_out < D) return refuse(FRT_E_INVALID, "ada_norm: ld_out < D");
+  if (gate_out != nullptr && ld_gout < D) return refuse(FRT_E_INVALID, "ada_norm: ld_gout < D");
+  if (y_f32 != nullptr && ld_y < D) return refuse(FRT_E_INVALID, "ada_norm: ld_y < D");
+  if (out_fp8 == nullptr && residual_out == nullptr && gate_out == nullptr && y_f32 == nullptr &&
+      amax_out == nullptr)
+    return refuse(FRT_E_INVALID, "ada_norm: no output requested");
+  if (M == 0) return ok();
+
+  // aliasing: residual_out may be residual itself (same ld); nothing else
+  const int64_t mrows = ld_mod ? M : 1, grows = ld_gate ? M : 1;
+  const Range in[] = {span(residual, M, D, ld_res, 2), span(x, M, D, ld_x, 2),
+                      span(gate, grows, D, ld_gate ? ld_gate : D, 2), span(weight, 1, D, D, 2),
+                      span(mod, mrows, 3 * D, ld_mod ? ld_mod : 3 * D, 2),
+                      span(act_scale, 1, 1, 1, 4)};
+  const Range outs[] = {span(residual_out, M, D, ld_rout, 2), span(out_fp8, M, D, ld_out, 1),
+                        span(gate_out, M, D, ld_gout, 2), span(y_f32, M, D, ld_y, 4),
+                        span(amax_out, 1, 1, 1, 4)};
+  const bool inplace = residual_out != nullptr && residual_out == residual && ld_rout == ld_res;
+  for (int o = 0; o < 5; ++o) {
+    for (int i = 0; i < 6; ++i) {
+      if (o == 0 && i == 0 && inplace) continue;
+      if (overlap(outs[o], in[i]))
+        return refuse(FRT_E_INVALID, "ada_norm: output %d overlaps input %d (only an exact in-place residual is allowed)", o, i);
+    }
+    for (int p = o + 1; p < 5; ++p)
+      if (overlap(outs[o], outs[p])) return refuse(FRT_E_INVALID, "ada_norm: outputs %d and %d overlap", o, p);
+  }
+
+  const bool vec8 = D % 8 == 0 && aligned(residual, 16) && ld_res % 8 == 0 &&
+                    (x == nullptr || (aligned(x, 16) && ld_x % 8 == 0)) &&
+                    (gate == nullptr || (aligned(gate, 16) && ld_gate % 8 == 0)) &&
+                    (weight == nullptr || aligned(weight, 16)) && aligned(mod, 16) && ld_mod % 8 == 0 &&
+                    (residual_out == nullptr || (aligned(residual_out, 16) && ld_rout % 8 == 0)) &&
+                    (out_fp8 == nullptr || (aligned(out_fp8, 8) && ld_out % 8 == 0)) &&
+                    (gate_out == nullptr || (aligned(gate_out, 16) && ld_gout % 8 == 0)) &&
+                    (y_f32 == nullptr || (aligned(y_f32, 16) && ld_y % 4 == 0));
+  if (!vec8) {
+    const bool a4 = aligned(residual, 4) && ld_res % 2 == 0 && (x == nullptr || (aligned(x, 4) && ld_x % 2 == 0)) &&
+                    (gate == nullptr || (aligned(gate, 4) && ld_gate % 2 == 0)) &&
+                    (weight == nullptr || aligned(weight, 4)) && aligned(mod, 4) && ld_mod % 2 == 0 &&
+                    (residual_out == nullptr || (aligned(residual_out, 4) && ld_rout % 2 == 0)) &&
+                    (out_fp8 == nullptr || (aligned(out_fp8, 2) && ld_out % 2 == 0)) &&
+                    (gate_out == nullptr || (aligned(gate_out, 4) && ld_gout % 2 == 0)) &&
+                    (y_f32 == nullptr || (aligned(y_f32, 8) && ld_y % 2 == 0));
+    if (!a4) return refuse(FRT_E_INVALID, "ada_norm: pointers/strides must be at least 4-byte aligned (2 elements)");
+  }
+  frt::AdaArgs a{residual, ld_res, x, ld_x, gate, ld_gate, weight, mod, ld_mod,
+                 act_scale, eps, residual_out, ld_rout, out_fp8, ld_out, gate_out, ld_gout,
+                 y_f32, ld_y, amax_out, M, (int)D};
+  if (x == nullptr || gate == nullptr) {
+    a.x = nullptr;
+    a.gate = nullptr;
+  }
+  return hip_status(frt::launch_ada_norm(a, vec8, (hipStream_t)stream), "ada_norm launch");
+}
+
+int frt_ptok_table_norm_quant_fp8(void* stream, int64_t R, int64_t D, int C, const uint16_t* x,
+                                  int64_t ld_x, const uint16_t* temb, int64_t ld_temb,
+                                  const float* table, const float* act_scale, int shift_idx,
+                                  int scale_idx, float eps, uint8_t* out_fp8, int64_t ld_out,
+                                  float* y_f32, int64_t ld_y, float* amax_out) {
+  if (R < 0) return refuse(FRT_E_INVALID, "ptok_norm: R=%lld < 0", (long long)R);
+  if (C != 6) return refuse(FRT_E_INVALID, "ptok_norm: %d-chunk table; the 6-chunk layout is served", C);
+  if (D < kDMin || D > kDMax || D % 2)
+    return refuse(FRT_E_INVALID, "ptok_norm: D=%lld outside [512, 16384] or odd", (long long)D);
+  if (R > (int64_t)0x7fffffff) return refuse(FRT_E_UNSUPPORTED, "ptok_norm: R too large");
+  if (shift_idx < 0 || shift_idx >= C || scale_idx < 0 || scale_idx >= C)
+    return refuse(FRT_E_INVALID, "ptok_norm: chunk index outside [0, %d)", C);
+  if (x == nullptr || temb == nullptr || table == nullptr)
+    return refuse(FRT_E_INVALID, "ptok_norm: x, temb and table are required");
+  if (ld_x < D) return refuse(FRT_E_INVALID, "ptok_norm: ld_x < D");
+  if (ld_temb < (int64_t)C * D) return refuse(FRT_E_INVALID, "ptok_norm: ld_temb < C*D");
+  if (out_fp8 != nullptr && act_scale == nullptr)
+    return refuse(FRT_E_INVALID, "ptok_norm: out_fp8 needs act_scale");
+  if (out_fp8 != nullptr && ld_out < D) return refuse(FRT_E_INVALID, "ptok_norm: ld_out < D");
+  if (y_f32 != nullptr && ld_y < D) return refuse(FRT_E_INVALID, "ptok_norm: ld_y < D");
+  if (out_fp8 == nullptr && y_f32 == nullptr && amax_out == nullptr)
+    return refuse(FRT_E_INVALID, "ptok_norm: no output requested");
+  if (R == 0) return ok();
+  const Range in[] = {span(x, R, D, ld_x, 2), span(temb, R, (int64_t)C * D, ld_temb, 2),
+                      span(table, C, D, D, 4), span(act_scale, 1, 1, 1, 4)};
+  const Range outs[] = {span(out_fp8, R, D, ld_out, 1), span(y_f32, R, D, ld_y, 4), span(amax_out, 1, 1, 1, 4)};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlap(outs[o], in[i])) return refuse(FRT_E_INVALID, "ptok_norm: output %d overlaps input %d", o, i);
+    for (int p = o + 1; p < 3; ++p)
+      if (overlap(outs[o], outs[p])) return refuse(FRT_E_INVALID, "ptok_norm: outputs %d and %d overlap", o, p);
+  }
+  const bool vec8 = D % 8 == 0 && aligned(x, 16) && ld_x % 8 == 0 && aligned(temb, 16) && ld_temb % 8 == 0 &&
+                    aligned(table, 16) && (out_fp8 == nullptr || (aligned(out_fp8, 8) && ld_out % 8 == 0)) &&
+                    (y_f32 == nullptr || (aligned(y_f32, 16) && ld_y % 4 == 0));
+  if (!vec8) {
+    const bool a4 = aligned(x, 4) && ld_x % 2 == 0 && aligned(temb, 4) && ld_temb % 2 == 0 && aligned(table, 8) &&
+                    (out_fp8 == nullptr || (aligned(out_fp8, 2) && ld_out % 2 == 0)) &&
+                    (y_f32 == nullptr || (aligned(y_f32, 8) && ld_y % 2 == 0));
+    if (!a4) return refuse(FRT_E_INVALID, "ptok_norm: pointers/strides must be at least 4-byte aligned (2 elements)");
+  }
+  frt::PtokArgs a{x, ld_x, temb, ld_temb, table, act_scale, eps, shift_idx, scale_idx,
+                  out_fp8, ld_out, y_f32, ld_y, amax_out, R, (int)D};
+  return hip_status(frt::launch_ptok_norm(a, vec8, (hipStream_t)stream), "ptok_norm launch");
+}
+
+int frt_pack_weights_fp8(void* stream, int n_sib, const int64_t* N_i, int64_t K,
+                         const uint16_t* const* W_i, const uint16_t* const* b_i, uint8_t* W8,
+                         float* w_scale, uint16_t* bias_cat) {
+  if (n_sib < 1 || n_sib > FRT_MAX_SPLITS)
+    return refuse(FRT_E_INVALID, "pack: n_sib=%d outside [1, %d]", n_sib, FRT_MAX_SPLITS);
+  if (N_i == nullptr || W_i == nullptr || W8 == nullptr || w_scale == nullptr)
+    return refuse(FRT_E_INVALID, "pack: N_i, W_i, W8 and w_scale are required");
+  if (K < 1) return refuse(FRT_E_INVALID, "pack: K=%lld < 1", (long long)K);
+  frt::PackSib sibs[FRT_MAX_SPLITS];
+  int64_t rows = 0;
+  for (int i = 0; i < n_sib; ++i) {
+    if (N_i[i] < 1) return refuse(FRT_E_INVALID, "pack: N_%d=%lld < 1", i, (long long)N_i[i]);
+    if (W_i[i] == nullptr) return refuse(FRT_E_INVALID, "pack: W_%d is NULL", i);
+    if (!aligned(W_i[i], 2)) return refuse(FRT_E_INVALID, "pack: W_%d misaligned", i);
+    sibs[i].w = W_i[i];
+    sibs[i].b = b_i != nullptr ? b_i[i] : nullptr;
+    sibs[i].rows = N_i[i];
+    sibs[i].row_off = rows;
+    sibs[i].elems = N_i[i] * K;
+    sibs[i].dst_off = rows * K;
+    rows += N_i[i];
+  }
+  if (rows * K > ((int64_t)1 << 40)) return refuse(FRT_E_UNSUPPORTED, "pack: matrix too large");
+  const Range w8r = span(W8, rows, K, K, 1), sr = span(w_scale, 1, 1, 1, 4), br = span(bias_cat, 1, rows, rows, 2);
+  if (overlap(w8r, sr) || overlap(w8r, br) || overlap(sr, br)) return refuse(FRT_E_INVALID, "pack: outputs overlap");
+  for (int i = 0; i < n_sib; ++i) {
+    const Range wr = span(sibs[i].w, sibs[i].rows, K, K, 2);
+    const Range bb = span(sibs[i].b, 1, sibs[i].rows, sibs[i].rows, 2);
+    if (overlap(wr, w8r) || overlap(wr, sr) || overlap(wr, br) || overlap(bb, w8r) || overlap(bb, sr) ||
+        overlap(bb, br))
+      return refuse(FRT_E_INVALID, "pack: sibling %d overlaps an output", i);
+  }
+  return hip_status(frt::launch_pack(sibs, n_sib, K, W8, w_scale, bias_cat, (hipStream_t)stream), "pack launch");
+}
+
+size_t frt_packed_gemm_fp8_workspace_size(int64_t M, int64_t N_total, int64_t K) {
+  if (M <= 0 || N_total <= 0 || K <= 0) return 0;
+  return frt::gemm_workspace_bytes(M, N_total, K);
+}
+
+int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K, const uint8_t* x8, int64_t ld_x,
+                              const uint8_t* W8, int64_t N_total, const float* act_scale,
+                              const float* w_scale, const uint16_t* bias_cat, int n_split,
+                              const int64_t* split_n, void* const* out, const int64_t* ld_out,
+                              int out_dtype, void* workspace, size_t ws_bytes) {
+  if (M < 0) return refuse(FRT_E_INVALID, "gemm: M=%lld < 0", (long long)M);
+  if (K < 512 || K > 16384) return refuse(FRT_E_INVALID, "gemm: K=%lld outside [512, 16384]", (long long)K);
+  if (K % 16) return refuse(FRT_E_UNSUPPORTED, "gemm: K=%lld not a multiple of 16", (long long)K);
+  if (N_total < 1) return refuse(FRT_E_INVALID, "gemm: N_total < 1");
+  if (M > (1 << 24) || N_total > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "gemm: M or N_total too large");
+  if (x8 == nullptr || W8 == nullptr || act_scale == nullptr || w_scale == nullptr)
+    return refuse(FRT_E_INVALID, "gemm: x8, W8, act_scale and w_scale are required");
+  if (ld_x < K || ld_x % 16) return refuse(FRT_E_INVALID, "gemm: ld_x must be >= K and a multiple of 16");
+  if (!aligned(x8, 16) || !aligned(W8, 16)) return refuse(FRT_E_INVALID, "gemm: x8 and W8 must be 16-byte aligned");
+  if ((M - 1) * ld_x + K > (int64_t)0x7fffffff || N_total * K > (int64_t)0x7fffffff)
+    return refuse(FRT_E_UNSUPPORTED, "gemm: operand larger than 2 GiB");
+  if (out_dtype != 0 && out_dtype != 1) return refuse(FRT_E_INVALID, "gemm: out_dtype must be 0 (bf16) or 1 (fp32)");
+  if (n_split < 1 || n_split > FRT_MAX_SPLITS)
+    return refuse(FRT_E_INVALID, "gemm: n_split=%d outside [1, %d]", n_split, FRT_MAX_SPLITS);
+  if (split_n == nullptr || out == nullptr || ld_out == nullptr)
+    return refuse(FRT_E_INVALID, "gemm: split_n, out and ld_out are required");
+  const int64_t es = out_dtype ? 4 : 2;
+  frt::GemmArgs a{};
+  int64_t tot = 0;
+  for (int s = 0; s < n_split; ++s) {
+    if (split_n[s] < 1) return refuse(FRT_E_INVALID, "gemm: split %d has width %lld < 1", s, (long long)split_n[s]);
+    if (out[s] == nullptr) return refuse(FRT_E_INVALID, "gemm: out[%d] is NULL", s);
+    if (ld_out[s] < split_n[s]) return refuse(FRT_E_INVALID, "gemm: ld_out[%d] < split width", s);
+    if (!aligned(out[s], (size_t)es)) return refuse(FRT_E_INVALID, "gemm: out[%d] misaligned", s);
+    a.sp.ptr[s] = out[s];
+    a.sp.ld[s] = ld_out[s];
+    a.sp.off[s] = (int)tot;
+    tot += split_n[s];
+  }
+  if (tot != N_total)
+    return refuse(FRT_E_INVALID, "gemm: splits sum to %lld, N_total is %lld", (long long)tot, (long long)N_total);
+  a.sp.off[n_split] = (int)tot;
+  for (int s = n_split + 1; s <= FRT_MAX_SPLITS; ++s) a.sp.off[s] = (int)tot;
+  a.sp.n = n_split;
+  const size_t need = frt::gemm_workspace_bytes(M, N_total, K);
+  if (need > 0 && (workspace == nullptr || ws_bytes < need))
+    return refuse(FRT_E_INVALID, "gemm: workspace of %zu bytes required", need);
+  if (M == 0) return ok();
+  // outputs must not overlap each other or the inputs
+  const Range xin = span(x8, M, K, ld_x, 1), win = span(W8, N_total, K, K, 1),
+              bin = span(bias_cat, 1, N_total, N_total, 2), sa = span(act_scale, 1, 1, 1, 4),
+              sw = span(w_scale, 1, 1, 1, 4), wsr = span(workspace, 1, (int64_t)need, (int64_t)need, 1);
+  for (int s = 0; s < n_split; ++s) {
+    const Range o = span(out[s], M, split_n[s], ld_out[s], es);
+    if (overlap(o, xin) || overlap(o, win) || overlap(o, bin) || overlap(o, sa) || overlap(o, sw) || overlap(o, wsr))
+      return refuse(FRT_E_INVALID, "gemm: output %d overlaps an input or the workspace", s);
+    for (int t = s + 1; t < n_split; ++t) {
+      const bool ov = ld_out[s] == ld_out[t]
+                          ? overlap_mat(out[s], M, split_n[s], out[t], M, split_n[t], ld_out[s], es)
+                          : overlap(o, span(out[t], M, split_n[t], ld_out[t], es));
+      if (ov) return refuse(FRT_E_INVALID, "gemm: outputs %d and %d overlap", s, t);
+    }
+  }
+  a.x = x8;
+  a.ld_x = ld_x;
+  a.w = W8;
+  a.act_scale = act_scale;
+  a.w_scale = w_scale;
+  a.bias = bias_cat;
+  a.M = (int)M;
+  a.N = (int)N_total;
+  a.K = (int)K;
+  a.out_f32 = out_dtype;
+  a.ws = workspace;
+  return hip_status(frt::launch_gemm(a, (hipStream_t)stream), "gemm launch");
+}
+
+}  // extern "C"

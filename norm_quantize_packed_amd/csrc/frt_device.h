@@ -1,0 +1,104 @@
+// Device helpers shared by the frt HIP kernels (gfx950 / CDNA4).
+//
+// bf16 <-> fp32, the static FP8 e4m3fn quantiser, and wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace frt {
+
+constexpr float kFp8Max = 448.0f;  // largest finite e4m3fn magnitude
+
+// bf16 halves of a 32-bit word (element 0 in the low half) -> fp32, exact.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? (((u >> 16) & 0x8000u) | 0x7fc0u) : r;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return f2bf(lo) | (f2bf(hi) << 16);
+}
+
+// Correctly rounded y / s, given rcp = RN(1 / s) and s > 0 normal.
+// q0 = y * rcp is within two ulps of y / s; one residual correction (the
+// remainder y - q*s is exact under FMA for a near-quotient) brings it within
+// half an ulp plus a tiny term, i.e. faithful; a second correction with the
+// correctly rounded reciprocal then yields the correctly rounded quotient
+// (Markstein's theorem on FMA-based division). Five VALU operations instead
+// of the general division expansion. The corrections can turn a -0
+// quotient into +0 (+0 + -0 = +0 under round-to-nearest); since s > 0 the
+// quotient always carries y's sign, which copysign restores.
+__device__ __forceinline__ float div_rn(float y, float s, float rcp) {
+  float q = y * rcp;
+  float r = __builtin_fmaf(-q, s, y);
+  q = __builtin_fmaf(r, rcp, q);
+  r = __builtin_fmaf(-q, s, y);
+  return __builtin_copysignf(__builtin_fmaf(r, rcp, q), y);
+}
+
+// clamp to [-448, 448] keeping NaN (the definition's clamp propagates NaN).
+__device__ __forceinline__ float clamp_fp8(float q) {
+  float c = __builtin_amdgcn_fmed3f(q, -kFp8Max, kFp8Max);
+  return (q != q) ? q : c;
+}
+
+// Four fp32 (already clamped) -> four e4m3fn codes in one dword, element 0
+// in the low byte. v_cvt_pk_fp8_f32 rounds to nearest even (OCP e4m3fn on
+// gfx950).
+__device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return uint32_t(w);
+}
+__device__ __forceinline__ uint32_t cvt2_fp8(float a, float b) {
+  return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xffffu;
+}
+
+// ---- wave64 reductions (DPP within rows of 16, readlane across rows) ----
+
+__device__ __forceinline__ float dpp_sum16(float v) {
+  // quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2),
+  // row_half_mirror (pairs the two quads of each 8-lane half),
+  // row_mirror (pairs the two halves of each 16-lane row)
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, true);
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xF, 0xF, true);
+  return v;
+}
+
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Sum over the 64 lanes; the result is wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_sum16(v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
+}
+
+__device__ __forceinline__ float dpp_max16(float v) {
+  v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, true));
+  v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, true));
+  v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, true));
+  v = fmaxf(v, __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xF, 0xF, true));
+  return v;
+}
+
+// Max over the 64 lanes of non-negative values (NaN-propagating through
+// the unsigned bit order: NaN bit patterns sort above +inf).
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+}  // namespace frt

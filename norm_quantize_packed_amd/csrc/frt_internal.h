@@ -1,0 +1,73 @@
+// Internal kernel-argument structs and launchers of the frt library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/frt.h"
+
+namespace frt {
+
+struct AdaArgs {
+  const uint16_t* res; int64_t ld_res;
+  const uint16_t* x; int64_t ld_x;
+  const uint16_t* gate; int64_t ld_gate;
+  const uint16_t* weight;
+  const uint16_t* mod; int64_t ld_mod;
+  const float* act_scale; float eps;
+  uint16_t* rout; int64_t ld_rout;
+  uint8_t* out; int64_t ld_out;
+  uint16_t* gout; int64_t ld_gout;
+  float* y; int64_t ld_y;
+  float* amax;
+  int64_t M; int D;
+};
+
+struct PtokArgs {
+  const uint16_t* x; int64_t ld_x;
+  const uint16_t* temb; int64_t ld_temb;
+  const float* table;
+  const float* act_scale; float eps;
+  int shift_idx, scale_idx;
+  uint8_t* out; int64_t ld_out;
+  float* y; int64_t ld_y;
+  float* amax;
+  int64_t R; int D;
+};
+
+hipError_t launch_ada_norm(const AdaArgs& a, bool vec8, hipStream_t st);
+hipError_t launch_ptok_norm(const PtokArgs& a, bool vec8, hipStream_t st);
+
+struct PackSib {
+  const uint16_t* w;      // bf16 [n, K]
+  const uint16_t* b;      // bf16 [n] or null
+  int64_t elems;          // n * K
+  int64_t dst_off;        // element offset of this sibling in W8
+  int64_t rows, row_off;  // n, sum of earlier n
+};
+
+hipError_t launch_pack(const PackSib* sibs, int n_sib, int64_t K, uint8_t* w8,
+                       float* w_scale, uint16_t* bias_cat, hipStream_t st);
+
+struct SplitTab {
+  void* ptr[FRT_MAX_SPLITS];
+  int64_t ld[FRT_MAX_SPLITS];
+  int off[FRT_MAX_SPLITS + 1];
+  int n;
+};
+
+struct GemmArgs {
+  const uint8_t* x; int64_t ld_x;
+  const uint8_t* w;
+  const float* act_scale; const float* w_scale;
+  const uint16_t* bias;
+  int M, N, K;
+  int out_f32;
+  SplitTab sp;
+  void* ws;
+};
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+
+}  // namespace frt

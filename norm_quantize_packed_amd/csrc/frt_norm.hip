@@ -1,0 +1,388 @@
+// Conditioned-norm producers with static per-tensor FP8 e4m3fn output.
+//
+//  - ada_norm_kernel: gated residual + AdaRMS (flashrt-structures 0.2.0,
+//    impls/adarms_stack/fp8_chain.py: the fused producer of `_band_elements`,
+//    the arithmetic of the stack tail in `_make_run`).
+//  - ptok_norm_kernel: per-token-table no-affine adaptive LayerNorm
+//    (impls/modnorm_qkv_chain/fp8_ptok_table.py, module docstring and
+//    `PerTokenModChainBlock.forward`).
+//
+// Layout: one row is owned by WPR wavefronts (WPR = 1, 2 or 4) of a
+// 256-thread block; the block holds 4 / WPR rows. Lane `l` of the row's
+// wave `w` handles the VEC-element vectors v = w*64 + l + i*64*WPR,
+// i < NV, so each load instruction of a wave covers 64 consecutive vectors
+// (fully coalesced 16-byte accesses on the VEC = 8 path). The row stays in
+// registers between the statistics pass and the output pass, so every input
+// byte is read from HBM once. Row statistics are reduced with DPP inside
+// rows of 16 lanes, readlane across the four rows of the wave, and LDS
+// across the WPR waves of a row.
+#include "frt_device.h"
+#include "frt_internal.h"
+
+namespace frt {
+
+namespace {
+
+template <int VEC>
+struct Vec;
+template <>
+struct Vec<8> {
+  uint32_t w[4];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    uint4 t = *reinterpret_cast<const uint4*>(p);
+    w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+  }
+  __device__ __forceinline__ void store(uint16_t* p) const {
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __device__ __forceinline__ float f(int e) const { return (e & 1) ? bf16hi(w[e >> 1]) : bf16lo(w[e >> 1]); }
+};
+template <>
+struct Vec<2> {
+  uint32_t w[1];
+  __device__ __forceinline__ void load(const uint16_t* p) { w[0] = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<uint32_t*>(p) = w[0]; }
+  __device__ __forceinline__ float f(int e) const { return e ? bf16hi(w[0]) : bf16lo(w[0]); }
+};
+
+template <int VEC>
+__device__ __forceinline__ void store_codes(uint8_t* p, const float* q);
+template <>
+__device__ __forceinline__ void store_codes<8>(uint8_t* p, const float* q) {
+  uint2 t;
+  t.x = cvt4_fp8(q[0], q[1], q[2], q[3]);
+  t.y = cvt4_fp8(q[4], q[5], q[6], q[7]);
+  *reinterpret_cast<uint2*>(p) = t;
+}
+template <>
+__device__ __forceinline__ void store_codes<2>(uint8_t* p, const float* q) {
+  *reinterpret_cast<uint16_t*>(p) = (uint16_t)cvt2_fp8(q[0], q[1]);
+}
+
+template <int VEC>
+__device__ __forceinline__ void store_f32(float* p, const float* v) {
+  if constexpr (VEC == 8) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  } else {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
+  }
+}
+
+template <int VEC>
+__device__ __forceinline__ void load_f32(const float* p, float* v) {
+  if constexpr (VEC == 8) {
+    float4 a = reinterpret_cast<const float4*>(p)[0];
+    float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    float2 a = *reinterpret_cast<const float2*>(p);
+    v[0] = a.x; v[1] = a.y;
+  }
+}
+
+// Sum of `v` over the WPR waves that own this row (wave-uniform result).
+// Every thread of the block must call it (it contains a barrier when
+// WPR > 1).
+template <int WPR>
+__device__ __forceinline__ float row_sum(float v, float* red, int wave) {
+  float s = wave_sum(v);
+  if constexpr (WPR == 1) {
+    return s;
+  } else {
+    __syncthreads();  // previous use of `red` finished
+    if ((threadIdx.x & 63) == 0) red[wave] = s;
+    __syncthreads();
+    const int base = wave - wave % WPR;
+    float t = 0.0f;
+#pragma unroll
+    for (int k = 0; k < WPR; ++k) t += red[base + k];
+    return t;
+  }
+}
+
+__device__ __forceinline__ void amax_commit(float* amax, float m) {
+  uint32_t u = wave_umax(__float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(amax), u);
+}
+
+}  // namespace
+
+template <int WPR, int NV, int VEC>
+__global__ __launch_bounds__(256) void ada_norm_kernel(AdaArgs a) {
+  constexpr int RPB = 4 / WPR;
+  __shared__ float red[4];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * RPB + wave / WPR;
+  const int sub = wave % WPR;
+  const bool row_ok = row < a.M;
+  const int nvec = a.D / VEC;
+
+  float h[NV][VEC];
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = sub * 64 + lane + i * 64 * WPR;
+    if (row_ok && v < nvec) {
+      const int64_t c = (int64_t)v * VEC;
+      Vec<VEC> r;
+      r.load(a.res + row * a.ld_res + c);
+      if (a.x != nullptr && a.gate != nullptr) {
+        Vec<VEC> x, g;
+        x.load(a.x + row * a.ld_x + c);
+        g.load(a.gate + row * a.ld_gate + c);  // ld_gate == 0: broadcast row
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) h[i][e] = __builtin_fmaf(g.f(e), x.f(e), r.f(e));
+      } else {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) h[i][e] = r.f(e);
+      }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) ss = __builtin_fmaf(h[i][e], h[i][e], ss);
+      if (a.rout != nullptr) {
+        Vec<VEC> o;
+#pragma unroll
+        for (int e = 0; e < VEC; e += 2) o.w[e >> 1] = pack_bf2(h[i][e], h[i][e + 1]);
+        o.store(a.rout + row * a.ld_rout + c);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) h[i][e] = 0.0f;
+    }
+  }
+  const float tot = row_sum<WPR>(ss, red, wave);
+  const float rr = __builtin_amdgcn_rsqf(tot / (float)a.D + a.eps);
+
+  float s = 1.0f, rcp = 1.0f;
+  if (a.out != nullptr) {
+    s = *a.act_scale;
+    rcp = 1.0f / s;
+  }
+  float amax = 0.0f;
+  if (row_ok) {
+    const uint16_t* mrow = a.mod + row * a.ld_mod;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = sub * 64 + lane + i * 64 * WPR;
+      if (v < nvec) {
+        const int64_t c = (int64_t)v * VEC;
+        Vec<VEC> sc, sh;
+        sc.load(mrow + c);
+        sh.load(mrow + a.D + c);
+        float y[VEC];
+        if (a.weight != nullptr) {
+          Vec<VEC> w;
+          w.load(a.weight + c);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) y[e] = h[i][e] * rr * w.f(e);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) y[e] = h[i][e] * rr;
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) y[e] = __builtin_fmaf(y[e], sc.f(e), y[e]) + sh.f(e);
+        if (a.y != nullptr) store_f32<VEC>(a.y + row * a.ld_y + c, y);
+        if (a.amax != nullptr) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) amax = __uint_as_float(max(__float_as_uint(amax), __float_as_uint(fabsf(y[e]))));
+        }
+        if (a.out != nullptr) {
+          float q[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) q[e] = clamp_fp8(div_rn(y[e], s, rcp));
+          store_codes<VEC>(a.out + row * a.ld_out + c, q);
+        }
+        if (a.gout != nullptr) {
+          Vec<VEC> g;
+          g.load(mrow + 2 * a.D + c);
+          g.store(a.gout + row * a.ld_gout + c);
+        }
+      }
+    }
+  }
+  if (a.amax != nullptr) amax_commit(a.amax, amax);
+}
+
+template <int WPR, int NV, int VEC>
+__global__ __launch_bounds__(256) void ptok_norm_kernel(PtokArgs a) {
+  constexpr int RPB = 4 / WPR;
+  __shared__ float red[4];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * RPB + wave / WPR;
+  const int sub = wave % WPR;
+  const bool row_ok = row < a.R;
+  const int nvec = a.D / VEC;
+
+  float x[NV][VEC];
+  Vec<VEC> tsh[NV], tsc[NV];
+  float sum = 0.0f;
+  const uint16_t* trow = a.temb + row * a.ld_temb;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = sub * 64 + lane + i * 64 * WPR;
+    if (row_ok && v < nvec) {
+      const int64_t c = (int64_t)v * VEC;
+      Vec<VEC> xv;
+      xv.load(a.x + row * a.ld_x + c);
+      tsh[i].load(trow + (int64_t)a.shift_idx * a.D + c);
+      tsc[i].load(trow + (int64_t)a.scale_idx * a.D + c);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        x[i][e] = xv.f(e);
+        sum += x[i][e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) x[i][e] = 0.0f;
+    }
+  }
+  const float inv_d = 1.0f / (float)a.D;
+  const float mu = row_sum<WPR>(sum, red, wave) * inv_d;
+  float sq = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = sub * 64 + lane + i * 64 * WPR;
+    if (row_ok && v < nvec) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const float d = x[i][e] - mu;
+        sq = __builtin_fmaf(d, d, sq);
+      }
+    }
+  }
+  const float var = row_sum<WPR>(sq, red, wave) * inv_d;
+  const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
+
+  float s = 1.0f, rcp = 1.0f;
+  if (a.out != nullptr) {
+    s = *a.act_scale;
+    rcp = 1.0f / s;
+  }
+  float amax = 0.0f;
+  if (row_ok) {
+    const float* tab_s = a.table + (int64_t)a.shift_idx * a.D;
+    const float* tab_c = a.table + (int64_t)a.scale_idx * a.D;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int v = sub * 64 + lane + i * 64 * WPR;
+      if (v < nvec) {
+        const int64_t c = (int64_t)v * VEC;
+        float ts[VEC], tc[VEC], y[VEC];
+        load_f32<VEC>(tab_s + c, ts);
+        load_f32<VEC>(tab_c + c, tc);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const float shift = ts[e] + tsh[i].f(e);
+          const float scale = tc[e] + tsc[i].f(e);
+          const float n = (x[i][e] - mu) * rstd;
+          y[e] = __builtin_fmaf(n, scale, n) + shift;
+        }
+        if (a.y != nullptr) store_f32<VEC>(a.y + row * a.ld_y + c, y);
+        if (a.amax != nullptr) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) amax = __uint_as_float(max(__float_as_uint(amax), __float_as_uint(fabsf(y[e]))));
+        }
+        if (a.out != nullptr) {
+          float q[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) q[e] = clamp_fp8(div_rn(y[e], s, rcp));
+          store_codes<VEC>(a.out + row * a.ld_out + c, q);
+        }
+      }
+    }
+  }
+  if (a.amax != nullptr) amax_commit(a.amax, amax);
+}
+
+// ---------------------------------------------------------------- launchers
+
+namespace {
+
+// Waves per row: enough vector slots per lane for D, and more waves when
+// rows are scarce so that short calls still spread across the chip.
+int pick_wpr(int64_t rows, int64_t D) {
+  int wpr = D > 8192 ? 4 : (D > 4096 ? 2 : 1);
+  if (rows < 2048 && D >= 2048 && wpr < 2) wpr = 2;
+  if (rows < 512 && D >= 2048) wpr = 4;
+  return wpr;
+}
+
+#define FRT_NV_SWITCH(NVV, ...)                    \
+  switch (NVV) {                                   \
+    case 1: { constexpr int NV = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int NV = 2; __VA_ARGS__; } break; \
+    case 3: { constexpr int NV = 3; __VA_ARGS__; } break; \
+    case 4: { constexpr int NV = 4; __VA_ARGS__; } break; \
+    case 5: { constexpr int NV = 5; __VA_ARGS__; } break; \
+    case 6: { constexpr int NV = 6; __VA_ARGS__; } break; \
+    case 7: { constexpr int NV = 7; __VA_ARGS__; } break; \
+    case 8: { constexpr int NV = 8; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;          \
+  }
+
+#define FRT_NV2_SWITCH(NVV, ...)                   \
+  switch (NVV) {                                   \
+    case 2: { constexpr int NV = 2; __VA_ARGS__; } break; \
+    case 4: { constexpr int NV = 4; __VA_ARGS__; } break; \
+    case 8: { constexpr int NV = 8; __VA_ARGS__; } break; \
+    case 16: { constexpr int NV = 16; __VA_ARGS__; } break; \
+    case 32: { constexpr int NV = 32; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;          \
+  }
+
+int pow2_slots(int64_t n) {
+  int p = 2;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+#define FRT_WPR_SWITCH(W, ...)                     \
+  switch (W) {                                     \
+    case 1: { constexpr int WPR = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int WPR = 2; __VA_ARGS__; } break; \
+    case 4: { constexpr int WPR = 4; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;          \
+  }
+
+}  // namespace
+
+hipError_t launch_ada_norm(const AdaArgs& a, bool vec8, hipStream_t st) {
+  const int vec = vec8 ? 8 : 2;
+  const int wpr = pick_wpr(a.M, a.D);
+  const int64_t nvec = a.D / vec;
+  const int nv = (int)((nvec + 64 * wpr - 1) / (64 * wpr));
+  const int rpb = 4 / wpr;
+  const dim3 grid((unsigned)((a.M + rpb - 1) / rpb));
+  if (vec8) {
+    FRT_WPR_SWITCH(wpr, FRT_NV_SWITCH(nv, hipLaunchKernelGGL((ada_norm_kernel<WPR, NV, 8>), grid, dim3(256), 0, st, a)))
+  } else {
+    // 4-byte path (unaligned or D % 8 != 0): one row per block, 4 waves,
+    // up to 32 two-element slots per lane
+    const int nv2 = pow2_slots((nvec + 255) / 256);
+    const dim3 grid4((unsigned)a.M);
+    FRT_NV2_SWITCH(nv2, hipLaunchKernelGGL((ada_norm_kernel<4, NV, 2>), grid4, dim3(256), 0, st, a))
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ptok_norm(const PtokArgs& a, bool vec8, hipStream_t st) {
+  const int wpr = pick_wpr(a.R, a.D);
+  if (vec8) {
+    const int64_t nvec = a.D / 8;
+    const int nv = (int)((nvec + 64 * wpr - 1) / (64 * wpr));
+    const int rpb = 4 / wpr;
+    const dim3 grid((unsigned)((a.R + rpb - 1) / rpb));
+    FRT_WPR_SWITCH(wpr, FRT_NV_SWITCH(nv, hipLaunchKernelGGL((ptok_norm_kernel<WPR, NV, 8>), grid, dim3(256), 0, st, a)))
+  } else {
+    const int64_t nvec = a.D / 2;
+    const int nv2 = pow2_slots((nvec + 255) / 256);
+    const dim3 grid4((unsigned)a.R);
+    FRT_NV2_SWITCH(nv2, hipLaunchKernelGGL((ptok_norm_kernel<4, NV, 2>), grid4, dim3(256), 0, st, a))
+  }
+  return hipGetLastError();
+}
+
+}  // namespace frt

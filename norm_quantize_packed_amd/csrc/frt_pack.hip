@@ -1,0 +1,143 @@
+// Joint-scale FP8 packing of sibling projections (flashrt-structures 0.2.0,
+// impls/qkv_pack/fp8_static.py `_pack_weights`).
+//
+// Four stream-ordered launches, no workspace:
+//   1. prep   : w_scale <- +0 (it accumulates max|W| as float bits while
+//               the call runs) and bias_cat <- concat(b_i or zeros)
+//   2. amax   : per sibling, wave max of |w| bits -> atomicMax on w_scale
+//   3. cast   : per sibling, codes = e4m3(clamp(fl32(w / s))), with
+//               s = max(fl32(amax / 448), 1e-8) derived from w_scale's bits
+//   4. final  : w_scale <- s
+// For non-negative floats the IEEE bit order equals the numeric order, so
+// an unsigned max over bit patterns is the float max (NaN sorts above +inf,
+// so a NaN weight propagates as the definition's max does).
+#include "frt_device.h"
+#include "frt_internal.h"
+
+namespace frt {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float pack_scale_from_amax(uint32_t amax_bits) {
+  const float s = __uint_as_float(amax_bits) / kFp8Max;  // correctly rounded
+  return (s != s) ? s : fmaxf(s, 1e-8f);
+}
+
+__global__ __launch_bounds__(kThreads) void pack_prep_kernel(
+    float* w_scale, uint16_t* bias_cat, const uint16_t* b, int64_t n, int64_t off, int first) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (first && t == 0) *reinterpret_cast<uint32_t*>(w_scale) = 0u;
+  if (bias_cat != nullptr && t < n) bias_cat[off + t] = (b != nullptr) ? b[t] : (uint16_t)0;
+}
+
+// Each thread folds 8 elements per step when the sibling is 16-byte
+// aligned and a multiple of 8 long, else one element per step.
+template <bool V8>
+__global__ __launch_bounds__(kThreads) void pack_amax_kernel(const uint16_t* w, int64_t elems,
+                                                              float* w_scale) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t m = 0;
+  if constexpr (V8) {
+    const uint4* w4 = reinterpret_cast<const uint4*>(w);
+    const int64_t n4 = elems / 8;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+      const uint4 t = w4[i];
+      const uint32_t ws[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // |bf16| as fp32 bits: clear the sign, widen to the high half-word
+        const uint32_t lo = (ws[k] & 0x7fffu) << 16;
+        const uint32_t hi = ws[k] & 0x7fff0000u;
+        m = max(m, max(lo, hi));
+      }
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < elems; i += stride)
+      m = max(m, (uint32_t)(w[i] & 0x7fffu) << 16);
+  }
+  m = wave_umax(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(w_scale), m);
+}
+
+template <bool V8>
+__global__ __launch_bounds__(kThreads) void pack_cast_kernel(const uint16_t* w, int64_t elems,
+                                                              uint8_t* dst, const float* w_scale) {
+  const float s = pack_scale_from_amax(*reinterpret_cast<const uint32_t*>(w_scale));
+  const float rcp = 1.0f / s;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  if constexpr (V8) {
+    const uint4* w4 = reinterpret_cast<const uint4*>(w);
+    uint2* d2 = reinterpret_cast<uint2*>(dst);
+    const int64_t n4 = elems / 8;
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+      const uint4 t = w4[i];
+      const uint32_t ws[4] = {t.x, t.y, t.z, t.w};
+      float q[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        q[2 * k] = clamp_fp8(div_rn(bf16lo(ws[k]), s, rcp));
+        q[2 * k + 1] = clamp_fp8(div_rn(bf16hi(ws[k]), s, rcp));
+      }
+      uint2 o;
+      o.x = cvt4_fp8(q[0], q[1], q[2], q[3]);
+      o.y = cvt4_fp8(q[4], q[5], q[6], q[7]);
+      d2[i] = o;
+    }
+  } else {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < elems; i += stride) {
+      const float q = clamp_fp8(div_rn(bf16f(w[i]), s, rcp));
+      dst[i] = (uint8_t)(cvt2_fp8(q, 0.0f) & 0xffu);
+    }
+  }
+}
+
+__global__ void pack_final_kernel(float* w_scale) {
+  if (threadIdx.x == 0 && blockIdx.x == 0)
+    *w_scale = pack_scale_from_amax(*reinterpret_cast<const uint32_t*>(w_scale));
+}
+
+unsigned grid_for(int64_t work) {
+  int64_t g = (work + kThreads - 1) / kThreads;
+  if (g > 4096) g = 4096;  // grid-stride beyond ~16 blocks per CU
+  if (g < 1) g = 1;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_pack(const PackSib* sibs, int n_sib, int64_t K, uint8_t* w8, float* w_scale,
+                       uint16_t* bias_cat, hipStream_t st) {
+  (void)K;
+  for (int i = 0; i < n_sib; ++i) {
+    const int64_t n = bias_cat != nullptr ? sibs[i].rows : 1;
+    hipLaunchKernelGGL(pack_prep_kernel, dim3(grid_for(n)), dim3(kThreads), 0, st, w_scale, bias_cat,
+                       sibs[i].b, sibs[i].rows, sibs[i].row_off, i == 0 ? 1 : 0);
+  }
+  for (int i = 0; i < n_sib; ++i) {
+    const PackSib& p = sibs[i];
+    const bool v8 = (p.elems % 8 == 0) && ((uintptr_t)p.w % 16 == 0);
+    if (v8)
+      hipLaunchKernelGGL(pack_amax_kernel<true>, dim3(grid_for(p.elems / 8)), dim3(kThreads), 0, st,
+                         p.w, p.elems, w_scale);
+    else
+      hipLaunchKernelGGL(pack_amax_kernel<false>, dim3(grid_for(p.elems)), dim3(kThreads), 0, st, p.w,
+                         p.elems, w_scale);
+  }
+  for (int i = 0; i < n_sib; ++i) {
+    const PackSib& p = sibs[i];
+    uint8_t* dst = w8 + p.dst_off;
+    const bool v8 = (p.elems % 8 == 0) && ((uintptr_t)p.w % 16 == 0) && ((uintptr_t)dst % 8 == 0);
+    if (v8)
+      hipLaunchKernelGGL(pack_cast_kernel<true>, dim3(grid_for(p.elems / 8)), dim3(kThreads), 0, st,
+                         p.w, p.elems, dst, w_scale);
+    else
+      hipLaunchKernelGGL(pack_cast_kernel<false>, dim3(grid_for(p.elems)), dim3(kThreads), 0, st, p.w,
+                         p.elems, dst, w_scale);
+  }
+  hipLaunchKernelGGL(pack_final_kernel, dim3(1), dim3(64), 0, st, w_scale);
+  return hipGetLastError();
+}
+
+}  // namespace frt

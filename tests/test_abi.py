@@ -1,0 +1,168 @@
+"""The C ABI without a GPU: the library loads, exports every entry point
+include/frt.h declares, and refuses out-of-contract calls on the host before
+any HIP call (fake, never dereferenced device addresses are passed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import norm_quantize_packed_amd as frt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "frt.h")
+
+FAKE = 0x7f0000000000       # a 16-byte-aligned address no call may touch
+MB = 1 << 20
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(frt_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(frt.library_path()):
+        pytest.fail("libfrt.so is not built; run python -m "
+                    "norm_quantize_packed_amd._build")
+    return frt.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"frt_ada_norm_quant_fp8", "frt_ptok_table_norm_quant_fp8",
+            "frt_pack_weights_fp8", "frt_packed_gemm_fp8_split",
+            "frt_packed_gemm_fp8_workspace_size",
+            "frt_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.frt_abi_version() == 1
+
+
+def _ada(lib, M=4, D=512, **kw):
+    a = dict(stream=None, M=M, D=D, residual=FAKE, ld_res=D, x=FAKE + MB,
+             ld_x=D, gate=FAKE + 2 * MB, ld_gate=0, weight=None,
+             mod=FAKE + 3 * MB, ld_mod=0, act_scale=FAKE + 4 * MB, eps=1e-6,
+             residual_out=FAKE + 5 * MB, ld_rout=D, out_fp8=FAKE + 6 * MB,
+             ld_out=D, gate_out=None, ld_gout=0, y_f32=None, ld_y=0,
+             amax_out=None)
+    a.update(kw)
+    return lib.frt_ada_norm_quant_fp8(*a.values())
+
+
+def test_ada_refusals(lib):
+    assert _ada(lib, D=500) == frt.FRT_E_INVALID
+    assert "D=500" in frt.frt_last_error()
+    assert _ada(lib, D=16386) == frt.FRT_E_INVALID
+    assert _ada(lib, D=513) == frt.FRT_E_INVALID
+    assert _ada(lib, M=-1) == frt.FRT_E_INVALID
+    assert _ada(lib, residual=None) == frt.FRT_E_INVALID
+    assert _ada(lib, act_scale=None) == frt.FRT_E_INVALID
+    assert _ada(lib, ld_res=100) == frt.FRT_E_INVALID
+    assert _ada(lib, ld_mod=700) == frt.FRT_E_INVALID
+    assert _ada(lib, out_fp8=None, residual_out=None) == frt.FRT_E_INVALID
+    # an output overlapping an input (other than the exact in-place residual)
+    assert _ada(lib, out_fp8=FAKE + MB + 64) == frt.FRT_E_INVALID
+    assert "overlaps" in frt.frt_last_error()
+    assert _ada(lib, residual_out=FAKE + 64) == frt.FRT_E_INVALID
+    # misaligned for every path
+    assert _ada(lib, residual=FAKE + 1) == frt.FRT_E_INVALID
+
+
+def test_ada_zero_rows_is_noop(lib):
+    assert _ada(lib, M=0) == frt.FRT_OK
+    # exact in-place residual passes validation (checked with M = 0)
+    assert _ada(lib, M=0, residual_out=FAKE) == frt.FRT_OK
+    assert frt.frt_last_error() == ""
+
+
+def _ptok(lib, R=4, D=512, C=6, **kw):
+    a = dict(stream=None, R=R, D=D, C=C, x=FAKE, ld_x=D, temb=FAKE + MB,
+             ld_temb=C * D, table=FAKE + 20 * MB, act_scale=FAKE + 21 * MB,
+             shift_idx=0, scale_idx=1, eps=1e-6, out_fp8=FAKE + 22 * MB,
+             ld_out=D, y_f32=None, ld_y=0, amax_out=None)
+    a.update(kw)
+    return lib.frt_ptok_table_norm_quant_fp8(*a.values())
+
+
+def test_ptok_refusals(lib):
+    assert _ptok(lib, C=5) == frt.FRT_E_INVALID
+    assert "6-chunk" in frt.frt_last_error()
+    assert _ptok(lib, D=256) == frt.FRT_E_INVALID
+    assert _ptok(lib, shift_idx=6) == frt.FRT_E_INVALID
+    assert _ptok(lib, scale_idx=-1) == frt.FRT_E_INVALID
+    assert _ptok(lib, ld_temb=512) == frt.FRT_E_INVALID
+    assert _ptok(lib, temb=None) == frt.FRT_E_INVALID
+    assert _ptok(lib, out_fp8=FAKE + MB + 512) == frt.FRT_E_INVALID
+    assert _ptok(lib, R=0) == frt.FRT_OK
+
+
+def _gemm(lib, M=16, K=512, splits=(512, 128, 128), N=None, outs=None,
+          lds=None, **kw):
+    n = len(splits)
+    N = sum(splits) if N is None else N
+    outs = outs or [FAKE + (40 + 4 * i) * MB for i in range(n)]
+    lds = lds or list(splits)
+    a = dict(stream=None, M=M, K=K, x8=FAKE, ld_x=K, W8=FAKE + MB, N=N,
+             act_scale=FAKE + 30 * MB, w_scale=FAKE + 31 * MB, bias=None,
+             n_split=n, split_n=(ctypes.c_int64 * n)(*splits),
+             out=(ctypes.c_void_p * n)(*outs),
+             ld_out=(ctypes.c_int64 * n)(*lds), out_dtype=0, ws=None,
+             ws_bytes=0)
+    a.update(kw)
+    return lib.frt_packed_gemm_fp8_split(*a.values())
+
+
+def test_gemm_refusals(lib):
+    assert _gemm(lib, N=700) == frt.FRT_E_INVALID
+    assert "sum" in frt.frt_last_error()
+    assert _gemm(lib, K=256) == frt.FRT_E_INVALID
+    assert _gemm(lib, K=520) == frt.FRT_E_UNSUPPORTED
+    assert _gemm(lib, ld_x=520) == frt.FRT_E_INVALID
+    assert _gemm(lib, x8=FAKE + 8) == frt.FRT_E_INVALID
+    assert _gemm(lib, out_dtype=2) == frt.FRT_E_INVALID
+    assert _gemm(lib, splits=(768,), lds=[100]) == frt.FRT_E_INVALID
+    assert _gemm(lib, splits=(768, 0)) == frt.FRT_E_INVALID
+    assert _gemm(lib, splits=tuple([1] * 17)) == frt.FRT_E_INVALID
+    # overlapping split outputs
+    o = FAKE + 40 * MB
+    assert _gemm(lib, outs=[o, o + 512, o + 2 * MB]) == frt.FRT_E_INVALID
+    assert "overlap" in frt.frt_last_error()
+    # an output over an input
+    assert _gemm(lib, outs=[FAKE + MB, o + MB, o + 2 * MB]) == frt.FRT_E_INVALID
+
+
+def test_gemm_zero_rows_and_workspace_query(lib):
+    assert _gemm(lib, M=0) == frt.FRT_OK
+    assert frt.frt_packed_gemm_fp8_workspace_size(0, 768, 512) == 0
+    assert frt.frt_packed_gemm_fp8_workspace_size(16, 768, 512) >= 0
+
+
+def test_pack_refusals(lib):
+    def call(n_sib=2, Ns=(64, 32), K=128, Ws=(FAKE, FAKE + MB), Bs=None,
+             W8=FAKE + 10 * MB, ws=FAKE + 11 * MB, bc=None):
+        n = max(n_sib, 1)
+        return lib.frt_pack_weights_fp8(
+            None, n_sib, (ctypes.c_int64 * n)(*Ns[:n]), K,
+            (ctypes.c_void_p * n)(*Ws[:n]),
+            None if Bs is None else (ctypes.c_void_p * n)(*Bs), W8, ws, bc)
+    assert call(n_sib=0) == frt.FRT_E_INVALID
+    assert call(n_sib=17, Ns=[1] * 17, Ws=[FAKE] * 17) == frt.FRT_E_INVALID
+    assert call(Ns=(64, 0)) == frt.FRT_E_INVALID
+    assert call(K=0) == frt.FRT_E_INVALID
+    assert call(Ws=(FAKE, None)) == frt.FRT_E_INVALID
+    assert call(W8=FAKE + 100) == frt.FRT_E_INVALID     # over sibling 0
+    assert "overlaps" in frt.frt_last_error()
+
+
+def test_gemm_same_stride_overlap_is_exact(lib):
+    """Splits written into one buffer with a shared row stride: columns
+    that collide are refused (the interleaved, disjoint case is exercised
+    on the GPU)."""
+    o = FAKE + 40 * MB
+    lds = [768, 768, 768]
+    assert _gemm(lib, outs=[o, o + 500 * 2, o + 640 * 2], lds=lds) == frt.FRT_E_INVALID
+    assert _gemm(lib, outs=[o + 600 * 2, o, o + 2 * MB], lds=lds) == frt.FRT_E_INVALID

@@ -1,0 +1,272 @@
+"""GPU parity of the two producers against the oracle, through the C ABI.
+
+Workloads 1, 2 and 4 (AdaRMS) run whole; workloads 3 and 5 (per-token table)
+run on a row slice the oracle finishes in seconds and, at full size in the
+bench's launch configuration, on sampled rows. Edge cases: the 4-byte path
+(D % 8 != 0), row strides, per-row modulation, the norm weight, a missing
+delta, in-place residual, calibration amax, D at both ends of the envelope.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import norm_quantize_packed_amd as frt
+import workloads as wl
+from oracle import producers, codecs
+from gpu_util import (Guarded, assert_codes_close, assert_codes_quantise_own_y,
+                      assert_rows_close, dev_bf16, dev_f32, host_bf16, host_u8,
+                      scalar)
+
+pytestmark = pytest.mark.gpu
+EPS = wl.EPS
+
+
+def _run_ada(inp, s, *, x_key="x", mod_key="mod", residual=None, weight=None,
+             ld_pad=0, want_y=True, inplace=False, gate_out=True):
+    R = inp["rows"]
+    D = inp["D"]
+    res_bits = inp["residual"] if residual is None else residual
+    res = dev_bf16(res_bits)
+    x = dev_bf16(inp[x_key]) if inp.get(x_key) is not None else None
+    gate = dev_bf16(inp["gate"]) if inp.get("gate") is not None else None
+    mod = dev_bf16(inp[mod_key])
+    w = dev_bf16(weight) if weight is not None else None
+    out = Guarded(R, D, torch.uint8, ld=D + ld_pad)
+    rout = None if inplace else Guarded(R, D, torch.bfloat16, ld=D + ld_pad)
+    gout = Guarded(R, D, torch.bfloat16) if gate_out else None
+    y = Guarded(R, D, torch.float32, ld=D + ld_pad) if want_y else None
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    frt.frt_ada_norm_quant_fp8(
+        res, mod, scalar(s), x=x, gate=gate, weight=w, eps=EPS,
+        residual_out=res if inplace else rout.view, out_fp8=out.view,
+        gate_out=gout.view if gout else None, y_f32=y.view if y else None,
+        amax_out=amax)
+    torch.cuda.synchronize()
+    for g in (out, rout, gout, y):
+        if g is not None:
+            g.check_guards()
+    return {
+        "codes": host_u8(out.view),
+        "residual_out": host_bf16(res if inplace else rout.view),
+        "gate_out": host_bf16(gout.view) if gout else None,
+        "y": y.view.cpu().numpy() if y else None,
+        "amax": float(amax.item()),
+    }
+
+
+def _check_ada(got, ref, s, what):
+    assert np.array_equal(got["residual_out"], ref["residual_out"]), \
+        f"{what}: residual write-back not bit-exact"
+    if got["gate_out"] is not None:
+        assert np.array_equal(got["gate_out"], ref["gate_out"])
+    if got["y"] is not None:
+        assert_rows_close(got["y"], ref["y"], what=what)
+        assert_codes_quantise_own_y(got["codes"], got["y"], s)
+        amax_ref = np.max(np.abs(ref["y"]))
+        assert abs(got["amax"] - amax_ref) <= 1e-5 * amax_ref
+    assert_codes_close(got["codes"], ref["codes"], what)
+
+
+def _calib_scale_ada(cid):
+    cal = wl.producer_inputs(cid, calib=True)
+    r = producers.ada_norm_quant_fp8(cal["residual"], cal["x"], cal["gate"],
+                                     cal["mod"], None, EPS)
+    return producers.calibrate_act_scale(r["y"]), cal, r
+
+
+@pytest.mark.parametrize("cid", [1, 4])
+def test_ada_workload(cid):
+    s, _, _ = _calib_scale_ada(cid)
+    inp = wl.producer_inputs(cid)
+    ref = producers.ada_norm_quant_fp8(inp["residual"], inp["x"],
+                                       inp["gate"], inp["mod"], s, EPS)
+    got = _run_ada(inp, s)
+    _check_ada(got, ref, s, f"workload {cid}")
+
+
+def test_ada_small_m_every_row_count():
+    """The latency band: every M in 1..64 (D = 4096, per-element gate)."""
+    s, _, _ = _calib_scale_ada(4)
+    full = wl.producer_inputs(4)
+    ref = producers.ada_norm_quant_fp8(full["residual"], full["x"],
+                                       full["gate"], full["mod"], s, EPS)
+    for M in list(range(1, 65)):
+        inp = wl.producer_inputs(4, rows=M)
+        got = _run_ada(inp, s, want_y=(M % 7 == 1))
+        sub = {k: (v[:M] if isinstance(v, np.ndarray) else v)
+               for k, v in ref.items()}
+        _check_ada(got, sub, s, f"M={M}")
+
+
+def test_ada_chained_sites_workload2():
+    """Site 1 writes the residual in place; site 2 takes it with site 1's
+    mod-row gate as its broadcast previous gate (the chain's hand-off)."""
+    cal = wl.producer_inputs(2, calib=True)
+    c1 = producers.ada_norm_quant_fp8(cal["residual"], cal["x"], cal["gate"],
+                                      cal["mod"], None, EPS)
+    D = cal["D"]
+    c2 = producers.ada_norm_quant_fp8(c1["residual_out"], cal["x2"],
+                                      cal["mod"][0, 2 * D:3 * D], cal["mod2"],
+                                      None, EPS)
+    s1 = producers.calibrate_act_scale(c1["y"])
+    s2 = producers.calibrate_act_scale(c2["y"])
+    inp = wl.producer_inputs(2)
+    r1 = producers.ada_norm_quant_fp8(inp["residual"], inp["x"], inp["gate"],
+                                      inp["mod"], s1, EPS)
+    r2 = producers.ada_norm_quant_fp8(r1["residual_out"], inp["x2"],
+                                      inp["mod"][0, 2 * D:3 * D], inp["mod2"],
+                                      s2, EPS)
+    # GPU: in place on one residual buffer, second site gated by the first
+    # site's mod-row gate chunk (a broadcast row)
+    R = inp["rows"]
+    res = dev_bf16(inp["residual"])
+    mod1, mod2 = dev_bf16(inp["mod"]), dev_bf16(inp["mod2"])
+    x1, x2 = dev_bf16(inp["x"]), dev_bf16(inp["x2"])
+    o1 = torch.empty(R, D, dtype=torch.uint8, device="cuda")
+    o2 = torch.empty_like(o1)
+    y1 = torch.empty(R, D, dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y1)
+    frt.frt_ada_norm_quant_fp8(res, mod1, scalar(s1), x=x1,
+                               gate=dev_bf16(inp["gate"]), eps=EPS,
+                               residual_out=res, out_fp8=o1, y_f32=y1)
+    frt.frt_ada_norm_quant_fp8(res, mod2, scalar(s2), x=x2,
+                               gate=mod1[0, 2 * D:3 * D], eps=EPS,
+                               residual_out=res, out_fp8=o2, y_f32=y2)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(res), r2["residual_out"])
+    assert_rows_close(y1.cpu().numpy(), r1["y"], what="site 1")
+    assert_rows_close(y2.cpu().numpy(), r2["y"], what="site 2")
+    assert_codes_close(host_u8(o1), r1["codes"], "site 1")
+    assert_codes_close(host_u8(o2), r2["codes"], "site 2")
+
+
+@pytest.mark.parametrize("D", [512, 514, 1000, 2050, 16384])
+def test_ada_edges(D):
+    """Vector (D % 8 == 0) and 4-byte paths, strided rows, per-row mod,
+    a norm weight, in-place residual, both envelope ends."""
+    rng = np.random.default_rng(D)
+    R = 37
+    bf = lambda a: wl.to_bf16_bits(np.asarray(a, np.float32))
+    inp = {"rows": R, "D": D,
+           "residual": bf(rng.standard_normal((R, D))),
+           "x": bf(rng.standard_normal((R, D))),
+           "gate": bf(rng.standard_normal((R, D)) * 0.5),
+           "mod": bf(rng.standard_normal((R, 3 * D)) * 0.1)}
+    w = bf(1 + 0.1 * rng.standard_normal(D))
+    ref0 = producers.ada_norm_quant_fp8(inp["residual"], inp["x"], inp["gate"],
+                                        inp["mod"], None, EPS, weight_bits=w)
+    s = producers.calibrate_act_scale(ref0["y"]) * np.float32(0.5)  # saturate
+    ref = producers.ada_norm_quant_fp8(inp["residual"], inp["x"], inp["gate"],
+                                       inp["mod"], s, EPS, weight_bits=w)
+    ref["gate_out"] = inp["mod"][:, 2 * D:3 * D]
+    got = _run_ada(inp, s, weight=w, ld_pad=8 if D % 8 == 0 else 2)
+    _check_ada(got, ref, s, f"D={D}")
+    got2 = _run_ada(inp, s, weight=w, inplace=True, gate_out=False)
+    assert np.array_equal(got2["residual_out"], ref["residual_out"])
+    assert np.array_equal(got2["codes"], got["codes"])
+
+
+def test_ada_no_delta_and_zero_rows():
+    inp = wl.producer_inputs(1)
+    s, _, _ = _calib_scale_ada(1)
+    ref = producers.ada_norm_quant_fp8(inp["residual"], None, None,
+                                       inp["mod"], s, EPS)
+    got = _run_ada(dict(inp, x=None, gate=None), s)
+    _check_ada(got, ref, s, "no delta")
+    # M = 0 is a no-op
+    res = dev_bf16(inp["residual"])
+    out = torch.full((16, 512), 7, dtype=torch.uint8, device="cuda")
+    frt.frt_ada_norm_quant_fp8(res, dev_bf16(inp["mod"]), scalar(s),
+                               out_fp8=out, M=0)
+    torch.cuda.synchronize()
+    assert (out == 7).all()
+
+
+# ------------------------------------------------------------- per-token table
+
+def _run_ptok(inp, s, *, want_y=True, ld_pad=0, temb_pad=0, rows=None):
+    x = dev_bf16(inp["x"])
+    R, D = inp["x"].shape
+    t = inp["temb"].reshape(R, -1)
+    if temb_pad:
+        t = np.concatenate([t, np.zeros((R, temb_pad), np.uint16)], axis=1)
+    temb = dev_bf16(t)
+    table = dev_f32(inp["table"])
+    out = Guarded(R, D, torch.uint8, ld=D + ld_pad)
+    y = Guarded(R, D, torch.float32, ld=D + ld_pad) if want_y else None
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    frt.frt_ptok_table_norm_quant_fp8(
+        x, temb, table, scalar(s), inp["shift_idx"], inp["scale_idx"],
+        eps=EPS, out_fp8=out.view, y_f32=y.view if y else None,
+        amax_out=amax)
+    torch.cuda.synchronize()
+    out.check_guards()
+    if y:
+        y.check_guards()
+    return {"codes": host_u8(out.view), "y": y.view.cpu().numpy() if y else None,
+            "amax": float(amax.item())}
+
+
+def _ptok_ref(inp, s, rows=None):
+    sl = slice(None) if rows is None else rows
+    return producers.ptok_norm_quant_fp8(inp["x"][sl], inp["temb"][sl],
+                                         inp["table"], s, inp["shift_idx"],
+                                         inp["scale_idx"], EPS)
+
+
+def _ptok_scale(cid, rows):
+    cal = wl.producer_inputs(cid, calib=True, rows=rows)
+    return producers.calibrate_act_scale(_ptok_ref(cal, None)["y"])
+
+
+@pytest.mark.parametrize("cid,rows", [(3, 1031), (5, 97)])
+def test_ptok_workload_slice(cid, rows):
+    s = _ptok_scale(cid, rows)
+    inp = wl.producer_inputs(cid, rows=rows)
+    ref = _ptok_ref(inp, s)
+    got = _run_ptok(inp, s)
+    assert_rows_close(got["y"], ref["y"], what=f"workload {cid}")
+    assert_codes_quantise_own_y(got["codes"], got["y"], s)
+    assert_codes_close(got["codes"], ref["codes"], f"workload {cid}")
+    amax_ref = np.max(np.abs(ref["y"]))
+    assert abs(got["amax"] - amax_ref) <= 1e-5 * amax_ref
+
+
+@pytest.mark.parametrize("cid", [3, 5])
+def test_ptok_workload_full_size_sampled(cid):
+    """Full workload size, the bench's launch (no y output); sampled rows
+    checked against the oracle."""
+    s = _ptok_scale(cid, 256)
+    inp = wl.producer_inputs(cid)
+    got = _run_ptok(inp, s, want_y=False)
+    R = inp["x"].shape[0]
+    rows = np.unique(np.concatenate([
+        np.random.default_rng(cid).integers(0, R, 96), [0, R - 1]]))
+    ref = _ptok_ref(inp, s, rows)
+    assert_codes_close(got["codes"][rows], ref["codes"], f"workload {cid}")
+    if cid == 5:
+        # heavy tails beyond the calibration amax saturate somewhere
+        assert (np.abs(codecs.e4m3_ordinal(got["codes"])) == 126).any()
+
+
+@pytest.mark.parametrize("D,s_idx,c_idx", [(512, 0, 1), (514, 3, 4),
+                                           (3000, 5, 2), (16384, 1, 0)])
+def test_ptok_edges(D, s_idx, c_idx):
+    rng = np.random.default_rng(D + s_idx)
+    R = 19
+    bf = lambda a: wl.to_bf16_bits(np.asarray(a, np.float32))
+    inp = {"x": bf(rng.standard_normal((R, D)) * 3 + 1),
+           "temb": bf(rng.standard_normal((R, 6, D)) * 0.2),
+           "table": (rng.standard_normal((6, D)) * 0.2).astype(np.float32),
+           "shift_idx": s_idx, "scale_idx": c_idx}
+    s = producers.calibrate_act_scale(_ptok_ref(inp, None)["y"])
+    ref = _ptok_ref(inp, s)
+    got = _run_ptok(inp, s, ld_pad=8 if D % 8 == 0 else 2,
+                    temb_pad=8 if D % 8 == 0 else 2)
+    assert_rows_close(got["y"], ref["y"], what=f"D={D}")
+    assert_codes_close(got["codes"], ref["codes"], f"D={D}")
+    # one row
+    got1 = _run_ptok({k: (v[:1] if k in ("x", "temb") else v)
+                      for k, v in inp.items()}, s)
+    assert np.array_equal(got1["codes"], got["codes"][:1])

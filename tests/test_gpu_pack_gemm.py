@@ -1,0 +1,192 @@
+"""GPU parity of the weight packer (bit-exact) and of the packed FP8 GEMM
+(from identical FP8 operands) against the oracle, through the C ABI."""
+
+import numpy as np
+import pytest
+import torch
+
+import norm_quantize_packed_amd as frt
+import workloads as wl
+from oracle import codecs, gemm, pack
+from gpu_util import (Guarded, assert_gemm_bf16, assert_gemm_f32, dev_bf16,
+                      dev_u8, host_bf16, host_u8, scalar)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_pack(Ws, bs, with_bias=True):
+    K = Ws[0].shape[1]
+    N = sum(w.shape[0] for w in Ws)
+    W8 = Guarded(N, K, torch.uint8)
+    ws = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+    bc = Guarded(1, N, torch.bfloat16) if with_bias else None
+    frt.frt_pack_weights_fp8([dev_bf16(w) for w in Ws],
+                             None if bs is None else
+                             [None if b is None else dev_bf16(b) for b in bs],
+                             W8.view, ws, bc.view[0] if bc else None)
+    torch.cuda.synchronize()
+    W8.check_guards()
+    if bc:
+        bc.check_guards()
+    return (host_u8(W8.view), np.float32(ws.item()),
+            host_bf16(bc.view)[0] if bc else None)
+
+
+@pytest.mark.parametrize("cid,site", [(1, 0), (2, 0), (2, 1), (3, 0), (4, 0)])
+def test_pack_workload_bit_exact(cid, site):
+    w = wl.weights(cid, site)
+    g8, gs, gb = _gpu_pack(w["W"], w["b"])
+    r8, rs, rb, _ = pack.pack_weights(w["W"], w["b"])
+    assert gs == rs
+    assert np.array_equal(gb, rb)
+    assert np.array_equal(g8, r8)
+
+
+def test_pack_full_widest_workload_sampled():
+    """Workload 5's 32768 x 16384 gate/up pack: the joint scale exactly, and
+    sampled rows bit-exact (the oracle packs those rows under that scale)."""
+    w = wl.weights(5, 0)
+    g8, gs, _ = _gpu_pack(w["W"], w["b"], with_bias=False)
+    amax = max(np.abs(codecs.bf16_to_f32(x)).max() for x in w["W"])
+    assert gs == np.float32(max(np.float32(amax / np.float32(448)),
+                                np.float32(1e-8)))
+    W = np.concatenate(w["W"], axis=0)
+    rows = np.random.default_rng(5).integers(0, W.shape[0], 64)
+    q = (codecs.bf16_to_f32(W[rows]) / gs).astype(np.float32)
+    ref = codecs.e4m3_encode(np.clip(q, -448, 448))
+    assert np.array_equal(g8[rows], ref)
+
+
+def test_pack_every_bf16_pattern_and_odd_shapes():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    fin = bits[np.isfinite(codecs.bf16_to_f32(bits))]
+    fin = np.concatenate([fin, np.zeros((-fin.size) % 256, np.uint16)])
+    W = fin.reshape(-1, 256)
+    for Ws in ([W], [W[:100, :255].copy(), W[100:, :255].copy()],
+               [(W[:, :200] & np.uint16(0x87FF)).copy()],
+               [np.zeros((16, 64), np.uint16)],
+               [W[:3, :7].copy(), W[3:9, :7].copy(), W[9:10, :7].copy()]):
+        g8, gs, gb = _gpu_pack(Ws, [None] * len(Ws))
+        r8, rs, rb, _ = pack.pack_weights(Ws, None)
+        assert gs == rs
+        assert np.array_equal(g8, r8)
+        assert not gb.any()
+
+
+# ------------------------------------------------------------------ GEMM
+
+def _gpu_gemm(x8, w8, s_a, s_w, bias, splits, *, f32, M=None, ld_pad=0):
+    M = x8.shape[0] if M is None else M
+    outs = [Guarded(M, n, torch.float32 if f32 else torch.bfloat16,
+                    ld=n + ld_pad) for n in splits]
+    frt.frt_packed_gemm_fp8_split(
+        dev_u8(x8), dev_u8(w8), scalar(s_a), scalar(s_w),
+        [o.view for o in outs], splits,
+        bias_cat=None if bias is None else dev_bf16(bias), M=M)
+    torch.cuda.synchronize()
+    for o in outs:
+        o.check_guards()
+    res = []
+    for o in outs:
+        if f32:
+            res.append(o.view.cpu().numpy())
+        else:
+            res.append(host_bf16(o.view))
+    return res
+
+
+def _check_gemm(x8, w8, s_a, s_w, bias, splits, what, ld_pad=0):
+    ref = gemm.packed_gemm_split(x8, w8, s_a, s_w, bias, splits)
+    got32 = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=True, ld_pad=ld_pad)
+    got16 = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
+    scale = max(np.max(np.abs(x)) for x in ref)
+    worst = 0.0
+    for i, (r, g32, g16) in enumerate(zip(ref, got32, got16)):
+        err = np.max(np.abs(g32.astype(np.float64) - r))
+        assert err <= 1e-3 * scale, f"{what} split {i}: {err:.3e}"
+        worst = max(worst, err / scale)
+        assert_gemm_bf16(g16, r, f"{what} split {i}")
+    print(f"{what}: fp32 max|d|/max|ref| = {worst:.2e}")
+    return ref
+
+
+def _operands(cid, site, M=None, seed=0):
+    if cid == 5:
+        # the widest workload's weights are exercised by the pack tests; the
+        # GEMM takes random codes of the same shape (identical operands)
+        wk = wl.WORKLOADS[5]
+        w8 = wl.random_codes(4100, (sum(wk.gemms[0]), wk.D))
+        M = wk.rows if M is None else M
+        x8 = wl.random_codes(4005 + seed, (M, wk.D))
+        return x8, w8, np.float32(0.01), np.float32(0.004), None, list(wk.gemms[0])
+    w = wl.weights(cid, site)
+    w8, s_w, bias, splits = pack.pack_weights(w["W"], w["b"])
+    K = w8.shape[1]
+    M = wl.WORKLOADS[cid].rows if M is None else M
+    x8 = wl.random_codes(4000 + cid + seed, (M, K))
+    # a realistic activation code spread: mostly small magnitudes
+    return x8, w8, np.float32(0.01), s_w, (bias if w["b"][0] is not None else None), splits
+
+
+@pytest.mark.parametrize("cid,site,M", [(1, 0, 16), (2, 0, 256), (2, 1, 256),
+                                        (3, 0, 600), (4, 0, 64), (4, 0, 1),
+                                        (4, 0, 17), (5, 0, 40)])
+def test_gemm_workload(cid, site, M):
+    x8, w8, s_a, s_w, bias, splits = _operands(cid, site, M)
+    _check_gemm(x8, w8, s_a, s_w, bias, splits, f"workload {cid}/{site} M={M}")
+
+
+@pytest.mark.parametrize("cid", [3, 5])
+def test_gemm_full_size_sampled(cid):
+    """Full workload size in the bench's launch (bf16 out); sampled outputs
+    computed one by one by the oracle."""
+    x8, w8, s_a, s_w, bias, splits = _operands(cid, 0)
+    M, N = x8.shape[0], w8.shape[0]
+    outs = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
+    full = np.concatenate(outs, axis=1)
+    rng = np.random.default_rng(cid)
+    rows = np.concatenate([rng.integers(0, M, 2000), [M - 1, 0]])
+    cols = np.concatenate([rng.integers(0, N, 2000), [N - 1, N - 1]])
+    acc = gemm.gemm_exact_at(x8, w8, rows, cols)
+    ref = gemm.epilogue(acc, s_a, s_w, None if bias is None else bias[cols])
+    # the whole output's scale bounds the accumulation error term
+    assert_gemm_bf16(full[rows, cols], ref, f"workload {cid} sampled")
+
+
+def test_gemm_edges_k_tail_strides_unaligned_splits():
+    rng = np.random.default_rng(9)
+    for (M, K, splits) in [(33, 528, (100, 28, 200)), (257, 1040, (96, 160)),
+                           (5, 4096, (1, 2, 3, 122)), (300, 512, (40,) * 16)]:
+        N = sum(splits)
+        w8 = wl.random_codes(int(rng.integers(1 << 30)), (N, K))
+        x8 = wl.random_codes(int(rng.integers(1 << 30)), (M, K))
+        bias = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+        _check_gemm(x8, w8, np.float32(0.003), np.float32(0.002), bias,
+                    list(splits), f"M={M} K={K}", ld_pad=6)
+
+
+def test_gemm_joint_slots_share_one_buffer():
+    """Two adjacent splits written into one [M, N0 + N1] region through
+    offset pointers with a shared row stride (a joint q|k consumer)."""
+    x8, w8, s_a, s_w, bias, splits = _operands(1, 0)
+    M = x8.shape[0]
+    ref = np.concatenate(gemm.packed_gemm_split(x8, w8, s_a, s_w, bias, splits), 1)
+    buf = torch.zeros(M, 640, dtype=torch.bfloat16, device="cuda")
+    v = torch.zeros(M, 128, dtype=torch.bfloat16, device="cuda")
+    frt.frt_packed_gemm_fp8_split(dev_u8(x8), dev_u8(w8), scalar(s_a),
+                                  scalar(s_w), [buf[:, :512], buf[:, 512:], v],
+                                  splits, bias_cat=None)
+    torch.cuda.synchronize()
+    got = np.concatenate([host_bf16(buf), host_bf16(v)], 1)
+    assert_gemm_bf16(got, ref, "joint slots")
+
+
+def test_gemm_row_capacity_writes_only_m_rows():
+    x8, w8, s_a, s_w, bias, splits = _operands(4, 0, 64)
+    out = [torch.full((64, n), 1.5, dtype=torch.bfloat16, device="cuda")
+           for n in splits]
+    frt.frt_packed_gemm_fp8_split(dev_u8(x8), dev_u8(w8), scalar(s_a),
+                                  scalar(s_w), out, splits, M=10)
+    torch.cuda.synchronize()
+    for o in out:
+        assert (o[10:].float() == 1.5).all()
