@@ -1,0 +1,423 @@
+"""Benchmark of the norm-quantize -> packed FP8 GEMM hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1..5]
+
+A step is one pass of the whole path over one batch: every producer site of
+the workload (gated-residual AdaRMS or per-token-table LayerNorm, static FP8
+out) followed by its packed sibling GEMM (dequant + bias + column split,
+bf16 out). The default workload is the AdaRMS decoder layer (256 tokens,
+D = 2048; QKV 2048|256|256 from site 1, gate|up 8192|8192 from site 2).
+
+Timing. Inputs and packed weights are resident in HBM before the timed
+region. Steps are captured into HIP graphs (the per-call host cost of the
+Python binding is larger than a step's GPU time) and replayed; the timed
+region is bracketed by device synchronisation. Each step reads a different
+copy of the weights and activations, rotating through enough copies that the
+working set is at least 512 MiB, so the 256 MiB Infinity Cache cannot serve
+repeated weight streams. Per-kernel durations come from HIP events around
+graph replays of that kernel alone on the launch stream (same rotation).
+
+Output: one JSON line on stdout (metric, value, roofline of the dominant
+kernel, the CPU oracle's throughput on a bounded sample, per-kernel table).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0       # dense FP8 MFMA (datasheet 5.0 PFLOP/s)
+RIDGE = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+ROTATE_BYTES = 512 << 20
+METRIC = "packed FP8 GEMM TFLOP/s (%MFMA peak) + norm-quant GB/s (%HBM peak)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--rows", type=int, default=None,
+                   help="override the producer row count (e.g. the small-M sweep)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--kernel-reps", type=int, default=20)
+    return p.parse_args()
+
+
+# ------------------------------------------------------------------ setup
+
+def bf16_dev(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+class Step:
+    """Device buffers of one rotation set and the launches of one step."""
+
+
+def build_sets(wid, rows, frt, torch):
+    import workloads as wl
+    w = wl.WORKLOADS[wid]
+    inp = wl.producer_inputs(wid, rows=rows)
+    cal = wl.producer_inputs(wid, calib=True, rows=rows)
+    D = w.D
+    R = inp["rows"]
+    dev = {}
+    if w.form == "adarms":
+        dev["res"] = bf16_dev(inp["residual"])
+        dev["x"] = bf16_dev(inp["x"])
+        dev["gate"] = bf16_dev(inp["gate"])
+        dev["mod"] = bf16_dev(inp["mod"])
+        if w.sites == 2:
+            dev["x2"] = bf16_dev(inp["x2"])
+            dev["mod2"] = bf16_dev(inp["mod2"])
+    else:
+        dev["x"] = bf16_dev(inp["x"])
+        dev["temb"] = bf16_dev(inp["temb"].reshape(R, -1))
+        dev["table"] = torch.from_numpy(inp["table"]).cuda()
+
+    # ---- calibration on the GPU: amax of each site's producer output on
+    # the calibration batch (the GEMM input), scale = amax / 448
+    scales = []
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    if w.form == "adarms":
+        cres = bf16_dev(cal["residual"])
+        cx = bf16_dev(cal["x"])
+        cg = bf16_dev(cal["gate"])
+        cm = bf16_dev(cal["mod"])
+        rout = torch.empty_like(cres)
+        frt.frt_ada_norm_quant_fp8(cres, cm, None, x=cx, gate=cg, eps=wl.EPS,
+                                   residual_out=rout, amax_out=amax)
+        torch.cuda.synchronize()
+        scales.append(np.float32(amax.item()) / np.float32(448.0))
+        if w.sites == 2:
+            amax.zero_()
+            cm2 = bf16_dev(cal["mod2"])
+            cx2 = bf16_dev(cal["x2"])
+            frt.frt_ada_norm_quant_fp8(rout, cm2, None, x=cx2,
+                                       gate=cm[0, 2 * D:3 * D], eps=wl.EPS,
+                                       amax_out=amax)
+            torch.cuda.synchronize()
+            scales.append(np.float32(amax.item()) / np.float32(448.0))
+    else:
+        frt.frt_ptok_table_norm_quant_fp8(
+            bf16_dev(cal["x"]), bf16_dev(cal["temb"].reshape(R, -1)),
+            torch.from_numpy(cal["table"]).cuda(), None, cal["shift_idx"],
+            cal["scale_idx"], eps=wl.EPS, amax_out=amax)
+        torch.cuda.synchronize()
+        scales.append(np.float32(amax.item()) / np.float32(448.0))
+    act = [torch.tensor([float(s)], dtype=torch.float32, device="cuda") for s in scales]
+
+    # ---- bind: pack every GEMM's siblings on the GPU (timed separately)
+    packs = []
+    pack_ms = []
+    for site in range(len(w.gemms)):
+        ww = wl.weights(wid, site)
+        Ws = [bf16_dev(x) for x in ww["W"]]
+        bs = [None if b is None else bf16_dev(b) for b in ww["b"]]
+        N = sum(ww["splits"])
+        W8 = torch.empty(N, D, dtype=torch.uint8, device="cuda")
+        wsc = torch.empty(1, dtype=torch.float32, device="cuda")
+        bc = torch.empty(N, dtype=torch.bfloat16, device="cuda") if w.bias else None
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        frt.frt_pack_weights_fp8(Ws, bs if w.bias else None, W8, wsc, bc)
+        e1.record()
+        torch.cuda.synchronize()
+        pack_ms.append(e0.elapsed_time(e1))
+        packs.append({"W8": W8, "ws": wsc, "bias": bc, "splits": list(ww["splits"])})
+        del Ws, bs
+    return w, dev, act, packs, pack_ms
+
+
+def make_rotation(w, dev, packs, rows, torch):
+    """Copies of activations and weights so one pass over the sets moves at
+    least ROTATE_BYTES."""
+    per = sum(t.numel() * t.element_size() for t in dev.values()
+              if t.dim() > 1 and t.shape[0] == rows)
+    per += sum(p["W8"].numel() for p in packs)
+    n = max(1, math.ceil(ROTATE_BYTES / max(per, 1)))
+    sets = []
+    for i in range(n):
+        s = {"dev": {}, "packs": []}
+        for k, t in dev.items():
+            rotate = t.dim() > 1 and t.shape[0] == rows
+            s["dev"][k] = t.clone() if (rotate and i > 0) else t
+        for p in packs:
+            q = dict(p)
+            if i > 0:
+                q["W8"] = p["W8"].clone()
+            s["packs"].append(q)
+        sets.append(s)
+    return sets, per
+
+
+def make_outputs(w, rows, packs, torch):
+    D = w.D
+    o = {"x8": [torch.empty(rows, D, dtype=torch.uint8, device="cuda")
+                for _ in packs]}
+    o["rout"] = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
+    o["rout2"] = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
+    o["gemm"] = [[torch.empty(rows, n, dtype=torch.bfloat16, device="cuda")
+                  for n in p["splits"]] for p in packs]
+    return o
+
+
+def step_launches(w, s, act, outs, rows, frt, eps):
+    """The step's launches for rotation set `s`: list of (kind, callable)."""
+    d = s["dev"]
+    D = w.D
+    L = []
+    if w.form == "adarms":
+        L.append(("norm1", lambda: frt.frt_ada_norm_quant_fp8(
+            d["res"], d["mod"], act[0], x=d["x"], gate=d["gate"], eps=eps,
+            residual_out=outs["rout"], out_fp8=outs["x8"][0])))
+    else:
+        L.append(("norm1", lambda: frt.frt_ptok_table_norm_quant_fp8(
+            d["x"], d["temb"], d["table"], act[0], w.shift_idx, w.scale_idx,
+            eps=eps, out_fp8=outs["x8"][0])))
+    p0 = s["packs"][0]
+    L.append(("gemm1", lambda: frt.frt_packed_gemm_fp8_split(
+        outs["x8"][0], p0["W8"], act[0], p0["ws"], outs["gemm"][0],
+        p0["splits"], bias_cat=p0["bias"])))
+    if len(s["packs"]) > 1:
+        p1 = s["packs"][1]
+        L.append(("norm2", lambda: frt.frt_ada_norm_quant_fp8(
+            outs["rout"], d["mod2"], act[1], x=d["x2"],
+            gate=d["mod"][0, 2 * D:3 * D], eps=eps, residual_out=outs["rout2"],
+            out_fp8=outs["x8"][1])))
+        L.append(("gemm2", lambda: frt.frt_packed_gemm_fp8_split(
+            outs["x8"][1], p1["W8"], act[1], p1["ws"], outs["gemm"][1],
+            p1["splits"], bias_cat=p1["bias"])))
+    return L
+
+
+def kernel_work(w, kind, rows, packs):
+    """Algorithmic bytes and FLOPs of one launch."""
+    D = w.D
+    if kind.startswith("norm"):
+        if w.form == "adarms":
+            gate = rows * D * 2 if (w.cid == 4 and kind == "norm1") else D * 2
+            if kind == "norm2":
+                gate = D * 2
+            b = rows * D * 2 * 3 + gate + 3 * D * 2 + rows * D   # res, x, rout; codes
+        else:
+            b = rows * D * 2 + rows * D * 4 + 2 * D * 4 + rows * D
+        return b, 0.0
+    p = packs[0 if kind == "gemm1" else 1]
+    N = sum(p["splits"])
+    b = rows * D + N * D + rows * N * 2 + (N * 2 if p["bias"] is not None else 0)
+    return b, 2.0 * rows * N * D
+
+
+# ------------------------------------------------------------------ timing
+
+def capture(fn_list, torch):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for fn in fn_list:
+            fn()
+    return g
+
+
+def time_graph(g, reps, torch):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline(w, rows, budget_s=20.0):
+    """The oracle as it stands on the host cores: the same step (producers
+    and exact GEMMs) on the same seeded inputs, repeated within a budget."""
+    import workloads as wl
+    from oracle import gemm, pack, producers
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [i.get("num_threads", 0) for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+        cores = max(blas) if blas else len(os.sched_getaffinity(0))
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    # a row sample bounded so that one pass stays within a few seconds
+    sample = rows if w.form == "adarms" and rows <= 256 else min(rows, 64)
+    inp = wl.producer_inputs(w.cid, rows=sample) if w.cid != 4 else \
+        wl.producer_inputs(w.cid, rows=min(sample, 64))
+    sample = inp["rows"]
+    # the GEMMs run on a sample of output rows of W when the whole packed
+    # matrix is too large for the host pass (FLOPs are counted on the sample)
+    packed = []
+    n_cols = 0
+    for site in range(len(w.gemms)):
+        ww = wl.weights(w.cid, site)
+        tot = sum(ww["splits"])
+        frac = min(1.0, 8192.0 / tot) if tot * w.D > (1 << 26) else 1.0
+        Ws = [x[:max(1, int(x.shape[0] * frac))] for x in ww["W"]]
+        bs = [None if b is None else b[:max(1, int(b.shape[0] * frac))] for b in ww["b"]]
+        packed.append(pack.pack_weights(Ws, bs))
+        n_cols += sum(x.shape[0] for x in Ws)
+    per_row_flops = 2.0 * n_cols * w.D
+    s_a = np.float32(0.01)
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while time.perf_counter() < t_end or not times:
+        t0 = time.perf_counter()
+        if w.form == "adarms":
+            r = producers.ada_norm_quant_fp8(inp["residual"], inp["x"], inp["gate"],
+                                             inp["mod"], s_a, wl.EPS)
+            codes = [r["codes"]]
+            if w.sites == 2:
+                D = w.D
+                r2 = producers.ada_norm_quant_fp8(r["residual_out"], inp["x2"],
+                                                  inp["mod"][0, 2 * D:3 * D],
+                                                  inp["mod2"], s_a, wl.EPS)
+                codes.append(r2["codes"])
+        else:
+            r = producers.ptok_norm_quant_fp8(inp["x"], inp["temb"], inp["table"],
+                                              s_a, w.shift_idx, w.scale_idx, wl.EPS)
+            codes = [r["codes"]]
+        for c, (w8, s_w, bias, splits) in zip(codes, packed):
+            gemm.packed_gemm_split(c, w8, s_a, s_w, bias if w.bias else None, splits)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 3 and time.perf_counter() > t_end - budget_s / 2:
+            break
+    t = float(np.median(times))
+    flops = per_row_flops * sample
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"workload {w.cid} step on {sample} of {rows} rows and "
+                      f"{n_cols} of {sum(sum(g) for g in w.gemms)} GEMM output "
+                      f"columns (producers + exact fp64 GEMMs), median of "
+                      f"{len(times)} runs, {t:.2f} s each"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not "
+              "supported (the path shards by rows/heads with no exchange; see "
+              "DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import norm_quantize_packed_amd as frt
+    import workloads as wl
+
+    torch.cuda.init()
+    frt.load_library()
+    w0 = wl.WORKLOADS[a.workload]
+    rows = a.rows if a.rows is not None else w0.rows
+    w, dev, act, packs, pack_ms = build_sets(a.workload, rows, frt, torch)
+    sets, per_set = make_rotation(w, dev, packs, rows, torch)
+    outs = make_outputs(w, rows, packs, torch)
+    nset = len(sets)
+
+    # eager reference of one step, then graph replays must reproduce it
+    steps_fns = [step_launches(w, s, act, outs, rows, frt, wl.EPS) for s in sets]
+    for _, fn in steps_fns[0]:
+        fn()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs["gemm"][-1]]
+    chunk = capture([fn for st in steps_fns for _, fn in st], torch)
+    singles = [capture([fn for _, fn in st], torch) for st in steps_fns]
+    for _ in range(3):
+        chunk.replay()
+        torch.cuda.synchronize()
+        singles[0].replay()
+        torch.cuda.synchronize()
+        for r, t in zip(ref, outs["gemm"][-1]):
+            if not torch.equal(r, t):
+                raise RuntimeError("graph replay differs from the eager step")
+
+    # warmup + timed steps (exactly a.steps steps)
+    def run_steps(k):
+        full, rem = divmod(k, nset)
+        for _ in range(full):
+            chunk.replay()
+        for i in range(rem):
+            singles[i].replay()
+
+    run_steps(a.warmup)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    run_steps(a.steps)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / a.steps
+
+    # per-kernel durations: graphs of one kernel kind over all sets
+    kinds = [k for k, _ in steps_fns[0]]
+    table = []
+    for ki, kind in enumerate(kinds):
+        g = capture([steps_fns[s][ki][1] for s in range(nset)], torch)
+        g.replay()
+        us = time_graph(g, a.kernel_reps, torch) * 1e3 / nset
+        b, f = kernel_work(w, kind, rows, packs)
+        row = {"kernel": kind, "us": round(us, 3), "bytes": int(b),
+               "GB/s": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+        if f:
+            row["TFLOP/s"] = round(f / us / 1e6, 2)
+            row["mfma_frac"] = round(f / us / 1e6 / FP8_PEAK_TFLOPS, 4)
+            row["bound"] = "mfma" if f / b > RIDGE else "hbm"
+        else:
+            row["bound"] = "hbm"
+        table.append(row)
+        del g
+
+    gemm_flops = sum(kernel_work(w, k, rows, packs)[1] for k in kinds)
+    norm_bytes = sum(kernel_work(w, k, rows, packs)[0] for k in kinds if k.startswith("norm"))
+    norm_us = sum(r["us"] for r in table if r["kernel"].startswith("norm"))
+    dom = max(table, key=lambda r: r["us"])
+    if dom["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": dom["TFLOP/s"], "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": dom["mfma_frac"], "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": dom["hbm_frac"], "traffic": None}
+    roof["kernel"] = dom["kernel"]
+
+    value = gemm_flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": rows, "D": w.D,
+                   "gemms": [list(g) for g in w.gemms], "bias": w.bias,
+                   "rotation_sets": nset, "rotation_mib": round(nset * per_set / 2**20, 1),
+                   "step_gemm_gflop": round(gemm_flops / 1e9, 3)},
+        "norm_gbps": round(norm_bytes / (norm_us * 1e3), 1) if norm_us else None,
+        "norm_hbm_frac": round(norm_bytes / (norm_us * 1e3) / HBM_PEAK_GBS, 4) if norm_us else None,
+        "roofline": roof,
+        "kernels": table,
+        "pack_ms": [round(x, 3) for x in pack_ms],
+        "wall_s_timed": round(wall, 4),
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
