@@ -53,6 +53,9 @@ def parse():
                    help="override the producer row count (e.g. the small-M sweep)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-reps", type=int, default=20)
+    p.add_argument("--prewarm-s", type=float, default=2.0,
+                   help="seconds of untimed replays before the warmup steps "
+                        "(engine clocks ramp up from idle over ~1 s)")
     return p.parse_args()
 
 
@@ -233,6 +236,18 @@ def capture(fn_list, torch):
     return g
 
 
+def prewarm(g, seconds, torch):
+    """Replay `g` until `seconds` of wall time have passed (clock ramp)."""
+    t_end = time.perf_counter() + seconds
+    n = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            g.replay()
+        torch.cuda.synchronize()
+        n += 8
+    return n
+
+
 def time_graph(g, reps, torch):
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -353,6 +368,7 @@ def main():
         for i in range(rem):
             singles[i].replay()
 
+    prewarm(chunk, a.prewarm_s, torch)
     run_steps(a.warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -370,7 +386,7 @@ def main():
     table = []
     for ki, kind in enumerate(kinds):
         g = capture([steps_fns[s][ki][1] for s in range(nset)], torch)
-        g.replay()
+        prewarm(g, 0.3, torch)
         us = time_graph(g, a.kernel_reps, torch) * 1e3 / nset
         b, f = kernel_work(w, kind, rows, packs)
         row = {"kernel": kind, "us": round(us, 3), "bytes": int(b),
@@ -412,6 +428,7 @@ def main():
         "roofline": roof,
         "kernels": table,
         "pack_ms": [round(x, 3) for x in pack_ms],
+        "prewarm_s": a.prewarm_s,
         "wall_s_timed": round(wall, 4),
     }
     if not a.no_cpu_baseline:

@@ -20,7 +20,7 @@ SOURCES = ["frt_api.hip", "frt_norm.hip", "frt_pack.hip", "frt_gemm.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+    "-O3", "-std=c++20", "-fPIC", f"--offload-arch={ARCH}",
     # no packed-FP32 VALU instructions (v_pk_*_f32) in any kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",

@@ -27,6 +27,9 @@
 // the logical tile index gives each XCD a contiguous run of tiles, and runs
 // are rastered in groups of GM tile-rows so that the tiles resident on one
 // XCD share A and B panels in that XCD's L2.
+#include <cstdlib>
+#include <type_traits>
+
 #include "frt_device.h"
 #include "frt_internal.h"
 
@@ -37,6 +40,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr uint32_t kOOB = 0x80000000u;  // offset past any record count
@@ -71,9 +75,26 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 
 }  // namespace
 
+// vmcnt(n) together with lgkmcnt(0) (expcnt left at its maximum)
+__device__ __forceinline__ constexpr int vm_lgkm0_imm(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4);
+}
+
 // BM x BN block tile, WM x WN per wave, 64-deep K steps, NSTAGE-deep LDS
-// ring.
-template <int BM, int BN, int WM, int WN, int NSTAGE, int GM>
+// ring (NSTAGE - 1 K steps in flight).
+//
+// Per K step kt a wave: issues the global->LDS loads of step kt+NSTAGE-1
+// (into the slot step kt-1 used), runs the first MFMAs of step kt on
+// fragments already in registers, waits until step kt+1's loads have
+// landed (its own: vmcnt; everyone's: one s_barrier), then reads step
+// kt+1's fragments into the other register set while the remaining MFMAs
+// of step kt run. One barrier per K step; the slot being refilled was last
+// read two barriers earlier.
+//
+// PP = false (no fragment ping-pong): the wave waits for step kt itself,
+// passes the barrier, refills the slot step kt-1 used, then reads step kt's
+// fragments and runs its MFMAs; half the fragment registers.
+template <int BM, int BN, int WM, int WN, int NSTAGE, int GM, bool PP, bool KTAIL>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(GemmArgs a) {
   constexpr int WAVES_N = BN / WN;
   constexpr int NW = (BM / WM) * WAVES_N;
@@ -82,8 +103,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
   constexpr int B_HF = (BN / 32) * 2;
   constexpr int HF = A_HF + B_HF;
   static_assert(HF % NW == 0, "loads must split evenly over the waves");
+  static_assert(NSTAGE >= 2, "at least double buffering");
   constexpr int LPW = HF / NW;  // load instructions per wave per stage
   constexpr int STAGE = HF * 1024;
+  constexpr int PRE = MI * NJ >= 8 ? 4 : (MI * NJ >= 4 ? 2 : 1);  // MFMAs before the barrier
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSTAGE * STAGE];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -100,9 +123,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, w_bytes);
 
   // per-lane source offsets of this wave's LPW half-fragments, K step 0
+  // (K byte within the step: h * 32 + (lane / 32) * 16, h = f & 1)
   uint32_t off[LPW];
-  bool isA[LPW];
-  int kin[LPW];
+  const int kl = (lane >> 5) * 16;
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
     const int f = wave + j * NW;
@@ -110,25 +133,61 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
     const int g = A ? f : f - A_HF;
     const int sub = g >> 1, h = g & 1;
     const int r = (A ? m0 : n0) + sub * 32 + (lane & 31);
-    const int kb = h * 32 + (lane >> 5) * 16;
     const bool ok = r < (A ? a.M : a.N);
-    isA[j] = A;
-    kin[j] = kb;
-    off[j] = ok ? (uint32_t)(A ? (int64_t)r * a.ld_x : (int64_t)r * a.K) + kb : kOOB;
+    off[j] = ok ? (uint32_t)(A ? (int64_t)r * a.ld_x : (int64_t)r * a.K) + h * 32 + kl : kOOB;
   }
 
-  auto issue = [&](int kt, int stage) {
+  const int KT = (a.K + 63) / 64;
+  auto issue = [&](int kt) {
     const int k0 = kt * 64;
+    uint8_t* sbase = smem + (kt % NSTAGE) * STAGE;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      const int f = wave + j * NW;
-      uint8_t* dst = smem + stage * STAGE + f * 1024;
-      const uint32_t o = (off[j] == kOOB || k0 + kin[j] >= a.K) ? kOOB : off[j] + k0;
-      if (isA[j])
+      const int f = wave + j * NW;  // f < A_HF is uniform per (wave, j)
+      uint8_t* dst = sbase + f * 1024;
+      uint32_t o = off[j] + k0;  // kOOB + k0 stays past every record count
+      if constexpr (KTAIL) {
+        if (k0 + (f & 1) * 32 + kl >= a.K) o = kOOB;
+      }
+      if (f < A_HF)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
     }
+  };
+  auto read_frags = [&](int kt, v8i* af, v8i* bf) {
+    const uint8_t* sb = smem + (kt % NSTAGE) * STAGE;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int sub = (wn0 >> 5) + j;
+      const v4i lo = *reinterpret_cast<const v4i*>(sb + (A_HF + 2 * sub) * 1024 + lane * 16);
+      const v4i hi = *reinterpret_cast<const v4i*>(sb + (A_HF + 2 * sub + 1) * 1024 + lane * 16);
+      bf[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int sub = (wm0 >> 5) + i;
+      const v4i lo = *reinterpret_cast<const v4i*>(sb + (2 * sub) * 1024 + lane * 16);
+      const v4i hi = *reinterpret_cast<const v4i*>(sb + (2 * sub + 1) * 1024 + lane * 16);
+      af[i] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  // wait (own loads) until at most `ahead` later stages are in flight, and
+  // for every LDS read; then the block barrier
+  auto sync_stage = [&](int ahead) {
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NSTAGE >= 4) {
+      if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(2 * LPW));
+      else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW));
+      else __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+    } else if constexpr (NSTAGE == 3) {
+      if (ahead >= 1) __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW));
+      else __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   v16f acc[MI][NJ];
@@ -139,44 +198,54 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int KT = (a.K + 63) / 64;
+  // prologue: NSTAGE-1 steps in flight
 #pragma unroll
   for (int s = 0; s < NSTAGE - 1; ++s)
-    if (s < KT) issue(s, s);
+    if (s < KT) issue(s);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int pre = kt + NSTAGE - 1;
-    if (pre < KT) issue(pre, pre % NSTAGE);
-    // wait until this K step's loads have landed (later steps may fly)
-    const int ahead = min(KT - 1 - kt, NSTAGE - 1);
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPW));
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPW));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-
-    const uint8_t* sb = smem + (kt % NSTAGE) * STAGE;
-    v8i af[MI], bf[NJ];
+  if constexpr (!PP) {
+    v8i fa[MI], fb[NJ];
+    for (int kt = 0; kt < KT; ++kt) {
+      // step kt landed (later steps may fly); everyone is past step kt-1
+      sync_stage(min(KT - 1 - kt, NSTAGE - 2));
+      if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
+      read_frags(kt, fa, fb);
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int sub = (wm0 >> 5) + i;
-      const v4i lo = *reinterpret_cast<const v4i*>(sb + (2 * sub) * 1024 + lane * 16);
-      const v4i hi = *reinterpret_cast<const v4i*>(sb + (2 * sub + 1) * 1024 + lane * 16);
-      af[i] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+  } else {
+  // step 0 landed and read
+  sync_stage(min(KT - 1, NSTAGE - 2));
+  v8i fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
+  read_frags(0, fa0, fb0);
+
+  auto kstep = [&](int kt, v8i* ca, v8i* cb, v8i* na, v8i* nb) {
+    if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
+    // first MFMAs of step kt (their fragments are already in registers)
+#pragma unroll
+    for (int q = 0; q < PRE; ++q) {
+      const int i = q / NJ, j = q % NJ;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ca[i], cb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+    if (kt + 1 < KT) {
+      // stages still allowed in flight beyond kt+1
+      sync_stage(min(KT - 2 - kt, NSTAGE - 2));
+      read_frags(kt + 1, na, nb);
     }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int sub = (wn0 >> 5) + j;
-      const v4i lo = *reinterpret_cast<const v4i*>(sb + (A_HF + 2 * sub) * 1024 + lane * 16);
-      const v4i hi = *reinterpret_cast<const v4i*>(sb + (A_HF + 2 * sub + 1) * 1024 + lane * 16);
-      bf[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    for (int q = PRE; q < MI * NJ; ++q) {
+      const int i = q / NJ, j = q % NJ;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ca[i], cb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, 0,
-                                                                    0, 0);
-    __syncthreads();  // every wave is done with this stage before refill
+  };
+
+  for (int kt = 0; kt < KT; kt += 2) {
+    kstep(kt, fa0, fb0, fa1, fb1);
+    if (kt + 1 < KT) kstep(kt + 1, fa1, fb1, fa0, fb0);
+  }
   }
 
   // ---- epilogue: alpha * acc + bias, column split, bf16 (or fp32) ----
@@ -216,31 +285,518 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel: 128-deep K stages staged as full 128-byte row segments.
+//
+// LDS holds each stage row-major, one 128-byte row segment per tile row, with
+// the eight 16-byte chunks of row r stored at chunk position
+// c ^ ((r >> 1) & 7) (an XOR swizzle). A direct buffer->LDS load
+// instruction of a wave therefore covers 8 rows x 128 contiguous bytes (whole
+// cache lines, 8 requests per KiB instead of 32), and each lane's destination
+// stays lane-contiguous as the instruction requires: lane L writes chunk
+// position L % 8 of row L / 8, so it fetches global chunk
+// (L % 8) ^ ((row >> 1) & 7). A 32x32x64 operand read (row l % 32, K bytes
+// [s*64 + (l/32)*32, +32)) takes chunks c0 = s*4 + (l/32)*2 and c0 + 1,
+// i.e. positions c0 ^ ((l >> 1) & 7) and that ^ 1. The LDS serves a
+// ds_read_b128 sixteen lanes (256 bytes, all 64 banks) at a time: sixteen
+// consecutive rows fall in two 128-byte halves by row parity and on eight
+// distinct positions within each half, so the reads are conflict free.
+//
+// Two stages (BK = 128 each), one barrier per stage, after which the freed
+// stage is refilled. Eight waves (two per SIMD): while one wave waits for
+// its fragment reads the other wave's MFMAs keep the matrix core busy, so
+// a wave holds a single fragment set (no spills at 2 waves per SIMD).
+template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(GemmArgs a) {
+  constexpr int WAVES_N = BN / WN;
+  constexpr int NW = (BM / WM) * WAVES_N;
+  constexpr int MI = WM / 32, NJ = WN / 32;
+  constexpr int ROWS = BM + BN;
+  constexpr int LOADS = ROWS / 8;  // 1 KiB load instructions per stage
+  static_assert(LOADS % NW == 0, "loads must split evenly over the waves");
+  constexpr int LPW = LOADS / NW;
+  constexpr int STAGE = ROWS * 128;
+  static_assert(NS >= 2 && LPW * (NS - 2) <= 63, "ring depth vs vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const TileXY t = tile_of(blockIdx.x, tiles_m, tiles_n, GM);
+  const int m0 = t.tm * BM, n0 = t.tn * BN;
+  const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
+
+  const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + a.K);
+  const uint32_t w_bytes = (uint32_t)((int64_t)a.N * a.K);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, w_bytes);
+
+  // this wave's load instructions: tile rows [8u, 8u + 8), u = wave + j*NW.
+  // One base offset per operand; instruction j adds a uniform multiple of
+  // the row stride. A row past M (N) lands past the buffer's record count
+  // ((M-1)*ld_x + K, resp. N*K, with ld_x >= K), which the hardware turns
+  // into a zero fill, so no per-load bound registers are kept.
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "A and B loads split evenly");
+  constexpr int LPA = BM / (8 * NW);  // the first LPA loads of a wave are A rows
+  const int lrow = lane >> 3;
+  // global chunk this lane fetches: rows 8u + lrow with u = wave + j*NW and
+  // NW even, so (row >> 1) & 7 = ((wave & 1) << 2) | (lrow >> 1) for every j
+  static_assert(NW % 2 == 0, "row swizzle assumes an even wave count");
+  const int cch = (lane & 7) ^ (((wave & 1) << 2) | (lrow >> 1));
+  const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
+  const uint32_t offB = (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
+  const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
+  const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)a.K;
+  const int KT = (a.K + 127) / 128;
+  // slot SL (= step parity) is a compile-time constant in every use, so all
+  // LDS addresses are one lane base plus immediates
+  auto issue = [&](int kt, auto SLC) {
+    constexpr int SL = decltype(SLC)::value;
+    const int k0 = kt * 128;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int u = wave + j * NW;
+      uint8_t* dst = smem + SL * STAGE + u * 1024;
+      const bool A = j < LPA;
+      uint32_t o = A ? offA + j * stepA + k0 : offB + (j - LPA) * stepB + k0;
+      if constexpr (KTAIL) {
+        if (k0 + cch * 16 >= a.K) o = kOOB;
+      }
+      if (A)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
+    }
+  };
+  // operand read of substep SUB from slot SL: two 16-byte chunks per lane
+  const int lrow32 = lane & 31;
+  const int sw = (lrow32 >> 1) & 7;  // (row >> 1) & 7 for rows 32k + lrow32
+  const uint8_t* lbase0 = smem + lrow32 * 128 + ((((lane >> 5) * 2) ^ sw) * 16);
+  const uint8_t* lbase1 = smem + lrow32 * 128 + ((((lane >> 5) * 2 + 4) ^ sw) * 16);
+  auto read_frags = [&](auto SLC, auto SUBC, v8i* af, v8i* bf) {
+    constexpr int SL = decltype(SLC)::value, SUB = decltype(SUBC)::value;
+    const uint8_t* lb = (SUB ? lbase1 : lbase0) + SL * STAGE;
+    // the second chunk sits at position ^ 1, i.e. +16 or -16 bytes
+    const int d1 = (sw & 1) ? -16 : 16;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint8_t* rowp = lb + (BM + wn0 + j * 32) * 128;
+      const v4i lo = *reinterpret_cast<const v4i*>(rowp);
+      const v4i hi = *reinterpret_cast<const v4i*>(rowp + d1);
+      bf[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const uint8_t* rowp = lb + (wm0 + i * 32) * 128;
+      const v4i lo = *reinterpret_cast<const v4i*>(rowp);
+      const v4i hi = *reinterpret_cast<const v4i*>(rowp + d1);
+      af[i] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  // own loads: at most `ahead` later stages still in flight; every LDS read
+  // done; then the block barrier
+  auto sync_stage = [&](int ahead) {
+    __builtin_amdgcn_sched_barrier(0);
+    switch (ahead) {
+      case 0: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS > 2 ? 1 : 0))); break;
+      case 2: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS > 3 ? 2 : 0))); break;
+      case 3: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS > 4 ? 3 : 0))); break;
+      case 4: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS > 5 ? 4 : 0))); break;
+      default: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS > 6 ? 5 : 0))); break;
+    }
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  v16f acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  v8i fa0[MI], fb0[NJ];
+  auto mfmas = [&](const v8i* fa, const v8i* fb) {
+#pragma unroll
+    for (int q = 0; q < MI * NJ; ++q) {
+      const int i = q / NJ, j = q % NJ;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+  };
+  // one 128-deep stage kt held in slot SL = kt % NS. The slot refilled
+  // first, (kt - 1) % NS, was last read before the previous barrier.
+  auto stage = [&](int kt, auto SLC) {
+    constexpr int SL = decltype(SLC)::value;
+    using PV = std::integral_constant<int, (SL + NS - 1) % NS>;
+    using NX = std::integral_constant<int, (SL + 1) % NS>;
+    if (kt + NS - 1 < KT) issue(kt + NS - 1, PV{});
+    mfmas(fa0, fb0);
+    read_frags(SLC, I1{}, fa0, fb0);
+    mfmas(fa0, fb0);
+    if (kt + 1 < KT) {
+      // step kt+1 landed everywhere (later ones may fly); step kt fully read
+      sync_stage(min(KT - 2 - kt, NS - 2));
+      read_frags(NX{}, I0{}, fa0, fb0);
+    }
+  };
+  auto ring = [&](int kt0, auto... SLs) {
+    int kt = kt0;
+    ((kt < KT ? (stage(kt, SLs), ++kt) : 0), ...);
+  };
+
+#pragma unroll
+  for (int s0 = 0; s0 < NS - 1; ++s0) {
+    if (s0 < KT) {
+      switch (s0) {
+        case 0: issue(s0, I0{}); break;
+        case 1: issue(s0, I1{}); break;
+        case 2: issue(s0, std::integral_constant<int, 2 % NS>{}); break;
+        case 3: issue(s0, std::integral_constant<int, 3 % NS>{}); break;
+        case 4: issue(s0, std::integral_constant<int, 4 % NS>{}); break;
+        default: issue(s0, std::integral_constant<int, 5 % NS>{}); break;
+      }
+    }
+  }
+  sync_stage(min(KT - 1, NS - 2));
+  read_frags(I0{}, I0{}, fa0, fb0);
+  for (int kt = 0; kt < KT; kt += NS) {
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      ring(kt, std::integral_constant<int, S>{}...);
+    }(std::make_integer_sequence<int, NS>{});
+  }
+
+  // ---- epilogue: alpha * acc + bias, column split, bf16 (or fp32) ----
+  const float alpha = (*a.act_scale) * (*a.w_scale);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn0 + j * 32 + (lane & 31);
+    if (n >= a.N) continue;
+    uint8_t* base = reinterpret_cast<uint8_t*>(a.sp.ptr[0]);
+    int64_t ld = a.sp.ld[0];
+    int off0 = 0;
+#pragma unroll
+    for (int s = 1; s < FRT_MAX_SPLITS; ++s) {
+      if (s < a.sp.n && n >= a.sp.off[s]) {
+        base = reinterpret_cast<uint8_t*>(a.sp.ptr[s]);
+        ld = a.sp.ld[s];
+        off0 = a.sp.off[s];
+      }
+    }
+    const float b = a.bias != nullptr ? bf16f(a.bias[n]) : 0.0f;
+    const int col = n - off0;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < a.M) {
+          const float v = alpha * acc[i][j][r] + b;
+          if (a.out_f32)
+            reinterpret_cast<float*>(base)[(int64_t)m * ld + col] = v;
+          else
+            reinterpret_cast<uint16_t*>(base)[(int64_t)m * ld + col] = (uint16_t)f2bf(v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Skinny kernel (M <= 64): weight streaming with split-K.
+//
+// A block owns 64 rows of W8 (16 per wave) and one K range of KS = 128*NCH
+// bytes (split s = blockIdx.y of S). Each wave loads its 16 W rows for the
+// whole K range straight into registers up front (NCH*2 loads of 16 bytes
+// per lane, all in flight at once); there is no barrier in the K loop. The
+// x rows (MG*16 rows, zero beyond M) of the K range are staged once in LDS
+// and read as MFMA operands; v_mfma_f32_16x16x128_f8f6f4 with A = 16 x rows,
+// B = 16 W rows, fp32 accumulate.
+//
+// Operand K order: within a 128-byte chunk, lane l (row l % 16, group
+// g = l / 16) holds bytes [g*16, +16) and [64 + g*16, +16), for W and x
+// alike; a W load instruction therefore reads 64 contiguous bytes of each
+// of 16 rows. x rows in LDS are KS bytes long with 16-byte chunk q of row r
+// stored at position q ^ (r & 15): the 16 rows a ds_read_b128 touches sit
+// on 16 distinct bank groups.
+//
+// With S > 1 every block writes its fp32 partial tile with device-coherent
+// (sc1) stores, waits for them, and bumps the tile's arrival counter (device
+// scope); the block that arrives last sums the S partials in split order
+// (the result does not depend on arrival order), applies the epilogue and
+// resets the counter to zero for the next call.
+template <int MG, int NCH, bool KTAIL>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int S) {
+  constexpr int KS = 128 * NCH;
+  constexpr int XR = MG * 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[XR * KS];
+  __shared__ int last_flag;
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tile = blockIdx.x;
+  const int split = blockIdx.y;
+  const int n0 = tile * 64 + wave * 16;
+  const int kb = split * KS;
+
+  // W: this wave's 16 rows, all chunks of the K range, into registers
+  const uint32_t w_bytes = (uint32_t)((int64_t)a.N * a.K);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, w_bytes);
+  const int r16 = lane & 15, g = lane >> 4;
+  const uint32_t wrow = (uint32_t)(n0 + r16) * (uint32_t)a.K;  // rows >= N read zeros
+  v4i wv[NCH][2];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = kb + c * 128 + h * 64 + g * 16;
+      uint32_t o = wrow + k;
+      if constexpr (KTAIL) {
+        if (k >= a.K) o = kOOB;
+      }
+      wv[c][h] = __builtin_amdgcn_raw_buffer_load_b128(wr, o, 0, 0);
+    }
+  }
+
+  // x: XR rows x KS bytes into LDS (direct loads; one row per KiB)
+  {
+    const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + a.K);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, x_bytes);
+    constexpr int LOADS = XR * KS / 1024;
+    constexpr int CPR = KS / 16;  // chunks per row
+#pragma unroll
+    for (int j = 0; j < (LOADS + 3) / 4; ++j) {
+      const int u = wave + j * 4;  // KiB index in the tile
+      if (LOADS % 4 == 0 || u < LOADS) {
+        const int t = u * 64 + lane;  // LDS chunk index
+        const int row = t / CPR, pos = t % CPR;
+        const int q = pos ^ (row & 15);
+        const int k = kb + q * 16;
+        uint32_t o = row < a.M ? (uint32_t)((int64_t)row * a.ld_x) + k : kOOB;
+        if constexpr (KTAIL) {
+          if (k >= a.K) o = kOOB;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xs + u * 1024), 16, o, 0, 0, 0);
+      }
+    }
+  }
+  // the x loads were issued after the W loads: vmcnt counts in order, so
+  // waiting for all of them also waits for W (needed soon anyway)
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+  __builtin_amdgcn_s_barrier();
+
+  v4f acc[MG];
+#pragma unroll
+  for (int m = 0; m < MG; ++m) acc[m] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    const v8i b = (v8i){wv[c][0][0], wv[c][0][1], wv[c][0][2], wv[c][0][3],
+                        wv[c][1][0], wv[c][1][1], wv[c][1][2], wv[c][1][3]};
+#pragma unroll
+    for (int m = 0; m < MG; ++m) {
+      const int row = m * 16 + r16;
+      const uint8_t* rp = xs + row * KS;
+      const int q0 = (c * 8 + g) ^ r16, q1 = (c * 8 + 4 + g) ^ r16;
+      const v4i lo = *reinterpret_cast<const v4i*>(rp + q0 * 16);
+      const v4i hi = *reinterpret_cast<const v4i*>(rp + q1 * 16);
+      const v8i av = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc[m] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, b, acc[m], 0, 0, 0, 0, 0, 0);
+    }
+  }
+
+  // C[m][n] layout of 16x16: lane holds n = n0 + (lane % 16), m = 4*(lane/16) + r
+  const int n = n0 + r16;
+  if (S > 1) {
+    float* ws = reinterpret_cast<float*>(a.ws);
+#pragma unroll
+    for (int m = 0; m < MG; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mm = m * 16 + g * 4 + r;
+        if (mm < a.M && n < a.N)
+          __hip_atomic_store(ws + ((int64_t)split * a.M + mm) * a.N + n, acc[m][r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+    __builtin_amdgcn_s_waitcnt(0);  // partial stores complete (device coherent)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned* cnt = a.cnt + tile;
+      const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = (prev == (unsigned)(S - 1));
+      if (last_flag) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last_flag) return;
+#pragma unroll
+    for (int m = 0; m < MG; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int mm = m * 16 + g * 4 + r;
+        float v = 0.0f;
+        if (mm < a.M && n < a.N) {
+          for (int z = 0; z < S; ++z)
+            v += __hip_atomic_load(ws + ((int64_t)z * a.M + mm) * a.N + n, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        acc[m][r] = v;
+      }
+  }
+
+  if (n >= a.N) return;
+  uint8_t* base = reinterpret_cast<uint8_t*>(a.sp.ptr[0]);
+  int64_t ld = a.sp.ld[0];
+  int off0 = 0;
+#pragma unroll
+  for (int s = 1; s < FRT_MAX_SPLITS; ++s) {
+    if (s < a.sp.n && n >= a.sp.off[s]) {
+      base = reinterpret_cast<uint8_t*>(a.sp.ptr[s]);
+      ld = a.sp.ld[s];
+      off0 = a.sp.off[s];
+    }
+  }
+  const float alpha = (*a.act_scale) * (*a.w_scale);
+  const float bias = a.bias != nullptr ? bf16f(a.bias[n]) : 0.0f;
+  const int col = n - off0;
+#pragma unroll
+  for (int m = 0; m < MG; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int mm = m * 16 + g * 4 + r;
+      if (mm < a.M) {
+        const float v = alpha * acc[m][r] + bias;
+        if (a.out_f32)
+          reinterpret_cast<float*>(base)[(int64_t)mm * ld + col] = v;
+        else
+          reinterpret_cast<uint16_t*>(base)[(int64_t)mm * ld + col] = (uint16_t)f2bf(v);
+      }
+    }
+}
+
 // ------------------------------------------------------------------ launch
 
+// ---- split-K plan of the skinny kernel and its workspace ----------------
+// Workspace = a fixed 64 KiB region of per-tile arrival counters (zero at
+// rest) followed by S fp32 partial planes [S][M][N].
+constexpr int64_t kCounterBytes = 64 * 1024;
+
+struct SkinnyPlan {
+  int mg, nch, splits, tiles;
+};
+
+SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K) {
+  SkinnyPlan p{};
+  p.mg = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  p.tiles = (int)((N + 63) / 64);
+  const int kt = (int)((K + 127) / 128);
+  p.nch = 8;
+  // more blocks when the N tiles alone cannot fill the chip
+  while (p.nch > 2 && (int64_t)p.tiles * ((kt + p.nch - 1) / p.nch) < 512) p.nch /= 2;
+  p.splits = (kt + p.nch - 1) / p.nch;
+  return p;
+}
+
+bool use_skinny(int64_t M, int64_t N) { return M <= 64 && (N + 63) / 64 <= kCounterBytes / 4; }
+
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  (void)M; (void)N; (void)K;
-  return 0;
+  return 0;  // the default plans need none (split-K skinny is opt-in)
+  if (!use_skinny(M, N)) return 0;
+  const SkinnyPlan p = skinny_plan(M, N, K);
+  if (p.splits <= 1) return 0;
+  return (size_t)(kCounterBytes + (int64_t)p.splits * M * N * 4);
 }
 
 namespace {
 
-template <int BM, int BN, int WM, int WN, int NSTAGE, int GM>
+template <int BM, int BN, int WM, int WN, int NSTAGE, int GM, bool PP>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t st) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WM, WN, NSTAGE, GM>), dim3(tiles), dim3(threads), 0, st,
-                     a);
+  if (a.K % 64 == 0)
+    hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WM, WN, NSTAGE, GM, PP, false>), dim3(tiles), dim3(threads),
+                       0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN, WM, WN, NSTAGE, GM, PP, true>), dim3(tiles), dim3(threads),
+                       0, st, a);
+  return hipGetLastError();
+}
+
+template <int MG, int NCH>
+hipError_t launch_skinny_k(const GemmArgs& a, const SkinnyPlan& p, hipStream_t st) {
+  const dim3 grid((unsigned)p.tiles, (unsigned)p.splits);
+  // the tail-free form needs every split's K range to lie inside K
+  if (a.K % (128 * NCH) == 0)
+    hipLaunchKernelGGL((gemm_skinny_kernel<MG, NCH, false>), grid, dim3(256), 0, st, a, p.splits);
+  else
+    hipLaunchKernelGGL((gemm_skinny_kernel<MG, NCH, true>), grid, dim3(256), 0, st, a, p.splits);
+  return hipGetLastError();
+}
+
+template <int MG>
+hipError_t launch_skinny_m(const GemmArgs& a, const SkinnyPlan& p, hipStream_t st) {
+  switch (p.nch) {
+    case 2: return launch_skinny_k<MG, 2>(a, p, st);
+    case 4: return launch_skinny_k<MG, 4>(a, p, st);
+    default: return launch_skinny_k<MG, 8>(a, p, st);
+  }
+}
+
+hipError_t launch_skinny(const GemmArgs& a_in, hipStream_t st) {
+  const SkinnyPlan p = skinny_plan(a_in.M, a_in.N, a_in.K);
+  GemmArgs a = a_in;
+  if (p.splits > 1) {  // counters first, then the partial planes
+    a.cnt = reinterpret_cast<unsigned*>(a_in.ws);
+    a.ws = reinterpret_cast<uint8_t*>(a_in.ws) + kCounterBytes;
+  }
+  switch (p.mg) {
+    case 1: return launch_skinny_m<1>(a, p, st);
+    case 2: return launch_skinny_m<2>(a, p, st);
+    default: return launch_skinny_m<4>(a, p, st);
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int NS, int GM>
+hipError_t launch_big(const GemmArgs& a, hipStream_t st) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  constexpr int threads = (BM / WM) * (BN / WN) * 64;
+  if (a.K % 128 == 0)
+    hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WM, WN, NS, GM, false>), dim3(tiles), dim3(threads), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WM, WN, NS, GM, true>), dim3(tiles), dim3(threads), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-  if (a.M >= 512) return launch_tiled<256, 256, 128, 128, 2, 4>(a, st);
-  if (a.M > 64) return launch_tiled<128, 128, 64, 64, 2, 2>(a, st);
-  if (a.M > 32) return launch_tiled<64, 64, 32, 32, 2, 1>(a, st);
-  return launch_tiled<32, 64, 32, 32, 2, 1>(a, st);
+  static const int variant = [] {
+    const char* e = getenv("FRT_GEMM_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  if (variant >= 10) {  // tile-shape exploration
+    switch (variant) {
+      case 10: return launch_big<128, 64, 32, 32, 4, 2>(a, st);   // 8 waves
+      case 11: return launch_big<128, 64, 32, 32, 6, 2>(a, st);
+      case 12: return launch_big<64, 64, 32, 32, 4, 1>(a, st);    // 4 waves
+      case 13: return launch_big<64, 64, 32, 32, 6, 1>(a, st);
+      case 14: return launch_big<64, 32, 32, 32, 6, 1>(a, st);    // 2 waves
+      case 15: return launch_big<32, 64, 32, 32, 6, 1>(a, st);    // 2 waves
+      case 16: return launch_big<128, 128, 64, 32, 4, 2>(a, st);  // 8 waves
+      case 17: return launch_big<256, 64, 64, 32, 4, 2>(a, st);   // 8 waves
+      default: break;
+    }
+  }
+  if (variant == 5 && use_skinny(a.M, a.N)) return launch_skinny(a, st);
+  if (a.M >= 512) return launch_big<256, 256, 128, 64, 2, 4>(a, st);
+  if (a.M > 64) {
+    // enough 128x128 tiles to fill the chip, else narrower ones
+    if (((a.M + 127) / 128) * ((a.N + 127) / 128) >= 192) return launch_big<128, 128, 64, 32, 4, 2>(a, st);
+    return launch_big<128, 64, 32, 32, 4, 2>(a, st);
+  }
+  return launch_big<64, 64, 32, 32, 4, 1>(a, st);
 }
 
 }  // namespace frt

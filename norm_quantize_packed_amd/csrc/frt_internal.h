@@ -64,7 +64,8 @@ struct GemmArgs {
   int M, N, K;
   int out_f32;
   SplitTab sp;
-  void* ws;
+  void* ws;       // split-K partial planes (skinny kernel), or null
+  unsigned* cnt;  // split-K per-tile arrival counters (zero at rest)
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

@@ -110,8 +110,8 @@ def _gemm(lib, M=16, K=512, splits=(512, 128, 128), N=None, outs=None,
              act_scale=FAKE + 30 * MB, w_scale=FAKE + 31 * MB, bias=None,
              n_split=n, split_n=(ctypes.c_int64 * n)(*splits),
              out=(ctypes.c_void_p * n)(*outs),
-             ld_out=(ctypes.c_int64 * n)(*lds), out_dtype=0, ws=None,
-             ws_bytes=0)
+             ld_out=(ctypes.c_int64 * n)(*lds), out_dtype=0,
+             ws=FAKE + 100 * MB, ws_bytes=16 * MB)
     a.update(kw)
     return lib.frt_packed_gemm_fp8_split(*a.values())
 
@@ -138,7 +138,15 @@ def test_gemm_refusals(lib):
 def test_gemm_zero_rows_and_workspace_query(lib):
     assert _gemm(lib, M=0) == frt.FRT_OK
     assert frt.frt_packed_gemm_fp8_workspace_size(0, 768, 512) == 0
-    assert frt.frt_packed_gemm_fp8_workspace_size(16, 768, 512) >= 0
+    need = frt.frt_packed_gemm_fp8_workspace_size(16, 768, 512)
+    assert need >= 0
+    if need:
+        # a too-small workspace is refused before anything is launched
+        assert _gemm(lib, ws_bytes=need - 1) == frt.FRT_E_INVALID
+        assert "workspace" in frt.frt_last_error()
+        assert _gemm(lib, ws=None, ws_bytes=0) == frt.FRT_E_INVALID
+    # large-M shapes need no workspace
+    assert frt.frt_packed_gemm_fp8_workspace_size(4096, 9216, 3072) == 0
 
 
 def test_pack_refusals(lib):

@@ -190,3 +190,27 @@ def test_gemm_row_capacity_writes_only_m_rows():
     torch.cuda.synchronize()
     for o in out:
         assert (o[10:].float() == 1.5).all()
+
+
+def test_gemm_split_k_repeatable_across_calls_and_shapes():
+    """The skinny path's split-K reduction: every call leaves its arrival
+    counters at zero, results do not depend on arrival order (bit-identical
+    across calls), and shapes of different split counts share one
+    workspace."""
+    shapes = [(64, 6144, 4096), (1, 6144, 4096), (16, 768, 512), (40, 2048, 1152)]
+    first = {}
+    for rep in range(3):
+        for (M, N, K) in shapes:
+            x8 = wl.random_codes(M * 7 + K, (M, K))
+            w8 = wl.random_codes(N * 3 + K, (N, K))
+            splits = [N // 2, N - N // 2]
+            got = _gpu_gemm(x8, w8, np.float32(0.01), np.float32(0.002), None,
+                            splits, f32=True)
+            out = np.concatenate(got, 1)
+            if rep == 0:
+                ref = np.concatenate(gemm.packed_gemm_split(
+                    x8, w8, np.float32(0.01), np.float32(0.002), None, splits), 1)
+                assert_gemm_f32(out, ref, f"{M}x{N}x{K}")
+                first[(M, N, K)] = out
+            else:
+                assert np.array_equal(out, first[(M, N, K)]), f"{M}x{N}x{K} rep {rep}"
