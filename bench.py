@@ -53,6 +53,9 @@ def parse():
                    help="override the producer row count (e.g. the small-M sweep)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--kernel-reps", type=int, default=20)
+    p.add_argument("--hbm-calibration", action="store_true",
+                   help="time a plain device copy of known size (HBM ceiling, "
+                        "and the reference for counter-derived traffic)")
     p.add_argument("--prewarm-s", type=float, default=2.0,
                    help="seconds of untimed replays before the warmup steps "
                         "(engine clocks ramp up from idle over ~1 s)")
@@ -323,8 +326,34 @@ def cpu_baseline(w, rows, budget_s=20.0):
                       f"{len(times)} runs, {t:.2f} s each"}
 
 
+def hbm_calibration(torch, nbytes=1 << 30, reps=20):
+    """A device-to-device copy of `nbytes` (read + write)."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    t_end = time.perf_counter() + 1.5
+    while time.perf_counter() < t_end:
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gbs = 2 * nbytes / us / 1e3
+    print(json.dumps({"hbm_calibration": "device copy", "bytes_read": nbytes,
+                      "bytes_written": nbytes, "us_per_copy": round(us, 2),
+                      "GB/s": round(gbs, 1),
+                      "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+
+
 def main():
     a = parse()
+    if a.hbm_calibration:
+        import torch
+        hbm_calibration(torch)
+        return
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not "
               "supported (the path shards by rows/heads with no exchange; see "

@@ -306,7 +306,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
 // stage is refilled. Eight waves (two per SIMD): while one wave waits for
 // its fragment reads the other wave's MFMAs keep the matrix core busy, so
 // a wave holds a single fragment set (no spills at 2 waves per SIMD).
-template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL>
+template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB = 1>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(GemmArgs a) {
   constexpr int WAVES_N = BN / WN;
   constexpr int NW = (BM / WM) * WAVES_N;
@@ -315,8 +315,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
   constexpr int LOADS = ROWS / 8;  // 1 KiB load instructions per stage
   static_assert(LOADS % NW == 0, "loads must split evenly over the waves");
   constexpr int LPW = LOADS / NW;
-  constexpr int STAGE = ROWS * 128;
-  static_assert(NS >= 2 && LPW * (NS - 2) <= 63, "ring depth vs vmcnt range");
+  constexpr int SUBB = ROWS * 128;     // one 128-deep sub-buffer
+  constexpr int STAGE = NSUB * SUBB;   // one stage = NSUB sub-buffers
+  constexpr int KST = 128 * NSUB;      // K bytes per stage
+  static_assert(NS >= 2 && NSUB * LPW * (NS - 2) <= 63, "ring depth vs vmcnt range");
+  static_assert(NS * STAGE <= 160 * 1024, "ring exceeds LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -348,25 +351,28 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
   const uint32_t offB = (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
   const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
   const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)a.K;
-  const int KT = (a.K + 127) / 128;
-  // slot SL (= step parity) is a compile-time constant in every use, so all
+  const int KT = (a.K + KST - 1) / KST;
+  // slot SL (= step mod NS) is a compile-time constant in every use, so all
   // LDS addresses are one lane base plus immediates
   auto issue = [&](int kt, auto SLC) {
     constexpr int SL = decltype(SLC)::value;
-    const int k0 = kt * 128;
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) {
-      const int u = wave + j * NW;
-      uint8_t* dst = smem + SL * STAGE + u * 1024;
-      const bool A = j < LPA;
-      uint32_t o = A ? offA + j * stepA + k0 : offB + (j - LPA) * stepB + k0;
-      if constexpr (KTAIL) {
-        if (k0 + cch * 16 >= a.K) o = kOOB;
+    for (int q = 0; q < NSUB; ++q) {
+      const int k0 = kt * KST + q * 128;
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) {
+        const int u = wave + j * NW;
+        uint8_t* dst = smem + SL * STAGE + q * SUBB + u * 1024;
+        const bool A = j < LPA;
+        uint32_t o = A ? offA + j * stepA + k0 : offB + (j - LPA) * stepB + k0;
+        if constexpr (KTAIL) {
+          if (k0 + cch * 16 >= a.K) o = kOOB;
+        }
+        if (A)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
       }
-      if (A)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
     }
   };
   // operand read of substep SUB from slot SL: two 16-byte chunks per lane
@@ -376,7 +382,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
   const uint8_t* lbase1 = smem + lrow32 * 128 + ((((lane >> 5) * 2 + 4) ^ sw) * 16);
   auto read_frags = [&](auto SLC, auto SUBC, v8i* af, v8i* bf) {
     constexpr int SL = decltype(SLC)::value, SUB = decltype(SUBC)::value;
-    const uint8_t* lb = (SUB ? lbase1 : lbase0) + SL * STAGE;
+    const uint8_t* lb = ((SUB & 1) ? lbase1 : lbase0) + SL * STAGE + (SUB >> 1) * SUBB;
     // the second chunk sits at position ^ 1, i.e. +16 or -16 bytes
     const int d1 = (sw & 1) ? -16 : 16;
 #pragma unroll
@@ -395,17 +401,13 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
     }
   };
   // own loads: at most `ahead` later stages still in flight; every LDS read
-  // done; then the block barrier
+  // done; then the block barrier (s_waitcnt takes an immediate: one case per
+  // possible depth)
   auto sync_stage = [&](int ahead) {
     __builtin_amdgcn_sched_barrier(0);
-    switch (ahead) {
-      case 0: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0)); break;
-      case 1: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS > 2 ? 1 : 0))); break;
-      case 2: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS > 3 ? 2 : 0))); break;
-      case 3: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS > 4 ? 3 : 0))); break;
-      case 4: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS > 5 ? 4 : 0))); break;
-      default: __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS > 6 ? 5 : 0))); break;
-    }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((ahead == I ? (__builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(NSUB * LPW * I)), 0) : 0), ...);
+    }(std::make_integer_sequence<int, NS - 1>{});
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -419,29 +421,61 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  v8i fa0[MI], fb0[NJ];
-  auto mfmas = [&](const v8i* fa, const v8i* fb) {
+  // Small wave tiles read every 64-deep substep of a stage right after the
+  // barrier (one LDS round trip per stage) and alternate between two
+  // independent accumulator sets, so consecutive MFMAs do not wait on each
+  // other; large wave tiles reuse one fragment set and one accumulator set.
+  constexpr int KSUB = 2 * NSUB;
+  constexpr bool ALL = MI * NJ * KSUB <= 8;
+  constexpr int NACC = (ALL && KSUB >= 2) ? 2 : 1;
+  constexpr int NF = ALL ? KSUB : 1;
+  v8i fa[NF][MI], fb[NF][NJ];
+  v16f acc2[NACC > 1 ? MI : 1][NACC > 1 ? NJ : 1];
+  if constexpr (NACC > 1) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc2[i][j][r] = 0.0f;
+  }
+  auto mfmas = [&](const v8i* af, const v8i* bf, auto ACC) {
 #pragma unroll
     for (int q = 0; q < MI * NJ; ++q) {
       const int i = q / NJ, j = q % NJ;
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+      if constexpr (decltype(ACC)::value == 0)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+      else
+        acc2[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc2[i][j], 0, 0, 0, 0, 0, 0);
     }
   };
-  // one 128-deep stage kt held in slot SL = kt % NS. The slot refilled
-  // first, (kt - 1) % NS, was last read before the previous barrier.
+  auto read_all = [&](auto SLC) {
+    [&]<int... U>(std::integer_sequence<int, U...>) {
+      (read_frags(SLC, std::integral_constant<int, U>{}, fa[U], fb[U]), ...);
+    }(std::make_integer_sequence<int, NF>{});
+  };
+  // one stage kt held in slot SL = kt % NS. The slot refilled first,
+  // (kt - 1) % NS, was last read before the previous barrier.
   auto stage = [&](int kt, auto SLC) {
     constexpr int SL = decltype(SLC)::value;
     using PV = std::integral_constant<int, (SL + NS - 1) % NS>;
     using NX = std::integral_constant<int, (SL + 1) % NS>;
     if (kt + NS - 1 < KT) issue(kt + NS - 1, PV{});
-    mfmas(fa0, fb0);
-    read_frags(SLC, I1{}, fa0, fb0);
-    mfmas(fa0, fb0);
+    if constexpr (ALL) {
+      [&]<int... U>(std::integer_sequence<int, U...>) {
+        (mfmas(fa[U], fb[U], std::integral_constant<int, U % NACC>{}), ...);
+      }(std::make_integer_sequence<int, KSUB>{});
+    } else {
+      [&]<int... U>(std::integer_sequence<int, U...>) {
+        ((U > 0 ? (read_frags(SLC, std::integral_constant<int, U>{}, fa[0], fb[0]), 0) : 0,
+          mfmas(fa[0], fb[0], std::integral_constant<int, 0>{})), ...);
+      }(std::make_integer_sequence<int, KSUB>{});
+    }
     if (kt + 1 < KT) {
       // step kt+1 landed everywhere (later ones may fly); step kt fully read
       sync_stage(min(KT - 2 - kt, NS - 2));
-      read_frags(NX{}, I0{}, fa0, fb0);
+      if constexpr (ALL) read_all(NX{});
+      else read_frags(NX{}, I0{}, fa[0], fb[0]);
     }
   };
   auto ring = [&](int kt0, auto... SLs) {
@@ -449,25 +483,23 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
     ((kt < KT ? (stage(kt, SLs), ++kt) : 0), ...);
   };
 
-#pragma unroll
-  for (int s0 = 0; s0 < NS - 1; ++s0) {
-    if (s0 < KT) {
-      switch (s0) {
-        case 0: issue(s0, I0{}); break;
-        case 1: issue(s0, I1{}); break;
-        case 2: issue(s0, std::integral_constant<int, 2 % NS>{}); break;
-        case 3: issue(s0, std::integral_constant<int, 3 % NS>{}); break;
-        case 4: issue(s0, std::integral_constant<int, 4 % NS>{}); break;
-        default: issue(s0, std::integral_constant<int, 5 % NS>{}); break;
-      }
-    }
-  }
+  // prologue: steps 0 .. NS-2 in flight (slot index = step)
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((I < KT ? (issue(I, std::integral_constant<int, I>{}), 0) : 0), ...);
+  }(std::make_integer_sequence<int, NS - 1>{});
   sync_stage(min(KT - 1, NS - 2));
-  read_frags(I0{}, I0{}, fa0, fb0);
+  if constexpr (ALL) read_all(I0{});
+  else read_frags(I0{}, I0{}, fa[0], fb[0]);
   for (int kt = 0; kt < KT; kt += NS) {
     [&]<int... S>(std::integer_sequence<int, S...>) {
       ring(kt, std::integral_constant<int, S>{}...);
     }(std::make_integer_sequence<int, NS>{});
+  }
+  if constexpr (NACC > 1) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] += acc2[i][j];
   }
 
   // ---- epilogue: alpha * acc + bias, column split, bf16 (or fp32) ----
@@ -758,14 +790,16 @@ hipError_t launch_skinny(const GemmArgs& a_in, hipStream_t st) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int GM>
+template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1>
 hipError_t launch_big(const GemmArgs& a, hipStream_t st) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  if (a.K % 128 == 0)
-    hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WM, WN, NS, GM, false>), dim3(tiles), dim3(threads), 0, st, a);
+  if (a.K % (128 * NSUB) == 0)
+    hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WM, WN, NS, GM, false, NSUB>), dim3(tiles), dim3(threads), 0, st,
+                       a);
   else
-    hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WM, WN, NS, GM, true>), dim3(tiles), dim3(threads), 0, st, a);
+    hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WM, WN, NS, GM, true, NSUB>), dim3(tiles), dim3(threads), 0, st,
+                       a);
   return hipGetLastError();
 }
 
@@ -786,6 +820,28 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
       case 15: return launch_big<32, 64, 32, 32, 6, 1>(a, st);    // 2 waves
       case 16: return launch_big<128, 128, 64, 32, 4, 2>(a, st);  // 8 waves
       case 17: return launch_big<256, 64, 64, 32, 4, 2>(a, st);   // 8 waves
+      case 20: return launch_big<128, 64, 32, 32, 3, 2>(a, st);   // 8 waves, 72 KiB
+      case 21: return launch_big<128, 128, 64, 32, 2, 2>(a, st);  // 8 waves, 64 KiB
+      case 22: return launch_big<256, 64, 64, 32, 3, 2>(a, st);   // 8 waves, 120 KiB
+      case 23: return launch_big<128, 64, 64, 32, 3, 2>(a, st);   // 4 waves, 72 KiB
+      case 24: return launch_big<64, 64, 32, 32, 3, 1>(a, st);    // 4 waves, 48 KiB
+      case 25: return launch_big<64, 32, 32, 32, 4, 1>(a, st);    // 2 waves, 48 KiB
+      case 26: return launch_big<128, 32, 32, 32, 4, 2>(a, st);   // 4 waves, 80 KiB
+      case 27: return launch_big<128, 128, 64, 32, 3, 2>(a, st);  // 8 waves, 96 KiB
+      case 30: return launch_big<64, 32, 32, 32, 8, 1>(a, st);    // 2 waves, 96 KiB
+      case 31: return launch_big<64, 32, 32, 32, 12, 1>(a, st);   // 2 waves, 144 KiB
+      case 32: return launch_big<64, 64, 32, 32, 8, 1>(a, st);    // 4 waves, 128 KiB
+      case 33: return launch_big<128, 64, 32, 32, 6, 2>(a, st);   // 8 waves, 144 KiB
+      case 34: return launch_big<64, 32, 32, 32, 6, 1>(a, st);    // 2 waves, 72 KiB (2/CU)
+      case 35: return launch_big<32, 64, 32, 32, 10, 1>(a, st);   // 2 waves, 120 KiB
+      case 36: return launch_big<128, 32, 32, 32, 6, 2>(a, st);   // 4 waves, 120 KiB
+      case 40: return launch_big<64, 64, 32, 32, 3, 1, 2>(a, st);   // 4 waves, K 256/stage, 96 KiB
+      case 41: return launch_big<64, 64, 32, 32, 4, 1, 2>(a, st);   // 128 KiB
+      case 42: return launch_big<64, 32, 32, 32, 4, 1, 2>(a, st);   // 2 waves, 96 KiB
+      case 43: return launch_big<64, 32, 32, 32, 6, 1, 2>(a, st);   // 2 waves, 144 KiB
+      case 44: return launch_big<128, 64, 32, 32, 3, 2, 2>(a, st);  // 8 waves, 144 KiB
+      case 45: return launch_big<128, 64, 32, 32, 2, 2, 2>(a, st);  // 8 waves, 96 KiB
+      case 46: return launch_big<32, 64, 32, 32, 4, 1, 2>(a, st);   // 2 waves, 96 KiB
       default: break;
     }
   }

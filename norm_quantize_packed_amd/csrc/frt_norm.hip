@@ -94,7 +94,7 @@ __device__ __forceinline__ float row_sum(float v, float* red, int wave) {
     __syncthreads();  // previous use of `red` finished
     if ((threadIdx.x & 63) == 0) red[wave] = s;
     __syncthreads();
-    const int base = wave - wave % WPR;
+    const int base = wave - wave % WPR;  // first wave of this row
     float t = 0.0f;
 #pragma unroll
     for (int k = 0; k < WPR; ++k) t += red[base + k];
@@ -110,17 +110,20 @@ __device__ __forceinline__ void amax_commit(float* amax, float m) {
 }  // namespace
 
 template <int WPR, int NV, int VEC>
-__global__ __launch_bounds__(256) void ada_norm_kernel(AdaArgs a) {
-  constexpr int RPB = 4 / WPR;
-  __shared__ float red[4];
+__global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ada_norm_kernel(AdaArgs a) {
+  constexpr int RPB = WPR <= 4 ? 4 / WPR : 1;
+  constexpr bool EARLY = NV <= 4;  // modulation loads issued before the reduction
+  __shared__ float red[WPR <= 4 ? 4 : WPR];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * RPB + wave / WPR;
   const int sub = wave % WPR;
   const bool row_ok = row < a.M;
   const int nvec = a.D / VEC;
+  const uint16_t* mrow = a.mod + row * a.ld_mod;
 
   float h[NV][VEC];
+  Vec<VEC> msc[EARLY ? NV : 1], msh[EARLY ? NV : 1], mw[EARLY ? NV : 1];
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -129,6 +132,11 @@ __global__ __launch_bounds__(256) void ada_norm_kernel(AdaArgs a) {
       const int64_t c = (int64_t)v * VEC;
       Vec<VEC> r;
       r.load(a.res + row * a.ld_res + c);
+      if constexpr (EARLY) {
+        msc[i].load(mrow + c);
+        msh[i].load(mrow + a.D + c);
+        if (a.weight != nullptr) mw[i].load(a.weight + c);
+      }
       if (a.x != nullptr && a.gate != nullptr) {
         Vec<VEC> x, g;
         x.load(a.x + row * a.ld_x + c);
@@ -162,19 +170,23 @@ __global__ __launch_bounds__(256) void ada_norm_kernel(AdaArgs a) {
   }
   float amax = 0.0f;
   if (row_ok) {
-    const uint16_t* mrow = a.mod + row * a.ld_mod;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = sub * 64 + lane + i * 64 * WPR;
       if (v < nvec) {
         const int64_t c = (int64_t)v * VEC;
-        Vec<VEC> sc, sh;
-        sc.load(mrow + c);
-        sh.load(mrow + a.D + c);
+        Vec<VEC> sc, sh, w;
+        if constexpr (EARLY) {
+          sc = msc[i];
+          sh = msh[i];
+          w = mw[i];
+        } else {
+          sc.load(mrow + c);
+          sh.load(mrow + a.D + c);
+          if (a.weight != nullptr) w.load(a.weight + c);
+        }
         float y[VEC];
         if (a.weight != nullptr) {
-          Vec<VEC> w;
-          w.load(a.weight + c);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) y[e] = h[i][e] * rr * w.f(e);
         } else {
@@ -206,18 +218,25 @@ __global__ __launch_bounds__(256) void ada_norm_kernel(AdaArgs a) {
 }
 
 template <int WPR, int NV, int VEC>
-__global__ __launch_bounds__(256) void ptok_norm_kernel(PtokArgs a) {
-  constexpr int RPB = 4 / WPR;
-  __shared__ float red[4];
+__global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ptok_norm_kernel(PtokArgs a) {
+  constexpr int RPB = WPR <= 4 ? 4 / WPR : 1;
+  // table loads issued before the reductions while the registers allow it
+  // (at 4 vectors per lane the extra 64 registers cost more occupancy than
+  // the early loads save)
+  constexpr bool EARLY = NV <= 3;
+  __shared__ float red[WPR <= 4 ? 4 : WPR];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * RPB + wave / WPR;
   const int sub = wave % WPR;
   const bool row_ok = row < a.R;
   const int nvec = a.D / VEC;
+  const float* tab_s = a.table + (int64_t)a.shift_idx * a.D;
+  const float* tab_c = a.table + (int64_t)a.scale_idx * a.D;
 
   float x[NV][VEC];
   Vec<VEC> tsh[NV], tsc[NV];
+  float ts[EARLY ? NV : 1][VEC], tc[EARLY ? NV : 1][VEC];
   float sum = 0.0f;
   const uint16_t* trow = a.temb + row * a.ld_temb;
 #pragma unroll
@@ -229,6 +248,10 @@ __global__ __launch_bounds__(256) void ptok_norm_kernel(PtokArgs a) {
       xv.load(a.x + row * a.ld_x + c);
       tsh[i].load(trow + (int64_t)a.shift_idx * a.D + c);
       tsc[i].load(trow + (int64_t)a.scale_idx * a.D + c);
+      if constexpr (EARLY) {
+        load_f32<VEC>(tab_s + c, ts[i]);
+        load_f32<VEC>(tab_c + c, tc[i]);
+      }
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
         x[i][e] = xv.f(e);
@@ -263,20 +286,26 @@ __global__ __launch_bounds__(256) void ptok_norm_kernel(PtokArgs a) {
   }
   float amax = 0.0f;
   if (row_ok) {
-    const float* tab_s = a.table + (int64_t)a.shift_idx * a.D;
-    const float* tab_c = a.table + (int64_t)a.scale_idx * a.D;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int v = sub * 64 + lane + i * 64 * WPR;
       if (v < nvec) {
         const int64_t c = (int64_t)v * VEC;
-        float ts[VEC], tc[VEC], y[VEC];
-        load_f32<VEC>(tab_s + c, ts);
-        load_f32<VEC>(tab_c + c, tc);
+        float tsv[VEC], tcv[VEC], y[VEC];
+        if constexpr (EARLY) {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            tsv[e] = ts[i][e];
+            tcv[e] = tc[i][e];
+          }
+        } else {
+          load_f32<VEC>(tab_s + c, tsv);
+          load_f32<VEC>(tab_c + c, tcv);
+        }
 #pragma unroll
         for (int e = 0; e < VEC; ++e) {
-          const float shift = ts[e] + tsh[i].f(e);
-          const float scale = tc[e] + tsc[i].f(e);
+          const float shift = tsv[e] + tsh[i].f(e);
+          const float scale = tcv[e] + tsc[i].f(e);
           const float n = (x[i][e] - mu) * rstd;
           y[e] = __builtin_fmaf(n, scale, n) + shift;
         }
@@ -301,14 +330,20 @@ __global__ __launch_bounds__(256) void ptok_norm_kernel(PtokArgs a) {
 
 namespace {
 
-// Waves per row: enough vector slots per lane for D, and more waves when
-// rows are scarce so that short calls still spread across the chip.
+// Waves per row: at most 32 elements per lane on the vector path (keeps
+// the row, its modulation and the statistics in registers at a useful
+// occupancy), and more waves when rows are scarce so that short calls still
+// spread across the chip. 8 waves per row use 512-thread blocks.
 int pick_wpr(int64_t rows, int64_t D) {
-  int wpr = D > 8192 ? 4 : (D > 4096 ? 2 : 1);
+  int wpr = 1;
+  while (wpr < 8 && D > (int64_t)wpr * 64 * 8 * 4) wpr *= 2;
   if (rows < 2048 && D >= 2048 && wpr < 2) wpr = 2;
-  if (rows < 512 && D >= 2048) wpr = 4;
+  if (rows < 512 && D >= 2048 && wpr < 4) wpr = 4;
   return wpr;
 }
+
+int block_threads(int wpr) { return wpr <= 4 ? 256 : 64 * wpr; }
+int rows_per_block(int wpr) { return wpr <= 4 ? 4 / wpr : 1; }
 
 #define FRT_NV_SWITCH(NVV, ...)                    \
   switch (NVV) {                                   \
@@ -344,6 +379,7 @@ int pow2_slots(int64_t n) {
     case 1: { constexpr int WPR = 1; __VA_ARGS__; } break; \
     case 2: { constexpr int WPR = 2; __VA_ARGS__; } break; \
     case 4: { constexpr int WPR = 4; __VA_ARGS__; } break; \
+    case 8: { constexpr int WPR = 8; __VA_ARGS__; } break; \
     default: return hipErrorInvalidValue;          \
   }
 
@@ -354,10 +390,11 @@ hipError_t launch_ada_norm(const AdaArgs& a, bool vec8, hipStream_t st) {
   const int wpr = pick_wpr(a.M, a.D);
   const int64_t nvec = a.D / vec;
   const int nv = (int)((nvec + 64 * wpr - 1) / (64 * wpr));
-  const int rpb = 4 / wpr;
+  const int rpb = rows_per_block(wpr);
   const dim3 grid((unsigned)((a.M + rpb - 1) / rpb));
+  const dim3 block((unsigned)block_threads(wpr));
   if (vec8) {
-    FRT_WPR_SWITCH(wpr, FRT_NV_SWITCH(nv, hipLaunchKernelGGL((ada_norm_kernel<WPR, NV, 8>), grid, dim3(256), 0, st, a)))
+    FRT_WPR_SWITCH(wpr, FRT_NV_SWITCH(nv, hipLaunchKernelGGL((ada_norm_kernel<WPR, NV, 8>), grid, block, 0, st, a)))
   } else {
     // 4-byte path (unaligned or D % 8 != 0): one row per block, 4 waves,
     // up to 32 two-element slots per lane
@@ -373,9 +410,10 @@ hipError_t launch_ptok_norm(const PtokArgs& a, bool vec8, hipStream_t st) {
   if (vec8) {
     const int64_t nvec = a.D / 8;
     const int nv = (int)((nvec + 64 * wpr - 1) / (64 * wpr));
-    const int rpb = 4 / wpr;
+    const int rpb = rows_per_block(wpr);
     const dim3 grid((unsigned)((a.R + rpb - 1) / rpb));
-    FRT_WPR_SWITCH(wpr, FRT_NV_SWITCH(nv, hipLaunchKernelGGL((ptok_norm_kernel<WPR, NV, 8>), grid, dim3(256), 0, st, a)))
+    const dim3 block((unsigned)block_threads(wpr));
+    FRT_WPR_SWITCH(wpr, FRT_NV_SWITCH(nv, hipLaunchKernelGGL((ptok_norm_kernel<WPR, NV, 8>), grid, block, 0, st, a)))
   } else {
     const int64_t nvec = a.D / 2;
     const int nv2 = pow2_slots((nvec + 255) / 256);
