@@ -59,6 +59,19 @@ def parse():
     p.add_argument("--prewarm-s", type=float, default=2.0,
                    help="seconds of untimed replays before the warmup steps "
                         "(engine clocks ramp up from idle over ~1 s)")
+    # counter passes (run under rocprofv3 --pmc) and their summary
+    p.add_argument("--profile-kernel", default=None,
+                   help="launch only this kernel of the step (norm1, gemm1, "
+                        "norm2, gemm2) --launches times over the rotation sets")
+    p.add_argument("--copy-kernel", action="store_true",
+                   help="launch a plain device copy of COPY_BYTES --launches "
+                        "times (the reference for counter scaling)")
+    p.add_argument("--launches", type=int, default=20)
+    p.add_argument("--summarize-pmc", nargs=4, default=None,
+                   metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                   help="turn four rocprofv3 --pmc output folders (FETCH_SIZE and "
+                        "WRITE_SIZE of --profile-kernel, then of --copy-kernel) into "
+                        "profiles/traffic_w<workload>_<kernel>.json")
     return p.parse_args()
 
 
@@ -326,33 +339,161 @@ def cpu_baseline(w, rows, budget_s=20.0):
                       f"{len(times)} runs, {t:.2f} s each"}
 
 
+# ------------------------------------------------------- counter traffic
+
+COPY_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_sources_sha():
+    """sha256 over the HIP sources and headers: a counter record is used only
+    while the kernels it measured are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "norm_quantize_packed_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def copy_kernel(torch, launches):
+    """Plain device copies of COPY_BYTES, rotating over 4 buffer pairs
+    (2 GiB) so the copies stream from and to HBM."""
+    pairs = [(torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1),
+              torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")) for _ in range(4)]
+    torch.cuda.synchronize()
+    for i in range(launches):
+        src, dst = pairs[i % 4]
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def _pmc_values(folder, counter, name_filter):
+    """Per-dispatch values of `counter` for kernels whose name passes
+    `name_filter`, from a rocprofv3 --pmc --output-format csv folder."""
+    import csv
+    vals = []
+    for dirpath, _, files in os.walk(folder):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                with open(os.path.join(dirpath, f)) as fh:
+                    for r in csv.DictReader(fh):
+                        if r["Counter_Name"] == counter and name_filter(r["Kernel_Name"]):
+                            vals.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return [v for _, v in sorted(vals)]
+
+
+def summarize_pmc(a):
+    fetch_dir, write_dir, cfetch_dir, cwrite_dir = a.summarize_pmc
+    kind = a.profile_kernel
+    if kind is None:
+        raise SystemExit("--summarize-pmc needs --profile-kernel (the kernel it covers)")
+    is_gemm = kind.startswith("gemm")
+    want = (lambda n: "gemm" in n and "frt::" in n) if is_gemm else \
+        (lambda n: "norm_kernel" in n and "frt::" in n)
+    is_copy = lambda n: "copyBuffer" in n  # noqa: E731
+    # the profiled launches are the last --launches dispatches of their kind
+    # (set-up launches of the same kernels come first)
+    n = a.launches
+    fk = _pmc_values(fetch_dir, "FETCH_SIZE", want)[-n:]
+    wk = _pmc_values(write_dir, "WRITE_SIZE", want)[-n:]
+    fc = _pmc_values(cfetch_dir, "FETCH_SIZE", is_copy)[-n:]
+    wc = _pmc_values(cwrite_dir, "WRITE_SIZE", is_copy)[-n:]
+    if not (fk and wk and fc and wc):
+        raise SystemExit("missing counter rows: %d %d %d %d" % (len(fk), len(wk), len(fc), len(wc)))
+    med = lambda v: float(np.median(v))  # noqa: E731
+    # counters are KiB per dispatch; the copy moves COPY_BYTES each way
+    f_scale = COPY_BYTES / (med(fc) * 1024.0)
+    w_scale = COPY_BYTES / (med(wc) * 1024.0)
+    fetch_b = med(fk) * 1024.0 * f_scale
+    write_b = med(wk) * 1024.0 * w_scale
+    rec = {"workload": a.workload, "kernel": kind, "dispatches": [len(fk), len(wk)],
+           "fetch_kib_median": med(fk), "write_kib_median": med(wk),
+           "copy_fetch_kib_median": med(fc), "copy_write_kib_median": med(wc),
+           "copy_bytes_each_way": COPY_BYTES,
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
+           "traffic_bytes": round(fetch_b + write_b),
+           "sources_sha256": kernel_sources_sha()}
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"traffic_w{a.workload}_{kind}.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+
+
+def load_traffic(wid, kind):
+    """Counter-derived HBM bytes per launch, or None when no record exists
+    or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_w{wid}_{kind}.json")
+    try:
+        with open(path) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_sha256") != kernel_sources_sha():
+        return None
+    return int(rec["traffic_bytes"])
+
+
 def hbm_calibration(torch, nbytes=1 << 30, reps=20):
-    """A device-to-device copy of `nbytes` (read + write)."""
+    """Reference rates: a device-to-device copy of `nbytes` (read + write),
+    a read-only reduction over `nbytes`, and the per-launch floor of an
+    almost empty kernel replayed from a graph (every kernel pays it)."""
+    def timed(fn, n):
+        t_end = time.perf_counter() + 1.5
+        while time.perf_counter() < t_end:
+            fn()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
-    t_end = time.perf_counter() + 1.5
-    while time.perf_counter() < t_end:
-        dst.copy_(src)
-        torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / reps
+    us = timed(lambda: dst.copy_(src), reps)
     gbs = 2 * nbytes / us / 1e3
     print(json.dumps({"hbm_calibration": "device copy", "bytes_read": nbytes,
                       "bytes_written": nbytes, "us_per_copy": round(us, 2),
                       "GB/s": round(gbs, 1),
                       "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+    del dst
+    f = src.view(torch.float32)
+    us = timed(lambda: f.sum(), reps)
+    gbs = nbytes / us / 1e3
+    print(json.dumps({"hbm_calibration": "read-only reduction (sum)", "bytes_read": nbytes,
+                      "us": round(us, 2), "GB/s": round(gbs, 1),
+                      "frac_of_8TBs": round(gbs / HBM_PEAK_GBS, 4)}), flush=True)
+    del src, f
+    tiny = torch.zeros(64, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(20):
+            tiny.add_(1.0)
+    us = timed(g.replay, 200) / 20
+    print(json.dumps({"hbm_calibration": "launch floor (64-element add, graph replay)",
+                      "us_per_launch": round(us, 3)}), flush=True)
 
 
 def main():
     a = parse()
+    if a.summarize_pmc:
+        summarize_pmc(a)
+        return
     if a.hbm_calibration:
         import torch
         hbm_calibration(torch)
+        return
+    if a.copy_kernel:
+        import torch
+        copy_kernel(torch, a.launches)
         return
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not "
@@ -372,8 +513,24 @@ def main():
     outs = make_outputs(w, rows, packs, torch)
     nset = len(sets)
 
-    # eager reference of one step, then graph replays must reproduce it
     steps_fns = [step_launches(w, s, act, outs, rows, frt, wl.EPS) for s in sets]
+    if a.profile_kernel:
+        # one kernel kind, eagerly, over the rotation sets (after one full
+        # step so every input it reads is defined)
+        for _, fn in steps_fns[0]:
+            fn()
+        kinds = dict(steps_fns[0])
+        if a.profile_kernel not in kinds:
+            raise SystemExit(f"--profile-kernel: choose one of {sorted(kinds)}")
+        torch.cuda.synchronize()
+        for i in range(a.launches):
+            dict(steps_fns[i % nset])[a.profile_kernel]()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_kernel": a.profile_kernel, "launches": a.launches,
+                          "workload": w.name, "rotation_sets": nset}), flush=True)
+        return
+
+    # eager reference of one step, then graph replays must reproduce it
     for _, fn in steps_fns[0]:
         fn()
     torch.cuda.synchronize()
@@ -433,13 +590,16 @@ def main():
     norm_bytes = sum(kernel_work(w, k, rows, packs)[0] for k in kinds if k.startswith("norm"))
     norm_us = sum(r["us"] for r in table if r["kernel"].startswith("norm"))
     dom = max(table, key=lambda r: r["us"])
+    traffic = load_traffic(a.workload, dom["kernel"]) if a.rows is None else None
     if dom["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dom["TFLOP/s"], "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": dom["mfma_frac"], "traffic": None}
+                "unit": "TFLOP/s", "frac": dom["mfma_frac"], "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": dom["hbm_frac"], "traffic": None}
+                "unit": "GB/s", "frac": dom["hbm_frac"], "traffic": traffic}
     roof["kernel"] = dom["kernel"]
+    roof["algorithmic_bytes"] = dom["bytes"]
+    roof["traffic_unit"] = "bytes/launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
 
     value = gemm_flops / (ms * 1e-3) / 1e12
     res = {

@@ -44,6 +44,11 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr uint32_t kOOB = 0x80000000u;  // offset past any record count
+// cache-policy operand of buffer loads/stores: sc1, i.e. coherent at agent
+// scope (the instruction form of a relaxed agent-scope atomic access: stores
+// are written through to the device-coherent level, loads never hit a line
+// another XCD's writes could have left stale)
+constexpr int kCoherent = 0x10;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   // flags: default data format for raw buffer loads on gfx9
@@ -306,7 +311,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_tiled_kernel(
 // stage is refilled. Eight waves (two per SIMD): while one wave waits for
 // its fragment reads the other wave's MFMAs keep the matrix core busy, so
 // a wave holds a single fragment set (no spills at 2 waves per SIMD).
-template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB = 1>
+template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB = 1, bool SK = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(GemmArgs a) {
   constexpr int WAVES_N = BN / WN;
   constexpr int NW = (BM / WM) * WAVES_N;
@@ -347,11 +352,15 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
   // NW even, so (row >> 1) & 7 = ((wave & 1) << 2) | (lrow >> 1) for every j
   static_assert(NW % 2 == 0, "row swizzle assumes an even wave count");
   const int cch = (lane & 7) ^ (((wave & 1) << 2) | (lrow >> 1));
-  const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
-  const uint32_t offB = (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
+  // split-K: this block covers K bytes [kb, kb + kc) (kc a multiple of
+  // KST; the planner leaves no split empty)
+  const int kb = SK ? (int)blockIdx.y * a.kc : 0;
+  const int klen = SK ? min(a.kc, a.K - kb) : a.K;
+  const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + kb + cch * 16;
+  const uint32_t offB = (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + kb + cch * 16;
   const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
   const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)a.K;
-  const int KT = (a.K + KST - 1) / KST;
+  const int KT = (klen + KST - 1) / KST;
   // slot SL (= step mod NS) is a compile-time constant in every use, so all
   // LDS addresses are one lane base plus immediates
   auto issue = [&](int kt, auto SLC) {
@@ -366,7 +375,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
         const bool A = j < LPA;
         uint32_t o = A ? offA + j * stepA + k0 : offB + (j - LPA) * stepB + k0;
         if constexpr (KTAIL) {
-          if (k0 + cch * 16 >= a.K) o = kOOB;
+          if (k0 + cch * 16 >= klen) o = kOOB;
         }
         if (A)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
@@ -500,6 +509,74 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] += acc2[i][j];
+  }
+
+  if constexpr (SK) {
+    // Split-K: every split stores its fp32 partial tile in fragment order
+    // (lane-contiguous 16-byte groups, so each store instruction writes one
+    // contiguous KiB) with agent-coherent stores, then bumps the tile's
+    // arrival counter; the last block to arrive sums the partials of
+    // splits 0..S-1 in that order (the result does not depend on which
+    // block finishes last), resets the counter and runs the epilogue.
+    __shared__ int last_flag;
+    constexpr int FR = MI * NJ * 4;        // 16-byte groups per lane
+    constexpr int TILE_B = BM * BN * 4;    // bytes per partial tile
+    const int S = a.nsplit;
+    const uint32_t wave_off = (uint32_t)wave * (FR * 1024) + lane * 16;
+    const uint32_t plane = (uint32_t)gridDim.x * TILE_B;
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.ws, plane * (uint32_t)S);
+    const uint32_t tile_off = (uint32_t)blockIdx.x * TILE_B + wave_off;
+    {
+      const uint32_t o = blockIdx.y * plane + tile_off;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const v4f v = (v4f){acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4i, v), pr,
+                                                   o + ((i * NJ + j) * 4 + g) * 1024, 0, kCoherent);
+          }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // partial stores performed at agent scope
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned* c = a.cnt + blockIdx.x;
+      const unsigned prev = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = prev == (unsigned)(S - 1);
+      if (last_flag) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!last_flag) return;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int z = 0; z < S; ++z) {
+      const uint32_t o = (uint32_t)z * plane + tile_off;
+      v4i part[MI][NJ][4];
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            part[i][j][g] = __builtin_amdgcn_raw_buffer_load_b128(pr, o + ((i * NJ + j) * 4 + g) * 1024, 0,
+                                                                  kCoherent);
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const v4f v = __builtin_bit_cast(v4f, part[i][j][g]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += v[e];
+          }
+    }
   }
 
   // ---- epilogue: alpha * acc + bias, column split, bf16 (or fp32) ----
@@ -719,22 +796,85 @@ struct SkinnyPlan {
   int mg, nch, splits, tiles;
 };
 
+// exploration switch (0 = the default plans)
+int gemm_variant() {
+  static const int v = [] {
+    const char* e = getenv("FRT_GEMM_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K) {
   SkinnyPlan p{};
   p.mg = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.tiles = (int)((N + 63) / 64);
   const int kt = (int)((K + 127) / 128);
-  p.nch = 8;
-  // more blocks when the N tiles alone cannot fill the chip
-  while (p.nch > 2 && (int64_t)p.tiles * ((kt + p.nch - 1) / p.nch) < 512) p.nch /= 2;
+  static const int force = [] {
+    const char* e = getenv("FRT_SKINNY_NCH");
+    return e ? atoi(e) : 0;
+  }();
+  if (force == 2 || force == 4 || force == 8) {
+    p.nch = force;
+  } else {
+    p.nch = 8;
+    // more blocks when the N tiles alone cannot fill the chip
+    while (p.nch > 2 && (int64_t)p.tiles * ((kt + p.nch - 1) / p.nch) < 512) p.nch /= 2;
+  }
   p.splits = (kt + p.nch - 1) / p.nch;
   return p;
 }
 
-bool use_skinny(int64_t M, int64_t N) { return M <= 64 && (N + 63) / 64 <= kCounterBytes / 4; }
+bool use_skinny(int64_t M, int64_t N) {
+  return gemm_variant() == 5 && M <= 64 && (N + 63) / 64 <= kCounterBytes / 4;
+}
+
+// ---- split-K plans of the tiled kernel ----------------------------------
+// Workspace = the 64 KiB counter region followed by S partial planes of
+// `tiles` fp32 tiles each.
+struct SkPlan {
+  int bm, bn, kst;  // tile and K bytes per pipeline stage
+  int S, kc, tiles;
+};
+
+// split-K configurations selectable for exploration
+bool sk_config(int variant, SkPlan& p) {
+  switch (variant) {
+    case 60: p.bm = 64; p.bn = 64; p.kst = 128; return true;
+    case 61: p.bm = 64; p.bn = 32; p.kst = 128; return true;
+    case 62: p.bm = 64; p.bn = 128; p.kst = 128; return true;
+    case 63: p.bm = 32; p.bn = 64; p.kst = 128; return true;
+    case 64: p.bm = 64; p.bn = 32; p.kst = 128; return true;
+    case 65: p.bm = 64; p.bn = 64; p.kst = 256; return true;
+    default: return false;
+  }
+}
+
+// S splits requested; each split gets a whole number of stages and none is
+// empty
+void sk_finish(SkPlan& p, int64_t M, int64_t N, int64_t K, int S_req) {
+  const int kt = (int)((K + p.kst - 1) / p.kst);
+  int S = std::max(1, std::min(S_req, kt));
+  const int per = (kt + S - 1) / S;
+  p.S = (kt + per - 1) / per;
+  p.kc = per * p.kst;
+  p.tiles = (int)(((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn));
+}
+
+bool sk_plan(int64_t M, int64_t N, int64_t K, SkPlan& p) {
+  if (!sk_config(gemm_variant(), p)) return false;
+  static const int S_env = [] {
+    const char* e = getenv("FRT_GEMM_SPLITK");
+    return e ? atoi(e) : 2;
+  }();
+  sk_finish(p, M, N, K, S_env);
+  return p.S > 1 && p.tiles <= kCounterBytes / 4 &&
+         (int64_t)p.S * p.tiles * p.bm * p.bn * 4 < ((int64_t)1 << 31);
+}
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  return 0;  // the default plans need none (split-K skinny is opt-in)
+  SkPlan q{};
+  if (sk_plan(M, N, K, q)) return (size_t)(kCounterBytes + (int64_t)q.S * q.tiles * q.bm * q.bn * 4);
   if (!use_skinny(M, N)) return 0;
   const SkinnyPlan p = skinny_plan(M, N, K);
   if (p.splits <= 1) return 0;
@@ -803,14 +943,39 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1>
+hipError_t launch_big_sk(const GemmArgs& a_in, const SkPlan& p, hipStream_t st) {
+  GemmArgs a = a_in;
+  a.cnt = reinterpret_cast<unsigned*>(a_in.ws);
+  a.ws = reinterpret_cast<uint8_t*>(a_in.ws) + kCounterBytes;
+  a.kc = p.kc;
+  a.nsplit = p.S;
+  constexpr int threads = (BM / WM) * (BN / WN) * 64;
+  const dim3 grid((unsigned)p.tiles, (unsigned)p.S);
+  if (a.K % (128 * NSUB) == 0)
+    hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, true>), grid, dim3(threads), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WM, WN, NS, GM, true, NSUB, true>), grid, dim3(threads), 0, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-  static const int variant = [] {
-    const char* e = getenv("FRT_GEMM_VARIANT");
-    return e ? atoi(e) : 0;
-  }();
-  if (variant >= 10) {  // tile-shape exploration
+  const int variant = gemm_variant();
+  SkPlan sk{};
+  if (sk_plan(a.M, a.N, a.K, sk)) {
+    switch (variant) {
+      case 60: return launch_big_sk<64, 64, 32, 32, 3, 1>(a, sk, st);
+      case 61: return launch_big_sk<64, 32, 32, 32, 4, 1>(a, sk, st);
+      case 62: return launch_big_sk<64, 128, 32, 64, 3, 1>(a, sk, st);
+      case 63: return launch_big_sk<32, 64, 32, 32, 4, 1>(a, sk, st);
+      case 64: return launch_big_sk<64, 32, 32, 32, 6, 1>(a, sk, st);
+      case 65: return launch_big_sk<64, 64, 32, 32, 3, 1, 2>(a, sk, st);
+      default: break;
+    }
+  }
+  if (variant >= 10 && variant < 60) {  // tile-shape exploration
     switch (variant) {
       case 10: return launch_big<128, 64, 32, 32, 4, 2>(a, st);   // 8 waves
       case 11: return launch_big<128, 64, 32, 32, 6, 2>(a, st);
@@ -842,17 +1007,26 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
       case 44: return launch_big<128, 64, 32, 32, 3, 2, 2>(a, st);  // 8 waves, 144 KiB
       case 45: return launch_big<128, 64, 32, 32, 2, 2, 2>(a, st);  // 8 waves, 96 KiB
       case 46: return launch_big<32, 64, 32, 32, 4, 1, 2>(a, st);   // 2 waves, 96 KiB
+      case 47: return launch_big<128, 128, 32, 32, 4, 2>(a, st);   // 16 waves, 128 KiB
+      case 48: return launch_big<128, 128, 32, 32, 3, 2>(a, st);   // 16 waves, 96 KiB
+      case 49: return launch_big<256, 128, 64, 64, 3, 4>(a, st);   // 8 waves, 144 KiB
+      case 50: return launch_big<256, 128, 64, 32, 2, 4>(a, st);   // 16 waves, 96 KiB
+      case 51: return launch_big<128, 256, 64, 64, 3, 2>(a, st);   // 8 waves, 144 KiB
       default: break;
     }
   }
-  if (variant == 5 && use_skinny(a.M, a.N)) return launch_skinny(a, st);
+  if (use_skinny(a.M, a.N)) return launch_skinny(a, st);
+  // Default plans (measured on MI355X, graph-replayed launches):
+  //  M >= 512: 256x256 tiles, 8 waves of 128x64 (MFMA-bound shapes);
+  //  64 < M < 512: 128x128 tiles of sixteen 32x32 waves when they fill the
+  //    chip, else 64x64 tiles (more blocks for narrow N);
+  //  M <= 64: 64x32 tiles, 256-deep K stages (weight streaming).
   if (a.M >= 512) return launch_big<256, 256, 128, 64, 2, 4>(a, st);
   if (a.M > 64) {
-    // enough 128x128 tiles to fill the chip, else narrower ones
-    if (((a.M + 127) / 128) * ((a.N + 127) / 128) >= 192) return launch_big<128, 128, 64, 32, 4, 2>(a, st);
-    return launch_big<128, 64, 32, 32, 4, 2>(a, st);
+    if (((a.M + 127) / 128) * ((a.N + 127) / 128) >= 192) return launch_big<128, 128, 32, 32, 3, 2>(a, st);
+    return launch_big<64, 64, 32, 32, 4, 1>(a, st);
   }
-  return launch_big<64, 64, 32, 32, 4, 1>(a, st);
+  return launch_big<64, 32, 32, 32, 4, 1, 2>(a, st);
 }
 
 }  // namespace frt
