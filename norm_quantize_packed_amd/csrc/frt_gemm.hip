@@ -785,6 +785,202 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs a, int S) {
     }
 }
 
+// Epilogue of a wave's MI x NJ grid of 32x32 fp32 accumulators whose top
+// left output is (mw, nw): alpha * acc + bias, written to the split that
+// owns each column, bf16 (or fp32).
+template <int MI, int NJ>
+__device__ __forceinline__ void store_tile(const GemmArgs& a, const v16f (&acc)[MI][NJ], int mw, int nw,
+                                           int lane) {
+  const float alpha = (*a.act_scale) * (*a.w_scale);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int n = nw + j * 32 + (lane & 31);
+    if (n >= a.N) continue;
+    uint8_t* base = reinterpret_cast<uint8_t*>(a.sp.ptr[0]);
+    int64_t ld = a.sp.ld[0];
+    int off0 = 0;
+#pragma unroll
+    for (int s = 1; s < FRT_MAX_SPLITS; ++s) {
+      if (s < a.sp.n && n >= a.sp.off[s]) {
+        base = reinterpret_cast<uint8_t*>(a.sp.ptr[s]);
+        ld = a.sp.ld[s];
+        off0 = a.sp.off[s];
+      }
+    }
+    const float b = a.bias != nullptr ? bf16f(a.bias[n]) : 0.0f;
+    const int col = n - off0;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = mw + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < a.M) {
+          const float v = alpha * acc[i][j][r] + b;
+          if (a.out_f32)
+            reinterpret_cast<float*>(base)[(int64_t)m * ld + col] = v;
+          else
+            reinterpret_cast<uint16_t*>(base)[(int64_t)m * ld + col] = (uint16_t)f2bf(v);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 64-deep-stage kernel with double-buffered operand fragments.
+//
+// Each stage holds a 64-byte K slice of every tile row (row-major, 64-byte
+// rows), the four 16-byte chunks of row r at positions c ^ ((r >> 2) & 3).
+// One direct buffer->LDS load instruction fills 16 consecutive rows (1 KiB,
+// lane L -> row L / 4, position L % 4, so it fetches global chunk
+// (L % 4) ^ ((L / 4 >> 2) & 3): rows 16u..16u+15 repeat the same pattern
+// for every u). A 32x32x64 operand read (row l % 32, K bytes
+// [(l / 32) * 32, +32) = chunks c0 = 2 (l / 32) and c0 + 1) reads positions
+// c0 ^ f and c0 ^ f ^ 1, f = (row >> 2) & 3; the sixteen lanes of one
+// ds_read_b128 pass (rows r..r+15, one chunk) land on sixteen distinct
+// 16-byte bank groups, so reads are conflict free.
+//
+// Per stage: issue the loads of the stage NS-1 ahead; wait until the next
+// stage has landed (later ones stay in flight) and the block has passed a
+// barrier; issue the fragment reads of the next stage into the idle register
+// set; then run this stage's MFMAs from the set read one stage earlier.
+// After the barrier a wave therefore never waits on LDS before its MFMAs,
+// and the loads of a stage have NS-1 stages of MFMA time to land.
+template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_k64_kernel(GemmArgs a) {
+  constexpr int WAVES_N = BN / WN;
+  constexpr int NW = (BM / WM) * WAVES_N;
+  constexpr int MI = WM / 32, NJ = WN / 32;
+  constexpr int ROWS = BM + BN;
+  constexpr int STAGE = ROWS * 64;
+  static_assert(ROWS % (16 * NW) == 0 && BM % 16 == 0, "loads must split evenly over the waves");
+  constexpr int LPW = ROWS / (16 * NW);  // load instructions per wave per stage
+  static_assert(NS >= 2 && NS % 2 == 0, "even ring depth (register set = stage parity)");
+  static_assert(LPW * (NS - 2) <= 63, "ring depth vs vmcnt range");
+  static_assert(NS * STAGE <= 160 * 1024, "ring exceeds LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const TileXY t = tile_of(blockIdx.x, tiles_m, tiles_n, GM);
+  const int m0 = t.tm * BM, n0 = t.tn * BN;
+  const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
+
+  const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + a.K);
+  const uint32_t w_bytes = (uint32_t)((int64_t)a.N * a.K);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, w_bytes);
+
+  // load j of this wave fills tile rows 16u..16u+15, u = wave + j * NW;
+  // rows past M (N) fall past the record count and read zeros
+  // (tile rows 0..BM-1 are A rows, BM.. are B rows: wave-uniform per load)
+  const int lrow = lane >> 2;
+  const int cch = (lane & 3) ^ ((lrow >> 2) & 3);
+  uint32_t off[LPW];
+  bool isA[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int r0 = (wave + j * NW) * 16;
+    isA[j] = r0 < BM;
+    off[j] = isA[j] ? (uint32_t)((int64_t)(m0 + r0 + lrow) * a.ld_x) + cch * 16
+                    : (uint32_t)((int64_t)(n0 + r0 - BM + lrow) * a.K) + cch * 16;
+  }
+  const int KT = (a.K + 63) / 64;
+  auto issue = [&](int kt, auto SLC) {
+    constexpr int SL = decltype(SLC)::value;
+    const int k0 = kt * 64;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      uint8_t* dst = smem + SL * STAGE + (wave + j * NW) * 1024;
+      const bool A = isA[j];
+      uint32_t o = off[j] + k0;
+      if constexpr (KTAIL) {
+        if (k0 + cch * 16 >= a.K) o = kOOB;
+      }
+      if (A)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
+    }
+  };
+  const int lrow32 = lane & 31;
+  const int f = (lrow32 >> 2) & 3;
+  const uint8_t* lbase = smem + lrow32 * 64 + ((((lane >> 5) * 2) ^ f) * 16);
+  const int d1 = (f & 1) ? -16 : 16;  // the second chunk sits at position ^ 1
+  auto read_frags = [&](auto SLC, v8i* af, v8i* bf) {
+    constexpr int SL = decltype(SLC)::value;
+    const uint8_t* lb = lbase + SL * STAGE;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const uint8_t* rowp = lb + (wm0 + i * 32) * 64;
+      const v4i lo = *reinterpret_cast<const v4i*>(rowp);
+      const v4i hi = *reinterpret_cast<const v4i*>(rowp + d1);
+      af[i] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const uint8_t* rowp = lb + (BM + wn0 + j * 32) * 64;
+      const v4i lo = *reinterpret_cast<const v4i*>(rowp);
+      const v4i hi = *reinterpret_cast<const v4i*>(rowp + d1);
+      bf[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  };
+  // own loads: at most `ahead` later stages in flight; every LDS read done;
+  // then the block barrier
+  auto sync_stage = [&](int ahead) {
+    __builtin_amdgcn_sched_barrier(0);
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((ahead == I ? (__builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * I)), 0) : 0), ...);
+    }(std::make_integer_sequence<int, NS - 1>{});
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  v16f acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  v8i fa[2][MI], fb[2][NJ];
+
+  auto stage = [&](int kt, auto SLC) {
+    constexpr int SL = decltype(SLC)::value;
+    constexpr int SET = SL & 1;
+    using PV = std::integral_constant<int, (SL + NS - 1) % NS>;
+    using NX = std::integral_constant<int, (SL + 1) % NS>;
+    if (kt + NS - 1 < KT) issue(kt + NS - 1, PV{});
+    if (kt + 1 < KT) {
+      sync_stage(min(KT - 2 - kt, NS - 2));
+      read_frags(NX{}, fa[SET ^ 1], fb[SET ^ 1]);
+    }
+#pragma unroll
+    for (int q = 0; q < MI * NJ; ++q) {
+      const int i = q / NJ, j = q % NJ;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[SET][i], fb[SET][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+  };
+  auto ring = [&](int kt0, auto... SLs) {
+    int kt = kt0;
+    ((kt < KT ? (stage(kt, SLs), ++kt) : 0), ...);
+  };
+
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((I < KT ? (issue(I, std::integral_constant<int, I>{}), 0) : 0), ...);
+  }(std::make_integer_sequence<int, NS - 1>{});
+  sync_stage(min(KT - 1, NS - 2));
+  read_frags(std::integral_constant<int, 0>{}, fa[0], fb[0]);
+  for (int kt = 0; kt < KT; kt += NS) {
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      ring(kt, std::integral_constant<int, S>{}...);
+    }(std::make_integer_sequence<int, NS>{});
+  }
+  store_tile<MI, NJ>(a, acc, m0 + wm0, n0 + wn0, lane);
+}
+
 // ------------------------------------------------------------------ launch
 
 // ---- split-K plan of the skinny kernel and its workspace ----------------
@@ -943,6 +1139,17 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WM, int WN, int NS, int GM>
+hipError_t launch_k64(const GemmArgs& a, hipStream_t st) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  constexpr int threads = (BM / WM) * (BN / WN) * 64;
+  if (a.K % 64 == 0)
+    hipLaunchKernelGGL((gemm_k64_kernel<BM, BN, WM, WN, NS, GM, false>), dim3(tiles), dim3(threads), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm_k64_kernel<BM, BN, WM, WN, NS, GM, true>), dim3(tiles), dim3(threads), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1>
 hipError_t launch_big_sk(const GemmArgs& a_in, const SkPlan& p, hipStream_t st) {
   GemmArgs a = a_in;
@@ -1012,6 +1219,21 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
       case 49: return launch_big<256, 128, 64, 64, 3, 4>(a, st);   // 8 waves, 144 KiB
       case 50: return launch_big<256, 128, 64, 32, 2, 4>(a, st);   // 16 waves, 96 KiB
       case 51: return launch_big<128, 256, 64, 64, 3, 2>(a, st);   // 8 waves, 144 KiB
+      case 52: return launch_big<256, 256, 128, 128, 2, 4>(a, st);  // 4 waves, 128 KiB
+      case 53: return launch_big<256, 128, 128, 64, 2, 4>(a, st);   // 4 waves, 96 KiB
+      case 54: return launch_big<256, 256, 64, 128, 2, 4>(a, st);   // 8 waves, 128 KiB
+      case 57: return launch_big<128, 256, 64, 64, 3, 2>(a, st);    // 8 waves, 144 KiB
+      case 58: return launch_big<256, 128, 64, 64, 3, 4>(a, st);    // 8 waves, 144 KiB
+      case 59: return launch_big<256, 128, 128, 64, 3, 4>(a, st);   // 4 waves, 144 KiB
+      case 70: return launch_k64<256, 256, 128, 64, 4, 4>(a, st);   // 8 waves, 128 KiB
+      case 71: return launch_k64<256, 256, 64, 128, 4, 4>(a, st);   // 8 waves, 128 KiB
+      case 72: return launch_k64<256, 128, 64, 64, 6, 4>(a, st);    // 8 waves, 144 KiB
+      case 73: return launch_k64<128, 256, 64, 64, 6, 2>(a, st);    // 8 waves, 144 KiB
+      case 74: return launch_k64<128, 128, 64, 32, 8, 2>(a, st);    // 8 waves, 128 KiB
+      case 75: return launch_k64<128, 128, 32, 32, 8, 2>(a, st);    // 16 waves, 128 KiB
+      case 76: return launch_k64<64, 64, 32, 32, 8, 1>(a, st);      // 4 waves, 64 KiB
+      case 77: return launch_k64<64, 32, 32, 32, 8, 1>(a, st);      // 2 waves, 48 KiB
+      case 78: return launch_k64<256, 256, 128, 64, 2, 4>(a, st);   // 8 waves, 64 KiB
       default: break;
     }
   }
