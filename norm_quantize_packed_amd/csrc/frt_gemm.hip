@@ -27,6 +27,7 @@
 // the logical tile index gives each XCD a contiguous run of tiles, and runs
 // are rastered in groups of GM tile-rows so that the tiles resident on one
 // XCD share A and B panels in that XCD's L2.
+#include <algorithm>
 #include <cstdlib>
 #include <type_traits>
 
@@ -331,7 +332,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
   const int lane = threadIdx.x & 63;
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = (a.N + BN - 1) / BN;
-  const TileXY t = tile_of(blockIdx.x, tiles_m, tiles_n, GM);
+  // split-K decomposition: blocks [0, n_full) own whole tiles; each of the
+  // remaining tiles is split along K over nsplit consecutive blocks
+  int tile_id = blockIdx.x, zsplit = 0, S_eff = 1, tail = 0;
+  if constexpr (SK) {
+    if ((int)blockIdx.x >= a.n_full) {
+      const int q = blockIdx.x - a.n_full;
+      tail = q / a.nsplit;
+      zsplit = q % a.nsplit;
+      S_eff = a.nsplit;
+      tile_id = a.n_full + tail;
+    }
+  }
+  const TileXY t = tile_of(tile_id, tiles_m, tiles_n, GM);
   const int m0 = t.tm * BM, n0 = t.tn * BN;
   const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
 
@@ -354,8 +367,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
   const int cch = (lane & 7) ^ (((wave & 1) << 2) | (lrow >> 1));
   // split-K: this block covers K bytes [kb, kb + kc) (kc a multiple of
   // KST; the planner leaves no split empty)
-  const int kb = SK ? (int)blockIdx.y * a.kc : 0;
-  const int klen = SK ? min(a.kc, a.K - kb) : a.K;
+  const int kb = S_eff > 1 ? zsplit * a.kc : 0;
+  const int klen = S_eff > 1 ? min(a.kc, a.K - kb) : a.K;
   const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + kb + cch * 16;
   const uint32_t offB = (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + kb + cch * 16;
   const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
@@ -511,7 +524,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
       for (int j = 0; j < NJ; ++j) acc[i][j] += acc2[i][j];
   }
 
-  if constexpr (SK) {
+  if (SK && S_eff > 1) {
     // Split-K: every split stores its fp32 partial tile in fragment order
     // (lane-contiguous 16-byte groups, so each store instruction writes one
     // contiguous KiB) with agent-coherent stores, then bumps the tile's
@@ -521,13 +534,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
     __shared__ int last_flag;
     constexpr int FR = MI * NJ * 4;        // 16-byte groups per lane
     constexpr int TILE_B = BM * BN * 4;    // bytes per partial tile
-    const int S = a.nsplit;
+    const int S = S_eff;
+    const int n_tail = tiles_m * tiles_n - a.n_full;
     const uint32_t wave_off = (uint32_t)wave * (FR * 1024) + lane * 16;
-    const uint32_t plane = (uint32_t)gridDim.x * TILE_B;
+    const uint32_t plane = (uint32_t)n_tail * TILE_B;
     const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.ws, plane * (uint32_t)S);
-    const uint32_t tile_off = (uint32_t)blockIdx.x * TILE_B + wave_off;
+    const uint32_t tile_off = (uint32_t)tail * TILE_B + wave_off;
     {
-      const uint32_t o = blockIdx.y * plane + tile_off;
+      const uint32_t o = (uint32_t)zsplit * plane + tile_off;
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -542,7 +556,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
     __builtin_amdgcn_s_waitcnt(0);  // partial stores performed at agent scope
     __syncthreads();
     if (threadIdx.x == 0) {
-      unsigned* c = a.cnt + blockIdx.x;
+      unsigned* c = a.cnt + tail;
       const unsigned prev = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_flag = prev == (unsigned)(S - 1);
       if (last_flag) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -555,27 +569,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_big_kernel(Ge
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-    for (int z = 0; z < S; ++z) {
-      const uint32_t o = (uint32_t)z * plane + tile_off;
-      v4i part[MI][NJ][4];
+    // one accumulator row-block (NJ tiles) at a time, splits in order
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      for (int z = 0; z < S; ++z) {
+        const uint32_t o = (uint32_t)z * plane + tile_off;
+        v4i part[NJ][4];
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g)
-            part[i][j][g] = __builtin_amdgcn_raw_buffer_load_b128(pr, o + ((i * NJ + j) * 4 + g) * 1024, 0,
-                                                                  kCoherent);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
+            part[j][g] = __builtin_amdgcn_raw_buffer_load_b128(pr, o + ((i * NJ + j) * 4 + g) * 1024, 0, kCoherent);
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const v4f v = __builtin_bit_cast(v4f, part[i][j][g]);
+            const v4f v = __builtin_bit_cast(v4f, part[j][g]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[i][j][4 * g + e] += v[e];
           }
+      }
     }
   }
 
@@ -858,7 +871,29 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_k64_kernel(Ge
   static_assert(NS >= 2 && NS % 2 == 0, "even ring depth (register set = stage parity)");
   static_assert(LPW * (NS - 2) <= 63, "ring depth vs vmcnt range");
   static_assert(NS * STAGE <= 160 * 1024, "ring exceeds LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  // one LDS array per ring slot: the compiler can then tell the direct
+  // loads into one slot from the fragment reads of another, and does not
+  // make the reads wait for loads still in flight to other slots
+  static_assert(NS <= 8, "ring depth");
+  __shared__ __attribute__((aligned(1024))) uint8_t sm0[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm1[STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm2[NS > 2 ? STAGE : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm3[NS > 3 ? STAGE : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm4[NS > 4 ? STAGE : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm5[NS > 5 ? STAGE : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm6[NS > 6 ? STAGE : 1];
+  __shared__ __attribute__((aligned(1024))) uint8_t sm7[NS > 7 ? STAGE : 1];
+  auto slot = [&](auto SLC) -> uint8_t* {
+    constexpr int SL = decltype(SLC)::value;
+    if constexpr (SL == 0) return sm0;
+    else if constexpr (SL == 1) return sm1;
+    else if constexpr (SL == 2) return sm2;
+    else if constexpr (SL == 3) return sm3;
+    else if constexpr (SL == 4) return sm4;
+    else if constexpr (SL == 5) return sm5;
+    else if constexpr (SL == 6) return sm6;
+    else return sm7;
+  };
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -889,11 +924,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_k64_kernel(Ge
   }
   const int KT = (a.K + 63) / 64;
   auto issue = [&](int kt, auto SLC) {
-    constexpr int SL = decltype(SLC)::value;
     const int k0 = kt * 64;
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
-      uint8_t* dst = smem + SL * STAGE + (wave + j * NW) * 1024;
+      uint8_t* dst = slot(SLC) + (wave + j * NW) * 1024;
       const bool A = isA[j];
       uint32_t o = off[j] + k0;
       if constexpr (KTAIL) {
@@ -907,11 +941,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_k64_kernel(Ge
   };
   const int lrow32 = lane & 31;
   const int f = (lrow32 >> 2) & 3;
-  const uint8_t* lbase = smem + lrow32 * 64 + ((((lane >> 5) * 2) ^ f) * 16);
+  const int lofs = lrow32 * 64 + ((((lane >> 5) * 2) ^ f) * 16);
   const int d1 = (f & 1) ? -16 : 16;  // the second chunk sits at position ^ 1
   auto read_frags = [&](auto SLC, v8i* af, v8i* bf) {
-    constexpr int SL = decltype(SLC)::value;
-    const uint8_t* lb = lbase + SL * STAGE;
+    const uint8_t* lb = slot(SLC) + lofs;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const uint8_t* rowp = lb + (wm0 + i * 32) * 64;
@@ -967,13 +1000,40 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_k64_kernel(Ge
     int kt = kt0;
     ((kt < KT ? (stage(kt, SLs), ++kt) : 0), ...);
   };
+  // steady state: every stage issues a load and keeps NS-2 later stages in
+  // flight, so the wait depth is a constant and the code is branch free
+  // (the compiler then knows the previous stage's fragment reads are done
+  // and does not make the MFMAs wait for the reads just issued)
+  auto steady = [&](int kt, auto SLC) {
+    constexpr int SL = decltype(SLC)::value;
+    constexpr int SET = SL & 1;
+    using PV = std::integral_constant<int, (SL + NS - 1) % NS>;
+    using NX = std::integral_constant<int, (SL + 1) % NS>;
+    issue(kt + NS - 1, PV{});
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(LPW * (NS - 2)));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(NX{}, fa[SET ^ 1], fb[SET ^ 1]);
+#pragma unroll
+    for (int q = 0; q < MI * NJ; ++q) {
+      const int i = q / NJ, j = q % NJ;
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[SET][i], fb[SET][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+  };
 
   [&]<int... I>(std::integer_sequence<int, I...>) {
     ((I < KT ? (issue(I, std::integral_constant<int, I>{}), 0) : 0), ...);
   }(std::make_integer_sequence<int, NS - 1>{});
   sync_stage(min(KT - 1, NS - 2));
   read_frags(std::integral_constant<int, 0>{}, fa[0], fb[0]);
-  for (int kt = 0; kt < KT; kt += NS) {
+  int kt = 0;
+  for (; kt + 2 * NS - 2 < KT; kt += NS) {
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+      (steady(kt + S, std::integral_constant<int, S>{}), ...);
+    }(std::make_integer_sequence<int, NS>{});
+  }
+  for (; kt < KT; kt += NS) {
     [&]<int... S>(std::integer_sequence<int, S...>) {
       ring(kt, std::integral_constant<int, S>{}...);
     }(std::make_integer_sequence<int, NS>{});
@@ -1026,14 +1086,28 @@ bool use_skinny(int64_t M, int64_t N) {
 }
 
 // ---- split-K plans of the tiled kernel ----------------------------------
-// Workspace = the 64 KiB counter region followed by S partial planes of
-// `tiles` fp32 tiles each.
+// Tiles [0, n_full) run whole; each of the remaining tiles is split S ways
+// along K (S consecutive blocks). Workspace = the 64 KiB counter region
+// followed by S partial planes of (tiles - n_full) fp32 tiles each.
 struct SkPlan {
   int bm, bn, kst;  // tile and K bytes per pipeline stage
-  int S, kc, tiles;
+  int S, kc, tiles, n_full;
 };
 
-// split-K configurations selectable for exploration
+// compute units of the current device (the plan fills whole rounds of them)
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// split-K configurations selectable for exploration (every tile split)
 bool sk_config(int variant, SkPlan& p) {
   switch (variant) {
     case 60: p.bm = 64; p.bn = 64; p.kst = 128; return true;
@@ -1046,31 +1120,60 @@ bool sk_config(int variant, SkPlan& p) {
   }
 }
 
-// S splits requested; each split gets a whole number of stages and none is
-// empty
-void sk_finish(SkPlan& p, int64_t M, int64_t N, int64_t K, int S_req) {
+// S splits requested for the tail tiles; each split gets a whole number of
+// stages and none is empty
+void sk_finish(SkPlan& p, int64_t M, int64_t N, int64_t K, int S_req, int n_full) {
   const int kt = (int)((K + p.kst - 1) / p.kst);
   int S = std::max(1, std::min(S_req, kt));
   const int per = (kt + S - 1) / S;
   p.S = (kt + per - 1) / per;
   p.kc = per * p.kst;
   p.tiles = (int)(((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn));
+  p.n_full = std::min(n_full, p.tiles);
+}
+
+bool sk_valid(const SkPlan& p) {
+  const int64_t n_tail = p.tiles - p.n_full;
+  return p.S > 1 && n_tail > 0 && n_tail <= kCounterBytes / 4 &&
+         (int64_t)p.S * n_tail * p.bm * p.bn * 4 < ((int64_t)1 << 31);
+}
+
+// Tail plan for the large tile (256 x 256): split only the tiles of a last,
+// partial round over the chip, e.g. 1152 tiles on 256 CUs run 1024 whole
+// and split the other 128 in two.
+bool tail_plan(int64_t M, int64_t N, int64_t K, SkPlan& p) {
+  p.bm = 256; p.bn = 256; p.kst = 128;
+  const int64_t T = ((M + 255) / 256) * ((N + 255) / 256);
+  const int cus = device_cus();
+  if (T < cus) return false;
+  const int64_t n_full = (T / cus) * cus, n_tail = T - n_full;
+  if (n_tail == 0 || 2 * n_tail > cus) return false;  // a tail of more than half a round runs fine whole
+  const int S = (int)std::min<int64_t>(4, cus / n_tail);
+  if ((K + 127) / 128 < 4 * S) return false;  // keep at least 4 stages per split
+  sk_finish(p, M, N, K, S, (int)n_full);
+  return sk_valid(p);
 }
 
 bool sk_plan(int64_t M, int64_t N, int64_t K, SkPlan& p) {
-  if (!sk_config(gemm_variant(), p)) return false;
-  static const int S_env = [] {
-    const char* e = getenv("FRT_GEMM_SPLITK");
-    return e ? atoi(e) : 2;
-  }();
-  sk_finish(p, M, N, K, S_env);
-  return p.S > 1 && p.tiles <= kCounterBytes / 4 &&
-         (int64_t)p.S * p.tiles * p.bm * p.bn * 4 < ((int64_t)1 << 31);
+  if (sk_config(gemm_variant(), p)) {
+    static const int S_env = [] {
+      const char* e = getenv("FRT_GEMM_SPLITK");
+      return e ? atoi(e) : 2;
+    }();
+    sk_finish(p, M, N, K, S_env, 0);
+    return sk_valid(p);
+  }
+  // selectable only: measured slower than running the partial round whole
+  // (8192 x 9216 x 3072: 246 -> 278 us; the split tiles' partial traffic
+  // runs at the per-CU fill rate and their blocks lose L2 locality)
+  if (gemm_variant() == 66 && M >= 512) return tail_plan(M, N, K, p);
+  return false;
 }
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   SkPlan q{};
-  if (sk_plan(M, N, K, q)) return (size_t)(kCounterBytes + (int64_t)q.S * q.tiles * q.bm * q.bn * 4);
+  if (sk_plan(M, N, K, q))
+    return (size_t)(kCounterBytes + (int64_t)q.S * (q.tiles - q.n_full) * q.bm * q.bn * 4);
   if (!use_skinny(M, N)) return 0;
   const SkinnyPlan p = skinny_plan(M, N, K);
   if (p.splits <= 1) return 0;
@@ -1157,8 +1260,9 @@ hipError_t launch_big_sk(const GemmArgs& a_in, const SkPlan& p, hipStream_t st) 
   a.ws = reinterpret_cast<uint8_t*>(a_in.ws) + kCounterBytes;
   a.kc = p.kc;
   a.nsplit = p.S;
+  a.n_full = p.n_full;
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  const dim3 grid((unsigned)p.tiles, (unsigned)p.S);
+  const dim3 grid((unsigned)(p.n_full + (p.tiles - p.n_full) * p.S));
   if (a.K % (128 * NSUB) == 0)
     hipLaunchKernelGGL((gemm_big_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, true>), grid, dim3(threads), 0, st, a);
   else
@@ -1179,7 +1283,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
       case 63: return launch_big_sk<32, 64, 32, 32, 4, 1>(a, sk, st);
       case 64: return launch_big_sk<64, 32, 32, 32, 6, 1>(a, sk, st);
       case 65: return launch_big_sk<64, 64, 32, 32, 3, 1, 2>(a, sk, st);
-      default: break;
+      default: return launch_big_sk<256, 256, 128, 64, 2, 4>(a, sk, st);  // tail plan
     }
   }
   if (variant >= 10 && variant < 60) {  // tile-shape exploration

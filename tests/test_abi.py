@@ -145,8 +145,9 @@ def test_gemm_zero_rows_and_workspace_query(lib):
         assert _gemm(lib, ws_bytes=need - 1) == frt.FRT_E_INVALID
         assert "workspace" in frt.frt_last_error()
         assert _gemm(lib, ws=None, ws_bytes=0) == frt.FRT_E_INVALID
-    # large-M shapes need no workspace
-    assert frt.frt_packed_gemm_fp8_workspace_size(4096, 9216, 3072) == 0
+    # the default plans need no workspace
+    for shape in [(2048, 32768, 16384), (4096, 9216, 3072), (64, 6144, 4096)]:
+        assert frt.frt_packed_gemm_fp8_workspace_size(*shape) == 0
 
 
 def test_pack_refusals(lib):

@@ -214,3 +214,25 @@ def test_gemm_split_k_repeatable_across_calls_and_shapes():
                 first[(M, N, K)] = out
             else:
                 assert np.array_equal(out, first[(M, N, K)]), f"{M}x{N}x{K} rep {rep}"
+
+
+@pytest.mark.parametrize("K", [1024, 1040])
+def test_gemm_large_full_grid(K):
+    """Large-M plan at a shape with a partial last round (4096 x 6144: 384
+    tiles of 256 x 256 on 256 CUs). Every output is checked (fp32 out), with
+    a ragged K, and repeated calls are bit-identical."""
+    M, N = 4096, 6144
+    x8 = wl.random_codes(777 + K, (M, K))
+    w8 = wl.random_codes(778 + K, (N, K))
+    splits = [4096, 2048]
+    ref = np.concatenate(gemm.packed_gemm_split(
+        x8, w8, np.float32(0.01), np.float32(0.002), None, splits), 1)
+    first = None
+    for rep in range(2):
+        out = np.concatenate(_gpu_gemm(x8, w8, np.float32(0.01), np.float32(0.002),
+                                       None, splits, f32=True), 1)
+        if first is None:
+            assert_gemm_f32(out, ref, f"{M}x{N}x{K}")
+            first = out
+        else:
+            assert np.array_equal(out, first), f"{M}x{N}x{K} rep {rep}"
