@@ -150,6 +150,8 @@ def build_sets(wid, rows, frt, torch):
         W8 = torch.empty(N, D, dtype=torch.uint8, device="cuda")
         wsc = torch.empty(1, dtype=torch.float32, device="cuda")
         bc = torch.empty(N, dtype=torch.bfloat16, device="cuda") if w.bias else None
+        # the first call also loads the packer's kernels: time a second one
+        frt.frt_pack_weights_fp8(Ws, bs if w.bias else None, W8, wsc, bc)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()

@@ -4,7 +4,7 @@
 // Four stream-ordered launches, no workspace:
 //   1. prep   : w_scale <- +0 (it accumulates max|W| as float bits while
 //               the call runs) and bias_cat <- concat(b_i or zeros)
-//   2. amax   : per sibling, wave max of |w| bits -> atomicMax on w_scale
+//   2. amax   : per sibling, block max of |w| bits -> atomicMax on w_scale
 //   3. cast   : per sibling, codes = e4m3(clamp(fl32(w / s))), with
 //               s = max(fl32(amax / 448), 1e-8) derived from w_scale's bits
 //   4. final  : w_scale <- s
@@ -32,33 +32,51 @@ __global__ __launch_bounds__(kThreads) void pack_prep_kernel(
   if (bias_cat != nullptr && t < n) bias_cat[off + t] = (b != nullptr) ? b[t] : (uint16_t)0;
 }
 
-// Each thread folds 8 elements per step when the sibling is 16-byte
-// aligned and a multiple of 8 long, else one element per step.
+// |bf16| bit patterns of a word's two halves, widened to fp32 bit order
+__device__ __forceinline__ uint32_t absmax2(uint32_t w) {
+  return max((w & 0x7fffu) << 16, w & 0x7fff0000u);
+}
+
+// Each thread folds 8 elements per load when the sibling is 16-byte aligned
+// and a multiple of 8 long (four independent loads per step), else one
+// element per step. The block's four wave maxima meet in LDS; one thread
+// then raises w_scale, skipping the atomic when the agent-coherent value is
+// already at least as large (most blocks, once the first ones have run).
 template <bool V8>
 __global__ __launch_bounds__(kThreads) void pack_amax_kernel(const uint16_t* w, int64_t elems,
                                                               float* w_scale) {
+  __shared__ uint32_t red[kThreads / 64];
   const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t t0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   uint32_t m = 0;
   if constexpr (V8) {
     const uint4* w4 = reinterpret_cast<const uint4*>(w);
     const int64_t n4 = elems / 8;
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
-      const uint4 t = w4[i];
-      const uint32_t ws[4] = {t.x, t.y, t.z, t.w};
+    int64_t i = t0;
+    for (; i + 3 * stride < n4; i += 4 * stride) {
+      uint4 t[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        // |bf16| as fp32 bits: clear the sign, widen to the high half-word
-        const uint32_t lo = (ws[k] & 0x7fffu) << 16;
-        const uint32_t hi = ws[k] & 0x7fff0000u;
-        m = max(m, max(lo, hi));
-      }
+      for (int u = 0; u < 4; ++u) t[u] = w4[i + u * stride];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        m = max(m, max(max(absmax2(t[u].x), absmax2(t[u].y)), max(absmax2(t[u].z), absmax2(t[u].w))));
+    }
+    for (; i < n4; i += stride) {
+      const uint4 t = w4[i];
+      m = max(m, max(max(absmax2(t.x), absmax2(t.y)), max(absmax2(t.z), absmax2(t.w))));
     }
   } else {
-    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < elems; i += stride)
-      m = max(m, (uint32_t)(w[i] & 0x7fffu) << 16);
+    for (int64_t i = t0; i < elems; i += stride) m = max(m, (uint32_t)(w[i] & 0x7fffu) << 16);
   }
   m = wave_umax(m);
-  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(w_scale), m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int k = 1; k < kThreads / 64; ++k) m = max(m, red[k]);
+    unsigned int* p = reinterpret_cast<unsigned int*>(w_scale);
+    if (m > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, m);
+  }
 }
 
 template <bool V8>
@@ -98,9 +116,9 @@ __global__ void pack_final_kernel(float* w_scale) {
     *w_scale = pack_scale_from_amax(*reinterpret_cast<const uint32_t*>(w_scale));
 }
 
-unsigned grid_for(int64_t work) {
+unsigned grid_for(int64_t work, int64_t cap = 4096) {
   int64_t g = (work + kThreads - 1) / kThreads;
-  if (g > 4096) g = 4096;  // grid-stride beyond ~16 blocks per CU
+  if (g > cap) g = cap;  // grid-stride beyond the cap
   if (g < 1) g = 1;
   return (unsigned)g;
 }
@@ -119,10 +137,10 @@ hipError_t launch_pack(const PackSib* sibs, int n_sib, int64_t K, uint8_t* w8, f
     const PackSib& p = sibs[i];
     const bool v8 = (p.elems % 8 == 0) && ((uintptr_t)p.w % 16 == 0);
     if (v8)
-      hipLaunchKernelGGL(pack_amax_kernel<true>, dim3(grid_for(p.elems / 8)), dim3(kThreads), 0, st,
+      hipLaunchKernelGGL(pack_amax_kernel<true>, dim3(grid_for(p.elems / 8, 1024)), dim3(kThreads), 0, st,
                          p.w, p.elems, w_scale);
     else
-      hipLaunchKernelGGL(pack_amax_kernel<false>, dim3(grid_for(p.elems)), dim3(kThreads), 0, st, p.w,
+      hipLaunchKernelGGL(pack_amax_kernel<false>, dim3(grid_for(p.elems, 1024)), dim3(kThreads), 0, st, p.w,
                          p.elems, w_scale);
   }
   for (int i = 0; i < n_sib; ++i) {
