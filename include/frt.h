@@ -185,9 +185,12 @@ int frt_pack_weights_fp8(void* stream, int n_sib, const int64_t* N_i,
                          float* w_scale, uint16_t* bias_cat);
 
 /*
- * Workspace bytes frt_packed_gemm_fp8_split needs for this shape (0 when
- * the chosen kernel needs none). The workspace must be zero-filled once
- * before its first use; every call leaves it zero-filled again.
+ * Workspace bytes frt_packed_gemm_fp8_split needs for this shape on the
+ * current device. The present tile plans need none, so this returns 0 for
+ * every shape; callers that query it and pass a workspace of at least this
+ * size stay correct if a later plan needs one (such a workspace would have
+ * to be zero-filled once before first use and be left zero-filled by every
+ * call; calls sharing one must not overlap).
  */
 size_t frt_packed_gemm_fp8_workspace_size(int64_t M, int64_t N_total,
                                           int64_t K);
@@ -223,8 +226,9 @@ size_t frt_packed_gemm_fp8_workspace_size(int64_t M, int64_t N_total,
  *                 other or the inputs. 4-byte aligned (bf16: ld even).
  *   ld_out  [host] int64 [n_split].
  *   out_dtype     0 = bf16, 1 = fp32 (parity / diagnostics).
- *   workspace, ws_bytes   see frt_packed_gemm_fp8_workspace_size; NULL/0
- *                 allowed when the size is 0.
+ *   workspace, ws_bytes   at least frt_packed_gemm_fp8_workspace_size
+ *                 bytes (NULL/0 allowed when that is 0, as it is for every
+ *                 shape today); a smaller one is refused before any launch.
  */
 int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K,
                               const uint8_t* x8, int64_t ld_x,

@@ -313,7 +313,6 @@ int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K, const uint8_t*
   a.N = (int)N_total;
   a.K = (int)K;
   a.out_f32 = out_dtype;
-  a.ws = workspace;
   return hip_status(frt::launch_gemm(a, (hipStream_t)stream), "gemm launch");
 }
 

@@ -64,11 +64,6 @@ struct GemmArgs {
   int M, N, K;
   int out_f32;
   SplitTab sp;
-  void* ws;       // split-K partial planes, or null
-  unsigned* cnt;  // split-K per-tile arrival counters (zero at rest)
-  int kc;         // split-K: K bytes per split (the launcher sets it)
-  int nsplit;     // split-K: number of K splits of each split tile
-  int n_full;     // split-K: tiles [0, n_full) are not split
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
