@@ -498,9 +498,10 @@ def main():
         copy_kernel(torch, a.launches)
         return
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {a.gpus} is not "
-              "supported (the path shards by rows/heads with no exchange; see "
-              "DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: the path runs on one GPU; --gpus {a.gpus} is not "
+              "supported (its producers and GEMMs shard by rows or heads with "
+              "no exchange on the forward path, so one GPU's shard is what is "
+              "measured)", file=sys.stderr)
         sys.exit(2)
     import torch
     import norm_quantize_packed_amd as frt

@@ -1,7 +1,7 @@
 """Build ``libfrt.so`` (the HIP kernels and the C ABI) for gfx950 in-tree.
 
 Usage: ``python -m norm_quantize_packed_amd._build`` (or ``build()`` from
-``__graft_entry__``). hipcc cross-compiles without a GPU.
+the repository's entry module). hipcc cross-compiles without a GPU.
 """
 
 from __future__ import annotations

@@ -17,7 +17,7 @@ a K-term sum stays below 2^53 for K <= 2^17: the fp64 matmul of the integer
 code values is therefore exact, whatever its summation order. The GEMM is
 the plain definition; there is no other rounding until the epilogue.
 
-Reading (listed in the design doc): the fused bias entry rounds once, so the
+Reading where the pages are silent: the fused bias entry rounds once, so the
 reference output is ``alpha * acc + bias`` formed in float64 (relative error
 at most 2^-52, far below either output format's rounding) and rounded once
 to the output type (bf16 by round-to-nearest-even); ``alpha`` is

@@ -21,7 +21,7 @@ Sources (flashrt-structures 0.2.0 wheel pages):
   (fp8_chain.py ``_quantize`` and the probe's forward pre-hooks); a site
   whose amax is not positive is refused.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 - the norm runs on the fp32 gated residual, not on its bf16 rounding;
 - the gated residual multiplies ``x`` by the *previous* site's gate (an
   input), and this row's gate chunk is only echoed to ``gate_out``;

@@ -12,7 +12,8 @@ Comparison rules (the tolerances of the path, applied element by element):
 - GEMM from identical FP8 operands: fp32 outputs within 1e-3 * max|ref| of
   the exact oracle; bf16 outputs within one bf16 ulp plus that tolerance.
   (The matrix cores' fp32 accumulation is not exact: on random codes that
-  span the whole e4m3 range it reaches ~1e-4 * max|ref|.)
+  span the whole e4m3 range it reaches ~1e-4 * max|ref|, an order of
+  magnitude inside the bound.)
 """
 
 from __future__ import annotations
