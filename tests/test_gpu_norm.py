@@ -141,7 +141,7 @@ def test_ada_chained_sites_workload2():
     assert_codes_close(host_u8(o2), r2["codes"], "site 2")
 
 
-@pytest.mark.parametrize("D", [512, 514, 1000, 2050, 16384])
+@pytest.mark.parametrize("D", [512, 514, 1000, 2048, 2050, 3072, 16384])
 def test_ada_edges(D):
     """Vector (D % 8 == 0) and 4-byte paths, strided rows, per-row mod,
     a norm weight, in-place residual, both envelope ends."""

@@ -130,7 +130,11 @@ def _operands(cid, site, M=None, seed=0):
 
 @pytest.mark.parametrize("cid,site,M", [(1, 0, 16), (2, 0, 256), (2, 1, 256),
                                         (3, 0, 600), (4, 0, 64), (4, 0, 1),
-                                        (4, 0, 17), (5, 0, 40)])
+                                        (4, 0, 17), (5, 0, 40),
+                                        # tile-plan boundaries: M = 65 leaves
+                                        # the small-M plan, 511 is the last
+                                        # mid-M size (ragged in M)
+                                        (4, 0, 65), (2, 1, 511)])
 def test_gemm_workload(cid, site, M):
     x8, w8, s_a, s_w, bias, splits = _operands(cid, site, M)
     _check_gemm(x8, w8, s_a, s_w, bias, splits, f"workload {cid}/{site} M={M}")
