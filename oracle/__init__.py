@@ -17,6 +17,8 @@ Modules:
              per-tensor FP8 quantisation, calibration scale
   pack       joint-scale sibling weight packing
   gemm       exact packed FP8 GEMM, dequant + bias epilogue, column split
+  ffn        tanh-GELU GEGLU of the merged gate/up output + static FP8,
+             and the merged gate/up GEMM -> GEGLU chain
 
 Parity status: every function is pinned by the ``-m "not gpu"`` tests in
 tests/test_oracle_*.py (closed forms, brute force, independent torch CPU
@@ -31,6 +33,7 @@ from .producers import (gated_residual, ada_rms_norm, ada_norm_quant_fp8,
 from .pack import pack_weights
 from .gemm import (gemm_exact, gemm_exact_at, epilogue, packed_gemm_split,
                    split_columns)
+from .ffn import gelu_tanh, geglu, geglu_quant_fp8, gate_up_gelu_quant
 
 __all__ = [
     "bf16_to_f32", "f32_to_bf16", "e4m3_decode", "e4m3_encode",
@@ -39,4 +42,5 @@ __all__ = [
     "ptok_layer_norm", "ptok_norm_quant_fp8", "quantize_static",
     "calibrate_act_scale", "pack_weights", "gemm_exact", "gemm_exact_at",
     "epilogue", "packed_gemm_split", "split_columns",
+    "gelu_tanh", "geglu", "geglu_quant_fp8", "gate_up_gelu_quant",
 ]

@@ -205,6 +205,20 @@ def weights(cid: int, site: int = 0) -> dict:
     return {"W": Ws, "b": bs, "splits": widths}
 
 
+# The FFN tail after a gate/up GEMM (workloads 2 and 5): the down
+# projection [D, H] that consumes the GEGLU output, drawn like the
+# workload's other weights (bias-free).
+FFN_HIDDEN: Dict[int, int] = {2: 8192, 5: 16384}
+
+
+def down_weights(cid: int) -> np.ndarray:
+    """Down-projection weight of workload ``cid`` as bf16 bits ``[D, H]``
+    (checkpoint layout, H contiguous)."""
+    w = WORKLOADS[cid]
+    H = FFN_HIDDEN[cid]
+    return normal_bf16(3000 + cid, 50, (w.D, H), w.w_std)
+
+
 def random_bf16(seed: int, shape, std: float = 1.0) -> np.ndarray:
     """Free-form helper for edge-case tests."""
     return normal_bf16(seed, 7, shape, std)
