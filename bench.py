@@ -19,6 +19,12 @@ graph replays of that kernel alone on the launch stream (same rotation).
 
 Output: one JSON line on stdout (metric, value, roofline of the dominant
 kernel, the CPU oracle's throughput on a bounded sample, per-kernel table).
+
+``--ffn`` (workloads 2 and 5) appends the FFN tail that follows the gate/up
+projection: the gate/up GEMM runs with the GEGLU quantiser as its epilogue
+(FP8 codes out instead of the bf16 gate|up output) and the down projection
+consumes those codes. The unfused pair (bf16 gate/up GEMM, standalone GEGLU
+quantiser) is timed beside it for comparison but is not part of the step.
 """
 
 from __future__ import annotations
@@ -52,6 +58,9 @@ def parse():
     p.add_argument("--rows", type=int, default=None,
                    help="override the producer row count (e.g. the small-M sweep)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--ffn", action="store_true",
+                   help="workloads 2 and 5: fuse GEGLU + FP8 into the gate/up "
+                        "GEMM and append the down projection")
     p.add_argument("--kernel-reps", type=int, default=20)
     p.add_argument("--hbm-calibration", action="store_true",
                    help="time a plain device copy of known size (HBM ceiling, "
@@ -164,12 +173,51 @@ def build_sets(wid, rows, frt, torch):
     return w, dev, act, packs, pack_ms
 
 
-def make_rotation(w, dev, packs, rows, torch):
+def build_ffn(w, rows, act, packs, frt, torch):
+    """The FFN tail's bind: pack the down projection and calibrate the
+    GEGLU output scale on the calibration batch (its producer codes through
+    the bf16 gate/up GEMM and the standalone quantiser's amax)."""
+    import workloads as wl
+    H = wl.FFN_HIDDEN[w.cid]
+    Wd = bf16_dev(wl.down_weights(w.cid))
+    Wd8 = torch.empty(w.D, H, dtype=torch.uint8, device="cuda")
+    wsd = torch.empty(1, dtype=torch.float32, device="cuda")
+    frt.frt_pack_weights_fp8([Wd], None, Wd8, wsd)
+    del Wd
+    cal = wl.producer_inputs(w.cid, calib=True, rows=rows)
+    x8 = torch.empty(rows, w.D, dtype=torch.uint8, device="cuda")
+    if w.form == "adarms":
+        D = w.D
+        rout = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
+        cm = bf16_dev(cal["mod"])
+        frt.frt_ada_norm_quant_fp8(bf16_dev(cal["residual"]), cm, None, x=bf16_dev(cal["x"]),
+                                   gate=bf16_dev(cal["gate"]), eps=wl.EPS, residual_out=rout)
+        frt.frt_ada_norm_quant_fp8(rout, bf16_dev(cal["mod2"]), act[1], x=bf16_dev(cal["x2"]),
+                                   gate=cm[0, 2 * D:3 * D], eps=wl.EPS, out_fp8=x8)
+    else:
+        frt.frt_ptok_table_norm_quant_fp8(
+            bf16_dev(cal["x"]), bf16_dev(cal["temb"].reshape(rows, -1)),
+            torch.from_numpy(cal["table"]).cuda(), act[0], cal["shift_idx"],
+            cal["scale_idx"], eps=wl.EPS, out_fp8=x8)
+    p = packs[-1]
+    gu = torch.empty(rows, 2 * H, dtype=torch.bfloat16, device="cuda")
+    frt.frt_packed_gemm_fp8_split(x8, p["W8"], act[-1], p["ws"], [gu], [2 * H])
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    frt.frt_geglu_quant_fp8(gu, H, None, amax_out=amax)
+    torch.cuda.synchronize()
+    s_h = np.float32(amax.item()) / np.float32(448.0)
+    return {"H": H, "W8": Wd8, "ws": wsd,
+            "scale": torch.tensor([float(s_h)], dtype=torch.float32, device="cuda")}
+
+
+def make_rotation(w, dev, packs, rows, torch, ffn=None):
     """Copies of activations and weights so one pass over the sets moves at
     least ROTATE_BYTES."""
     per = sum(t.numel() * t.element_size() for t in dev.values()
               if t.dim() > 1 and t.shape[0] == rows)
     per += sum(p["W8"].numel() for p in packs)
+    if ffn is not None:
+        per += ffn["W8"].numel()
     n = max(1, math.ceil(ROTATE_BYTES / max(per, 1)))
     sets = []
     for i in range(n):
@@ -182,11 +230,15 @@ def make_rotation(w, dev, packs, rows, torch):
             if i > 0:
                 q["W8"] = p["W8"].clone()
             s["packs"].append(q)
+        if ffn is not None:
+            s["ffn"] = dict(ffn)
+            if i > 0:
+                s["ffn"]["W8"] = ffn["W8"].clone()
         sets.append(s)
     return sets, per
 
 
-def make_outputs(w, rows, packs, torch):
+def make_outputs(w, rows, packs, torch, ffn=None):
     D = w.D
     o = {"x8": [torch.empty(rows, D, dtype=torch.uint8, device="cuda")
                 for _ in packs]}
@@ -194,11 +246,19 @@ def make_outputs(w, rows, packs, torch):
     o["rout2"] = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
     o["gemm"] = [[torch.empty(rows, n, dtype=torch.bfloat16, device="cuda")
                   for n in p["splits"]] for p in packs]
+    if ffn is not None:
+        H = ffn["H"]
+        o["hid8"] = torch.empty(rows, H, dtype=torch.uint8, device="cuda")
+        o["dn"] = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
+        o["gu"] = torch.empty(rows, 2 * H, dtype=torch.bfloat16, device="cuda")
+        o["hid8_unfused"] = torch.empty(rows, H, dtype=torch.uint8, device="cuda")
     return o
 
 
 def step_launches(w, s, act, outs, rows, frt, eps):
-    """The step's launches for rotation set `s`: list of (kind, callable)."""
+    """The step's launches for rotation set `s`: list of (kind, callable).
+    With the FFN tail the last (gate/up) GEMM becomes the GEGLU-fused one
+    and the down projection follows."""
     d = s["dev"]
     D = w.D
     L = []
@@ -223,12 +283,44 @@ def step_launches(w, s, act, outs, rows, frt, eps):
         L.append(("gemm2", lambda: frt.frt_packed_gemm_fp8_split(
             outs["x8"][1], p1["W8"], act[1], p1["ws"], outs["gemm"][1],
             p1["splits"], bias_cat=p1["bias"])))
+    f = s.get("ffn")
+    if f is not None:
+        last, pl = L[-1][0], s["packs"][-1]
+        L[-1] = (last + "_geglu", lambda: frt.frt_packed_gemm_fp8_geglu_quant(
+            outs["x8"][-1], pl["W8"], act[-1], pl["ws"], f["scale"], outs["hid8"],
+            bias_cat=pl["bias"]))
+        L.append(("gemm_down", lambda: frt.frt_packed_gemm_fp8_split(
+            outs["hid8"], f["W8"], f["scale"], f["ws"], [outs["dn"]], [w.D])))
     return L
 
 
-def kernel_work(w, kind, rows, packs):
+def unfused_launches(w, s, act, outs, frt):
+    """The unfused form of the fused gate/up GEGLU launch (timed for
+    comparison only): the bf16 gate|up GEMM and the standalone quantiser."""
+    f, pl = s["ffn"], s["packs"][-1]
+    H = f["H"]
+    return [("gateup_bf16", lambda: frt.frt_packed_gemm_fp8_split(
+                outs["x8"][-1], pl["W8"], act[-1], pl["ws"], [outs["gu"]], [2 * H],
+                bias_cat=pl["bias"])),
+            ("geglu", lambda: frt.frt_geglu_quant_fp8(
+                outs["gu"], H, f["scale"], out_fp8=outs["hid8_unfused"]))]
+
+
+def kernel_work(w, kind, rows, packs, ffn=None):
     """Algorithmic bytes and FLOPs of one launch."""
     D = w.D
+    if ffn is not None:
+        H = ffn["H"]
+        p = packs[-1]
+        bias = 2 * H * 2 if p["bias"] is not None else 0
+        if kind.endswith("_geglu"):     # x8 + W8 [2H, D] + codes [M, H]
+            return rows * D + 2 * H * D + rows * H + bias, 2.0 * rows * 2 * H * D
+        if kind == "gemm_down":         # codes + W8 [D, H] + bf16 [M, D]
+            return rows * H + D * H + rows * D * 2, 2.0 * rows * D * H
+        if kind == "gateup_bf16":
+            return rows * D + 2 * H * D + rows * 2 * H * 2 + bias, 2.0 * rows * 2 * H * D
+        if kind == "geglu":             # bf16 [M, 2H] in, codes out
+            return rows * 2 * H * 2 + rows * H, 0.0
     if kind.startswith("norm"):
         if w.form == "adarms":
             gate = rows * D * 2 if (w.cid == 4 and kind == "norm1") else D * 2
@@ -512,8 +604,14 @@ def main():
     w0 = wl.WORKLOADS[a.workload]
     rows = a.rows if a.rows is not None else w0.rows
     w, dev, act, packs, pack_ms = build_sets(a.workload, rows, frt, torch)
-    sets, per_set = make_rotation(w, dev, packs, rows, torch)
-    outs = make_outputs(w, rows, packs, torch)
+    ffn = None
+    if a.ffn:
+        if a.workload not in wl.FFN_HIDDEN:
+            raise SystemExit("--ffn: the FFN tail follows the gate/up GEMM of "
+                             f"workloads {sorted(wl.FFN_HIDDEN)}")
+        ffn = build_ffn(w, rows, act, packs, frt, torch)
+    sets, per_set = make_rotation(w, dev, packs, rows, torch, ffn)
+    outs = make_outputs(w, rows, packs, torch, ffn)
     nset = len(sets)
 
     steps_fns = [step_launches(w, s, act, outs, rows, frt, wl.EPS) for s in sets]
@@ -537,7 +635,8 @@ def main():
     for _, fn in steps_fns[0]:
         fn()
     torch.cuda.synchronize()
-    ref = [t.clone() for t in outs["gemm"][-1]]
+    final = [outs["dn"]] if ffn is not None else outs["gemm"][-1]
+    ref = [t.clone() for t in final]
     chunk = capture([fn for st in steps_fns for _, fn in st], torch)
     singles = [capture([fn for _, fn in st], torch) for st in steps_fns]
     for _ in range(3):
@@ -545,7 +644,7 @@ def main():
         torch.cuda.synchronize()
         singles[0].replay()
         torch.cuda.synchronize()
-        for r, t in zip(ref, outs["gemm"][-1]):
+        for r, t in zip(ref, final):
             if not torch.equal(r, t):
                 raise RuntimeError("graph replay differs from the eager step")
 
@@ -572,12 +671,18 @@ def main():
 
     # per-kernel durations: graphs of one kernel kind over all sets
     kinds = [k for k, _ in steps_fns[0]]
+    timed = [[fn for _, fn in st] for st in steps_fns]
+    all_kinds = list(kinds)
+    if ffn is not None:
+        extra = [unfused_launches(w, s, act, outs, frt) for s in sets]
+        all_kinds += [k for k, _ in extra[0]]
+        timed = [t + [fn for _, fn in e] for t, e in zip(timed, extra)]
     table = []
-    for ki, kind in enumerate(kinds):
-        g = capture([steps_fns[s][ki][1] for s in range(nset)], torch)
+    for ki, kind in enumerate(all_kinds):
+        g = capture([timed[s][ki] for s in range(nset)], torch)
         prewarm(g, 0.3, torch)
         us = time_graph(g, a.kernel_reps, torch) * 1e3 / nset
-        b, f = kernel_work(w, kind, rows, packs)
+        b, f = kernel_work(w, kind, rows, packs, ffn)
         row = {"kernel": kind, "us": round(us, 3), "bytes": int(b),
                "GB/s": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
         if f:
@@ -586,13 +691,15 @@ def main():
             row["bound"] = "mfma" if f / b > RIDGE else "hbm"
         else:
             row["bound"] = "hbm"
+        if kind not in kinds:
+            row["in_step"] = False      # the unfused comparison
         table.append(row)
         del g
 
-    gemm_flops = sum(kernel_work(w, k, rows, packs)[1] for k in kinds)
-    norm_bytes = sum(kernel_work(w, k, rows, packs)[0] for k in kinds if k.startswith("norm"))
+    gemm_flops = sum(kernel_work(w, k, rows, packs, ffn)[1] for k in kinds)
+    norm_bytes = sum(kernel_work(w, k, rows, packs, ffn)[0] for k in kinds if k.startswith("norm"))
     norm_us = sum(r["us"] for r in table if r["kernel"].startswith("norm"))
-    dom = max(table, key=lambda r: r["us"])
+    dom = max((r for r in table if r["kernel"] in kinds), key=lambda r: r["us"])
     traffic = load_traffic(a.workload, dom["kernel"]) if a.rows is None else None
     if dom["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dom["TFLOP/s"], "peak": FP8_PEAK_TFLOPS,
@@ -611,7 +718,8 @@ def main():
         "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": w.name, "rows": rows, "D": w.D,
+        "config": {"workload": w.name + ("+ffn_geglu_down" if ffn is not None else ""),
+                   "rows": rows, "D": w.D,
                    "gemms": [list(g) for g in w.gemms], "bias": w.bias,
                    "rotation_sets": nset, "rotation_mib": round(nset * per_set / 2**20, 1),
                    "step_gemm_gflop": round(gemm_flops / 1e9, 3)},
@@ -623,7 +731,9 @@ def main():
         "prewarm_s": a.prewarm_s,
         "wall_s_timed": round(wall, 4),
     }
-    if not a.no_cpu_baseline:
+    if ffn is not None:
+        res["config"]["ffn"] = {"H": ffn["H"], "down": [w.D, ffn["H"]]}
+    if not a.no_cpu_baseline and ffn is None:
         res["cpu_baseline"] = cpu_baseline(w, rows)
     print(json.dumps(res), flush=True)
 

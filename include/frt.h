@@ -11,7 +11,10 @@
  *   - impls/qkv_pack/fp8_static.py: `_pack_weights` (one joint per-tensor
  *     scale over the concatenated siblings) and `PackedLinear._run` (the
  *     packed FP8 GEMM with optional bias whose columns are handed out per
- *     sibling).
+ *     sibling);
+ *   - fp8_chain.py's FFN tail: the merged gate/up output turned into the
+ *     FP8 input of the down projection by a tanh-GELU GEGLU quantiser,
+ *     standalone or as the gate/up GEMM's epilogue.
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers unless marked [host].
@@ -238,6 +241,74 @@ int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K,
                               const int64_t* split_n, void* const* out,
                               const int64_t* ld_out, int out_dtype,
                               void* workspace, size_t ws_bytes);
+
+/*
+ * frt_geglu_quant_fp8 — GEGLU of a merged gate/up row + static per-tensor
+ * FP8 (the FFN's down-projection input).
+ *
+ * Source: fp8_chain.py, `_quantize` (gate and up packed as one matrix, gate
+ * rows first, so a merged output row is [gate | up]) and `_band_elements`
+ * (`down_project`: the merged GEGLU + static FP8 quantiser feeding the
+ * down projection); the chain's bind admits only tanh-GELU FFNs. For
+ * m < M, j < H:
+ *   y   = gelu_tanh(gu[m, j]) * gu[m, H + j]                       (fp32)
+ *         gelu_tanh(v) = 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
+ *   out_fp8[m, j] = e4m3_rne(clamp(fl32(y / act_scale), -448, 448))
+ *
+ *   M, H          rows; width of each half (1 <= H <= 2^24).
+ *   gu            bf16 [M, ld_gu], ld_gu >= 2H: gate in [0, H), up in
+ *                 [H, 2H).
+ *   act_scale     fp32 [1] (> 0). Required iff out_fp8.
+ *   out_fp8       e4m3fn [M, ld_out]; NULL => not written.
+ *   y_f32         fp32 [M, ld_y] pre-quantisation y (diagnostic); NULL =>
+ *                 not written.
+ *   amax_out      fp32 [1]: atomically raised to max |y| (calibration of
+ *                 the down projection's scale); the caller initialises it.
+ * At least one output. Outputs must not overlap each other or the inputs.
+ * H % 8 == 0 with gu 16-byte aligned, ld_gu % 8 == 0, out_fp8 8-byte
+ * aligned with ld_out % 8 == 0 and y_f32 16-byte aligned with ld_y % 4 == 0
+ * takes the vector path; any other layout runs one element per thread
+ * (gu 2-byte, y_f32 4-byte alignment required).
+ */
+int frt_geglu_quant_fp8(void* stream, int64_t M, int64_t H,
+                        const uint16_t* gu, int64_t ld_gu,
+                        const float* act_scale,
+                        uint8_t* out_fp8, int64_t ld_out,
+                        float* y_f32, int64_t ld_y, float* amax_out);
+
+/*
+ * frt_packed_gemm_fp8_geglu_quant — the merged gate/up FP8 GEMM with the
+ * GEGLU quantiser as its epilogue: the [M, 2H] bf16 gate/up output never
+ * reaches memory.
+ *
+ * Source: as frt_packed_gemm_fp8_split for the GEMM (one packed matrix,
+ * alpha = act_scale * w_scale, optional bias) followed by
+ * frt_geglu_quant_fp8 (fp8_chain.py `_band_elements`, `down_project`).
+ * For m < M, j < H, with acc as in frt_packed_gemm_fp8_split over W8 rows
+ * j (gate) and H + j (up):
+ *   g = bf16_rne(fl32(alpha * acc[m, j])     + bias_cat[j])
+ *   u = bf16_rne(fl32(alpha * acc[m, H + j]) + bias_cat[H + j])
+ *   out_fp8[m, j] = e4m3_rne(clamp(fl32(gelu_tanh(g) * u / out_scale), +-448))
+ * i.e. exactly frt_packed_gemm_fp8_split (bf16 out) followed by
+ * frt_geglu_quant_fp8 on its output.
+ *
+ *   M, K, x8, ld_x, act_scale, w_scale   as in frt_packed_gemm_fp8_split.
+ *   W8            e4m3fn [2H, K]: the H gate rows, then the H up rows (the
+ *                 frt_pack_weights_fp8 result for siblings {gate, up}).
+ *   H             hidden width; 2H <= 2^24.
+ *   bias_cat      bf16 [2H] or NULL.
+ *   out_scale     fp32 [1] static scale of the GEGLU output (> 0).
+ *   out_fp8       e4m3fn [M, ld_out], ld_out >= H; must not overlap an
+ *                 input.
+ */
+int frt_packed_gemm_fp8_geglu_quant(void* stream, int64_t M, int64_t K,
+                                    const uint8_t* x8, int64_t ld_x,
+                                    const uint8_t* W8, int64_t H,
+                                    const float* act_scale,
+                                    const float* w_scale,
+                                    const uint16_t* bias_cat,
+                                    const float* out_scale,
+                                    uint8_t* out_fp8, int64_t ld_out);
 
 #ifdef __cplusplus
 }

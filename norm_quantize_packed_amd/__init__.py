@@ -24,7 +24,8 @@ __all__ = [
     "FrtError", "load_library", "library_path",
     "frt_ada_norm_quant_fp8", "frt_ptok_table_norm_quant_fp8",
     "frt_pack_weights_fp8", "frt_packed_gemm_fp8_workspace_size",
-    "frt_packed_gemm_fp8_split", "frt_last_error", "frt_abi_version",
+    "frt_packed_gemm_fp8_split", "frt_geglu_quant_fp8",
+    "frt_packed_gemm_fp8_geglu_quant", "frt_last_error", "frt_abi_version",
     "FRT_OK", "FRT_E_INVALID", "FRT_E_UNSUPPORTED", "FRT_E_HIP",
 ]
 
@@ -57,6 +58,10 @@ _SIGNATURES = {
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i32,
         ctypes.POINTER(_i64), ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32,
         _p, _sz]),
+    "frt_geglu_quant_fp8": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p]),
+    "frt_packed_gemm_fp8_geglu_quant": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _p, _p, _i64]),
 }
 
 
@@ -309,3 +314,44 @@ def frt_packed_gemm_fp8_split(x8, W8, act_scale, w_scale, outs: Sequence,
         (_i64 * n)(*[int(s) for s in split_n]),
         (_p * n)(*[_ptr(o) for o in outs]),
         (_i64 * n)(*[_ld(o) for o in outs]), out_dtype, ws_ptr, ws_bytes))
+
+
+def frt_geglu_quant_fp8(gu, H: int, act_scale=None, *, out_fp8=None,
+                        y_f32=None, amax_out=None, M: Optional[int] = None,
+                        stream=None) -> None:
+    """GEGLU of the merged ``[M, >= 2H]`` bf16 gate|up rows + static FP8
+    (see include/frt.h)."""
+    _bf16_like(gu, "gu")
+    _u8_like(out_fp8, "out_fp8")
+    for t, n in ((act_scale, "act_scale"), (y_f32, "y_f32"),
+                 (amax_out, "amax_out")):
+        _f32_like(t, n)
+    Mv = gu.shape[0] if M is None else int(M)
+    lib = load_library()
+    _check(lib.frt_geglu_quant_fp8(
+        _stream(stream), Mv, int(H), _ptr(gu), _ld(gu), _ptr(act_scale),
+        _ptr(out_fp8), _ld(out_fp8), _ptr(y_f32), _ld(y_f32),
+        _ptr(amax_out)))
+
+
+def frt_packed_gemm_fp8_geglu_quant(x8, W8, act_scale, w_scale, out_scale,
+                                    out_fp8, bias_cat=None, *,
+                                    M: Optional[int] = None,
+                                    stream=None) -> None:
+    """Merged gate/up FP8 GEMM (``W8`` = ``[2H, K]``, gate rows first) with
+    the GEGLU quantiser as epilogue; ``out_fp8`` is ``[>= M, >= H]``."""
+    _u8_like(x8, "x8")
+    _u8_like(W8, "W8")
+    _u8_like(out_fp8, "out_fp8")
+    for t, n in ((act_scale, "act_scale"), (w_scale, "w_scale"),
+                 (out_scale, "out_scale")):
+        _f32_like(t, n)
+    _bf16_like(bias_cat, "bias_cat")
+    if W8.shape[0] % 2:
+        raise ValueError("frt: W8 must hold 2H rows (gate, then up)")
+    Mv = x8.shape[0] if M is None else int(M)
+    lib = load_library()
+    _check(lib.frt_packed_gemm_fp8_geglu_quant(
+        _stream(stream), Mv, int(x8.shape[1]), _ptr(x8), _ld(x8), _ptr(W8),
+        int(W8.shape[0] // 2), _ptr(act_scale), _ptr(w_scale),
+        _ptr(bias_cat), _ptr(out_scale), _ptr(out_fp8), _ld(out_fp8)))

@@ -316,4 +316,75 @@ int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K, const uint8_t*
   return hip_status(frt::launch_gemm(a, (hipStream_t)stream), "gemm launch");
 }
 
+int frt_geglu_quant_fp8(void* stream, int64_t M, int64_t H, const uint16_t* gu, int64_t ld_gu,
+                        const float* act_scale, uint8_t* out_fp8, int64_t ld_out, float* y_f32,
+                        int64_t ld_y, float* amax_out) {
+  if (M < 0) return refuse(FRT_E_INVALID, "geglu: M=%lld < 0", (long long)M);
+  if (H < 1 || H > (1 << 24)) return refuse(FRT_E_INVALID, "geglu: H=%lld outside [1, 2^24]", (long long)H);
+  if (gu == nullptr) return refuse(FRT_E_INVALID, "geglu: gu is required");
+  if (ld_gu < 2 * H) return refuse(FRT_E_INVALID, "geglu: ld_gu < 2*H");
+  if (out_fp8 != nullptr && act_scale == nullptr) return refuse(FRT_E_INVALID, "geglu: out_fp8 needs act_scale");
+  if (out_fp8 != nullptr && ld_out < H) return refuse(FRT_E_INVALID, "geglu: ld_out < H");
+  if (y_f32 != nullptr && ld_y < H) return refuse(FRT_E_INVALID, "geglu: ld_y < H");
+  if (out_fp8 == nullptr && y_f32 == nullptr && amax_out == nullptr)
+    return refuse(FRT_E_INVALID, "geglu: no output requested");
+  if (!aligned(gu, 2) || (y_f32 != nullptr && !aligned(y_f32, 4)))
+    return refuse(FRT_E_INVALID, "geglu: gu (y_f32) must be 2 (4)-byte aligned");
+  if (M == 0) return ok();
+  const Range in[] = {span(gu, M, 2 * H, ld_gu, 2), span(act_scale, 1, 1, 1, 4)};
+  const Range outs[] = {span(out_fp8, M, H, ld_out, 1), span(y_f32, M, H, ld_y, 4), span(amax_out, 1, 1, 1, 4)};
+  for (int o = 0; o < 3; ++o) {
+    for (int i = 0; i < 2; ++i)
+      if (overlap(outs[o], in[i])) return refuse(FRT_E_INVALID, "geglu: output %d overlaps input %d", o, i);
+    for (int p = o + 1; p < 3; ++p)
+      if (overlap(outs[o], outs[p])) return refuse(FRT_E_INVALID, "geglu: outputs %d and %d overlap", o, p);
+  }
+  const bool vec8 = H % 8 == 0 && aligned(gu, 16) && ld_gu % 8 == 0 &&
+                    (out_fp8 == nullptr || (aligned(out_fp8, 8) && ld_out % 8 == 0)) &&
+                    (y_f32 == nullptr || (aligned(y_f32, 16) && ld_y % 4 == 0));
+  frt::GegluArgs a{gu, ld_gu, act_scale, out_fp8, ld_out, y_f32, ld_y, amax_out, M, (int)H};
+  return hip_status(frt::launch_geglu(a, vec8 ? 8 : 1, (hipStream_t)stream), "geglu launch");
+}
+
+int frt_packed_gemm_fp8_geglu_quant(void* stream, int64_t M, int64_t K, const uint8_t* x8, int64_t ld_x,
+                                    const uint8_t* W8, int64_t H, const float* act_scale,
+                                    const float* w_scale, const uint16_t* bias_cat,
+                                    const float* out_scale, uint8_t* out_fp8, int64_t ld_out) {
+  if (M < 0) return refuse(FRT_E_INVALID, "gemm_geglu: M=%lld < 0", (long long)M);
+  if (K < 512 || K > 16384) return refuse(FRT_E_INVALID, "gemm_geglu: K=%lld outside [512, 16384]", (long long)K);
+  if (K % 16) return refuse(FRT_E_UNSUPPORTED, "gemm_geglu: K=%lld not a multiple of 16", (long long)K);
+  if (H < 1) return refuse(FRT_E_INVALID, "gemm_geglu: H < 1");
+  if (M > (1 << 24) || 2 * H > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "gemm_geglu: M or 2H too large");
+  if (x8 == nullptr || W8 == nullptr || act_scale == nullptr || w_scale == nullptr || out_scale == nullptr ||
+      out_fp8 == nullptr)
+    return refuse(FRT_E_INVALID, "gemm_geglu: x8, W8, act_scale, w_scale, out_scale and out_fp8 are required");
+  if (ld_x < K || ld_x % 16) return refuse(FRT_E_INVALID, "gemm_geglu: ld_x must be >= K and a multiple of 16");
+  if (!aligned(x8, 16) || !aligned(W8, 16))
+    return refuse(FRT_E_INVALID, "gemm_geglu: x8 and W8 must be 16-byte aligned");
+  if ((M - 1) * ld_x + K > (int64_t)0x7fffffff || 2 * H * K > (int64_t)0x7fffffff)
+    return refuse(FRT_E_UNSUPPORTED, "gemm_geglu: operand larger than 2 GiB");
+  if (ld_out < H) return refuse(FRT_E_INVALID, "gemm_geglu: ld_out < H");
+  if (M == 0) return ok();
+  const Range o = span(out_fp8, M, H, ld_out, 1);
+  const Range in[] = {span(x8, M, K, ld_x, 1), span(W8, 2 * H, K, K, 1), span(bias_cat, 1, 2 * H, 2 * H, 2),
+                      span(act_scale, 1, 1, 1, 4), span(w_scale, 1, 1, 1, 4), span(out_scale, 1, 1, 1, 4)};
+  for (int i = 0; i < 6; ++i)
+    if (overlap(o, in[i])) return refuse(FRT_E_INVALID, "gemm_geglu: out_fp8 overlaps input %d", i);
+  frt::GemmArgs a{};
+  a.x = x8;
+  a.ld_x = ld_x;
+  a.w = W8;
+  a.act_scale = act_scale;
+  a.w_scale = w_scale;
+  a.bias = bias_cat;
+  a.M = (int)M;
+  a.N = (int)(2 * H);
+  a.K = (int)K;
+  a.H = (int)H;
+  a.q8 = out_fp8;
+  a.ld_q8 = ld_out;
+  a.q_scale = out_scale;
+  return hip_status(frt::launch_gemm_geglu(a, (hipStream_t)stream), "gemm_geglu launch");
+}
+
 }  // extern "C"

@@ -1,6 +1,7 @@
 // Device helpers shared by the frt HIP kernels (gfx950 / CDNA4).
 //
-// bf16 <-> fp32, the static FP8 e4m3fn quantiser, and wave64 reductions.
+// bf16 <-> fp32, the static FP8 e4m3fn quantiser, the tanh-form GELU and
+// wave64 reductions.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -58,6 +59,17 @@ __device__ __forceinline__ uint32_t cvt4_fp8(float a, float b, float c, float d)
 }
 __device__ __forceinline__ uint32_t cvt2_fp8(float a, float b) {
   return uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xffffu;
+}
+
+// Tanh-form GELU, 0.5 v (1 + tanh(z)) with z = sqrt(2/pi) (v + 0.044715 v^3),
+// evaluated through the identity 0.5 (1 + tanh z) = 1 / (1 + e^(-2z)):
+// gelu(v) = v / (1 + 2^(c v (1 + 0.044715 v^2))), c = -2 sqrt(2/pi) log2(e).
+// No cancellation at either tail: for v -> -inf the power overflows to inf
+// and the quotient is -0 (the tanh form's limit); for v -> +inf it is v.
+__device__ __forceinline__ float gelu_tanh(float v) {
+  constexpr float c = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+  const float t = c * v * __builtin_fmaf(0.044715f, v * v, 1.0f);
+  return v / (1.0f + __builtin_amdgcn_exp2f(t));
 }
 
 // ---- wave64 reductions (DPP within rows of 16, readlane across rows) ----

@@ -97,13 +97,25 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // [AE, BM) unloaded: their MFMA results only reach output rows >= M, which
 // the epilogue never stores, and every wave still issues the same number of
 // loads per stage, so the vmcnt counts stay exact.
-template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB, int AE = BM>
+//
+// GLU: the gate/up GEGLU form. W8 holds 2H rows (gate rows, then up rows)
+// and a tile covers BN/2 gate columns [g0, g0 + BN/2) together with the
+// matching up columns: tile-local B row r is gate row g0 + (r/64)*32 + r%32
+// when (r/32) is even and the up row H + (the same) when it is odd. A
+// 64-column wave tile therefore holds gate column c in accumulator pair
+// 2q and up column c in 2q + 1 of the same lane, and the epilogue writes
+// e4m3(gelu_tanh(bf16(gate)) * bf16(up) / q_scale) for H columns. Gate rows
+// past H (a ragged last tile) read up rows, whose results are never stored;
+// up rows past 2H read zeros.
+template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB, int AE = BM,
+          bool GLU = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a) {
   constexpr int WAVES_N = BN / WN;
   constexpr int NW = (BM / WM) * WAVES_N;
   constexpr int MI = WM / 32, NJ = WN / 32;
   constexpr int ROWS = BM + BN;
   static_assert(AE <= BM && AE % 16 == 0, "A rows loaded");
+  static_assert(!GLU || (NJ % 2 == 0 && WN % 64 == 0), "GEGLU pairs need 64-column wave tiles");
   constexpr int LOADS = (AE + BN) / 8;  // 1 KiB load instructions per stage
   static_assert(LOADS % NW == 0, "loads must split evenly over the waves");
   constexpr int LPW = LOADS / NW;
@@ -119,7 +131,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = (a.N + BN - 1) / BN;
   const TileXY t = tile_of(blockIdx.x, tiles_m, tiles_n, GM);
-  const int m0 = t.tm * BM, n0 = t.tn * BN;
+  // n0: first output column (GLU: first gate column g0)
+  const int m0 = t.tm * BM, n0 = t.tn * (GLU ? BN / 2 : BN);
   const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
 
   const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + a.K);
@@ -140,7 +153,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   static_assert(NW % 2 == 0, "row swizzle assumes an even wave count");
   const int cch = (lane & 7) ^ (((wave & 1) << 2) | (lrow >> 1));
   const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
-  const uint32_t offB = (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
+  const uint32_t offB = GLU ? (uint32_t)(lrow * a.K + cch * 16)
+                            : (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
   const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
   const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)a.K;
   const int KT = (a.K + KST - 1) / KST;
@@ -157,7 +171,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
         // A rows 8u.., B rows BM + 8u.. (u counts this operand's loads)
         const int u = wave + (A ? j : j - LPA) * NW + (A ? 0 : BM / 8);
         uint8_t* dst = smem + SL * STAGE + q * SUBB + u * 1024;
-        uint32_t o = A ? offA + j * stepA + k0 : offB + (j - LPA) * stepB + k0;
+        uint32_t o;
+        if (A) {
+          o = offA + j * stepA + k0;
+        } else if constexpr (GLU) {
+          // B unit ub (tile-local rows 8ub .. 8ub + 7): gate or up half by
+          // (ub / 4) % 2, 32-column pair ub / 8, 8-row group ub % 4
+          const int ub = wave + (j - LPA) * NW;
+          const int row = ((ub >> 2) & 1) * a.H + n0 + (ub >> 3) * 32 + (ub & 3) * 8;
+          o = offB + (uint32_t)row * (uint32_t)a.K + k0;
+        } else {
+          o = offB + (j - LPA) * stepB + k0;
+        }
         if constexpr (KTAIL) {
           if (k0 + cch * 16 >= a.K) o = kOOB;
         }
@@ -297,6 +322,32 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 
   // ---- epilogue: alpha * acc + bias, column split, bf16 (or fp32) ----
   const float alpha = (*a.act_scale) * (*a.w_scale);
+  if constexpr (GLU) {
+    // gate and up rounded to bf16 as the unfused GEMM output would be,
+    // then the GEGLU quantiser of frt_ffn.hip
+    const float qs = *a.q_scale, qr = 1.0f / qs;
+#pragma unroll
+    for (int q = 0; q < NJ / 2; ++q) {
+      const int gc = n0 + (wn0 >> 1) + q * 32 + (lane & 31);
+      if (gc >= a.H) continue;
+      const float bg = a.bias != nullptr ? bf16f(a.bias[gc]) : 0.0f;
+      const float bu = a.bias != nullptr ? bf16f(a.bias[a.H + gc]) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          if (m < a.M) {
+            const float vg = alpha * acc[i][2 * q][r] + bg;
+            const float vu = alpha * acc[i][2 * q + 1][r] + bu;
+            const float y = gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
+            a.q8[(int64_t)m * a.ld_q8 + gc] = (uint8_t)cvt2_fp8(clamp_fp8(div_rn(y, qs, qr)), 0.0f);
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int n = n0 + wn0 + j * 32 + (lane & 31);
@@ -331,16 +382,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1, int AE = BM>
+template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1, int AE = BM, bool GLU = false>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
+  // (GLU: N = 2H, so this is also ceil(H / (BN / 2)) column tiles)
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
   if (a.K % (128 * NSUB) == 0)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE>), dim3(tiles), dim3(threads), 0, st,
-                       a);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU>), dim3(tiles), dim3(threads), 0,
+                       st, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, true, NSUB, AE>), dim3(tiles), dim3(threads), 0, st,
-                       a);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, true, NSUB, AE, GLU>), dim3(tiles), dim3(threads), 0,
+                       st, a);
   return hipGetLastError();
 }
 
@@ -368,6 +420,16 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 16) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 16>(a, st);
   if (a.M <= 32) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 32>(a, st);
   return launch_tiles<64, 32, 32, 32, 4, 1, 2>(a, st);
+}
+
+// GEGLU plans: the same tiles with 64-column wave tiles (a gate/up pair per
+// lane): 256x256 at M >= 512, 128x128 of eight 32x64 waves when they fill
+// the chip, else 64x64 of two 32x64 waves.
+hipError_t launch_gemm_geglu(const GemmArgs& a, hipStream_t st) {
+  if (a.M >= 512) return launch_tiles<256, 256, 128, 64, 2, 4, 1, 256, true>(a, st);
+  if (a.M > 64 && ((a.M + 127) / 128) * ((a.N + 127) / 128) >= 192)
+    return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, true>(a, st);
+  return launch_tiles<64, 64, 32, 64, 4, 1, 1, 64, true>(a, st);
 }
 
 }  // namespace frt

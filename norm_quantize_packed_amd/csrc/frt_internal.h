@@ -64,9 +64,26 @@ struct GemmArgs {
   int M, N, K;
   int out_f32;
   SplitTab sp;
+  // gate/up GEGLU epilogue (launch_gemm_geglu): W8 holds 2H rows, gate
+  // first; codes of gelu_tanh(gate) * up go to q8 [M, ld_q8] at q_scale
+  int H;
+  uint8_t* q8; int64_t ld_q8;
+  const float* q_scale;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_geglu(const GemmArgs& a, hipStream_t st);
+
+struct GegluArgs {
+  const uint16_t* gu; int64_t ld_gu;
+  const float* act_scale;
+  uint8_t* out; int64_t ld_out;
+  float* y; int64_t ld_y;
+  float* amax;
+  int64_t M; int H;
+};
+
+hipError_t launch_geglu(const GegluArgs& a, int vec, hipStream_t st);
 
 }  // namespace frt

@@ -175,3 +175,52 @@ def test_gemm_same_stride_overlap_is_exact(lib):
     lds = [768, 768, 768]
     assert _gemm(lib, outs=[o, o + 500 * 2, o + 640 * 2], lds=lds) == frt.FRT_E_INVALID
     assert _gemm(lib, outs=[o + 600 * 2, o, o + 2 * MB], lds=lds) == frt.FRT_E_INVALID
+
+
+def _geglu(lib, M=4, H=512, **kw):
+    a = dict(stream=None, M=M, H=H, gu=FAKE, ld_gu=2 * H,
+             act_scale=FAKE + 10 * MB, out_fp8=FAKE + 11 * MB, ld_out=H,
+             y_f32=None, ld_y=0, amax_out=None)
+    a.update(kw)
+    return lib.frt_geglu_quant_fp8(*a.values())
+
+
+def test_geglu_refusals(lib):
+    assert _geglu(lib, H=0) == frt.FRT_E_INVALID
+    assert _geglu(lib, M=-1) == frt.FRT_E_INVALID
+    assert _geglu(lib, gu=None) == frt.FRT_E_INVALID
+    assert _geglu(lib, ld_gu=1000) == frt.FRT_E_INVALID
+    assert "ld_gu" in frt.frt_last_error()
+    assert _geglu(lib, act_scale=None) == frt.FRT_E_INVALID
+    assert _geglu(lib, ld_out=100) == frt.FRT_E_INVALID
+    assert _geglu(lib, out_fp8=None) == frt.FRT_E_INVALID      # no output
+    assert _geglu(lib, gu=FAKE + 1) == frt.FRT_E_INVALID        # misaligned
+    assert _geglu(lib, out_fp8=FAKE + 512) == frt.FRT_E_INVALID  # over gu
+    assert "overlaps" in frt.frt_last_error()
+    assert _geglu(lib, y_f32=FAKE + 11 * MB + 256, ld_y=512) == frt.FRT_E_INVALID
+    assert _geglu(lib, M=0) == frt.FRT_OK
+    # odd H and unaligned strides are legal (the element-wise path)
+    assert _geglu(lib, M=0, H=1001, ld_gu=2003, ld_out=1001) == frt.FRT_OK
+
+
+def _gemm_geglu(lib, M=16, K=512, H=256, **kw):
+    a = dict(stream=None, M=M, K=K, x8=FAKE, ld_x=K, W8=FAKE + MB, H=H,
+             act_scale=FAKE + 30 * MB, w_scale=FAKE + 31 * MB, bias=None,
+             out_scale=FAKE + 32 * MB, out_fp8=FAKE + 40 * MB, ld_out=H)
+    a.update(kw)
+    return lib.frt_packed_gemm_fp8_geglu_quant(*a.values())
+
+
+def test_gemm_geglu_refusals(lib):
+    assert _gemm_geglu(lib, K=256) == frt.FRT_E_INVALID
+    assert _gemm_geglu(lib, K=520) == frt.FRT_E_UNSUPPORTED
+    assert _gemm_geglu(lib, H=0) == frt.FRT_E_INVALID
+    assert _gemm_geglu(lib, out_scale=None) == frt.FRT_E_INVALID
+    assert _gemm_geglu(lib, out_fp8=None) == frt.FRT_E_INVALID
+    assert _gemm_geglu(lib, ld_out=100) == frt.FRT_E_INVALID
+    assert _gemm_geglu(lib, ld_x=520) == frt.FRT_E_INVALID
+    assert _gemm_geglu(lib, W8=FAKE + MB + 8) == frt.FRT_E_INVALID
+    # the codes over the packed weight (2H rows)
+    assert _gemm_geglu(lib, out_fp8=FAKE + MB + 2 * 256 * 512 - 64) == frt.FRT_E_INVALID
+    assert "overlaps" in frt.frt_last_error()
+    assert _gemm_geglu(lib, M=0) == frt.FRT_OK
