@@ -23,6 +23,7 @@
 // the logical tile index gives each XCD a contiguous run of tiles, and runs
 // are rastered in groups of GM tile-rows so that the tiles resident on one
 // XCD share A and B panels in that XCD's L2.
+#include <cstdint>
 #include <type_traits>
 #include <utility>
 
@@ -401,18 +402,55 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
 // The current plans use no workspace (the argument is kept in the ABI).
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
-// Tile plans (chosen by measurement on MI355X, graph-replayed launches with
-// HBM-resident weights):
-//  M >= 512: 256x256 tiles, 8 waves of 128x64 (MFMA-bound shapes);
-//  64 < M < 512: 128x128 tiles of sixteen 32x32 waves when they fill the
-//    chip, else 64x64 tiles (more blocks for narrow N);
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+                   ? n
+                   : 256;
+  }
+  return cus[dev];
+}
+
+// Operand bytes (per K byte) that the busiest CU loads under a BM x BN tile
+// plan: tiles are dealt one per CU per round, and a tile loads BM + BN rows
+// of K bytes. The per-CU fill rate bounds these kernels, so among plans the
+// one with the smallest figure wins (ties go to the larger tile, which moves
+// fewer bytes in total).
+int64_t plan_cost(const GemmArgs& a, int BM, int BN, int cus) {
+  const int64_t tiles = (int64_t)((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  return ((tiles + cus - 1) / cus) * (BM + BN);
+}
+
+// Tile plans (measured on MI355X, graph-replayed launches with HBM-resident
+// weights):
+//  M > 64: the plan of least per-CU load (plan_cost) among 256x256 tiles of
+//    eight 128x64 waves (M >= 512 only: the MFMA-bound shapes), 128x128 of
+//    sixteen 32x32 waves, 64x64 of four 32x32 waves and 64x32 with 256-deep
+//    stages. E.g. 256 x 16384 -> 128x128; 256 x 2560 -> 64x64 (160 tiles);
+//    256 x 2048 over K = 8192 -> 64x32 (256 tiles: 17 us against 22 us for
+//    the 128 tiles of 64x64);
 //  M <= 64: 64x32 tiles with 256-deep stages (weight streaming), loading
 //    only the first 16 or 32 A rows when M is at most that.
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
-  if (a.M >= 512) return launch_tiles<256, 256, 128, 64, 2, 4>(a, st);
   if (a.M > 64) {
-    if (((a.M + 127) / 128) * ((a.N + 127) / 128) >= 192) return launch_tiles<128, 128, 32, 32, 3, 2>(a, st);
-    return launch_tiles<64, 64, 32, 32, 4, 1>(a, st);
+    const int cus = device_cus();
+    int best = 0;
+    int64_t c = INT64_MAX;
+    const int64_t cost[4] = {a.M >= 512 ? plan_cost(a, 256, 256, cus) : INT64_MAX, plan_cost(a, 128, 128, cus),
+                             plan_cost(a, 64, 64, cus), plan_cost(a, 64, 32, cus)};
+    for (int p = 0; p < 4; ++p)
+      if (cost[p] < c) c = cost[p], best = p;
+    switch (best) {
+      case 0: return launch_tiles<256, 256, 128, 64, 2, 4>(a, st);
+      case 1: return launch_tiles<128, 128, 32, 32, 3, 2>(a, st);
+      case 2: return launch_tiles<64, 64, 32, 32, 4, 1>(a, st);
+      default: return launch_tiles<64, 32, 32, 32, 4, 1, 2>(a, st);
+    }
   }
   // rows past M are not loaded (at M <= 16, 8 of every 12 load
   // instructions would only fetch zeros): M = 1 9.3 -> 8.8 us, M = 16
@@ -423,12 +461,16 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
 }
 
 // GEGLU plans: the same tiles with 64-column wave tiles (a gate/up pair per
-// lane): 256x256 at M >= 512, 128x128 of eight 32x64 waves when they fill
-// the chip, else 64x64 of two 32x64 waves.
+// lane), chosen by plan_cost: 256x256 (M >= 512), 128x128 of eight 32x64
+// waves, 64x64 of two 32x64 waves (also every M <= 64).
 hipError_t launch_gemm_geglu(const GemmArgs& a, hipStream_t st) {
-  if (a.M >= 512) return launch_tiles<256, 256, 128, 64, 2, 4, 1, 256, true>(a, st);
-  if (a.M > 64 && ((a.M + 127) / 128) * ((a.N + 127) / 128) >= 192)
-    return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, true>(a, st);
+  if (a.M > 64) {
+    const int cus = device_cus();
+    const int64_t c256 = a.M >= 512 ? plan_cost(a, 256, 256, cus) : INT64_MAX;
+    const int64_t c128 = plan_cost(a, 128, 128, cus), c64 = plan_cost(a, 64, 64, cus);
+    if (c256 <= c128 && c256 <= c64) return launch_tiles<256, 256, 128, 64, 2, 4, 1, 256, true>(a, st);
+    if (c128 <= c64) return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, true>(a, st);
+  }
   return launch_tiles<64, 64, 32, 64, 4, 1, 1, 64, true>(a, st);
 }
 
