@@ -19,6 +19,8 @@ Modules:
   gemm       exact packed FP8 GEMM, dequant + bias epilogue, column split
   ffn        tanh-GELU GEGLU of the merged gate/up output + static FP8,
              and the merged gate/up GEMM -> GEGLU chain
+  rope       q/k pair interleave, QKV split + adjacent-pair RoPE + KV-cache
+             write
 
 Parity status: every function is pinned by the ``-m "not gpu"`` tests in
 tests/test_oracle_*.py (closed forms, brute force, independent torch CPU
@@ -34,6 +36,7 @@ from .pack import pack_weights
 from .gemm import (gemm_exact, gemm_exact_at, epilogue, packed_gemm_split,
                    split_columns)
 from .ffn import gelu_tanh, geglu, geglu_quant_fp8, gate_up_gelu_quant
+from .rope import pair_perm, interleave_rows, rotate_pairs, qkv_split_rope_kvcache
 
 __all__ = [
     "bf16_to_f32", "f32_to_bf16", "e4m3_decode", "e4m3_encode",
@@ -43,4 +46,5 @@ __all__ = [
     "calibrate_act_scale", "pack_weights", "gemm_exact", "gemm_exact_at",
     "epilogue", "packed_gemm_split", "split_columns",
     "gelu_tanh", "geglu", "geglu_quant_fp8", "gate_up_gelu_quant",
+    "pair_perm", "interleave_rows", "rotate_pairs", "qkv_split_rope_kvcache",
 ]

@@ -219,6 +219,27 @@ def down_weights(cid: int) -> np.ndarray:
     return normal_bf16(3000 + cid, 50, (w.D, H), w.w_std)
 
 
+# The attention heads behind workload 2's merged QKV (2048 | 256 | 256 =
+# 8 query heads and one KV head of 256), and the KV-cache geometry of the
+# suffix pass: P prefix rows already cached, the 256 suffix tokens written
+# behind them (T = P + S rows).
+QKV_HEADS: Dict[int, Tuple[int, int, int]] = {2: (8, 1, 256)}
+ROPE_PREFIX: Dict[int, int] = {2: 768}
+
+
+def rope_table(S: int, hd: int, P: int, base: float = 10000.0) -> np.ndarray:
+    """bf16 bits ``[S, hd]`` of the rotary table for positions P .. P + S - 1:
+    the cosine of pair i at column 2i and its sine at 2i + 1, angle
+    ``pos * base^(-2i / hd)`` (the standard rotary frequencies)."""
+    half = hd // 2
+    inv = base ** (-np.arange(half, dtype=np.float64) * 2.0 / hd)
+    ang = (P + np.arange(S, dtype=np.float64))[:, None] * inv[None, :]
+    t = np.empty((S, hd), dtype=np.float32)
+    t[:, 0::2] = np.cos(ang)
+    t[:, 1::2] = np.sin(ang)
+    return to_bf16_bits(t)
+
+
 def random_bf16(seed: int, shape, std: float = 1.0) -> np.ndarray:
     """Free-form helper for edge-case tests."""
     return normal_bf16(seed, 7, shape, std)
