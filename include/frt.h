@@ -14,7 +14,10 @@
  *     sibling);
  *   - fp8_chain.py's FFN tail: the merged gate/up output turned into the
  *     FP8 input of the down projection by a tanh-GELU GEGLU quantiser,
- *     standalone or as the gate/up GEMM's epilogue.
+ *     standalone or as the gate/up GEMM's epilogue;
+ *   - fp8_chain.py's attention head: the merged QKV output split, rotated
+ *     by adjacent-pair RoPE and written to q and the KV caches, standalone
+ *     or as the QKV GEMM's epilogue.
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers unless marked [host].
@@ -309,6 +312,95 @@ int frt_packed_gemm_fp8_geglu_quant(void* stream, int64_t M, int64_t K,
                                     const uint16_t* bias_cat,
                                     const float* out_scale,
                                     uint8_t* out_fp8, int64_t ld_out);
+
+/*
+ * frt_interleave_pairs_bf16 — the pack-time permutation of q or k
+ * projection rows that turns the host's rotate-half rotary pairs
+ * (i, i + hd/2) into adjacent pairs (2i, 2i + 1).
+ *
+ * Source: fp8_chain.py, module docstring (the two RoPE layouts and why a
+ * shared permutation of the head dimension leaves attention unchanged),
+ * `_quantize` (`_interleave_rows` on the q and k weights before packing;
+ * V keeps host order) and the `kperm` gather (position 2i takes dimension
+ * i, 2i + 1 takes i + hd/2). For h < nheads, j < hd, k < K:
+ *   dst[h*hd + j, k] = src[h*hd + perm(j), k],
+ *   perm(2i) = i, perm(2i + 1) = i + hd/2.
+ *
+ *   nheads, hd    heads and (even) head dim of the projection.
+ *   K             row length (input width), >= 1.
+ *   src, dst      bf16 [nheads*hd, K] row-packed; must not overlap.
+ * Rows are copied bit for bit; apply it to the q and k siblings before
+ * frt_pack_weights_fp8 when the GEMM feeds a RoPE consumer.
+ */
+int frt_interleave_pairs_bf16(void* stream, int nheads, int hd, int64_t K,
+                              const uint16_t* src, uint16_t* dst);
+
+/*
+ * frt_qkv_split_rope_kvcache — split the merged QKV output, rotate q and k
+ * by adjacent-pair RoPE, write q and the suffix rows of the K/V caches.
+ *
+ * Source: fp8_chain.py `_make_run` (`qkv_split_rope_kvcache_bf16(qkv3,
+ * rope, nh, kv, hd, P, q_out=, k_cache=, v_cache=, max_seq_len=T)` with the
+ * suffix K/V written behind P prefix rows, T = P + S), `_build_rope` (the
+ * table layout) and the module docstring (adjacent pairs). For token m < S,
+ * head h, pair i < hd/2, with (c, s) = (rope[m, 2i], rope[m, 2i + 1]):
+ *   (a, b) = the pair's two values of q (or k) head h
+ *   a' = bf16_rne(a c - b s),  b' = bf16_rne(b c + a s)
+ *   q_out[m, h, :]      = rotated q head h
+ *   k_cache[P + m, h, :] = rotated k head h   (h < kv)
+ *   v_cache[P + m, h, :] = v head h, copied   (h < kv)
+ * Cache rows outside [P, P + S) are not touched. Both products are exact
+ * in fp32, so the rotated values are the single rounding of the exact
+ * result (bit-exact to the definition).
+ *
+ *   S             tokens (rows of qkv; 0 => no-op).
+ *   nh, kv, hd    query heads, KV heads (>= 1), even head dim.
+ *   qkv           bf16 [S, ld_qkv], columns q (nh*hd) | k (kv*hd) |
+ *                 v (kv*hd); q and k pair-interleaved (see
+ *                 frt_interleave_pairs_bf16). 4-byte aligned, ld even.
+ *   rope          bf16 [S, hd]: cos at even, sin at odd columns. 4-byte
+ *                 aligned.
+ *   P, T          first cache row written and the caches' rows (P + S <= T).
+ *   q_out         bf16 [S, nh, hd] contiguous.
+ *   k_cache, v_cache   bf16 [T, kv, hd] contiguous.
+ * Outputs must not overlap each other, qkv or rope. hd % 8 == 0 with every
+ * pointer 16-byte aligned and ld_qkv % 8 == 0 takes the vector path.
+ */
+int frt_qkv_split_rope_kvcache(void* stream, int64_t S, int nh, int kv,
+                               int hd, const uint16_t* qkv, int64_t ld_qkv,
+                               const uint16_t* rope, int64_t P, int64_t T,
+                               uint16_t* q_out, uint16_t* k_cache,
+                               uint16_t* v_cache);
+
+/*
+ * frt_packed_gemm_fp8_qkv_rope — the merged QKV FP8 GEMM with the split +
+ * RoPE + KV-cache write as its epilogue (the bf16 QKV buffer never reaches
+ * memory).
+ *
+ * Source: as frt_packed_gemm_fp8_split for the GEMM and
+ * frt_qkv_split_rope_kvcache for the consumer. For m < M and column n of
+ * the [M, (nh + 2kv) hd] product:
+ *   v = bf16_rne(fl32(alpha * acc[m, n]) + bias_cat[n])
+ * then exactly frt_qkv_split_rope_kvcache on those values (token m = row
+ * m), i.e. the same results as frt_packed_gemm_fp8_split (bf16 out)
+ * followed by frt_qkv_split_rope_kvcache.
+ *
+ *   M, K, x8, ld_x, act_scale, w_scale, bias_cat   as in
+ *                 frt_packed_gemm_fp8_split (bias_cat [(nh + 2kv) hd]).
+ *   W8            e4m3fn [(nh + 2kv) hd, K]: q rows, k rows (both
+ *                 pair-interleaved before packing), v rows.
+ *   nh, kv, hd, rope, P, T, q_out, k_cache, v_cache   as in
+ *                 frt_qkv_split_rope_kvcache (S = M).
+ */
+int frt_packed_gemm_fp8_qkv_rope(void* stream, int64_t M, int64_t K,
+                                 const uint8_t* x8, int64_t ld_x,
+                                 const uint8_t* W8, int nh, int kv, int hd,
+                                 const float* act_scale,
+                                 const float* w_scale,
+                                 const uint16_t* bias_cat,
+                                 const uint16_t* rope, int64_t P, int64_t T,
+                                 uint16_t* q_out, uint16_t* k_cache,
+                                 uint16_t* v_cache);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,9 @@ __all__ = [
     "frt_ada_norm_quant_fp8", "frt_ptok_table_norm_quant_fp8",
     "frt_pack_weights_fp8", "frt_packed_gemm_fp8_workspace_size",
     "frt_packed_gemm_fp8_split", "frt_geglu_quant_fp8",
-    "frt_packed_gemm_fp8_geglu_quant", "frt_last_error", "frt_abi_version",
+    "frt_packed_gemm_fp8_geglu_quant", "frt_interleave_pairs_bf16",
+    "frt_qkv_split_rope_kvcache", "frt_packed_gemm_fp8_qkv_rope",
+    "frt_last_error", "frt_abi_version",
     "FRT_OK", "FRT_E_INVALID", "FRT_E_UNSUPPORTED", "FRT_E_HIP",
 ]
 
@@ -62,6 +64,12 @@ _SIGNATURES = {
         _p, _i64, _i64, _p, _i64, _p, _p, _i64, _p, _i64, _p]),
     "frt_packed_gemm_fp8_geglu_quant": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _p, _p, _i64]),
+    "frt_interleave_pairs_bf16": (_i32, [_p, _i32, _i32, _i64, _p, _p]),
+    "frt_qkv_split_rope_kvcache": (_i32, [
+        _p, _i64, _i32, _i32, _i32, _p, _i64, _p, _i64, _i64, _p, _p, _p]),
+    "frt_packed_gemm_fp8_qkv_rope": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _i32, _i32, _i32, _p, _p, _p, _p,
+        _i64, _i64, _p, _p, _p]),
 }
 
 
@@ -355,3 +363,58 @@ def frt_packed_gemm_fp8_geglu_quant(x8, W8, act_scale, w_scale, out_scale,
         _stream(stream), Mv, int(x8.shape[1]), _ptr(x8), _ld(x8), _ptr(W8),
         int(W8.shape[0] // 2), _ptr(act_scale), _ptr(w_scale),
         _ptr(bias_cat), _ptr(out_scale), _ptr(out_fp8), _ld(out_fp8)))
+
+
+def frt_interleave_pairs_bf16(src, dst, nheads: int, hd: int, *,
+                              stream=None) -> None:
+    """Pack-time pair interleave of ``[nheads * hd, K]`` bf16 q or k rows."""
+    _bf16_like(src, "src")
+    _bf16_like(dst, "dst")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("frt: src and dst must be contiguous")
+    _check(load_library().frt_interleave_pairs_bf16(
+        _stream(stream), int(nheads), int(hd), int(src.shape[-1]), _ptr(src),
+        _ptr(dst)))
+
+
+def _cache_args(rope, q_out, k_cache, v_cache):
+    for t, n in ((rope, "rope"), (q_out, "q_out"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache")):
+        _bf16_like(t, n)
+        if not t.is_contiguous():
+            raise ValueError(f"frt: {n} must be contiguous")
+
+
+def frt_qkv_split_rope_kvcache(qkv, rope, nh: int, kv: int, hd: int, P: int,
+                               q_out, k_cache, v_cache, *,
+                               S: Optional[int] = None, stream=None) -> None:
+    """Split the ``[S, (nh + 2kv) hd]`` QKV rows, rotate q/k by adjacent-pair
+    RoPE, write ``q_out [S, nh, hd]`` and cache rows ``P .. P + S - 1`` of
+    ``[T, kv, hd]`` caches."""
+    _bf16_like(qkv, "qkv")
+    _cache_args(rope, q_out, k_cache, v_cache)
+    Sv = qkv.shape[0] if S is None else int(S)
+    T = k_cache.numel() // (kv * hd)
+    _check(load_library().frt_qkv_split_rope_kvcache(
+        _stream(stream), Sv, int(nh), int(kv), int(hd), _ptr(qkv), _ld(qkv),
+        _ptr(rope), int(P), int(T), _ptr(q_out), _ptr(k_cache), _ptr(v_cache)))
+
+
+def frt_packed_gemm_fp8_qkv_rope(x8, W8, act_scale, w_scale, nh: int, kv: int,
+                                 hd: int, rope, P: int, q_out, k_cache, v_cache,
+                                 bias_cat=None, *, M: Optional[int] = None,
+                                 stream=None) -> None:
+    """Merged QKV FP8 GEMM with the split + RoPE + KV-cache epilogue."""
+    _u8_like(x8, "x8")
+    _u8_like(W8, "W8")
+    for t, n in ((act_scale, "act_scale"), (w_scale, "w_scale")):
+        _f32_like(t, n)
+    _bf16_like(bias_cat, "bias_cat")
+    _cache_args(rope, q_out, k_cache, v_cache)
+    Mv = x8.shape[0] if M is None else int(M)
+    T = k_cache.numel() // (kv * hd)
+    _check(load_library().frt_packed_gemm_fp8_qkv_rope(
+        _stream(stream), Mv, int(x8.shape[1]), _ptr(x8), _ld(x8), _ptr(W8),
+        int(nh), int(kv), int(hd), _ptr(act_scale), _ptr(w_scale),
+        _ptr(bias_cat), _ptr(rope), int(P), int(T), _ptr(q_out),
+        _ptr(k_cache), _ptr(v_cache)))

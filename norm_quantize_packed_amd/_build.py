@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libfrt.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["frt_api.hip", "frt_norm.hip", "frt_pack.hip", "frt_gemm.hip", "frt_ffn.hip"]
+SOURCES = ["frt_api.hip", "frt_norm.hip", "frt_pack.hip", "frt_gemm.hip", "frt_ffn.hip", "frt_rope.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

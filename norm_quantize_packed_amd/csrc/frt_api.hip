@@ -387,4 +387,109 @@ int frt_packed_gemm_fp8_geglu_quant(void* stream, int64_t M, int64_t K, const ui
   return hip_status(frt::launch_gemm_geglu(a, (hipStream_t)stream), "gemm_geglu launch");
 }
 
+int frt_interleave_pairs_bf16(void* stream, int nheads, int hd, int64_t K, const uint16_t* src, uint16_t* dst) {
+  if (nheads < 1 || hd < 2 || hd % 2) return refuse(FRT_E_INVALID, "interleave: nheads >= 1 and an even hd >= 2");
+  if (K < 1) return refuse(FRT_E_INVALID, "interleave: K < 1");
+  if ((int64_t)nheads * hd > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "interleave: too many rows");
+  if (src == nullptr || dst == nullptr) return refuse(FRT_E_INVALID, "interleave: src and dst are required");
+  if (!aligned(src, 2) || !aligned(dst, 2)) return refuse(FRT_E_INVALID, "interleave: src/dst misaligned");
+  const int64_t rows = (int64_t)nheads * hd;
+  if (overlap(span(src, rows, K, K, 2), span(dst, rows, K, K, 2)))
+    return refuse(FRT_E_INVALID, "interleave: dst overlaps src");
+  const int vec = (K % 8 == 0 && aligned(src, 16) && aligned(dst, 16)) ? 8 : 1;
+  return hip_status(frt::launch_interleave(src, dst, nheads, hd, K, vec, (hipStream_t)stream), "interleave launch");
+}
+
+namespace {
+
+// Shared contract of the split + RoPE + KV-cache outputs.
+int check_rope_outputs(const char* who, int64_t S, int nh, int kv, int hd, const uint16_t* rope, int64_t P,
+                       int64_t T, const uint16_t* q_out, const uint16_t* k_cache, const uint16_t* v_cache,
+                       const Range* inputs, int n_in) {
+  if (S < 0) return refuse(FRT_E_INVALID, "%s: S=%lld < 0", who, (long long)S);
+  if (nh < 1 || kv < 1 || hd < 2 || hd % 2)
+    return refuse(FRT_E_INVALID, "%s: nh >= 1, kv >= 1 and an even hd >= 2 are required", who);
+  if ((int64_t)(nh + 2 * kv) * hd > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "%s: too many columns", who);
+  if (P < 0 || T < 1 || P + S > T)
+    return refuse(FRT_E_INVALID, "%s: cache rows P .. P+S-1 must lie in [0, T)", who);
+  if (rope == nullptr || q_out == nullptr || k_cache == nullptr || v_cache == nullptr)
+    return refuse(FRT_E_INVALID, "%s: rope, q_out, k_cache and v_cache are required", who);
+  if (!aligned(rope, 4) || !aligned(q_out, 2) || !aligned(k_cache, 2) || !aligned(v_cache, 2))
+    return refuse(FRT_E_INVALID, "%s: rope must be 4-byte and the outputs 2-byte aligned", who);
+  if (S == 0) return FRT_OK;
+  const int64_t nk = (int64_t)kv * hd;
+  const Range outs[3] = {span(q_out, S, (int64_t)nh * hd, (int64_t)nh * hd, 2),
+                         span(k_cache + P * nk, S, nk, nk, 2), span(v_cache + P * nk, S, nk, nk, 2)};
+  const Range rr = span(rope, S, hd, hd, 2);
+  for (int o = 0; o < 3; ++o) {
+    if (overlap(outs[o], rr)) return refuse(FRT_E_INVALID, "%s: output %d overlaps rope", who, o);
+    for (int i = 0; i < n_in; ++i)
+      if (overlap(outs[o], inputs[i])) return refuse(FRT_E_INVALID, "%s: output %d overlaps input %d", who, o, i);
+    for (int q = o + 1; q < 3; ++q)
+      if (overlap(outs[o], outs[q])) return refuse(FRT_E_INVALID, "%s: outputs %d and %d overlap", who, o, q);
+  }
+  return FRT_OK;
+}
+
+}  // namespace
+
+int frt_qkv_split_rope_kvcache(void* stream, int64_t S, int nh, int kv, int hd, const uint16_t* qkv,
+                               int64_t ld_qkv, const uint16_t* rope, int64_t P, int64_t T, uint16_t* q_out,
+                               uint16_t* k_cache, uint16_t* v_cache) {
+  const int64_t ncol = (int64_t)(nh + 2 * kv) * hd;
+  if (qkv == nullptr) return refuse(FRT_E_INVALID, "rope_split: qkv is required");
+  if (nh >= 1 && kv >= 1 && ld_qkv < ncol) return refuse(FRT_E_INVALID, "rope_split: ld_qkv < (nh + 2kv) hd");
+  if (!aligned(qkv, 4) || ld_qkv % 2)
+    return refuse(FRT_E_INVALID, "rope_split: qkv must be 4-byte aligned with an even ld_qkv");
+  const Range in[1] = {span(qkv, S, ncol, ld_qkv, 2)};
+  const int rc = check_rope_outputs("rope_split", S, nh, kv, hd, rope, P, T, q_out, k_cache, v_cache, in, 1);
+  if (rc != FRT_OK) return rc;
+  if (S == 0) return ok();
+  const bool vec8 = hd % 8 == 0 && ld_qkv % 8 == 0 && aligned(qkv, 16) && aligned(rope, 16) && aligned(q_out, 16) &&
+                    aligned(k_cache, 16) && aligned(v_cache, 16);
+  frt::RopeArgs a{qkv, ld_qkv, rope, nh, kv, hd, S, P, q_out, k_cache, v_cache};
+  return hip_status(frt::launch_rope_split(a, vec8 ? 8 : 2, (hipStream_t)stream), "rope_split launch");
+}
+
+int frt_packed_gemm_fp8_qkv_rope(void* stream, int64_t M, int64_t K, const uint8_t* x8, int64_t ld_x,
+                                 const uint8_t* W8, int nh, int kv, int hd, const float* act_scale,
+                                 const float* w_scale, const uint16_t* bias_cat, const uint16_t* rope, int64_t P,
+                                 int64_t T, uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache) {
+  if (M < 0) return refuse(FRT_E_INVALID, "gemm_rope: M=%lld < 0", (long long)M);
+  if (K < 512 || K > 16384) return refuse(FRT_E_INVALID, "gemm_rope: K=%lld outside [512, 16384]", (long long)K);
+  if (K % 16) return refuse(FRT_E_UNSUPPORTED, "gemm_rope: K=%lld not a multiple of 16", (long long)K);
+  if (M > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "gemm_rope: M too large");
+  if (x8 == nullptr || W8 == nullptr || act_scale == nullptr || w_scale == nullptr)
+    return refuse(FRT_E_INVALID, "gemm_rope: x8, W8, act_scale and w_scale are required");
+  if (ld_x < K || ld_x % 16) return refuse(FRT_E_INVALID, "gemm_rope: ld_x must be >= K and a multiple of 16");
+  if (!aligned(x8, 16) || !aligned(W8, 16)) return refuse(FRT_E_INVALID, "gemm_rope: x8 and W8 must be 16-byte aligned");
+  const int64_t N = (nh >= 1 && kv >= 1 && hd >= 2) ? (int64_t)(nh + 2 * kv) * hd : 0;
+  if ((M - 1) * ld_x + K > (int64_t)0x7fffffff || N * K > (int64_t)0x7fffffff)
+    return refuse(FRT_E_UNSUPPORTED, "gemm_rope: operand larger than 2 GiB");
+  const Range in[5] = {span(x8, M, K, ld_x, 1), span(W8, N, K, K, 1), span(bias_cat, 1, N, N, 2),
+                       span(act_scale, 1, 1, 1, 4), span(w_scale, 1, 1, 1, 4)};
+  const int rc = check_rope_outputs("gemm_rope", M, nh, kv, hd, rope, P, T, q_out, k_cache, v_cache, in, 5);
+  if (rc != FRT_OK) return rc;
+  if (M == 0) return ok();
+  frt::GemmArgs a{};
+  a.x = x8;
+  a.ld_x = ld_x;
+  a.w = W8;
+  a.act_scale = act_scale;
+  a.w_scale = w_scale;
+  a.bias = bias_cat;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.rope = rope;
+  a.nh = nh;
+  a.kv = kv;
+  a.hd = hd;
+  a.P = P;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  return hip_status(frt::launch_gemm_rope(a, (hipStream_t)stream), "gemm_rope launch");
+}
+
 }  // extern "C"

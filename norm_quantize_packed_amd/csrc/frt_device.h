@@ -72,6 +72,13 @@ __device__ __forceinline__ float gelu_tanh(float v) {
   return v / (1.0f + __builtin_amdgcn_exp2f(t));
 }
 
+// The value held by lane l ^ 1 (DPP quad_perm [1,0,3,2]; the builtin is
+// declared int-valued but moves the operand's bits, so the cast compiles
+// to a plain DPP move).
+__device__ __forceinline__ float lane_xor1(float v) {
+  return static_cast<float>(__builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, true));
+}
+
 // ---- wave64 reductions (DPP within rows of 16, readlane across rows) ----
 
 __device__ __forceinline__ float dpp_sum16(float v) {

@@ -108,8 +108,16 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // e4m3(gelu_tanh(bf16(gate)) * bf16(up) / q_scale) for H columns. Gate rows
 // past H (a ragged last tile) read up rows, whose results are never stored;
 // up rows past 2H read zeros.
+//
+// ROPE: the QKV split + RoPE + KV-cache form. Columns [0, nh hd) are q,
+// the next kv hd are k, the last kv hd are v, with the q and k rows
+// pair-interleaved at pack time so that each rotary pair is two adjacent
+// columns, i.e. lanes l and l ^ 1 of the MFMA layout: each lane rounds its
+// value to bf16 as the split output would be, takes its partner's through
+// DPP, rotates q and k with the pair's (cos, sin) from the token's rope row,
+// and writes q_out row m, or cache row P + m of k or v.
 template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB, int AE = BM,
-          bool GLU = false>
+          bool GLU = false, bool ROPE = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a) {
   constexpr int WAVES_N = BN / WN;
   constexpr int NW = (BM / WM) * WAVES_N;
@@ -323,6 +331,49 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 
   // ---- epilogue: alpha * acc + bias, column split, bf16 (or fp32) ----
   const float alpha = (*a.act_scale) * (*a.w_scale);
+  if constexpr (ROPE) {
+    const int nq = a.nh * a.hd, nk = a.kv * a.hd;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = n0 + wn0 + j * 32 + (lane & 31);
+      const bool nok = n < a.N;
+      const bool rot = n < nq + nk;
+      const int d = n % a.hd;
+      const float b = (a.bias != nullptr && nok) ? bf16f(a.bias[n]) : 0.0f;
+      uint16_t* dst;
+      int64_t ld;
+      if (n < nq) {
+        dst = a.q_out + n;
+        ld = nq;
+      } else if (rot) {
+        dst = a.k_cache + a.P * nk + (n - nq);
+        ld = nk;
+      } else {
+        dst = a.v_cache + a.P * nk + (n - nq - nk);
+        ld = nk;
+      }
+      // a' = a c - b s on the even column, b' = b c + a s on the odd one
+      const float sgn = (n & 1) ? 1.0f : -1.0f;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const float v = __uint_as_float(f2bf(alpha * acc[i][j][r] + b) << 16);
+          const float p = lane_xor1(v);
+          if (nok && m < a.M) {
+            float o = v;
+            if (rot) {
+              const uint32_t cs = *reinterpret_cast<const uint32_t*>(a.rope + (int64_t)m * a.hd + (d & ~1));
+              o = __builtin_fmaf(v, bf16lo(cs), sgn * (p * bf16hi(cs)));
+            }
+            dst[(int64_t)m * ld] = (uint16_t)f2bf(o);
+          }
+        }
+      }
+    }
+    return;
+  }
   if constexpr (GLU) {
     // gate and up rounded to bf16 as the unfused GEMM output would be,
     // then the GEGLU quantiser of frt_ffn.hip
@@ -383,17 +434,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1, int AE = BM, bool GLU = false>
+template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1, int AE = BM, bool GLU = false,
+          bool ROPE = false>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   // (GLU: N = 2H, so this is also ceil(H / (BN / 2)) column tiles)
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
   if (a.K % (128 * NSUB) == 0)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU>), dim3(tiles), dim3(threads), 0,
-                       st, a);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE>), dim3(tiles),
+                       dim3(threads), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, true, NSUB, AE, GLU>), dim3(tiles), dim3(threads), 0,
-                       st, a);
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, true, NSUB, AE, GLU, ROPE>), dim3(tiles),
+                       dim3(threads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -436,7 +488,8 @@ int64_t plan_cost(const GemmArgs& a, int BM, int BN, int cus) {
 //    the 128 tiles of 64x64);
 //  M <= 64: 64x32 tiles with 256-deep stages (weight streaming), loading
 //    only the first 16 or 32 A rows when M is at most that.
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+template <bool ROPE>
+hipError_t launch_planned(const GemmArgs& a, hipStream_t st) {
   if (a.M > 64) {
     const int cus = device_cus();
     int best = 0;
@@ -446,19 +499,25 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     for (int p = 0; p < 4; ++p)
       if (cost[p] < c) c = cost[p], best = p;
     switch (best) {
-      case 0: return launch_tiles<256, 256, 128, 64, 2, 4>(a, st);
-      case 1: return launch_tiles<128, 128, 32, 32, 3, 2>(a, st);
-      case 2: return launch_tiles<64, 64, 32, 32, 4, 1>(a, st);
-      default: return launch_tiles<64, 32, 32, 32, 4, 1, 2>(a, st);
+      case 0: return launch_tiles<256, 256, 128, 64, 2, 4, 1, 256, false, ROPE>(a, st);
+      case 1: return launch_tiles<128, 128, 32, 32, 3, 2, 1, 128, false, ROPE>(a, st);
+      case 2: return launch_tiles<64, 64, 32, 32, 4, 1, 1, 64, false, ROPE>(a, st);
+      default: return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, ROPE>(a, st);
     }
   }
   // rows past M are not loaded (at M <= 16, 8 of every 12 load
   // instructions would only fetch zeros): M = 1 9.3 -> 8.8 us, M = 16
   // 9.8 -> 9.3 us for 6144 x 4096 weights
-  if (a.M <= 16) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 16>(a, st);
-  if (a.M <= 32) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 32>(a, st);
-  return launch_tiles<64, 32, 32, 32, 4, 1, 2>(a, st);
+  if (a.M <= 16) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 16, false, ROPE>(a, st);
+  if (a.M <= 32) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 32, false, ROPE>(a, st);
+  return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, ROPE>(a, st);
 }
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) { return launch_planned<false>(a, st); }
+
+// The RoPE epilogue runs on the split plans (any tile keeps a rotary pair in
+// adjacent lanes).
+hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st) { return launch_planned<true>(a, st); }
 
 // GEGLU plans: the same tiles with 64-column wave tiles (a gate/up pair per
 // lane), chosen by plan_cost: 256x256 (M >= 512), 128x128 of eight 32x64

@@ -69,6 +69,13 @@ struct GemmArgs {
   int H;
   uint8_t* q8; int64_t ld_q8;
   const float* q_scale;
+  // QKV split + RoPE + KV-cache epilogue (launch_gemm_rope): N = (nh + 2kv)
+  // hd columns q | k | v, q/k rows pair-interleaved; token m uses rope row
+  // m, writes q_out row m and cache row P + m
+  const uint16_t* rope;
+  int nh, kv, hd;
+  int64_t P;
+  uint16_t* q_out; uint16_t* k_cache; uint16_t* v_cache;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -85,5 +92,19 @@ struct GegluArgs {
 };
 
 hipError_t launch_geglu(const GegluArgs& a, int vec, hipStream_t st);
+
+hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st);
+
+struct RopeArgs {
+  const uint16_t* qkv; int64_t ld_qkv;
+  const uint16_t* rope;
+  int nh, kv, hd;
+  int64_t S, P;
+  uint16_t* q_out; uint16_t* k_cache; uint16_t* v_cache;
+};
+
+hipError_t launch_rope_split(const RopeArgs& a, int vec, hipStream_t st);
+hipError_t launch_interleave(const uint16_t* src, uint16_t* dst, int nheads, int hd, int64_t K, int vec,
+                             hipStream_t st);
 
 }  // namespace frt

@@ -224,3 +224,51 @@ def test_gemm_geglu_refusals(lib):
     assert _gemm_geglu(lib, out_fp8=FAKE + MB + 2 * 256 * 512 - 64) == frt.FRT_E_INVALID
     assert "overlaps" in frt.frt_last_error()
     assert _gemm_geglu(lib, M=0) == frt.FRT_OK
+
+
+def test_interleave_refusals(lib):
+    f = lib.frt_interleave_pairs_bf16
+    assert f(None, 2, 7, 64, FAKE, FAKE + MB) == frt.FRT_E_INVALID      # odd hd
+    assert f(None, 0, 8, 64, FAKE, FAKE + MB) == frt.FRT_E_INVALID
+    assert f(None, 2, 8, 0, FAKE, FAKE + MB) == frt.FRT_E_INVALID
+    assert f(None, 2, 8, 64, FAKE, None) == frt.FRT_E_INVALID
+    assert f(None, 2, 8, 64, FAKE, FAKE + 64) == frt.FRT_E_INVALID       # overlap
+    assert "overlaps" in frt.frt_last_error()
+
+
+def _rope(lib, S=4, nh=2, kv=1, hd=64, P=8, T=16, **kw):
+    a = dict(stream=None, S=S, nh=nh, kv=kv, hd=hd, qkv=FAKE, ld_qkv=(nh + 2 * kv) * hd,
+             rope=FAKE + MB, P=P, T=T, q_out=FAKE + 2 * MB, k_cache=FAKE + 3 * MB,
+             v_cache=FAKE + 4 * MB)
+    a.update(kw)
+    return lib.frt_qkv_split_rope_kvcache(*a.values())
+
+
+def test_rope_split_refusals(lib):
+    assert _rope(lib, hd=63) == frt.FRT_E_INVALID
+    assert _rope(lib, kv=0) == frt.FRT_E_INVALID
+    assert _rope(lib, P=13) == frt.FRT_E_INVALID          # P + S > T
+    assert "cache rows" in frt.frt_last_error()
+    assert _rope(lib, ld_qkv=100) == frt.FRT_E_INVALID
+    assert _rope(lib, rope=None) == frt.FRT_E_INVALID
+    assert _rope(lib, rope=FAKE + MB + 2) == frt.FRT_E_INVALID   # 4-byte rope
+    # the written k rows over the v cache's written rows
+    assert _rope(lib, v_cache=FAKE + 3 * MB) == frt.FRT_E_INVALID
+    assert _rope(lib, q_out=FAKE + 64) == frt.FRT_E_INVALID       # over qkv
+    assert _rope(lib, S=0) == frt.FRT_OK
+
+
+def test_gemm_rope_refusals(lib):
+    def call(**kw):
+        a = dict(stream=None, M=16, K=512, x8=FAKE, ld_x=512, W8=FAKE + MB, nh=2, kv=1, hd=64,
+                 act_scale=FAKE + 30 * MB, w_scale=FAKE + 31 * MB, bias=None,
+                 rope=FAKE + 32 * MB, P=0, T=16, q_out=FAKE + 40 * MB,
+                 k_cache=FAKE + 41 * MB, v_cache=FAKE + 42 * MB)
+        a.update(kw)
+        return lib.frt_packed_gemm_fp8_qkv_rope(*a.values())
+    assert call(K=520) == frt.FRT_E_UNSUPPORTED
+    assert call(hd=3) == frt.FRT_E_INVALID
+    assert call(T=15) == frt.FRT_E_INVALID
+    assert call(q_out=FAKE + MB) == frt.FRT_E_INVALID      # over W8
+    assert call(w_scale=None) == frt.FRT_E_INVALID
+    assert call(M=0) == frt.FRT_OK
