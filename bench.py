@@ -25,6 +25,12 @@ projection: the gate/up GEMM runs with the GEGLU quantiser as its epilogue
 (FP8 codes out instead of the bf16 gate|up output) and the down projection
 consumes those codes. The unfused pair (bf16 gate/up GEMM, standalone GEGLU
 quantiser) is timed beside it for comparison but is not part of the step.
+
+``--rope`` (workload 2) makes the QKV GEMM feed the attention head directly:
+its epilogue splits q | k | v, rotates q and k by adjacent-pair RoPE (the q
+and k weight rows pair-interleaved at bind) and writes q and the suffix
+rows of the K/V caches; the unfused pair (bf16 QKV GEMM, standalone split +
+RoPE + cache kernel) is timed beside it.
 """
 
 from __future__ import annotations
@@ -61,6 +67,9 @@ def parse():
     p.add_argument("--ffn", action="store_true",
                    help="workloads 2 and 5: fuse GEGLU + FP8 into the gate/up "
                         "GEMM and append the down projection")
+    p.add_argument("--rope", action="store_true",
+                   help="workload 2: the QKV GEMM writes RoPE'd q and the KV "
+                        "caches through its epilogue")
     p.add_argument("--kernel-reps", type=int, default=20)
     p.add_argument("--hbm-calibration", action="store_true",
                    help="time a plain device copy of known size (HBM ceiling, "
@@ -95,7 +104,7 @@ class Step:
     """Device buffers of one rotation set and the launches of one step."""
 
 
-def build_sets(wid, rows, frt, torch):
+def build_sets(wid, rows, frt, torch, rope=False):
     import workloads as wl
     w = wl.WORKLOADS[wid]
     inp = wl.producer_inputs(wid, rows=rows)
@@ -154,6 +163,13 @@ def build_sets(wid, rows, frt, torch):
     for site in range(len(w.gemms)):
         ww = wl.weights(wid, site)
         Ws = [bf16_dev(x) for x in ww["W"]]
+        if rope and site == 0:
+            # q and k rows pair-interleaved before packing (bind time)
+            nh, kv, hd = wl.QKV_HEADS[wid]
+            for i, heads in ((0, nh), (1, kv)):
+                t = torch.empty_like(Ws[i])
+                frt.frt_interleave_pairs_bf16(Ws[i], t, heads, hd)
+                Ws[i] = t
         bs = [None if b is None else bf16_dev(b) for b in ww["b"]]
         N = sum(ww["splits"])
         W8 = torch.empty(N, D, dtype=torch.uint8, device="cuda")
@@ -238,6 +254,20 @@ def make_rotation(w, dev, packs, rows, torch, ffn=None):
     return sets, per
 
 
+def make_rope(w, rows, torch):
+    """Rope table, q output and the K/V caches of the attention head."""
+    import workloads as wl
+    nh, kv, hd = wl.QKV_HEADS[w.cid]
+    P = wl.ROPE_PREFIX[w.cid]
+    T = P + rows
+    return {"nh": nh, "kv": kv, "hd": hd, "P": P, "T": T,
+            "table": bf16_dev(wl.rope_table(rows, hd, P)),
+            "q": torch.empty(rows, nh, hd, dtype=torch.bfloat16, device="cuda"),
+            "kc": torch.zeros(T, kv, hd, dtype=torch.bfloat16, device="cuda"),
+            "vc": torch.zeros(T, kv, hd, dtype=torch.bfloat16, device="cuda"),
+            "qkv": torch.empty(rows, (nh + 2 * kv) * hd, dtype=torch.bfloat16, device="cuda")}
+
+
 def make_outputs(w, rows, packs, torch, ffn=None):
     D = w.D
     o = {"x8": [torch.empty(rows, D, dtype=torch.uint8, device="cuda")
@@ -283,6 +313,11 @@ def step_launches(w, s, act, outs, rows, frt, eps):
         L.append(("gemm2", lambda: frt.frt_packed_gemm_fp8_split(
             outs["x8"][1], p1["W8"], act[1], p1["ws"], outs["gemm"][1],
             p1["splits"], bias_cat=p1["bias"])))
+    r = s.get("rope")
+    if r is not None:
+        L[1] = ("gemm1_rope", lambda: frt.frt_packed_gemm_fp8_qkv_rope(
+            outs["x8"][0], p0["W8"], act[0], p0["ws"], r["nh"], r["kv"], r["hd"],
+            r["table"], r["P"], r["q"], r["kc"], r["vc"], bias_cat=p0["bias"]))
     f = s.get("ffn")
     if f is not None:
         last, pl = L[-1][0], s["packs"][-1]
@@ -295,20 +330,42 @@ def step_launches(w, s, act, outs, rows, frt, eps):
 
 
 def unfused_launches(w, s, act, outs, frt):
-    """The unfused form of the fused gate/up GEGLU launch (timed for
-    comparison only): the bf16 gate|up GEMM and the standalone quantiser."""
-    f, pl = s["ffn"], s["packs"][-1]
-    H = f["H"]
-    return [("gateup_bf16", lambda: frt.frt_packed_gemm_fp8_split(
-                outs["x8"][-1], pl["W8"], act[-1], pl["ws"], [outs["gu"]], [2 * H],
-                bias_cat=pl["bias"])),
-            ("geglu", lambda: frt.frt_geglu_quant_fp8(
-                outs["gu"], H, f["scale"], out_fp8=outs["hid8_unfused"]))]
+    """The unfused forms of the fused launches (timed for comparison only):
+    the bf16 gate|up GEMM and the standalone GEGLU quantiser; the bf16 QKV
+    GEMM and the standalone split + RoPE + cache kernel."""
+    L = []
+    f = s.get("ffn")
+    if f is not None:
+        pl = s["packs"][-1]
+        H = f["H"]
+        L += [("gateup_bf16", lambda: frt.frt_packed_gemm_fp8_split(
+                  outs["x8"][-1], pl["W8"], act[-1], pl["ws"], [outs["gu"]], [2 * H],
+                  bias_cat=pl["bias"])),
+              ("geglu", lambda: frt.frt_geglu_quant_fp8(
+                  outs["gu"], H, f["scale"], out_fp8=outs["hid8_unfused"]))]
+    r = s.get("rope")
+    if r is not None:
+        p0 = s["packs"][0]
+        width = (r["nh"] + 2 * r["kv"]) * r["hd"]
+        L += [("qkv_bf16", lambda: frt.frt_packed_gemm_fp8_split(
+                  outs["x8"][0], p0["W8"], act[0], p0["ws"], [r["qkv"]], [width],
+                  bias_cat=p0["bias"])),
+              ("rope_split", lambda: frt.frt_qkv_split_rope_kvcache(
+                  r["qkv"], r["table"], r["nh"], r["kv"], r["hd"], r["P"],
+                  r["q"], r["kc"], r["vc"]))]
+    return L
 
 
-def kernel_work(w, kind, rows, packs, ffn=None):
+def kernel_work(w, kind, rows, packs, ffn=None, rope=None):
     """Algorithmic bytes and FLOPs of one launch."""
     D = w.D
+    if rope is not None and kind in ("gemm1_rope", "qkv_bf16", "rope_split"):
+        N = (rope["nh"] + 2 * rope["kv"]) * rope["hd"]
+        table = rows * rope["hd"] * 2
+        if kind == "rope_split":        # bf16 qkv in, q + k/v rows out, table
+            return rows * N * 2 * 2 + table, 0.0
+        out = rows * N * 2 + (table if kind == "gemm1_rope" else 0)
+        return rows * D + N * D + out, 2.0 * rows * N * D
     if ffn is not None:
         H = ffn["H"]
         p = packs[-1]
@@ -603,7 +660,9 @@ def main():
     frt.load_library()
     w0 = wl.WORKLOADS[a.workload]
     rows = a.rows if a.rows is not None else w0.rows
-    w, dev, act, packs, pack_ms = build_sets(a.workload, rows, frt, torch)
+    if a.rope and a.workload not in wl.QKV_HEADS:
+        raise SystemExit(f"--rope: the attention head is defined for workloads {sorted(wl.QKV_HEADS)}")
+    w, dev, act, packs, pack_ms = build_sets(a.workload, rows, frt, torch, rope=a.rope)
     ffn = None
     if a.ffn:
         if a.workload not in wl.FFN_HIDDEN:
@@ -612,6 +671,10 @@ def main():
         ffn = build_ffn(w, rows, act, packs, frt, torch)
     sets, per_set = make_rotation(w, dev, packs, rows, torch, ffn)
     outs = make_outputs(w, rows, packs, torch, ffn)
+    rp = make_rope(w, rows, torch) if a.rope else None
+    if rp is not None:
+        for st in sets:
+            st["rope"] = rp
     nset = len(sets)
 
     steps_fns = [step_launches(w, s, act, outs, rows, frt, wl.EPS) for s in sets]
@@ -673,7 +736,7 @@ def main():
     kinds = [k for k, _ in steps_fns[0]]
     timed = [[fn for _, fn in st] for st in steps_fns]
     all_kinds = list(kinds)
-    if ffn is not None:
+    if ffn is not None or rp is not None:
         extra = [unfused_launches(w, s, act, outs, frt) for s in sets]
         all_kinds += [k for k, _ in extra[0]]
         timed = [t + [fn for _, fn in e] for t, e in zip(timed, extra)]
@@ -682,7 +745,7 @@ def main():
         g = capture([timed[s][ki] for s in range(nset)], torch)
         prewarm(g, 0.3, torch)
         us = time_graph(g, a.kernel_reps, torch) * 1e3 / nset
-        b, f = kernel_work(w, kind, rows, packs, ffn)
+        b, f = kernel_work(w, kind, rows, packs, ffn, rp)
         row = {"kernel": kind, "us": round(us, 3), "bytes": int(b),
                "GB/s": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
         if f:
@@ -696,8 +759,8 @@ def main():
         table.append(row)
         del g
 
-    gemm_flops = sum(kernel_work(w, k, rows, packs, ffn)[1] for k in kinds)
-    norm_bytes = sum(kernel_work(w, k, rows, packs, ffn)[0] for k in kinds if k.startswith("norm"))
+    gemm_flops = sum(kernel_work(w, k, rows, packs, ffn, rp)[1] for k in kinds)
+    norm_bytes = sum(kernel_work(w, k, rows, packs, ffn, rp)[0] for k in kinds if k.startswith("norm"))
     norm_us = sum(r["us"] for r in table if r["kernel"].startswith("norm"))
     dom = max((r for r in table if r["kernel"] in kinds), key=lambda r: r["us"])
     traffic = load_traffic(a.workload, dom["kernel"]) if a.rows is None else None
@@ -718,7 +781,8 @@ def main():
         "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": w.name + ("+ffn_geglu_down" if ffn is not None else ""),
+        "config": {"workload": w.name + ("+qkv_rope_kvcache" if rp is not None else "")
+                               + ("+ffn_geglu_down" if ffn is not None else ""),
                    "rows": rows, "D": w.D,
                    "gemms": [list(g) for g in w.gemms], "bias": w.bias,
                    "rotation_sets": nset, "rotation_mib": round(nset * per_set / 2**20, 1),
@@ -733,7 +797,9 @@ def main():
     }
     if ffn is not None:
         res["config"]["ffn"] = {"H": ffn["H"], "down": [w.D, ffn["H"]]}
-    if not a.no_cpu_baseline and ffn is None:
+    if rp is not None:
+        res["config"]["rope"] = {k: rp[k] for k in ("nh", "kv", "hd", "P", "T")}
+    if not a.no_cpu_baseline and ffn is None and rp is None:
         res["cpu_baseline"] = cpu_baseline(w, rows)
     print(json.dumps(res), flush=True)
 
