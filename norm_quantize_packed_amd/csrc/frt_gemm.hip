@@ -356,19 +356,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       const float sgn = (n & 1) ? 1.0f : -1.0f;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
+        // the (cos, sin) words of this lane's 16 rows, loaded together (rows
+        // past M read row M - 1 and are not stored)
+        uint32_t cs[16];
+        const uint16_t* rp = a.rope + (d & ~1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = min(m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), a.M - 1);
+          cs[r] = rot ? *reinterpret_cast<const uint32_t*>(rp + (int64_t)m * a.hd) : 0u;
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
           const float v = __uint_as_float(f2bf(alpha * acc[i][j][r] + b) << 16);
           const float p = lane_xor1(v);
-          if (nok && m < a.M) {
-            float o = v;
-            if (rot) {
-              const uint32_t cs = *reinterpret_cast<const uint32_t*>(a.rope + (int64_t)m * a.hd + (d & ~1));
-              o = __builtin_fmaf(v, bf16lo(cs), sgn * (p * bf16hi(cs)));
-            }
-            dst[(int64_t)m * ld] = (uint16_t)f2bf(o);
-          }
+          const float o = rot ? __builtin_fmaf(v, bf16lo(cs[r]), sgn * (p * bf16hi(cs[r]))) : v;
+          if (nok && m < a.M) dst[(int64_t)m * ld] = (uint16_t)f2bf(o);
         }
       }
     }
