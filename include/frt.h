@@ -17,7 +17,9 @@
  *     standalone or as the gate/up GEMM's epilogue;
  *   - fp8_chain.py's attention head: the merged QKV output split, rotated
  *     by adjacent-pair RoPE and written to q and the KV caches, standalone
- *     or as the QKV GEMM's epilogue.
+ *     or as the QKV GEMM's epilogue;
+ *   - projections without a producer: the static quantiser of a bf16
+ *     tensor and the bf16-input form of the packed GEMM.
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers unless marked [host].
@@ -312,6 +314,64 @@ int frt_packed_gemm_fp8_geglu_quant(void* stream, int64_t M, int64_t K,
                                     const uint16_t* bias_cat,
                                     const float* out_scale,
                                     uint8_t* out_fp8, int64_t ld_out);
+
+/*
+ * frt_quantize_fp8_static — static per-tensor FP8 of a bf16 tensor (the
+ * producers' quantiser without a norm).
+ *
+ * Source: fp8_chain.py `_band_elements` (`out_project`: the attention
+ * output quantised by `quantize_fp8_static_bf16` before the O projection's
+ * FP8 GEMM) and impls/linear_proj/fp8_static.py (the quantize that
+ * precedes the FP8 GEMM when the projection's input arrives in bf16).
+ * For m < M, j < D:
+ *   out_fp8[m, j] = e4m3_rne(clamp(fl32(x[m, j] / act_scale), -448, 448))
+ * (x is exact in fp32; the division is correctly rounded, so the codes are
+ * bit-exact to the definition).
+ *
+ *   M, D          rows; row width (1 <= D <= 2^24).
+ *   x             bf16 [M, ld_x].
+ *   act_scale     fp32 [1] (> 0). Required iff out_fp8.
+ *   out_fp8       e4m3fn [M, ld_out]; NULL => not written.
+ *   amax_out      fp32 [1] raised to max |x| (calibration); NULL => off.
+ * At least one output; outputs must not overlap x. D % 8 == 0 with x
+ * 16-byte aligned, ld_x % 8 == 0 and out_fp8 8-byte aligned with
+ * ld_out % 8 == 0 takes the vector path.
+ */
+int frt_quantize_fp8_static(void* stream, int64_t M, int64_t D,
+                            const uint16_t* x, int64_t ld_x,
+                            const float* act_scale,
+                            uint8_t* out_fp8, int64_t ld_out,
+                            float* amax_out);
+
+/*
+ * frt_packed_gemm_bf16in_split — the packed FP8 GEMM for a projection whose
+ * input arrives in bf16: the input is quantised with the static scale into
+ * the caller's FP8 buffer x8, then the GEMM runs on it.
+ *
+ * Source: qkv_pack/fp8_static.py `PackedLinear._run` (the non-FP8 input
+ * form: `bf16_fp8_linear_bias_bf16(flat, w8, bias_cat, act_scale, w_scale,
+ * input_fp8=x8_buf, out=...)`) and impls/linear_proj/fp8_static.py (the
+ * fused-quantize form). Exactly frt_quantize_fp8_static(x -> x8) followed
+ * by frt_packed_gemm_fp8_split(x8, ...): two launches, the bias added in
+ * the GEMM's epilogue.
+ *
+ *   x             bf16 [M, ld_x], ld_x >= K.
+ *   x8            e4m3fn [M, ld_x8] written with the codes of x (the
+ *                 contract of frt_packed_gemm_fp8_split's x8: 16-byte
+ *                 aligned, ld_x8 >= K and a multiple of 16); must not
+ *                 overlap x, the weights, scales, bias or outputs.
+ *   all other arguments as in frt_packed_gemm_fp8_split.
+ * Every check runs before the first launch.
+ */
+int frt_packed_gemm_bf16in_split(void* stream, int64_t M, int64_t K,
+                                 const uint16_t* x, int64_t ld_x,
+                                 uint8_t* x8, int64_t ld_x8,
+                                 const uint8_t* W8, int64_t N_total,
+                                 const float* act_scale, const float* w_scale,
+                                 const uint16_t* bias_cat, int n_split,
+                                 const int64_t* split_n, void* const* out,
+                                 const int64_t* ld_out, int out_dtype,
+                                 void* workspace, size_t ws_bytes);
 
 /*
  * frt_interleave_pairs_bf16 — the pack-time permutation of q or k

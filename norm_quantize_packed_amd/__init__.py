@@ -26,6 +26,7 @@ __all__ = [
     "frt_pack_weights_fp8", "frt_packed_gemm_fp8_workspace_size",
     "frt_packed_gemm_fp8_split", "frt_geglu_quant_fp8",
     "frt_packed_gemm_fp8_geglu_quant", "frt_interleave_pairs_bf16",
+    "frt_quantize_fp8_static", "frt_packed_gemm_bf16in_split",
     "frt_qkv_split_rope_kvcache", "frt_packed_gemm_fp8_qkv_rope",
     "frt_last_error", "frt_abi_version",
     "FRT_OK", "FRT_E_INVALID", "FRT_E_UNSUPPORTED", "FRT_E_HIP",
@@ -65,6 +66,11 @@ _SIGNATURES = {
     "frt_packed_gemm_fp8_geglu_quant": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _p, _p, _i64]),
     "frt_interleave_pairs_bf16": (_i32, [_p, _i32, _i32, _i64, _p, _p]),
+    "frt_quantize_fp8_static": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p, _i64, _p]),
+    "frt_packed_gemm_bf16in_split": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i32,
+        ctypes.POINTER(_i64), ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32,
+        _p, _sz]),
     "frt_qkv_split_rope_kvcache": (_i32, [
         _p, _i64, _i32, _i32, _i32, _p, _i64, _p, _i64, _i64, _p, _p, _p]),
     "frt_packed_gemm_fp8_qkv_rope": (_i32, [
@@ -418,3 +424,42 @@ def frt_packed_gemm_fp8_qkv_rope(x8, W8, act_scale, w_scale, nh: int, kv: int,
         int(nh), int(kv), int(hd), _ptr(act_scale), _ptr(w_scale),
         _ptr(bias_cat), _ptr(rope), int(P), int(T), _ptr(q_out),
         _ptr(k_cache), _ptr(v_cache)))
+
+
+def frt_quantize_fp8_static(x, act_scale=None, *, out_fp8=None, amax_out=None,
+                            M: Optional[int] = None, stream=None) -> None:
+    """Static per-tensor FP8 of a bf16 ``[M, D]`` tensor."""
+    _bf16_like(x, "x")
+    _u8_like(out_fp8, "out_fp8")
+    for t, n in ((act_scale, "act_scale"), (amax_out, "amax_out")):
+        _f32_like(t, n)
+    Mv = x.shape[0] if M is None else int(M)
+    _check(load_library().frt_quantize_fp8_static(
+        _stream(stream), Mv, int(x.shape[-1]), _ptr(x), _ld(x), _ptr(act_scale),
+        _ptr(out_fp8), _ld(out_fp8), _ptr(amax_out)))
+
+
+def frt_packed_gemm_bf16in_split(x, x8, W8, act_scale, w_scale, outs: Sequence,
+                                 split_n: Sequence[int], bias_cat=None, *,
+                                 M: Optional[int] = None, stream=None) -> None:
+    """bf16-input packed GEMM: ``x`` quantised into ``x8``, then
+    ``frt_packed_gemm_fp8_split`` on it."""
+    import torch
+    _bf16_like(x, "x")
+    _u8_like(x8, "x8")
+    _u8_like(W8, "W8")
+    _f32_like(act_scale, "act_scale")
+    _f32_like(w_scale, "w_scale")
+    _bf16_like(bias_cat, "bias_cat")
+    n = len(split_n)
+    if len(outs) != n:
+        raise ValueError("frt: one output per split")
+    dts = {o.dtype for o in outs}
+    out_dtype = 1 if dts == {torch.float32} else 0
+    Mv = x.shape[0] if M is None else int(M)
+    K = x.shape[1]
+    _check(load_library().frt_packed_gemm_bf16in_split(
+        _stream(stream), Mv, K, _ptr(x), _ld(x), _ptr(x8), _ld(x8), _ptr(W8),
+        int(W8.shape[0]), _ptr(act_scale), _ptr(w_scale), _ptr(bias_cat), n,
+        (_i64 * n)(*[int(v) for v in split_n]), (_p * n)(*[_ptr(o) for o in outs]),
+        (_i64 * n)(*[_ld(o) for o in outs]), out_dtype, 0, 0))

@@ -245,11 +245,17 @@ size_t frt_packed_gemm_fp8_workspace_size(int64_t M, int64_t N_total, int64_t K)
   return frt::gemm_workspace_bytes(M, N_total, K);
 }
 
-int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K, const uint8_t* x8, int64_t ld_x,
-                              const uint8_t* W8, int64_t N_total, const float* act_scale,
-                              const float* w_scale, const uint16_t* bias_cat, int n_split,
-                              const int64_t* split_n, void* const* out, const int64_t* ld_out,
-                              int out_dtype, void* workspace, size_t ws_bytes) {
+}  // extern "C"
+
+namespace {
+
+// Every check of the packed split GEMM's contract (shapes, strides,
+// alignment, splits, workspace, overlaps) and its kernel arguments; no
+// launch. FRT_OK with a.M == 0 means there is nothing to run.
+int gemm_prepare(int64_t M, int64_t K, const uint8_t* x8, int64_t ld_x, const uint8_t* W8, int64_t N_total,
+                 const float* act_scale, const float* w_scale, const uint16_t* bias_cat, int n_split,
+                 const int64_t* split_n, void* const* out, const int64_t* ld_out, int out_dtype, void* workspace,
+                 size_t ws_bytes, frt::GemmArgs& a) {
   if (M < 0) return refuse(FRT_E_INVALID, "gemm: M=%lld < 0", (long long)M);
   if (K < 512 || K > 16384) return refuse(FRT_E_INVALID, "gemm: K=%lld outside [512, 16384]", (long long)K);
   if (K % 16) return refuse(FRT_E_UNSUPPORTED, "gemm: K=%lld not a multiple of 16", (long long)K);
@@ -267,7 +273,7 @@ int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K, const uint8_t*
   if (split_n == nullptr || out == nullptr || ld_out == nullptr)
     return refuse(FRT_E_INVALID, "gemm: split_n, out and ld_out are required");
   const int64_t es = out_dtype ? 4 : 2;
-  frt::GemmArgs a{};
+  a = frt::GemmArgs{};
   int64_t tot = 0;
   for (int s = 0; s < n_split; ++s) {
     if (split_n[s] < 1) return refuse(FRT_E_INVALID, "gemm: split %d has width %lld < 1", s, (long long)split_n[s]);
@@ -287,7 +293,7 @@ int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K, const uint8_t*
   const size_t need = frt::gemm_workspace_bytes(M, N_total, K);
   if (need > 0 && (workspace == nullptr || ws_bytes < need))
     return refuse(FRT_E_INVALID, "gemm: workspace of %zu bytes required", need);
-  if (M == 0) return ok();
+  if (M == 0) return FRT_OK;
   // outputs must not overlap each other or the inputs
   const Range xin = span(x8, M, K, ld_x, 1), win = span(W8, N_total, K, K, 1),
               bin = span(bias_cat, 1, N_total, N_total, 2), sa = span(act_scale, 1, 1, 1, 4),
@@ -313,6 +319,23 @@ int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K, const uint8_t*
   a.N = (int)N_total;
   a.K = (int)K;
   a.out_f32 = out_dtype;
+  return FRT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K, const uint8_t* x8, int64_t ld_x,
+                              const uint8_t* W8, int64_t N_total, const float* act_scale,
+                              const float* w_scale, const uint16_t* bias_cat, int n_split,
+                              const int64_t* split_n, void* const* out, const int64_t* ld_out,
+                              int out_dtype, void* workspace, size_t ws_bytes) {
+  frt::GemmArgs a;
+  const int rc = gemm_prepare(M, K, x8, ld_x, W8, N_total, act_scale, w_scale, bias_cat, n_split, split_n, out,
+                              ld_out, out_dtype, workspace, ws_bytes, a);
+  if (rc != FRT_OK) return rc;
+  if (M == 0) return ok();
   return hip_status(frt::launch_gemm(a, (hipStream_t)stream), "gemm launch");
 }
 
@@ -385,6 +408,58 @@ int frt_packed_gemm_fp8_geglu_quant(void* stream, int64_t M, int64_t K, const ui
   a.ld_q8 = ld_out;
   a.q_scale = out_scale;
   return hip_status(frt::launch_gemm_geglu(a, (hipStream_t)stream), "gemm_geglu launch");
+}
+
+int frt_quantize_fp8_static(void* stream, int64_t M, int64_t D, const uint16_t* x, int64_t ld_x,
+                            const float* act_scale, uint8_t* out_fp8, int64_t ld_out, float* amax_out) {
+  if (M < 0) return refuse(FRT_E_INVALID, "quantize: M=%lld < 0", (long long)M);
+  if (D < 1 || D > (1 << 24)) return refuse(FRT_E_INVALID, "quantize: D=%lld outside [1, 2^24]", (long long)D);
+  if (x == nullptr) return refuse(FRT_E_INVALID, "quantize: x is required");
+  if (ld_x < D) return refuse(FRT_E_INVALID, "quantize: ld_x < D");
+  if (out_fp8 != nullptr && act_scale == nullptr) return refuse(FRT_E_INVALID, "quantize: out_fp8 needs act_scale");
+  if (out_fp8 != nullptr && ld_out < D) return refuse(FRT_E_INVALID, "quantize: ld_out < D");
+  if (out_fp8 == nullptr && amax_out == nullptr) return refuse(FRT_E_INVALID, "quantize: no output requested");
+  if (!aligned(x, 2)) return refuse(FRT_E_INVALID, "quantize: x misaligned");
+  if (M == 0) return ok();
+  const Range in[] = {span(x, M, D, ld_x, 2), span(act_scale, 1, 1, 1, 4)};
+  const Range outs[] = {span(out_fp8, M, D, ld_out, 1), span(amax_out, 1, 1, 1, 4)};
+  for (int o = 0; o < 2; ++o)
+    for (int i = 0; i < 2; ++i)
+      if (overlap(outs[o], in[i])) return refuse(FRT_E_INVALID, "quantize: output %d overlaps input %d", o, i);
+  if (overlap(outs[0], outs[1])) return refuse(FRT_E_INVALID, "quantize: outputs overlap");
+  const bool vec8 = D % 8 == 0 && aligned(x, 16) && ld_x % 8 == 0 &&
+                    (out_fp8 == nullptr || (aligned(out_fp8, 8) && ld_out % 8 == 0));
+  frt::GegluArgs a{x, ld_x, act_scale, out_fp8, ld_out, nullptr, 0, amax_out, M, (int)D};
+  return hip_status(frt::launch_quant(a, vec8 ? 8 : 1, (hipStream_t)stream), "quantize launch");
+}
+
+int frt_packed_gemm_bf16in_split(void* stream, int64_t M, int64_t K, const uint16_t* x, int64_t ld_x, uint8_t* x8,
+                                 int64_t ld_x8, const uint8_t* W8, int64_t N_total, const float* act_scale,
+                                 const float* w_scale, const uint16_t* bias_cat, int n_split,
+                                 const int64_t* split_n, void* const* out, const int64_t* ld_out, int out_dtype,
+                                 void* workspace, size_t ws_bytes) {
+  if (x == nullptr || x8 == nullptr) return refuse(FRT_E_INVALID, "gemm_bf16in: x and x8 are required");
+  if (ld_x < K) return refuse(FRT_E_INVALID, "gemm_bf16in: ld_x < K");
+  if (!aligned(x, 2)) return refuse(FRT_E_INVALID, "gemm_bf16in: x misaligned");
+  // the GEMM's whole contract on the FP8 operand the call writes
+  frt::GemmArgs a;
+  const int rc = gemm_prepare(M, K, x8, ld_x8, W8, N_total, act_scale, w_scale, bias_cat, n_split, split_n, out,
+                              ld_out, out_dtype, workspace, ws_bytes, a);
+  if (rc != FRT_OK) return rc;
+  if (M == 0) return ok();
+  const Range xr = span(x, M, K, ld_x, 2), x8r = span(x8, M, K, ld_x8, 1);
+  if (overlap(x8r, xr) || overlap(x8r, span(W8, N_total, K, K, 1)) || overlap(x8r, span(act_scale, 1, 1, 1, 4)) ||
+      overlap(x8r, span(w_scale, 1, 1, 1, 4)) || overlap(x8r, span(bias_cat, 1, N_total, N_total, 2)))
+    return refuse(FRT_E_INVALID, "gemm_bf16in: x8 overlaps an input");
+  for (int s = 0; s < n_split; ++s) {
+    const Range o = span(out[s], M, split_n[s], ld_out[s], out_dtype ? 4 : 2);
+    if (overlap(o, xr) || overlap(o, x8r)) return refuse(FRT_E_INVALID, "gemm_bf16in: output %d overlaps x or x8", s);
+  }
+  const bool vec8 = K % 8 == 0 && aligned(x, 16) && ld_x % 8 == 0;  // x8: 16-byte aligned, ld % 16 (GEMM contract)
+  frt::GegluArgs q{x, ld_x, act_scale, x8, ld_x8, nullptr, 0, nullptr, M, (int)K};
+  const hipError_t e = frt::launch_quant(q, vec8 ? 8 : 1, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_status(e, "gemm_bf16in quantize launch");
+  return hip_status(frt::launch_gemm(a, (hipStream_t)stream), "gemm_bf16in launch");
 }
 
 int frt_interleave_pairs_bf16(void* stream, int nheads, int hd, int64_t K, const uint16_t* src, uint16_t* dst) {

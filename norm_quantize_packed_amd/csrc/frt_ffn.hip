@@ -14,6 +14,12 @@
 // the gate and the up half cover 64 consecutive 16-byte vectors (VEC = 8).
 // The same epilogue also runs inside the gate/up GEMM (frt_gemm.hip), which
 // skips the bf16 round trip through HBM.
+//
+// quant_kernel: the plain static quantiser of a bf16 tensor (fp8_chain.py
+// `_band_elements`, `out_project`: `quantize_fp8_static_bf16` of the
+// attention output before the O projection; impls/linear_proj/
+// fp8_static.py: the quantize that precedes the FP8 GEMM when the input
+// arrives in bf16).
 #include "frt_device.h"
 #include "frt_internal.h"
 
@@ -84,7 +90,69 @@ __global__ __launch_bounds__(256) void geglu_kernel(GegluArgs a) {
   }
 }
 
+// Static per-tensor FP8 of a bf16 tensor (the producers minus their norm):
+// out[m, j] = e4m3_rne(clamp(fl32(x[m, j] / act_scale), -448, 448)), the
+// same layout as geglu_kernel (x in the gate slot, no up half).
+template <int VEC>
+__global__ __launch_bounds__(256) void quant_kernel(GegluArgs a) {
+  const int nv = a.H / VEC;
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  const bool ok = v < nv;
+  float s = 1.0f, rcp = 1.0f;
+  if (a.out != nullptr) {
+    s = *a.act_scale;
+    rcp = 1.0f / s;
+  }
+  float amax = 0.0f;
+  for (int64_t m = blockIdx.y; m < a.M && ok; m += gridDim.y) {
+    const uint16_t* row = a.gu + m * a.ld_gu;
+    const int64_t c = (int64_t)v * VEC;
+    float y[VEC];
+    if constexpr (VEC == 8) {
+      const uint4 g = *reinterpret_cast<const uint4*>(row + c);
+      const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (e & 1) ? bf16hi(gw[e >> 1]) : bf16lo(gw[e >> 1]);
+    } else {
+      y[0] = bf16f(row[c]);
+    }
+    if (a.amax != nullptr) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+        amax = __uint_as_float(max(__float_as_uint(amax), __float_as_uint(fabsf(y[e]))));
+    }
+    if (a.out != nullptr) {
+      float q[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) q[e] = clamp_fp8(div_rn(y[e], s, rcp));
+      uint8_t* op = a.out + m * a.ld_out + c;
+      if constexpr (VEC == 8) {
+        uint2 t;
+        t.x = cvt4_fp8(q[0], q[1], q[2], q[3]);
+        t.y = cvt4_fp8(q[4], q[5], q[6], q[7]);
+        *reinterpret_cast<uint2*>(op) = t;
+      } else {
+        op[0] = (uint8_t)cvt2_fp8(q[0], 0.0f);
+      }
+    }
+  }
+  if (a.amax != nullptr) {
+    const uint32_t u = wave_umax(__float_as_uint(amax));
+    if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(a.amax), u);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quant(const GegluArgs& a, int vec, hipStream_t st) {
+  const int64_t nv = a.H / vec;
+  const dim3 grid((unsigned)((nv + 255) / 256), (unsigned)(a.M < 65535 ? a.M : 65535));
+  if (vec == 8)
+    hipLaunchKernelGGL((quant_kernel<8>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((quant_kernel<1>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_geglu(const GegluArgs& a, int vec, hipStream_t st) {
   const int64_t nv = a.H / vec;

@@ -92,6 +92,8 @@ struct GegluArgs {
 };
 
 hipError_t launch_geglu(const GegluArgs& a, int vec, hipStream_t st);
+// static FP8 of a bf16 [M, H] tensor (GegluArgs with gu = x, no up half)
+hipError_t launch_quant(const GegluArgs& a, int vec, hipStream_t st);
 
 hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st);
 

@@ -272,3 +272,32 @@ def test_gemm_rope_refusals(lib):
     assert call(q_out=FAKE + MB) == frt.FRT_E_INVALID      # over W8
     assert call(w_scale=None) == frt.FRT_E_INVALID
     assert call(M=0) == frt.FRT_OK
+
+
+def test_quantize_refusals(lib):
+    f = lib.frt_quantize_fp8_static
+    assert f(None, 4, 0, FAKE, 8, FAKE + MB, FAKE + 2 * MB, 8, None) == frt.FRT_E_INVALID
+    assert f(None, 4, 512, FAKE, 500, FAKE + MB, FAKE + 2 * MB, 512, None) == frt.FRT_E_INVALID
+    assert f(None, 4, 512, FAKE, 512, None, FAKE + 2 * MB, 512, None) == frt.FRT_E_INVALID
+    assert f(None, 4, 512, FAKE, 512, FAKE + MB, None, 0, None) == frt.FRT_E_INVALID
+    assert f(None, 4, 512, FAKE, 512, FAKE + MB, FAKE + 100, 512, None) == frt.FRT_E_INVALID
+    assert "overlaps" in frt.frt_last_error()
+    assert f(None, 0, 512, FAKE, 512, FAKE + MB, FAKE + 2 * MB, 512, None) == frt.FRT_OK
+
+
+def test_gemm_bf16in_refusals(lib):
+    def call(M=16, K=512, x=FAKE + 200 * MB, ld_x=512, x8=FAKE, ld_x8=512, **kw):
+        splits = (768,)
+        a = dict(stream=None, M=M, K=K, x=x, ld_x=ld_x, x8=x8, ld_x8=ld_x8, W8=FAKE + MB, N=768,
+                 act_scale=FAKE + 30 * MB, w_scale=FAKE + 31 * MB, bias=None, n_split=1,
+                 split_n=(ctypes.c_int64 * 1)(*splits), out=(ctypes.c_void_p * 1)(FAKE + 40 * MB),
+                 ld_out=(ctypes.c_int64 * 1)(768), out_dtype=0, ws=None, ws_bytes=0)
+        a.update(kw)
+        return lib.frt_packed_gemm_bf16in_split(*a.values())
+    assert call(x=None) == frt.FRT_E_INVALID
+    assert call(ld_x=100) == frt.FRT_E_INVALID
+    assert call(ld_x8=520) == frt.FRT_E_INVALID                   # the GEMM's x8 contract
+    assert call(x8=FAKE + 200 * MB + 64) == frt.FRT_E_INVALID     # x8 over x
+    assert call(x8=FAKE + MB) == frt.FRT_E_INVALID                # x8 over W8
+    assert call(x=FAKE + 40 * MB) == frt.FRT_E_INVALID            # output over x
+    assert call(M=0) == frt.FRT_OK
