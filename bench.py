@@ -31,6 +31,10 @@ its epilogue splits q | k | v, rotates q and k by adjacent-pair RoPE (the q
 and k weight rows pair-interleaved at bind) and writes q and the suffix
 rows of the K/V caches; the unfused pair (bf16 QKV GEMM, standalone split +
 RoPE + cache kernel) is timed beside it.
+
+``--oproj`` (workload 2) adds the O projection of a seeded attention output:
+the static FP8 quantiser and the packed GEMM. With ``--rope --oproj --ffn``
+a step is the whole decoder layer around the attention core.
 """
 
 from __future__ import annotations
@@ -67,6 +71,9 @@ def parse():
     p.add_argument("--ffn", action="store_true",
                    help="workloads 2 and 5: fuse GEGLU + FP8 into the gate/up "
                         "GEMM and append the down projection")
+    p.add_argument("--oproj", action="store_true",
+                   help="workload 2: quantise a seeded attention output and "
+                        "run the O projection")
     p.add_argument("--rope", action="store_true",
                    help="workload 2: the QKV GEMM writes RoPE'd q and the KV "
                         "caches through its epilogue")
@@ -254,6 +261,26 @@ def make_rotation(w, dev, packs, rows, torch, ffn=None):
     return sets, per
 
 
+def make_oproj(w, rows, frt, torch):
+    """O projection: packed W_o, the attention output and its calibrated
+    static scale, the FP8 input and the bf16 output buffers."""
+    import workloads as wl
+    inp, cal = wl.o_proj_inputs(w.cid), wl.o_proj_inputs(w.cid, calib=True)
+    Wo = bf16_dev(inp["W_o"])
+    W8 = torch.empty(Wo.shape, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(1, dtype=torch.float32, device="cuda")
+    frt.frt_pack_weights_fp8([Wo], None, W8, ws)
+    amax = torch.zeros(1, dtype=torch.float32, device="cuda")
+    frt.frt_quantize_fp8_static(bf16_dev(cal["att"]), None, amax_out=amax)
+    torch.cuda.synchronize()
+    s = np.float32(amax.item()) / np.float32(448.0)
+    att = bf16_dev(inp["att"])
+    return {"W8": W8, "ws": ws, "att": att,
+            "scale": torch.tensor([float(s)], dtype=torch.float32, device="cuda"),
+            "o8": torch.empty(att.shape, dtype=torch.uint8, device="cuda"),
+            "out": torch.empty(rows, w.D, dtype=torch.bfloat16, device="cuda")}
+
+
 def make_rope(w, rows, torch):
     """Rope table, q output and the K/V caches of the attention head."""
     import workloads as wl
@@ -313,6 +340,12 @@ def step_launches(w, s, act, outs, rows, frt, eps):
         L.append(("gemm2", lambda: frt.frt_packed_gemm_fp8_split(
             outs["x8"][1], p1["W8"], act[1], p1["ws"], outs["gemm"][1],
             p1["splits"], bias_cat=p1["bias"])))
+    o = s.get("oproj")
+    if o is not None:
+        L.insert(2, ("quant_o", lambda: frt.frt_quantize_fp8_static(
+            o["att"], o["scale"], out_fp8=o["o8"])))
+        L.insert(3, ("gemm_o", lambda: frt.frt_packed_gemm_fp8_split(
+            o["o8"], o["W8"], o["scale"], o["ws"], [o["out"]], [w.D])))
     r = s.get("rope")
     if r is not None:
         L[1] = ("gemm1_rope", lambda: frt.frt_packed_gemm_fp8_qkv_rope(
@@ -356,9 +389,14 @@ def unfused_launches(w, s, act, outs, frt):
     return L
 
 
-def kernel_work(w, kind, rows, packs, ffn=None, rope=None):
+def kernel_work(w, kind, rows, packs, ffn=None, rope=None, oproj=None):
     """Algorithmic bytes and FLOPs of one launch."""
     D = w.D
+    if oproj is not None and kind in ("quant_o", "gemm_o"):
+        Ko = oproj["att"].shape[1]
+        if kind == "quant_o":           # bf16 in, codes out
+            return rows * Ko * 3, 0.0
+        return rows * Ko + D * Ko + rows * D * 2, 2.0 * rows * D * Ko
     if rope is not None and kind in ("gemm1_rope", "qkv_bf16", "rope_split"):
         N = (rope["nh"] + 2 * rope["kv"]) * rope["hd"]
         table = rows * rope["hd"] * 2
@@ -660,7 +698,7 @@ def main():
     frt.load_library()
     w0 = wl.WORKLOADS[a.workload]
     rows = a.rows if a.rows is not None else w0.rows
-    if a.rope and a.workload not in wl.QKV_HEADS:
+    if (a.rope or a.oproj) and a.workload not in wl.QKV_HEADS:
         raise SystemExit(f"--rope: the attention head is defined for workloads {sorted(wl.QKV_HEADS)}")
     w, dev, act, packs, pack_ms = build_sets(a.workload, rows, frt, torch, rope=a.rope)
     ffn = None
@@ -672,9 +710,12 @@ def main():
     sets, per_set = make_rotation(w, dev, packs, rows, torch, ffn)
     outs = make_outputs(w, rows, packs, torch, ffn)
     rp = make_rope(w, rows, torch) if a.rope else None
-    if rp is not None:
-        for st in sets:
+    op = make_oproj(w, rows, frt, torch) if a.oproj else None
+    for i, st in enumerate(sets):
+        if rp is not None:
             st["rope"] = rp
+        if op is not None:   # each rotation set streams its own W_o copy
+            st["oproj"] = dict(op, W8=op["W8"] if i == 0 else op["W8"].clone())
     nset = len(sets)
 
     steps_fns = [step_launches(w, s, act, outs, rows, frt, wl.EPS) for s in sets]
@@ -745,7 +786,7 @@ def main():
         g = capture([timed[s][ki] for s in range(nset)], torch)
         prewarm(g, 0.3, torch)
         us = time_graph(g, a.kernel_reps, torch) * 1e3 / nset
-        b, f = kernel_work(w, kind, rows, packs, ffn, rp)
+        b, f = kernel_work(w, kind, rows, packs, ffn, rp, op)
         row = {"kernel": kind, "us": round(us, 3), "bytes": int(b),
                "GB/s": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
         if f:
@@ -759,8 +800,8 @@ def main():
         table.append(row)
         del g
 
-    gemm_flops = sum(kernel_work(w, k, rows, packs, ffn, rp)[1] for k in kinds)
-    norm_bytes = sum(kernel_work(w, k, rows, packs, ffn, rp)[0] for k in kinds if k.startswith("norm"))
+    gemm_flops = sum(kernel_work(w, k, rows, packs, ffn, rp, op)[1] for k in kinds)
+    norm_bytes = sum(kernel_work(w, k, rows, packs, ffn, rp, op)[0] for k in kinds if k.startswith("norm"))
     norm_us = sum(r["us"] for r in table if r["kernel"].startswith("norm"))
     dom = max((r for r in table if r["kernel"] in kinds), key=lambda r: r["us"])
     traffic = load_traffic(a.workload, dom["kernel"]) if a.rows is None else None
@@ -782,6 +823,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
         "data": "synthetic",
         "config": {"workload": w.name + ("+qkv_rope_kvcache" if rp is not None else "")
+                               + ("+o_proj" if op is not None else "")
                                + ("+ffn_geglu_down" if ffn is not None else ""),
                    "rows": rows, "D": w.D,
                    "gemms": [list(g) for g in w.gemms], "bias": w.bias,
@@ -799,7 +841,7 @@ def main():
         res["config"]["ffn"] = {"H": ffn["H"], "down": [w.D, ffn["H"]]}
     if rp is not None:
         res["config"]["rope"] = {k: rp[k] for k in ("nh", "kv", "hd", "P", "T")}
-    if not a.no_cpu_baseline and ffn is None and rp is None:
+    if not a.no_cpu_baseline and ffn is None and rp is None and op is None:
         res["cpu_baseline"] = cpu_baseline(w, rows)
     print(json.dumps(res), flush=True)
 

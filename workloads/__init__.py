@@ -227,6 +227,18 @@ QKV_HEADS: Dict[int, Tuple[int, int, int]] = {2: (8, 1, 256)}
 ROPE_PREFIX: Dict[int, int] = {2: 768}
 
 
+def o_proj_inputs(cid: int, calib: bool = False) -> dict:
+    """The O projection of workload ``cid``'s attention heads: a seeded
+    attention output ``att`` (bf16 ``[rows, nh*hd]``, N(0,1); the
+    calibration batch with ``calib``) and the weight ``W_o`` (bf16
+    ``[D, nh*hd]``, drawn like the workload's other weights, no bias)."""
+    w = WORKLOADS[cid]
+    nh, kv, hd = QKV_HEADS[cid]
+    seed = (2000 if calib else 1000) + cid
+    return {"att": normal_bf16(seed, 70, (w.rows, nh * hd), 1.0),
+            "W_o": normal_bf16(3000 + cid, 60, (w.D, nh * hd), w.w_std)}
+
+
 def rope_table(S: int, hd: int, P: int, base: float = 10000.0) -> np.ndarray:
     """bf16 bits ``[S, hd]`` of the rotary table for positions P .. P + S - 1:
     the cosine of pair i at column 2i and its sine at 2i + 1, angle
