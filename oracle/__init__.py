@@ -21,6 +21,7 @@ Modules:
              and the merged gate/up GEMM -> GEGLU chain
   rope       q/k pair interleave, QKV split + adjacent-pair RoPE + KV-cache
              write
+  mxfp4      OCP MX FP4 codec, block quantiser, block-scaled GEMM
 
 Parity status: every function is pinned by the ``-m "not gpu"`` tests in
 tests/test_oracle_*.py (closed forms, brute force, independent torch CPU
@@ -37,6 +38,7 @@ from .gemm import (gemm_exact, gemm_exact_at, epilogue, packed_gemm_split,
                    split_columns)
 from .ffn import gelu_tanh, geglu, geglu_quant_fp8, gate_up_gelu_quant
 from .rope import pair_perm, interleave_rows, rotate_pairs, qkv_split_rope_kvcache
+from . import mxfp4
 
 __all__ = [
     "bf16_to_f32", "f32_to_bf16", "e4m3_decode", "e4m3_encode",
