@@ -19,7 +19,9 @@
  *     by adjacent-pair RoPE and written to q and the KV caches, standalone
  *     or as the QKV GEMM's epilogue;
  *   - projections without a producer: the static quantiser of a bf16
- *     tensor and the bf16-input form of the packed GEMM.
+ *     tensor and the bf16-input form of the packed GEMM;
+ *   - an MXFP4 band (producer, weight pack, GEMM) in the place of the
+ *     pages' NVFP4 band.
  *
  * Conventions shared by every entry point
  *   - All pointers are DEVICE pointers unless marked [host].
@@ -372,6 +374,92 @@ int frt_packed_gemm_bf16in_split(void* stream, int64_t M, int64_t K,
                                  const int64_t* split_n, void* const* out,
                                  const int64_t* ld_out, int out_dtype,
                                  void* workspace, size_t ws_bytes);
+
+/*
+ * MXFP4 band — the MI355X counterpart of the pages' NVFP4 band (fp8_chain.py
+ * `BANDS`, the `fp4` row: the norm-fed projections in 4-bit with dynamic
+ * block scales, the down projection kept in static FP8). The format is OCP
+ * MX FP4, which the gfx950 matrix cores take natively:
+ *   - e2m1 codes (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 = sign), two
+ *     per byte, the lower-indexed element in the low nibble;
+ *   - one E8M0 scale byte (2^(s-127), 0xFF = NaN) per 32 consecutive
+ *     elements along the reduction axis (rows of activations, rows of
+ *     [N, K] weights);
+ *   - conversion by the OCP rule: scale = 2^(floor(log2(max|v|)) - 2) of the
+ *     fp32 block values (byte 0 for a zero or subnormal maximum, 0xFF for
+ *     NaN or inf), code = e2m1 round-to-nearest-even of v / scale,
+ *     saturating at 6;
+ *   - scale layout: within each run of 8 consecutive blocks (256 elements)
+ *     of a row, the bytes are stored in the order of blocks 0, 2, 4, 6, 1,
+ *     3, 5, 7 (the order in which the GEMM's lanes consume them).
+ */
+
+/*
+ * frt_pack_weights_mxfp4 — MXFP4 pack of sibling projections (per-block
+ * scales, so no joint per-tensor scale is needed).
+ *
+ *   n_sib, N_i [host], W_i [host], b_i [host]   as in frt_pack_weights_fp8;
+ *                 every W_i 16-byte aligned.
+ *   K             multiple of 512 in [512, 16384].
+ *   W4            [sum N_i, K/2] code bytes (4-byte aligned).
+ *   S4            [sum N_i, K/32] scale bytes (GEMM order).
+ *   bias_cat      bf16 [sum N_i] or NULL.
+ */
+int frt_pack_weights_mxfp4(void* stream, int n_sib, const int64_t* N_i,
+                           int64_t K, const uint16_t* const* W_i,
+                           const uint16_t* const* b_i, uint8_t* W4,
+                           uint8_t* S4, uint16_t* bias_cat);
+
+/*
+ * frt_ada_norm_quant_mxfp4 — the gated-residual AdaRMS producer with an
+ * MXFP4 output (the FP4 twin of frt_ada_norm_quant_fp8; the pages'
+ * `gate_res_ada_rms_norm_quant_nvfp4_swizzled_bf16` role). y is computed
+ * exactly as in frt_ada_norm_quant_fp8, then block-quantised along each
+ * row (blocks of 32 columns, dynamic scales).
+ *
+ *   M, D          rows; D a multiple of 256 in [512, 16384].
+ *   residual, x, gate, weight, mod, eps, residual_out, gate_out   as in
+ *                 frt_ada_norm_quant_fp8 (16-byte aligned, ld % 8 == 0).
+ *   out_fp4       [M, ld_out] code bytes, ld_out >= D/2, a multiple of 4.
+ *   out_scale     [M, ld_sc] scale bytes, ld_sc >= D/32 (GEMM order).
+ */
+int frt_ada_norm_quant_mxfp4(void* stream, int64_t M, int64_t D,
+                             const uint16_t* residual, int64_t ld_res,
+                             const uint16_t* x, int64_t ld_x,
+                             const uint16_t* gate, int64_t ld_gate,
+                             const uint16_t* weight,
+                             const uint16_t* mod, int64_t ld_mod, float eps,
+                             uint16_t* residual_out, int64_t ld_rout,
+                             uint8_t* out_fp4, int64_t ld_out,
+                             uint8_t* out_scale, int64_t ld_sc,
+                             uint16_t* gate_out, int64_t ld_gout);
+
+/*
+ * frt_packed_gemm_mxfp4_split — the packed GEMM on MXFP4 operands with the
+ * bias + column-split epilogue. For m < M, n < N_total:
+ *   acc[m, n] = sum_k dec(x[m, k]) * dec(W[n, k])   (block-scaled e2m1,
+ *               the matrix cores' fp32 accumulation)
+ *   out_s[m, n - off_s] = bf16_rne(acc[m, n] + bias_cat[n])   (or fp32)
+ *
+ *   M, K          rows; K a multiple of 512 in [512, 16384].
+ *   x4, ld_x4     [M, ld_x4] code bytes (16-byte aligned, ld_x4 >= K/2, a
+ *                 multiple of 16).
+ *   xs, ld_xs     [M, ld_xs] scale bytes (4-byte aligned, ld_xs >= K/32, a
+ *                 multiple of 4).
+ *   W4, S4        [N_total, K/2] codes (16-byte aligned) and [N_total, K/32]
+ *                 scales (4-byte aligned), as frt_pack_weights_mxfp4 writes.
+ *   bias_cat, n_split, split_n, out, ld_out, out_dtype   as in
+ *                 frt_packed_gemm_fp8_split (outputs must not overlap the
+ *                 operands or the scales).
+ */
+int frt_packed_gemm_mxfp4_split(void* stream, int64_t M, int64_t K,
+                                const uint8_t* x4, int64_t ld_x4,
+                                const uint8_t* xs, int64_t ld_xs,
+                                const uint8_t* W4, const uint8_t* S4,
+                                int64_t N_total, const uint16_t* bias_cat,
+                                int n_split, const int64_t* split_n,
+                                void* const* out, const int64_t* ld_out,
+                                int out_dtype);
 
 /*
  * frt_interleave_pairs_bf16 — the pack-time permutation of q or k

@@ -27,6 +27,8 @@ __all__ = [
     "frt_packed_gemm_fp8_split", "frt_geglu_quant_fp8",
     "frt_packed_gemm_fp8_geglu_quant", "frt_interleave_pairs_bf16",
     "frt_quantize_fp8_static", "frt_packed_gemm_bf16in_split",
+    "frt_pack_weights_mxfp4", "frt_ada_norm_quant_mxfp4",
+    "frt_packed_gemm_mxfp4_split",
     "frt_qkv_split_rope_kvcache", "frt_packed_gemm_fp8_qkv_rope",
     "frt_last_error", "frt_abi_version",
     "FRT_OK", "FRT_E_INVALID", "FRT_E_UNSUPPORTED", "FRT_E_HIP",
@@ -67,6 +69,15 @@ _SIGNATURES = {
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _p, _p, _p, _i64]),
     "frt_interleave_pairs_bf16": (_i32, [_p, _i32, _i32, _i64, _p, _p]),
     "frt_quantize_fp8_static": (_i32, [_p, _i64, _i64, _p, _i64, _p, _p, _i64, _p]),
+    "frt_pack_weights_mxfp4": (_i32, [
+        _p, _i32, ctypes.POINTER(_i64), _i64, ctypes.POINTER(_p),
+        ctypes.POINTER(_p), _p, _p, _p]),
+    "frt_ada_norm_quant_mxfp4": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _f32,
+        _p, _i64, _p, _i64, _p, _i64, _p, _i64]),
+    "frt_packed_gemm_mxfp4_split": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32,
+        ctypes.POINTER(_i64), ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32]),
     "frt_packed_gemm_bf16in_split": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i32,
         ctypes.POINTER(_i64), ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32,
@@ -463,3 +474,69 @@ def frt_packed_gemm_bf16in_split(x, x8, W8, act_scale, w_scale, outs: Sequence,
         int(W8.shape[0]), _ptr(act_scale), _ptr(w_scale), _ptr(bias_cat), n,
         (_i64 * n)(*[int(v) for v in split_n]), (_p * n)(*[_ptr(o) for o in outs]),
         (_i64 * n)(*[_ld(o) for o in outs]), out_dtype, 0, 0))
+
+
+def frt_pack_weights_mxfp4(weights: Sequence, biases: Optional[Sequence], W4, S4,
+                           bias_cat=None, *, stream=None) -> None:
+    """MXFP4 packing of sibling ``[N_i, K]`` bf16 weights: codes ``W4``
+    ``[sum N, K/2]`` and E8M0 scales ``S4`` ``[sum N, K/32]``."""
+    n = len(weights)
+    K = weights[0].shape[1]
+    for i, w in enumerate(weights):
+        _bf16_like(w, f"W_{i}")
+        if not w.is_contiguous():
+            raise ValueError("frt: sibling weights must be contiguous")
+    _u8_like(W4, "W4")
+    _u8_like(S4, "S4")
+    _bf16_like(bias_cat, "bias_cat")
+    Ns = (_i64 * n)(*[int(w.shape[0]) for w in weights])
+    Ws = (_p * n)(*[_ptr(w) for w in weights])
+    Bs = None if biases is None else (_p * n)(*[_ptr(b) for b in biases])
+    _check(load_library().frt_pack_weights_mxfp4(_stream(stream), n, Ns, K, Ws, Bs,
+                                                  _ptr(W4), _ptr(S4), _ptr(bias_cat)))
+
+
+def frt_ada_norm_quant_mxfp4(residual, mod, out_fp4, out_scale, *, x=None,
+                             gate=None, weight=None, eps: float = 1e-6,
+                             residual_out=None, gate_out=None,
+                             M: Optional[int] = None, stream=None) -> None:
+    """Gated residual + AdaRMS with an MXFP4 output (codes ``[M, D/2]``,
+    scales ``[M, D/32]``)."""
+    for t, n in ((residual, "residual"), (mod, "mod"), (x, "x"),
+                 (gate, "gate"), (weight, "weight"),
+                 (residual_out, "residual_out"), (gate_out, "gate_out")):
+        _bf16_like(t, n)
+    _u8_like(out_fp4, "out_fp4")
+    _u8_like(out_scale, "out_scale")
+    Mv = residual.shape[0] if M is None else int(M)
+    D = residual.shape[-1]
+    ld_mod = 0 if (mod.dim() == 1 or mod.shape[0] == 1) else _ld(mod)
+    ld_gate = 0 if (gate is None or gate.dim() == 1 or gate.shape[0] == 1) \
+        else _ld(gate)
+    _check(load_library().frt_ada_norm_quant_mxfp4(
+        _stream(stream), Mv, D, _ptr(residual), _ld(residual), _ptr(x), _ld(x),
+        _ptr(gate), ld_gate, _ptr(weight), _ptr(mod), ld_mod, float(eps),
+        _ptr(residual_out), _ld(residual_out), _ptr(out_fp4), _ld(out_fp4),
+        _ptr(out_scale), _ld(out_scale), _ptr(gate_out), _ld(gate_out)))
+
+
+def frt_packed_gemm_mxfp4_split(x4, xs, W4, S4, outs: Sequence,
+                                split_n: Sequence[int], bias_cat=None, *,
+                                M: Optional[int] = None, stream=None) -> None:
+    """Packed GEMM on MXFP4 operands (codes ``x4 [M, K/2]``, scales
+    ``xs [M, K/32]``; ``W4``/``S4`` from ``frt_pack_weights_mxfp4``)."""
+    import torch
+    for t, nme in ((x4, "x4"), (xs, "xs"), (W4, "W4"), (S4, "S4")):
+        _u8_like(t, nme)
+    _bf16_like(bias_cat, "bias_cat")
+    n = len(split_n)
+    if len(outs) != n:
+        raise ValueError("frt: one output per split")
+    out_dtype = 1 if {o.dtype for o in outs} == {torch.float32} else 0
+    Mv = x4.shape[0] if M is None else int(M)
+    K = int(W4.shape[1]) * 2
+    _check(load_library().frt_packed_gemm_mxfp4_split(
+        _stream(stream), Mv, K, _ptr(x4), _ld(x4), _ptr(xs), _ld(xs), _ptr(W4),
+        _ptr(S4), int(W4.shape[0]), _ptr(bias_cat), n,
+        (_i64 * n)(*[int(v) for v in split_n]), (_p * n)(*[_ptr(o) for o in outs]),
+        (_i64 * n)(*[_ld(o) for o in outs]), out_dtype))

@@ -252,7 +252,9 @@ namespace {
 // Every check of the packed split GEMM's contract (shapes, strides,
 // alignment, splits, workspace, overlaps) and its kernel arguments; no
 // launch. FRT_OK with a.M == 0 means there is nothing to run.
-int gemm_prepare(int64_t M, int64_t K, const uint8_t* x8, int64_t ld_x, const uint8_t* W8, int64_t N_total,
+// kb: operand bytes per row (K for FP8, K / 2 for MXFP4 codes).
+int gemm_prepare(int64_t M, int64_t K, int64_t kb, const uint8_t* x8, int64_t ld_x, const uint8_t* W8,
+                 int64_t N_total,
                  const float* act_scale, const float* w_scale, const uint16_t* bias_cat, int n_split,
                  const int64_t* split_n, void* const* out, const int64_t* ld_out, int out_dtype, void* workspace,
                  size_t ws_bytes, frt::GemmArgs& a) {
@@ -263,9 +265,9 @@ int gemm_prepare(int64_t M, int64_t K, const uint8_t* x8, int64_t ld_x, const ui
   if (M > (1 << 24) || N_total > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "gemm: M or N_total too large");
   if (x8 == nullptr || W8 == nullptr || act_scale == nullptr || w_scale == nullptr)
     return refuse(FRT_E_INVALID, "gemm: x8, W8, act_scale and w_scale are required");
-  if (ld_x < K || ld_x % 16) return refuse(FRT_E_INVALID, "gemm: ld_x must be >= K and a multiple of 16");
+  if (ld_x < kb || ld_x % 16) return refuse(FRT_E_INVALID, "gemm: ld_x must be >= the row bytes and a multiple of 16");
   if (!aligned(x8, 16) || !aligned(W8, 16)) return refuse(FRT_E_INVALID, "gemm: x8 and W8 must be 16-byte aligned");
-  if ((M - 1) * ld_x + K > (int64_t)0x7fffffff || N_total * K > (int64_t)0x7fffffff)
+  if ((M - 1) * ld_x + kb > (int64_t)0x7fffffff || N_total * kb > (int64_t)0x7fffffff)
     return refuse(FRT_E_UNSUPPORTED, "gemm: operand larger than 2 GiB");
   if (out_dtype != 0 && out_dtype != 1) return refuse(FRT_E_INVALID, "gemm: out_dtype must be 0 (bf16) or 1 (fp32)");
   if (n_split < 1 || n_split > FRT_MAX_SPLITS)
@@ -295,7 +297,7 @@ int gemm_prepare(int64_t M, int64_t K, const uint8_t* x8, int64_t ld_x, const ui
     return refuse(FRT_E_INVALID, "gemm: workspace of %zu bytes required", need);
   if (M == 0) return FRT_OK;
   // outputs must not overlap each other or the inputs
-  const Range xin = span(x8, M, K, ld_x, 1), win = span(W8, N_total, K, K, 1),
+  const Range xin = span(x8, M, kb, ld_x, 1), win = span(W8, N_total, kb, kb, 1),
               bin = span(bias_cat, 1, N_total, N_total, 2), sa = span(act_scale, 1, 1, 1, 4),
               sw = span(w_scale, 1, 1, 1, 4), wsr = span(workspace, 1, (int64_t)need, (int64_t)need, 1);
   for (int s = 0; s < n_split; ++s) {
@@ -332,7 +334,7 @@ int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K, const uint8_t*
                               const int64_t* split_n, void* const* out, const int64_t* ld_out,
                               int out_dtype, void* workspace, size_t ws_bytes) {
   frt::GemmArgs a;
-  const int rc = gemm_prepare(M, K, x8, ld_x, W8, N_total, act_scale, w_scale, bias_cat, n_split, split_n, out,
+  const int rc = gemm_prepare(M, K, K, x8, ld_x, W8, N_total, act_scale, w_scale, bias_cat, n_split, split_n, out,
                               ld_out, out_dtype, workspace, ws_bytes, a);
   if (rc != FRT_OK) return rc;
   if (M == 0) return ok();
@@ -443,7 +445,7 @@ int frt_packed_gemm_bf16in_split(void* stream, int64_t M, int64_t K, const uint1
   if (!aligned(x, 2)) return refuse(FRT_E_INVALID, "gemm_bf16in: x misaligned");
   // the GEMM's whole contract on the FP8 operand the call writes
   frt::GemmArgs a;
-  const int rc = gemm_prepare(M, K, x8, ld_x8, W8, N_total, act_scale, w_scale, bias_cat, n_split, split_n, out,
+  const int rc = gemm_prepare(M, K, K, x8, ld_x8, W8, N_total, act_scale, w_scale, bias_cat, n_split, split_n, out,
                               ld_out, out_dtype, workspace, ws_bytes, a);
   if (rc != FRT_OK) return rc;
   if (M == 0) return ok();
@@ -460,6 +462,126 @@ int frt_packed_gemm_bf16in_split(void* stream, int64_t M, int64_t K, const uint1
   const hipError_t e = frt::launch_quant(q, vec8 ? 8 : 1, (hipStream_t)stream);
   if (e != hipSuccess) return hip_status(e, "gemm_bf16in quantize launch");
   return hip_status(frt::launch_gemm(a, (hipStream_t)stream), "gemm_bf16in launch");
+}
+
+int frt_pack_weights_mxfp4(void* stream, int n_sib, const int64_t* N_i, int64_t K, const uint16_t* const* W_i,
+                           const uint16_t* const* b_i, uint8_t* W4, uint8_t* S4, uint16_t* bias_cat) {
+  if (n_sib < 1 || n_sib > FRT_MAX_SPLITS)
+    return refuse(FRT_E_INVALID, "pack_mxfp4: n_sib=%d outside [1, %d]", n_sib, FRT_MAX_SPLITS);
+  if (N_i == nullptr || W_i == nullptr || W4 == nullptr || S4 == nullptr)
+    return refuse(FRT_E_INVALID, "pack_mxfp4: N_i, W_i, W4 and S4 are required");
+  if (K < 512 || K > 16384 || K % 512)
+    return refuse(FRT_E_INVALID, "pack_mxfp4: K=%lld must be a multiple of 512 in [512, 16384]", (long long)K);
+  if (!aligned(W4, 4)) return refuse(FRT_E_INVALID, "pack_mxfp4: W4 must be 4-byte aligned");
+  frt::PackSib sibs[FRT_MAX_SPLITS];
+  int64_t rows = 0;
+  for (int i = 0; i < n_sib; ++i) {
+    if (N_i[i] < 1) return refuse(FRT_E_INVALID, "pack_mxfp4: N_%d=%lld < 1", i, (long long)N_i[i]);
+    if (W_i[i] == nullptr || !aligned(W_i[i], 16))
+      return refuse(FRT_E_INVALID, "pack_mxfp4: W_%d must be 16-byte aligned", i);
+    sibs[i].w = W_i[i];
+    sibs[i].b = b_i != nullptr ? b_i[i] : nullptr;
+    sibs[i].rows = N_i[i];
+    sibs[i].row_off = rows;
+    sibs[i].elems = N_i[i] * K;
+    sibs[i].dst_off = rows * (K / 2);
+    rows += N_i[i];
+  }
+  if (rows > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "pack_mxfp4: too many rows");
+  const Range w4r = span(W4, rows, K / 2, K / 2, 1), s4r = span(S4, rows, K / 32, K / 32, 1),
+              br = span(bias_cat, 1, rows, rows, 2);
+  if (overlap(w4r, s4r) || overlap(w4r, br) || overlap(s4r, br)) return refuse(FRT_E_INVALID, "pack_mxfp4: outputs overlap");
+  for (int i = 0; i < n_sib; ++i) {
+    const Range wr = span(sibs[i].w, sibs[i].rows, K, K, 2), bb = span(sibs[i].b, 1, sibs[i].rows, sibs[i].rows, 2);
+    if (overlap(wr, w4r) || overlap(wr, s4r) || overlap(wr, br) || overlap(bb, w4r) || overlap(bb, s4r) ||
+        overlap(bb, br))
+      return refuse(FRT_E_INVALID, "pack_mxfp4: sibling %d overlaps an output", i);
+  }
+  return hip_status(frt::launch_pack_mxfp4(sibs, n_sib, K, W4, S4, bias_cat, (hipStream_t)stream), "pack_mxfp4 launch");
+}
+
+int frt_ada_norm_quant_mxfp4(void* stream, int64_t M, int64_t D, const uint16_t* residual, int64_t ld_res,
+                             const uint16_t* x, int64_t ld_x, const uint16_t* gate, int64_t ld_gate,
+                             const uint16_t* weight, const uint16_t* mod, int64_t ld_mod, float eps,
+                             uint16_t* residual_out, int64_t ld_rout, uint8_t* out_fp4, int64_t ld_out,
+                             uint8_t* out_scale, int64_t ld_sc, uint16_t* gate_out, int64_t ld_gout) {
+  if (M < 0) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: M=%lld < 0", (long long)M);
+  if (D < kDMin || D > kDMax || D % 256)
+    return refuse(FRT_E_INVALID, "ada_norm_mxfp4: D=%lld must be a multiple of 256 in [512, 16384]", (long long)D);
+  if (M > (int64_t)0x7fffffff) return refuse(FRT_E_UNSUPPORTED, "ada_norm_mxfp4: M too large");
+  if (residual == nullptr || mod == nullptr || out_fp4 == nullptr || out_scale == nullptr)
+    return refuse(FRT_E_INVALID, "ada_norm_mxfp4: residual, mod, out_fp4 and out_scale are required");
+  if (ld_res < D || (x != nullptr && ld_x < D)) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld < D");
+  if (gate != nullptr && ld_gate != 0 && ld_gate < D)
+    return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_gate must be 0 (broadcast) or >= D");
+  if (ld_mod != 0 && ld_mod < 3 * D) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_mod must be 0 or >= 3*D");
+  if (ld_out < D / 2 || ld_out % 4) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_out must be >= D/2 and a multiple of 4");
+  if (ld_sc < D / 32) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_sc < D/32");
+  if (residual_out != nullptr && ld_rout < D) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_rout < D");
+  if (gate_out != nullptr && ld_gout < D) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_gout < D");
+  const bool al = aligned(residual, 16) && ld_res % 8 == 0 && (x == nullptr || (aligned(x, 16) && ld_x % 8 == 0)) &&
+                  (gate == nullptr || (aligned(gate, 16) && ld_gate % 8 == 0)) &&
+                  (weight == nullptr || aligned(weight, 16)) && aligned(mod, 16) && ld_mod % 8 == 0 &&
+                  (residual_out == nullptr || (aligned(residual_out, 16) && ld_rout % 8 == 0)) &&
+                  aligned(out_fp4, 4) && (gate_out == nullptr || (aligned(gate_out, 16) && ld_gout % 8 == 0));
+  if (!al) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: 16-byte aligned inputs with ld % 8 == 0 (out_fp4: 4-byte) required");
+  if (M == 0) return ok();
+  const int64_t mrows = ld_mod ? M : 1, grows = ld_gate ? M : 1;
+  const Range in[] = {span(residual, M, D, ld_res, 2), span(x, M, D, ld_x, 2),
+                      span(gate, grows, D, ld_gate ? ld_gate : D, 2), span(weight, 1, D, D, 2),
+                      span(mod, mrows, 3 * D, ld_mod ? ld_mod : 3 * D, 2)};
+  const Range outs[] = {span(residual_out, M, D, ld_rout, 2), span(out_fp4, M, D / 2, ld_out, 1),
+                        span(out_scale, M, D / 32, ld_sc, 1), span(gate_out, M, D, ld_gout, 2)};
+  const bool inplace = residual_out != nullptr && residual_out == residual && ld_rout == ld_res;
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 5; ++i) {
+      if (o == 0 && i == 0 && inplace) continue;
+      if (overlap(outs[o], in[i])) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: output %d overlaps input %d", o, i);
+    }
+    for (int p = o + 1; p < 4; ++p)
+      if (overlap(outs[o], outs[p])) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: outputs %d and %d overlap", o, p);
+  }
+  frt::AdaArgs a{residual, ld_res, x, ld_x, gate, ld_gate, weight, mod, ld_mod,
+                 nullptr, eps, residual_out, ld_rout, out_fp4, ld_out, gate_out, ld_gout,
+                 nullptr, 0, nullptr, M, (int)D, out_scale, ld_sc};
+  if (x == nullptr || gate == nullptr) {
+    a.x = nullptr;
+    a.gate = nullptr;
+  }
+  return hip_status(frt::launch_ada_norm_mxfp4(a, (hipStream_t)stream), "ada_norm_mxfp4 launch");
+}
+
+int frt_packed_gemm_mxfp4_split(void* stream, int64_t M, int64_t K, const uint8_t* x4, int64_t ld_x4,
+                                const uint8_t* xs, int64_t ld_xs, const uint8_t* W4, const uint8_t* S4,
+                                int64_t N_total, const uint16_t* bias_cat, int n_split, const int64_t* split_n,
+                                void* const* out, const int64_t* ld_out, int out_dtype) {
+  if (M < 0) return refuse(FRT_E_INVALID, "gemm_mxfp4: M=%lld < 0", (long long)M);
+  if (K < 512 || K > 16384 || K % 512)
+    return refuse(FRT_E_INVALID, "gemm_mxfp4: K=%lld must be a multiple of 512 in [512, 16384]", (long long)K);
+  if (xs == nullptr || S4 == nullptr) return refuse(FRT_E_INVALID, "gemm_mxfp4: xs and S4 are required");
+  if (ld_xs < K / 32 || !aligned(xs, 4) || ld_xs % 4 || !aligned(S4, 4))
+    return refuse(FRT_E_INVALID, "gemm_mxfp4: scales must be 4-byte aligned with ld_xs >= K/32, a multiple of 4");
+  // the packed GEMM's own contract on the code bytes (K/2 per row): shapes,
+  // 16-byte alignment, ld % 16, splits and output overlaps; the FP8 scale
+  // pointers are not used, so the scale buffers stand in for them
+  frt::GemmArgs a;
+  const int rc = gemm_prepare(M, K, K / 2, x4, ld_x4, W4, N_total, reinterpret_cast<const float*>(xs),
+                              reinterpret_cast<const float*>(S4), bias_cat, n_split, split_n, out, ld_out,
+                              out_dtype, nullptr, 0, a);
+  if (rc != FRT_OK) return rc;
+  if (M == 0) return ok();
+  const Range sar = span(xs, M, K / 32, ld_xs, 1), sbr = span(S4, N_total, K / 32, K / 32, 1);
+  for (int s = 0; s < n_split; ++s) {
+    const Range o = span(out[s], M, split_n[s], ld_out[s], out_dtype ? 4 : 2);
+    if (overlap(o, sar) || overlap(o, sbr)) return refuse(FRT_E_INVALID, "gemm_mxfp4: output %d overlaps a scale buffer", s);
+  }
+  a.K = (int)K;
+  a.act_scale = nullptr;
+  a.w_scale = nullptr;
+  a.sa = xs;
+  a.ld_sa = ld_xs;
+  a.sb = S4;
+  return hip_status(frt::launch_gemm_mxfp4(a, (hipStream_t)stream), "gemm_mxfp4 launch");
 }
 
 int frt_interleave_pairs_bf16(void* stream, int nheads, int hd, int64_t K, const uint16_t* src, uint16_t* dst) {

@@ -72,6 +72,51 @@ __device__ __forceinline__ float gelu_tanh(float v) {
   return v / (1.0f + __builtin_amdgcn_exp2f(t));
 }
 
+// ---- MXFP4 (OCP MX: e2m1 elements, one E8M0 scale per block of 32) ----
+
+// e2m1 code of q (a value already divided by its block scale): nearest of
+// 0, .5, 1, 1.5, 2, 3, 4, 6 with ties to the even code, saturating at 6;
+// the sign bit is kept (bit 3).
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  const float m = fabsf(q);
+  const uint32_t idx = (uint32_t)(m > 0.25f) + (uint32_t)(m >= 0.75f) + (uint32_t)(m > 1.25f) +
+                       (uint32_t)(m >= 1.75f) + (uint32_t)(m > 2.5f) + (uint32_t)(m >= 3.5f) + (uint32_t)(m > 5.0f);
+  return idx | ((__float_as_uint(q) >> 28) & 8u);
+}
+
+// E8M0 byte of a block from the fp32 bits of its max |v|: the OCP rule
+// floor(log2(amax)) - 2, clamped at the bottom of the range (zero and
+// subnormal maxima give byte 0); NaN or infinity give 0xFF.
+__device__ __forceinline__ uint32_t e8m0_of_amax(uint32_t amax_bits) {
+  const uint32_t e = (amax_bits >> 23) & 0xFFu;
+  return e == 0xFFu ? 0xFFu : (e > 2u ? e - 2u : 0u);
+}
+
+// Eight values of one block -> eight e2m1 codes, element 0 in the low
+// nibble; v / 2^(s - 127) is the exact power-of-two scaling ldexp.
+__device__ __forceinline__ uint32_t mxfp4_pack8(const float* v, uint32_t sbyte) {
+  const int sh = 127 - (int)sbyte;
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w |= e2m1_code(__builtin_ldexpf(v[e], sh)) << (4 * e);
+  return w;
+}
+
+// Position of block b's scale byte in a row: within each run of 8 blocks
+// the bytes are ordered 0, 2, 4, 6, 1, 3, 5, 7 (the order the MXFP4 GEMM
+// reads them in).
+__device__ __forceinline__ int64_t e8m0_pos(int64_t b) {
+  const int j = (int)(b & 7);
+  return (b & ~(int64_t)7) | ((j & 1) ? 4 + (j >> 1) : (j >> 1));
+}
+
+// Max of the four lanes of a quad (DPP xor 1, xor 2).
+__device__ __forceinline__ uint32_t quad_umax(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));
+  return v;
+}
+
 // The value held by lane l ^ 1 (DPP quad_perm [1,0,3,2]; the builtin is
 // declared int-valued but moves the operand's bits, so the cast compiles
 // to a plain DPP move).

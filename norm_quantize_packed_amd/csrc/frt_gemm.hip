@@ -116,8 +116,19 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // value to bf16 as the split output would be, takes its partner's through
 // DPP, rotates q and k with the pair's (cos, sin) from the token's rope row,
 // and writes q_out row m, or cache row P + m of k or v.
+//
+// FP4: the MXFP4 form. x and W hold e2m1 codes, two per byte (K/2 bytes a
+// row), with one E8M0 scale per 32 K-elements in sa [M, ld_sa] and sb
+// [N, K/32]. A 128-byte stage row holds 256 K-elements, i.e. four 64-deep
+// MFMA steps, each reading one 16-byte chunk per operand (lane l: row l % 32,
+// K half l / 32 = exactly one scale block). The scales are stored in the
+// MFMA order: within each run of 8 blocks (256 K-elements) the bytes are
+// blocks 0, 2, 4, 6, 1, 3, 5, 7, so the lanes of K half h load one dword
+// holding their blocks h, 2 + h, 4 + h, 6 + h and step s selects byte s.
+// The scales of a stage are loaded into registers by the same issue call
+// as its tiles (so the wait counts cover them); alpha is 1.
 template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB, int AE = BM,
-          bool GLU = false, bool ROPE = false>
+          bool GLU = false, bool ROPE = false, bool FP4 = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a) {
   constexpr int WAVES_N = BN / WN;
   constexpr int NW = (BM / WM) * WAVES_N;
@@ -131,7 +142,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   constexpr int SUBB = ROWS * 128;     // one 128-deep sub-buffer
   constexpr int STAGE = NSUB * SUBB;   // one stage = NSUB sub-buffers
   constexpr int KST = 128 * NSUB;      // K bytes per stage
-  static_assert(NS >= 2 && NSUB * LPW * (NS - 2) <= 63, "ring depth vs vmcnt range");
+  static_assert(!FP4 || (!KTAIL && !GLU && !ROPE), "MXFP4 form: whole stages, split epilogue");
+  constexpr int SCL = FP4 ? MI + NJ : 0;  // scale loads per sub-buffer
+  static_assert(NS >= 2 && NSUB * (LPW + SCL) * (NS - 2) <= 63, "ring depth vs vmcnt range");
   static_assert(NS * STAGE <= 160 * 1024, "ring exceeds LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
@@ -144,8 +157,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const int m0 = t.tm * BM, n0 = t.tn * (GLU ? BN / 2 : BN);
   const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
 
-  const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + a.K);
-  const uint32_t w_bytes = (uint32_t)((int64_t)a.N * a.K);
+  const int Kb = FP4 ? a.K / 2 : a.K;  // operand bytes per row
+  const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + Kb);
+  const uint32_t w_bytes = (uint32_t)((int64_t)a.N * Kb);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, x_bytes);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, w_bytes);
 
@@ -163,10 +177,25 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const int cch = (lane & 7) ^ (((wave & 1) << 2) | (lrow >> 1));
   const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
   const uint32_t offB = GLU ? (uint32_t)(lrow * a.K + cch * 16)
-                            : (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
+                            : (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * Kb) + cch * 16;
   const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
-  const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)a.K;
-  const int KT = (a.K + KST - 1) / KST;
+  const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)Kb;
+  const int KT = (Kb + KST - 1) / KST;
+  // MXFP4 scales: this lane's MFMA rows (rows past M or N read the last
+  // row: their results are never stored), a ring slot per stage
+  constexpr int SNS = FP4 ? NS : 1, SNB = FP4 ? NSUB : 1;
+  unsigned scA[SNS][SNB][FP4 ? MI : 1], scB[SNS][SNB][FP4 ? NJ : 1];
+  const uint8_t* sa_row[FP4 ? MI : 1];
+  const uint8_t* sb_row[FP4 ? NJ : 1];
+  if constexpr (FP4) {
+    const int h4 = (lane >> 5) * 4;  // this K half's dword of a run
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+      sa_row[i] = a.sa + (int64_t)min(m0 + wm0 + i * 32 + (lane & 31), a.M - 1) * a.ld_sa + h4;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      sb_row[j] = a.sb + (int64_t)min(n0 + wn0 + j * 32 + (lane & 31), a.N - 1) * (a.K / 32) + h4;
+  }
   // slot SL (= step mod NS) is a compile-time constant in every use, so all
   // LDS addresses are one lane base plus immediates
   auto issue = [&](int kt, auto SLC) {
@@ -200,6 +229,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
       }
+      if constexpr (FP4) {
+        // this lane's 4 block scales of the sub-buffer (256 K-elements)
+        const int blk = (kt * NSUB + q) * 8;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) scA[SL][q][i] = *reinterpret_cast<const unsigned*>(sa_row[i] + blk);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) scB[SL][q][j] = *reinterpret_cast<const unsigned*>(sb_row[j] + blk);
+      }
     }
   };
   // operand read of substep SUB from slot SL: two 16-byte chunks per lane
@@ -207,8 +244,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const int sw = (lrow32 >> 1) & 7;  // (row >> 1) & 7 for rows 32k + lrow32
   const uint8_t* lbase0 = smem + lrow32 * 128 + ((((lane >> 5) * 2) ^ sw) * 16);
   const uint8_t* lbase1 = smem + lrow32 * 128 + ((((lane >> 5) * 2 + 4) ^ sw) * 16);
-  auto read_frags = [&](auto SLC, auto SUBC, v8i* af, v8i* bf) {
+  auto read_frags = [&](auto SLC, auto SUBC, auto* af, auto* bf) {
     constexpr int SL = decltype(SLC)::value, SUB = decltype(SUBC)::value;
+    if constexpr (FP4) {
+      // step SUB % 4 of sub-buffer SUB / 4: chunk 2 (SUB % 4) + l / 32
+      const uint8_t* lb = smem + lrow32 * 128 + ((((SUB & 3) * 2 + (lane >> 5)) ^ sw) * 16) + SL * STAGE +
+                          (SUB >> 2) * SUBB;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const v4i*>(lb + (BM + wn0 + j * 32) * 128);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) af[i] = *reinterpret_cast<const v4i*>(lb + (wm0 + i * 32) * 128);
+      return;
+    } else {
     const uint8_t* lb = ((SUB & 1) ? lbase1 : lbase0) + SL * STAGE + (SUB >> 1) * SUBB;
     // the second chunk sits at position ^ 1, i.e. +16 or -16 bytes
     const int d1 = (sw & 1) ? -16 : 16;
@@ -226,6 +273,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       const v4i hi = *reinterpret_cast<const v4i*>(rowp + d1);
       af[i] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+    }
   };
   // own loads: at most `ahead` later stages still in flight; every LDS read
   // done; then the block barrier (s_waitcnt takes an immediate: one case per
@@ -233,7 +281,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   auto sync_stage = [&](int ahead) {
     __builtin_amdgcn_sched_barrier(0);
     [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((ahead == I ? (__builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(NSUB * LPW * I)), 0) : 0), ...);
+      ((ahead == I ? (__builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(NSUB * (LPW + SCL) * I)), 0) : 0), ...);
     }(std::make_integer_sequence<int, NS - 1>{});
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -252,11 +300,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   // barrier (one LDS round trip per stage) and alternate between two
   // independent accumulator sets, so consecutive MFMAs do not wait on each
   // other; large wave tiles reuse one fragment set and one accumulator set.
-  constexpr int KSUB = 2 * NSUB;
+  constexpr int KSUB = (FP4 ? 4 : 2) * NSUB;
   constexpr bool ALL = MI * NJ * KSUB <= 8;
   constexpr int NACC = (ALL && KSUB >= 2) ? 2 : 1;
   constexpr int NF = ALL ? KSUB : 1;
-  v8i fa[NF][MI], fb[NF][NJ];
+  // (FP4 fragments use the low four dwords only; the MFMA reads four
+  // registers per operand for e2m1)
+  typedef std::conditional_t<FP4, v4i, v8i> frag_t;
+  frag_t fa[NF][MI], fb[NF][NJ];
   v16f acc2[NACC > 1 ? MI : 1][NACC > 1 ? NJ : 1];
   if constexpr (NACC > 1) {
 #pragma unroll
@@ -266,14 +317,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc2[i][j][r] = 0.0f;
   }
-  auto mfmas = [&](const v8i* af, const v8i* bf, auto ACC) {
+  auto mfmas = [&](const frag_t* af, const frag_t* bf, auto ACC, auto SLC, auto SUBC) {
+    constexpr int SL = decltype(SLC)::value, SUB = decltype(SUBC)::value;
 #pragma unroll
     for (int q = 0; q < MI * NJ; ++q) {
       const int i = q / NJ, j = q % NJ;
-      if constexpr (decltype(ACC)::value == 0)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, 0, 0, 0);
-      else
-        acc2[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc2[i][j], 0, 0, 0, 0, 0, 0);
+      v16f& c = decltype(ACC)::value == 0 ? acc[i][j] : acc2[NACC > 1 ? i : 0][NACC > 1 ? j : 0];
+      if constexpr (FP4) {
+        // step s of the sub-buffer: byte s of the lane's scale dword
+        constexpr int s = SUB & 3, sb = SUB >> 2;
+        const v8i a8 = {af[i][0], af[i][1], af[i][2], af[i][3], 0, 0, 0, 0};
+        const v8i b8 = {bf[j][0], bf[j][1], bf[j][2], bf[j][3], 0, 0, 0, 0};
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, s, (int)scA[SL][sb][i], s,
+                                                           (int)scB[SL][sb][j]);
+      } else {
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], c, 0, 0, 0, 0, 0, 0);
+      }
     }
   };
   auto read_all = [&](auto SLC) {
@@ -290,12 +349,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
     if (kt + NS - 1 < KT) issue(kt + NS - 1, PV{});
     if constexpr (ALL) {
       [&]<int... U>(std::integer_sequence<int, U...>) {
-        (mfmas(fa[U], fb[U], std::integral_constant<int, U % NACC>{}), ...);
+        (mfmas(fa[U], fb[U], std::integral_constant<int, U % NACC>{}, SLC, std::integral_constant<int, U>{}), ...);
       }(std::make_integer_sequence<int, KSUB>{});
     } else {
       [&]<int... U>(std::integer_sequence<int, U...>) {
         ((U > 0 ? (read_frags(SLC, std::integral_constant<int, U>{}, fa[0], fb[0]), 0) : 0,
-          mfmas(fa[0], fb[0], std::integral_constant<int, 0>{})), ...);
+          mfmas(fa[0], fb[0], std::integral_constant<int, 0>{}, SLC, std::integral_constant<int, U>{})), ...);
       }(std::make_integer_sequence<int, KSUB>{});
     }
     if (kt + 1 < KT) {
@@ -330,7 +389,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   }
 
   // ---- epilogue: alpha * acc + bias, column split, bf16 (or fp32) ----
-  const float alpha = (*a.act_scale) * (*a.w_scale);
+  const float alpha = FP4 ? 1.0f : (*a.act_scale) * (*a.w_scale);
   if constexpr (ROPE) {
     const int nq = a.nh * a.hd, nk = a.kv * a.hd;
 #pragma unroll
@@ -438,11 +497,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1, int AE = BM, bool GLU = false,
-          bool ROPE = false>
+          bool ROPE = false, bool FP4 = false>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   // (GLU: N = 2H, so this is also ceil(H / (BN / 2)) column tiles)
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
+  if constexpr (FP4) {  // K % 512 == 0 (whole stages) is part of the contract
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, false, false, true>), dim3(tiles),
+                       dim3(threads), 0, st, a);
+    return hipGetLastError();
+  }
   if (a.K % (128 * NSUB) == 0)
     hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE>), dim3(tiles),
                        dim3(threads), 0, st, a);
@@ -521,6 +585,25 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) { return launch_planne
 // The RoPE epilogue runs on the split plans (any tile keeps a rotary pair in
 // adjacent lanes).
 hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st) { return launch_planned<true>(a, st); }
+
+// MXFP4 plans (K % 512 == 0: whole 256- or 512-element stages): the
+// small-M plan for M <= 64; above, the least per-CU load among 128x128 of
+// eight 32x64 waves (the sixteen-wave form exceeds its 128 registers with
+// the scale ring), 64x64 and 64x32. Half the bytes per row as FP8 move the
+// balance toward larger tiles only through plan_cost's row counts.
+hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st) {
+  if (a.M > 64) {
+    const int cus = device_cus();
+    const int64_t c128 = plan_cost(a, 128, 128, cus), c64 = plan_cost(a, 64, 64, cus),
+                  c32 = plan_cost(a, 64, 32, cus);
+    if (c128 <= c64 && c128 <= c32) return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, false, false, true>(a, st);
+    if (c64 <= c32) return launch_tiles<64, 64, 32, 32, 4, 1, 1, 64, false, false, true>(a, st);
+    return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, false, true>(a, st);
+  }
+  if (a.M <= 16) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 16, false, false, true>(a, st);
+  if (a.M <= 32) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 32, false, false, true>(a, st);
+  return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, false, true>(a, st);
+}
 
 // GEGLU plans: the same tiles with 64-column wave tiles (a gate/up pair per
 // lane), chosen by plan_cost: 256x256 (M >= 512), 128x128 of eight 32x64

@@ -21,6 +21,9 @@ struct AdaArgs {
   float* y; int64_t ld_y;
   float* amax;
   int64_t M; int D;
+  // MXFP4 output (launch_ada_norm_mxfp4): e2m1 codes in out ([M, ld_out]
+  // bytes, two per byte) and E8M0 block scales in sc [M, ld_sc]
+  uint8_t* sc; int64_t ld_sc;
 };
 
 struct PtokArgs {
@@ -36,6 +39,7 @@ struct PtokArgs {
 };
 
 hipError_t launch_ada_norm(const AdaArgs& a, bool vec8, hipStream_t st);
+hipError_t launch_ada_norm_mxfp4(const AdaArgs& a, hipStream_t st);
 hipError_t launch_ptok_norm(const PtokArgs& a, bool vec8, hipStream_t st);
 
 struct PackSib {
@@ -48,6 +52,9 @@ struct PackSib {
 
 hipError_t launch_pack(const PackSib* sibs, int n_sib, int64_t K, uint8_t* w8,
                        float* w_scale, uint16_t* bias_cat, hipStream_t st);
+// MXFP4 pack: codes [sum N, K/2], E8M0 scales [sum N, K/32] (GEMM order)
+hipError_t launch_pack_mxfp4(const PackSib* sibs, int n_sib, int64_t K, uint8_t* w4, uint8_t* s4,
+                             uint16_t* bias_cat, hipStream_t st);
 
 struct SplitTab {
   void* ptr[FRT_MAX_SPLITS];
@@ -76,6 +83,10 @@ struct GemmArgs {
   int nh, kv, hd;
   int64_t P;
   uint16_t* q_out; uint16_t* k_cache; uint16_t* v_cache;
+  // MXFP4 operands (launch_gemm_mxfp4): x, w hold e2m1 codes (K/2 bytes a
+  // row, ld_x in bytes); E8M0 block scales sa [M, ld_sa], sb [N, K/32]
+  const uint8_t* sa; int64_t ld_sa;
+  const uint8_t* sb;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
@@ -96,6 +107,7 @@ hipError_t launch_geglu(const GegluArgs& a, int vec, hipStream_t st);
 hipError_t launch_quant(const GegluArgs& a, int vec, hipStream_t st);
 
 hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st);
 
 struct RopeArgs {
   const uint16_t* qkv; int64_t ld_qkv;

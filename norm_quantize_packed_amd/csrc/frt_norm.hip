@@ -110,7 +110,11 @@ __device__ __forceinline__ void amax_commit(float* amax, float m) {
 
 }  // namespace
 
-template <int WPR, int NV, int VEC>
+// MX: MXFP4 output instead of static FP8 (vector path, D % 256 == 0): the
+// four lanes of a quad hold 32 consecutive columns, one block; its max
+// comes from two DPP steps, then each lane writes its 8 codes (4 bytes) and
+// the quad's first lane the block's scale byte.
+template <int WPR, int NV, int VEC, bool MX = false>
 __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ada_norm_kernel(AdaArgs a) {
   constexpr int RPB = WPR <= 4 ? 4 / WPR : 1;
   constexpr bool EARLY = NV <= 4;  // modulation loads issued before the reduction
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ada_norm_kernel(Ada
   const float rr = __builtin_amdgcn_rsqf(tot / (float)a.D + a.eps);
 
   float s = 1.0f, rcp = 1.0f;
-  if (a.out != nullptr) {
+  if (!MX && a.out != nullptr) {
     s = *a.act_scale;
     rcp = 1.0f / s;
   }
@@ -201,7 +205,15 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ada_norm_kernel(Ada
 #pragma unroll
           for (int e = 0; e < VEC; ++e) amax = __uint_as_float(max(__float_as_uint(amax), __float_as_uint(fabsf(y[e]))));
         }
-        if (a.out != nullptr) {
+        if constexpr (MX) {
+          static_assert(!MX || VEC == 8, "MXFP4 output takes the vector path");
+          uint32_t am = 0;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) am = max(am, __float_as_uint(fabsf(y[e])));
+          const uint32_t sbyte = e8m0_of_amax(quad_umax(am));
+          *reinterpret_cast<uint32_t*>(a.out + row * a.ld_out + c / 2) = mxfp4_pack8(y, sbyte);
+          if ((lane & 3) == 0) a.sc[row * a.ld_sc + e8m0_pos(c / 32)] = (uint8_t)sbyte;
+        } else if (a.out != nullptr) {
           float q[VEC];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) q[e] = clamp_fp8(div_rn(y[e], s, rcp));
@@ -404,6 +416,17 @@ hipError_t launch_ada_norm(const AdaArgs& a, bool vec8, hipStream_t st) {
     const dim3 grid4((unsigned)a.M);
     FRT_NV2_SWITCH(nv2, hipLaunchKernelGGL((ada_norm_kernel<4, NV, 2>), grid4, dim3(256), 0, st, a))
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ada_norm_mxfp4(const AdaArgs& a, hipStream_t st) {
+  const int wpr = pick_wpr(a.M, a.D);
+  const int64_t nvec = a.D / 8;
+  const int nv = (int)((nvec + 64 * wpr - 1) / (64 * wpr));
+  const int rpb = rows_per_block(wpr);
+  const dim3 grid((unsigned)((a.M + rpb - 1) / rpb));
+  const dim3 block((unsigned)block_threads(wpr));
+  FRT_WPR_SWITCH(wpr, FRT_NV_SWITCH(nv, hipLaunchKernelGGL((ada_norm_kernel<WPR, NV, 8, true>), grid, block, 0, st, a)))
   return hipGetLastError();
 }
 

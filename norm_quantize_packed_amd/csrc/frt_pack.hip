@@ -4,6 +4,8 @@
 // Four stream-ordered launches, no workspace:
 //   1. prep   : w_scale <- +0 (it accumulates max|W| as float bits while
 //               the call runs) and bias_cat <- concat(b_i or zeros)
+//   pack_mx:    the MXFP4 form: per-row blocks of 32 along K, e2m1 codes and
+//               E8M0 scales (OCP MX rule), see frt_device.h
 //   2. amax   : per sibling, block max of |w| bits -> atomicMax on w_scale
 //   3. cast   : per sibling, codes = e4m3(clamp(fl32(w / s))), with
 //               s = max(fl32(amax / 448), 1e-8) derived from w_scale's bits
@@ -123,7 +125,48 @@ unsigned grid_for(int64_t work, int64_t cap = 4096) {
   return (unsigned)g;
 }
 
+// MXFP4 pack of one sibling (K % 256 == 0): thread t takes 8 consecutive
+// elements of a row (16-byte load), the four threads of a quad one block of
+// 32; rows follow each other, so a quad never straddles a row. Threads past
+// the end still take part in the quad max (with zeros) and store nothing.
+__global__ __launch_bounds__(kThreads) void pack_mx_kernel(const uint16_t* w, int64_t rows, int64_t K,
+                                                           uint8_t* codes, uint8_t* scales) {
+  const int64_t nv = K / 8;
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const bool ok = t < rows * nv;
+  float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  const int64_t row = ok ? t / nv : 0, vv = ok ? t - row * nv : 0;
+  if (ok) {
+    const uint4 q = *reinterpret_cast<const uint4*>(w + row * K + vv * 8);
+    const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (e & 1) ? bf16hi(wd[e >> 1]) : bf16lo(wd[e >> 1]);
+  }
+  uint32_t am = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(fabsf(v[e])));
+  const uint32_t sbyte = e8m0_of_amax(quad_umax(am));
+  if (ok) {
+    *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + vv * 4) = mxfp4_pack8(v, sbyte);
+    if ((threadIdx.x & 3) == 0) scales[row * (K / 32) + e8m0_pos(vv / 4)] = (uint8_t)sbyte;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pack_mxfp4(const PackSib* sibs, int n_sib, int64_t K, uint8_t* w4, uint8_t* s4,
+                             uint16_t* bias_cat, hipStream_t st) {
+  for (int i = 0; i < n_sib; ++i) {
+    if (bias_cat != nullptr)
+      hipLaunchKernelGGL(pack_prep_kernel, dim3(grid_for(sibs[i].rows)), dim3(kThreads), 0, st, nullptr,
+                         bias_cat, sibs[i].b, sibs[i].rows, sibs[i].row_off, 0);
+    const int64_t threads = sibs[i].rows * (K / 8);
+    hipLaunchKernelGGL(pack_mx_kernel, dim3((unsigned)((threads + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       st, sibs[i].w, sibs[i].rows, K, w4 + sibs[i].row_off * (K / 2),
+                       s4 + sibs[i].row_off * (K / 32));
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const PackSib* sibs, int n_sib, int64_t K, uint8_t* w8, float* w_scale,
                        uint16_t* bias_cat, hipStream_t st) {

@@ -28,7 +28,10 @@ Readings where the pages and the specification leave a step open:
 - a block whose maximum is 0 gets the smallest scale (byte 0) and zero
   codes; a NaN in a block makes its scale byte 0xFF;
 - codes are stored two per byte, the lower-indexed element in the low
-  nibble; scales one byte per block.
+  nibble; scales one byte per block, each run of 8 blocks stored in the
+  order 0, 2, 4, 6, 1, 3, 5, 7 (``scales_to_gemm_order``: the library's
+  layout, in which the GEMM's lanes read their blocks);
+- a NaN or an infinity in a block makes its scale byte 0xFF.
 """
 
 from __future__ import annotations
@@ -91,13 +94,13 @@ def quantize_mxfp4(v):
     if K % BLOCK:
         raise ValueError("K must be a multiple of 32")
     blocks = v32.reshape(rows, K // BLOCK, BLOCK)
-    nan = np.isnan(blocks).any(-1)
-    amax = np.max(np.abs(np.where(np.isnan(blocks), 0, blocks)), axis=-1)
+    nan = (~np.isfinite(blocks)).any(-1)
+    amax = np.max(np.abs(np.where(np.isfinite(blocks), blocks, 0)), axis=-1)
     e = block_scale_exponent(amax)
     scales = np.where(nan, 255, e + 127).astype(np.uint8)
     # v / 2^e is exact (a power-of-two scaling of an fp32 value)
     q = blocks.astype(np.float64) / np.ldexp(1.0, e.astype(np.int32))[..., None]
-    q = np.where(np.isnan(q), 0.0, q)
+    q = np.where(np.isfinite(q), q, 0.0)
     codes = e2m1_encode(q).reshape(rows, K)
     return codes, scales
 
@@ -121,6 +124,25 @@ def unpack_nibbles(packed):
     out[:, 0::2] = p & 0xF
     out[:, 1::2] = p >> 4
     return out
+
+
+_RUN = np.array([0, 2, 4, 6, 1, 3, 5, 7])
+
+
+def scales_to_gemm_order(scales):
+    """Reorder each run of 8 block scales of a row to blocks 0, 2, 4, 6, 1,
+    3, 5, 7 (the layout the library stores; K/32 a multiple of 8)."""
+    s = np.asarray(scales)
+    r, nb = s.shape
+    return s.reshape(r, nb // 8, 8)[:, :, _RUN].reshape(r, nb)
+
+
+def scales_from_gemm_order(stored):
+    s = np.asarray(stored)
+    r, nb = s.shape
+    out = np.empty_like(s.reshape(r, nb // 8, 8))
+    out[:, :, _RUN] = s.reshape(r, nb // 8, 8)
+    return out.reshape(r, nb)
 
 
 def gemm_mxfp4(a_codes, a_scales, b_codes, b_scales):

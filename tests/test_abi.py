@@ -301,3 +301,40 @@ def test_gemm_bf16in_refusals(lib):
     assert call(x8=FAKE + MB) == frt.FRT_E_INVALID                # x8 over W8
     assert call(x=FAKE + 40 * MB) == frt.FRT_E_INVALID            # output over x
     assert call(M=0) == frt.FRT_OK
+
+
+def test_mxfp4_refusals(lib):
+    def pack(K=512, W=FAKE, W4=FAKE + 10 * MB, S4=FAKE + 11 * MB):
+        return lib.frt_pack_weights_mxfp4(None, 1, (ctypes.c_int64 * 1)(64), K,
+                                          (ctypes.c_void_p * 1)(W), None, W4, S4, None)
+    assert pack(K=768) == frt.FRT_E_INVALID            # not a multiple of 512
+    assert pack(W=FAKE + 8) == frt.FRT_E_INVALID       # 16-byte weights
+    assert pack(S4=FAKE + 10 * MB + 100) == frt.FRT_E_INVALID   # S4 over W4
+    assert "overlap" in frt.frt_last_error()
+
+    def norm(D=512, **kw):
+        a = dict(stream=None, M=4, D=D, residual=FAKE, ld_res=D, x=None, ld_x=0, gate=None, ld_gate=0,
+                 weight=None, mod=FAKE + MB, ld_mod=0, eps=1e-6, residual_out=None, ld_rout=0,
+                 out_fp4=FAKE + 2 * MB, ld_out=D // 2, out_scale=FAKE + 3 * MB, ld_sc=D // 32,
+                 gate_out=None, ld_gout=0)
+        a.update(kw)
+        return lib.frt_ada_norm_quant_mxfp4(*a.values())
+    assert norm(D=640) == frt.FRT_E_INVALID               # D % 256
+    assert norm(ld_out=200) == frt.FRT_E_INVALID
+    assert norm(out_scale=None) == frt.FRT_E_INVALID
+    assert norm(out_fp4=FAKE + 64) == frt.FRT_E_INVALID   # over residual
+    assert norm(M=0) == frt.FRT_OK
+
+    def gemm(K=512, **kw):
+        a = dict(stream=None, M=16, K=K, x4=FAKE, ld_x4=K // 2, xs=FAKE + MB, ld_xs=K // 32,
+                 W4=FAKE + 2 * MB, S4=FAKE + 3 * MB, N=768, bias=None, n_split=1,
+                 split_n=(ctypes.c_int64 * 1)(768), out=(ctypes.c_void_p * 1)(FAKE + 40 * MB),
+                 ld_out=(ctypes.c_int64 * 1)(768), out_dtype=0)
+        a.update(kw)
+        return lib.frt_packed_gemm_mxfp4_split(*a.values())
+    assert gemm(K=1000) == frt.FRT_E_INVALID
+    assert gemm(ld_x4=200) == frt.FRT_E_INVALID
+    assert gemm(xs=None) == frt.FRT_E_INVALID
+    assert gemm(ld_xs=10) == frt.FRT_E_INVALID
+    assert gemm(out=(ctypes.c_void_p * 1)(FAKE + 3 * MB)) == frt.FRT_E_INVALID   # over S4
+    assert gemm(M=0) == frt.FRT_OK

@@ -118,3 +118,19 @@ def test_gemm_brute_force():
                 xb = Fraction(_e2m1_formula(int(bc[n, k]))) * Fraction(2) ** (int(bs[n, k // 32]) - 127)
                 acc += xa * xb
             assert got[m, n] == float(acc)
+
+
+def test_scale_order_round_trip():
+    s = np.arange(2 * 16, dtype=np.uint8).reshape(2, 16)
+    g = mxfp4.scales_to_gemm_order(s)
+    assert g[0, :8].tolist() == [0, 2, 4, 6, 1, 3, 5, 7]
+    assert g[1, 8:].tolist() == [24, 26, 28, 30, 25, 27, 29, 31]
+    assert np.array_equal(mxfp4.scales_from_gemm_order(g), s)
+
+
+def test_non_finite_block_gets_nan_scale():
+    v = np.zeros((1, 64))
+    v[0, 3] = np.inf
+    v[0, 40] = np.nan
+    _, s = mxfp4.quantize_mxfp4(v)
+    assert s.tolist() == [[255, 255]]
