@@ -32,6 +32,11 @@ and k weight rows pair-interleaved at bind) and writes q and the suffix
 rows of the K/V caches; the unfused pair (bf16 QKV GEMM, standalone split +
 RoPE + cache kernel) is timed beside it.
 
+``--mxfp4`` (AdaRMS workloads 1, 2, 4) runs the MXFP4 band instead: the
+producers emit OCP MX FP4 (dynamic per-32 block scales) and the norm-fed
+GEMMs take MXFP4 weights packed at bind; metric and roofline are the same,
+with the FP4 matrix-core peak.
+
 ``--oproj`` (workload 2) adds the O projection of a seeded attention output:
 the static FP8 quantiser and the packed GEMM. With ``--rope --oproj --ffn``
 a step is the whole decoder layer around the attention core.
@@ -54,6 +59,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0       # dense FP8 MFMA (datasheet 5.0 PFLOP/s)
+FP4_PEAK_TFLOPS = 10100.0      # dense FP4 MFMA (datasheet 10.1 PFLOP/s)
 RIDGE = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 ROTATE_BYTES = 512 << 20
 METRIC = "packed FP8 GEMM TFLOP/s (%MFMA peak) + norm-quant GB/s (%HBM peak)"
@@ -71,6 +77,8 @@ def parse():
     p.add_argument("--ffn", action="store_true",
                    help="workloads 2 and 5: fuse GEGLU + FP8 into the gate/up "
                         "GEMM and append the down projection")
+    p.add_argument("--mxfp4", action="store_true",
+                   help="AdaRMS workloads: MXFP4 producers and GEMMs (the FP4 band)")
     p.add_argument("--oproj", action="store_true",
                    help="workload 2: quantise a seeded attention output and "
                         "run the O projection")
@@ -111,7 +119,7 @@ class Step:
     """Device buffers of one rotation set and the launches of one step."""
 
 
-def build_sets(wid, rows, frt, torch, rope=False):
+def build_sets(wid, rows, frt, torch, rope=False, mx=False):
     import workloads as wl
     w = wl.WORKLOADS[wid]
     inp = wl.producer_inputs(wid, rows=rows)
@@ -179,15 +187,21 @@ def build_sets(wid, rows, frt, torch, rope=False):
                 Ws[i] = t
         bs = [None if b is None else bf16_dev(b) for b in ww["b"]]
         N = sum(ww["splits"])
-        W8 = torch.empty(N, D, dtype=torch.uint8, device="cuda")
-        wsc = torch.empty(1, dtype=torch.float32, device="cuda")
         bc = torch.empty(N, dtype=torch.bfloat16, device="cuda") if w.bias else None
+        if mx:
+            W8 = torch.empty(N, D // 2, dtype=torch.uint8, device="cuda")
+            wsc = torch.empty(D // 256, N, 8, dtype=torch.uint8, device="cuda")
+            pack = lambda: frt.frt_pack_weights_mxfp4(Ws, bs if w.bias else None, W8, wsc, bc)  # noqa: E731
+        else:
+            W8 = torch.empty(N, D, dtype=torch.uint8, device="cuda")
+            wsc = torch.empty(1, dtype=torch.float32, device="cuda")
+            pack = lambda: frt.frt_pack_weights_fp8(Ws, bs if w.bias else None, W8, wsc, bc)  # noqa: E731
         # the first call also loads the packer's kernels: time a second one
-        frt.frt_pack_weights_fp8(Ws, bs if w.bias else None, W8, wsc, bc)
+        pack()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        frt.frt_pack_weights_fp8(Ws, bs if w.bias else None, W8, wsc, bc)
+        pack()
         e1.record()
         torch.cuda.synchronize()
         pack_ms.append(e0.elapsed_time(e1))
@@ -252,6 +266,8 @@ def make_rotation(w, dev, packs, rows, torch, ffn=None):
             q = dict(p)
             if i > 0:
                 q["W8"] = p["W8"].clone()
+                if p["ws"].numel() > 1:      # MXFP4 block scales rotate with their codes
+                    q["ws"] = p["ws"].clone()
             s["packs"].append(q)
         if ffn is not None:
             s["ffn"] = dict(ffn)
@@ -310,6 +326,29 @@ def make_outputs(w, rows, packs, torch, ffn=None):
         o["gu"] = torch.empty(rows, 2 * H, dtype=torch.bfloat16, device="cuda")
         o["hid8_unfused"] = torch.empty(rows, H, dtype=torch.uint8, device="cuda")
     return o
+
+
+def step_launches_mx(w, s, outs, rows, frt, eps):
+    """The MXFP4 band's step: the AdaRMS producers emit MXFP4, the packed
+    GEMMs take MXFP4 operands."""
+    d = s["dev"]
+    D = w.D
+    o4 = outs["x4"]
+    L = [("norm1_mx", lambda: frt.frt_ada_norm_quant_mxfp4(
+        d["res"], d["mod"], o4[0][0], o4[0][1], x=d["x"], gate=d["gate"], eps=eps,
+        residual_out=outs["rout"]))]
+    p0 = s["packs"][0]
+    L.append(("gemm1_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
+        o4[0][0], o4[0][1], p0["W8"], p0["ws"], outs["gemm"][0], p0["splits"], bias_cat=p0["bias"])))
+    if len(s["packs"]) > 1:
+        p1 = s["packs"][1]
+        L.append(("norm2_mx", lambda: frt.frt_ada_norm_quant_mxfp4(
+            outs["rout"], d["mod2"], o4[1][0], o4[1][1], x=d["x2"],
+            gate=d["mod"][0, 2 * D:3 * D], eps=eps, residual_out=outs["rout2"])))
+        L.append(("gemm2_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
+            o4[1][0], o4[1][1], p1["W8"], p1["ws"], outs["gemm"][1], p1["splits"],
+            bias_cat=p1["bias"])))
+    return L
 
 
 def step_launches(w, s, act, outs, rows, frt, eps):
@@ -392,6 +431,15 @@ def unfused_launches(w, s, act, outs, frt):
 def kernel_work(w, kind, rows, packs, ffn=None, rope=None, oproj=None):
     """Algorithmic bytes and FLOPs of one launch."""
     D = w.D
+    if kind.endswith("_mx"):
+        if kind.startswith("norm"):     # res, x, rout bf16; codes D/2; scales D/32
+            gate = rows * D * 2 if (w.cid == 4 and kind == "norm1_mx") else D * 2
+            return rows * D * 2 * 3 + gate + 3 * D * 2 + rows * (D // 2 + D // 32), 0.0
+        p = packs[0 if kind == "gemm1_mx" else 1]
+        N = sum(p["splits"])
+        b = rows * (D // 2 + D // 32) + N * (D // 2 + D // 32) + rows * N * 2 + \
+            (N * 2 if p["bias"] is not None else 0)
+        return b, 2.0 * rows * N * D
     if oproj is not None and kind in ("quant_o", "gemm_o"):
         Ko = oproj["att"].shape[1]
         if kind == "quant_o":           # bf16 in, codes out
@@ -700,7 +748,10 @@ def main():
     rows = a.rows if a.rows is not None else w0.rows
     if (a.rope or a.oproj) and a.workload not in wl.QKV_HEADS:
         raise SystemExit(f"--rope: the attention head is defined for workloads {sorted(wl.QKV_HEADS)}")
-    w, dev, act, packs, pack_ms = build_sets(a.workload, rows, frt, torch, rope=a.rope)
+    if a.mxfp4 and (wl.WORKLOADS[a.workload].form != "adarms" or a.ffn or a.rope or a.oproj):
+        raise SystemExit("--mxfp4: the MXFP4 band covers the AdaRMS workloads' producer + packed "
+                         "GEMM step (1, 2, 4), alone")
+    w, dev, act, packs, pack_ms = build_sets(a.workload, rows, frt, torch, rope=a.rope, mx=a.mxfp4)
     ffn = None
     if a.ffn:
         if a.workload not in wl.FFN_HIDDEN:
@@ -709,6 +760,9 @@ def main():
         ffn = build_ffn(w, rows, act, packs, frt, torch)
     sets, per_set = make_rotation(w, dev, packs, rows, torch, ffn)
     outs = make_outputs(w, rows, packs, torch, ffn)
+    if a.mxfp4:
+        outs["x4"] = [(torch.empty(rows, w.D // 2, dtype=torch.uint8, device="cuda"),
+                       torch.empty(w.D // 256, rows, 8, dtype=torch.uint8, device="cuda")) for _ in packs]
     rp = make_rope(w, rows, torch) if a.rope else None
     op = make_oproj(w, rows, frt, torch) if a.oproj else None
     for i, st in enumerate(sets):
@@ -718,7 +772,8 @@ def main():
             st["oproj"] = dict(op, W8=op["W8"] if i == 0 else op["W8"].clone())
     nset = len(sets)
 
-    steps_fns = [step_launches(w, s, act, outs, rows, frt, wl.EPS) for s in sets]
+    steps_fns = [step_launches_mx(w, s, outs, rows, frt, wl.EPS) if a.mxfp4 else
+                 step_launches(w, s, act, outs, rows, frt, wl.EPS) for s in sets]
     if a.profile_kernel:
         # one kernel kind, eagerly, over the rotation sets (after one full
         # step so every input it reads is defined)
@@ -790,9 +845,10 @@ def main():
         row = {"kernel": kind, "us": round(us, 3), "bytes": int(b),
                "GB/s": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
         if f:
+            peak = FP4_PEAK_TFLOPS if kind.endswith("_mx") else FP8_PEAK_TFLOPS
             row["TFLOP/s"] = round(f / us / 1e6, 2)
-            row["mfma_frac"] = round(f / us / 1e6 / FP8_PEAK_TFLOPS, 4)
-            row["bound"] = "mfma" if f / b > RIDGE else "hbm"
+            row["mfma_frac"] = round(f / us / 1e6 / peak, 4)
+            row["bound"] = "mfma" if f / b > peak * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
         else:
             row["bound"] = "hbm"
         if kind not in kinds:
@@ -806,7 +862,8 @@ def main():
     dom = max((r for r in table if r["kernel"] in kinds), key=lambda r: r["us"])
     traffic = load_traffic(a.workload, dom["kernel"]) if a.rows is None else None
     if dom["bound"] == "mfma":
-        roof = {"bound": "mfma", "achieved": dom["TFLOP/s"], "peak": FP8_PEAK_TFLOPS,
+        roof = {"bound": "mfma", "achieved": dom["TFLOP/s"],
+                "peak": FP4_PEAK_TFLOPS if dom["kernel"].endswith("_mx") else FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": dom["mfma_frac"], "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS,
@@ -820,9 +877,10 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4_e2m1" if a.mxfp4 else "fp8_e4m3",
         "data": "synthetic",
-        "config": {"workload": w.name + ("+qkv_rope_kvcache" if rp is not None else "")
+        "config": {"workload": w.name + ("+mxfp4" if a.mxfp4 else "")
+                               + ("+qkv_rope_kvcache" if rp is not None else "")
                                + ("+o_proj" if op is not None else "")
                                + ("+ffn_geglu_down" if ffn is not None else ""),
                    "rows": rows, "D": w.D,
@@ -841,7 +899,7 @@ def main():
         res["config"]["ffn"] = {"H": ffn["H"], "down": [w.D, ffn["H"]]}
     if rp is not None:
         res["config"]["rope"] = {k: rp[k] for k in ("nh", "kv", "hd", "P", "T")}
-    if not a.no_cpu_baseline and ffn is None and rp is None and op is None:
+    if not a.no_cpu_baseline and ffn is None and rp is None and op is None and not a.mxfp4:
         res["cpu_baseline"] = cpu_baseline(w, rows)
     print(json.dumps(res), flush=True)
 

@@ -389,9 +389,11 @@ int frt_packed_gemm_bf16in_split(void* stream, int64_t M, int64_t K,
  *     fp32 block values (byte 0 for a zero or subnormal maximum, 0xFF for
  *     NaN or inf), code = e2m1 round-to-nearest-even of v / scale,
  *     saturating at 6;
- *   - scale layout: within each run of 8 consecutive blocks (256 elements)
- *     of a row, the bytes are stored in the order of blocks 0, 2, 4, 6, 1,
- *     3, 5, 7 (the order in which the GEMM's lanes consume them).
+ *   - scale layout: run-major [K/256][rows][8]: the 8 block scales of each
+ *     run of 256 elements of a row sit together, ordered blocks 0, 2, 4, 6,
+ *     1, 3, 5, 7, and the runs of all rows for one K range are contiguous
+ *     (rows 8 bytes apart, runs `ld` bytes apart), so the GEMM reads a
+ *     32-row block's scales for a K range as 256 contiguous bytes.
  */
 
 /*
@@ -402,7 +404,7 @@ int frt_packed_gemm_bf16in_split(void* stream, int64_t M, int64_t K,
  *                 every W_i 16-byte aligned.
  *   K             multiple of 512 in [512, 16384].
  *   W4            [sum N_i, K/2] code bytes (4-byte aligned).
- *   S4            [sum N_i, K/32] scale bytes (GEMM order).
+ *   S4            scale bytes, [K/256][sum N_i][8] (run stride 8 * sum N_i).
  *   bias_cat      bf16 [sum N_i] or NULL.
  */
 int frt_pack_weights_mxfp4(void* stream, int n_sib, const int64_t* N_i,
@@ -421,7 +423,8 @@ int frt_pack_weights_mxfp4(void* stream, int n_sib, const int64_t* N_i,
  *   residual, x, gate, weight, mod, eps, residual_out, gate_out   as in
  *                 frt_ada_norm_quant_fp8 (16-byte aligned, ld % 8 == 0).
  *   out_fp4       [M, ld_out] code bytes, ld_out >= D/2, a multiple of 4.
- *   out_scale     [M, ld_sc] scale bytes, ld_sc >= D/32 (GEMM order).
+ *   out_scale     scale bytes [D/256][rows][8]; ld_sc = the run stride in
+ *                 bytes, >= 8*M (8 * the buffer's row capacity).
  */
 int frt_ada_norm_quant_mxfp4(void* stream, int64_t M, int64_t D,
                              const uint16_t* residual, int64_t ld_res,
@@ -444,10 +447,12 @@ int frt_ada_norm_quant_mxfp4(void* stream, int64_t M, int64_t D,
  *   M, K          rows; K a multiple of 512 in [512, 16384].
  *   x4, ld_x4     [M, ld_x4] code bytes (16-byte aligned, ld_x4 >= K/2, a
  *                 multiple of 16).
- *   xs, ld_xs     [M, ld_xs] scale bytes (4-byte aligned, ld_xs >= K/32, a
- *                 multiple of 4).
- *   W4, S4        [N_total, K/2] codes (16-byte aligned) and [N_total, K/32]
- *                 scales (4-byte aligned), as frt_pack_weights_mxfp4 writes.
+ *   xs, ld_xs     scale bytes [K/256][rows][8], ld_xs the run stride
+ *                 (>= 8*M, a multiple of 4; 4-byte aligned), as
+ *                 frt_ada_norm_quant_mxfp4 writes.
+ *   W4, S4        [N_total, K/2] codes (16-byte aligned) and the scales
+ *                 [K/256][N_total][8] (4-byte aligned), as
+ *                 frt_pack_weights_mxfp4 writes.
  *   bias_cat, n_split, split_n, out, ld_out, out_dtype   as in
  *                 frt_packed_gemm_fp8_split (outputs must not overlap the
  *                 operands or the scales).

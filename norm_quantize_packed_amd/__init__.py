@@ -479,7 +479,7 @@ def frt_packed_gemm_bf16in_split(x, x8, W8, act_scale, w_scale, outs: Sequence,
 def frt_pack_weights_mxfp4(weights: Sequence, biases: Optional[Sequence], W4, S4,
                            bias_cat=None, *, stream=None) -> None:
     """MXFP4 packing of sibling ``[N_i, K]`` bf16 weights: codes ``W4``
-    ``[sum N, K/2]`` and E8M0 scales ``S4`` ``[sum N, K/32]``."""
+    ``[sum N, K/2]`` and E8M0 scales ``S4`` ``[K/256, sum N, 8]``."""
     n = len(weights)
     K = weights[0].shape[1]
     for i, w in enumerate(weights):
@@ -501,7 +501,7 @@ def frt_ada_norm_quant_mxfp4(residual, mod, out_fp4, out_scale, *, x=None,
                              residual_out=None, gate_out=None,
                              M: Optional[int] = None, stream=None) -> None:
     """Gated residual + AdaRMS with an MXFP4 output (codes ``[M, D/2]``,
-    scales ``[M, D/32]``)."""
+    scales ``[D/256, rows, 8]``; the run stride is ``stride(0)``)."""
     for t, n in ((residual, "residual"), (mod, "mod"), (x, "x"),
                  (gate, "gate"), (weight, "weight"),
                  (residual_out, "residual_out"), (gate_out, "gate_out")):
@@ -524,7 +524,7 @@ def frt_packed_gemm_mxfp4_split(x4, xs, W4, S4, outs: Sequence,
                                 split_n: Sequence[int], bias_cat=None, *,
                                 M: Optional[int] = None, stream=None) -> None:
     """Packed GEMM on MXFP4 operands (codes ``x4 [M, K/2]``, scales
-    ``xs [M, K/32]``; ``W4``/``S4`` from ``frt_pack_weights_mxfp4``)."""
+    ``xs [K/256, rows, 8]``; ``W4``/``S4`` from ``frt_pack_weights_mxfp4``)."""
     import torch
     for t, nme in ((x4, "x4"), (xs, "xs"), (W4, "W4"), (S4, "S4")):
         _u8_like(t, nme)

@@ -488,7 +488,7 @@ int frt_pack_weights_mxfp4(void* stream, int n_sib, const int64_t* N_i, int64_t 
     rows += N_i[i];
   }
   if (rows > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "pack_mxfp4: too many rows");
-  const Range w4r = span(W4, rows, K / 2, K / 2, 1), s4r = span(S4, rows, K / 32, K / 32, 1),
+  const Range w4r = span(W4, rows, K / 2, K / 2, 1), s4r = span(S4, K / 256, rows * 8, rows * 8, 1),
               br = span(bias_cat, 1, rows, rows, 2);
   if (overlap(w4r, s4r) || overlap(w4r, br) || overlap(s4r, br)) return refuse(FRT_E_INVALID, "pack_mxfp4: outputs overlap");
   for (int i = 0; i < n_sib; ++i) {
@@ -516,7 +516,7 @@ int frt_ada_norm_quant_mxfp4(void* stream, int64_t M, int64_t D, const uint16_t*
     return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_gate must be 0 (broadcast) or >= D");
   if (ld_mod != 0 && ld_mod < 3 * D) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_mod must be 0 or >= 3*D");
   if (ld_out < D / 2 || ld_out % 4) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_out must be >= D/2 and a multiple of 4");
-  if (ld_sc < D / 32) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_sc < D/32");
+  if (ld_sc < 8 * M) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_sc (the scale run stride) < 8*M");
   if (residual_out != nullptr && ld_rout < D) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_rout < D");
   if (gate_out != nullptr && ld_gout < D) return refuse(FRT_E_INVALID, "ada_norm_mxfp4: ld_gout < D");
   const bool al = aligned(residual, 16) && ld_res % 8 == 0 && (x == nullptr || (aligned(x, 16) && ld_x % 8 == 0)) &&
@@ -531,7 +531,7 @@ int frt_ada_norm_quant_mxfp4(void* stream, int64_t M, int64_t D, const uint16_t*
                       span(gate, grows, D, ld_gate ? ld_gate : D, 2), span(weight, 1, D, D, 2),
                       span(mod, mrows, 3 * D, ld_mod ? ld_mod : 3 * D, 2)};
   const Range outs[] = {span(residual_out, M, D, ld_rout, 2), span(out_fp4, M, D / 2, ld_out, 1),
-                        span(out_scale, M, D / 32, ld_sc, 1), span(gate_out, M, D, ld_gout, 2)};
+                        span(out_scale, D / 256, 8 * M, ld_sc, 1), span(gate_out, M, D, ld_gout, 2)};
   const bool inplace = residual_out != nullptr && residual_out == residual && ld_rout == ld_res;
   for (int o = 0; o < 4; ++o) {
     for (int i = 0; i < 5; ++i) {
@@ -559,8 +559,8 @@ int frt_packed_gemm_mxfp4_split(void* stream, int64_t M, int64_t K, const uint8_
   if (K < 512 || K > 16384 || K % 512)
     return refuse(FRT_E_INVALID, "gemm_mxfp4: K=%lld must be a multiple of 512 in [512, 16384]", (long long)K);
   if (xs == nullptr || S4 == nullptr) return refuse(FRT_E_INVALID, "gemm_mxfp4: xs and S4 are required");
-  if (ld_xs < K / 32 || !aligned(xs, 4) || ld_xs % 4 || !aligned(S4, 4))
-    return refuse(FRT_E_INVALID, "gemm_mxfp4: scales must be 4-byte aligned with ld_xs >= K/32, a multiple of 4");
+  if (ld_xs < 8 * M || !aligned(xs, 4) || ld_xs % 4 || !aligned(S4, 4))
+    return refuse(FRT_E_INVALID, "gemm_mxfp4: scales 4-byte aligned, ld_xs (run stride) >= 8*M and a multiple of 4");
   // the packed GEMM's own contract on the code bytes (K/2 per row): shapes,
   // 16-byte alignment, ld % 16, splits and output overlaps; the FP8 scale
   // pointers are not used, so the scale buffers stand in for them
@@ -570,7 +570,7 @@ int frt_packed_gemm_mxfp4_split(void* stream, int64_t M, int64_t K, const uint8_
                               out_dtype, nullptr, 0, a);
   if (rc != FRT_OK) return rc;
   if (M == 0) return ok();
-  const Range sar = span(xs, M, K / 32, ld_xs, 1), sbr = span(S4, N_total, K / 32, K / 32, 1);
+  const Range sar = span(xs, K / 256, 8 * M, ld_xs, 1), sbr = span(S4, K / 256, 8 * N_total, 8 * N_total, 1);
   for (int s = 0; s < n_split; ++s) {
     const Range o = span(out[s], M, split_n[s], ld_out[s], out_dtype ? 4 : 2);
     if (overlap(o, sar) || overlap(o, sbr)) return refuse(FRT_E_INVALID, "gemm_mxfp4: output %d overlaps a scale buffer", s);

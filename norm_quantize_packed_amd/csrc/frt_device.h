@@ -102,12 +102,12 @@ __device__ __forceinline__ uint32_t mxfp4_pack8(const float* v, uint32_t sbyte) 
   return w;
 }
 
-// Position of block b's scale byte in a row: within each run of 8 blocks
-// the bytes are ordered 0, 2, 4, 6, 1, 3, 5, 7 (the order the MXFP4 GEMM
-// reads them in).
-__device__ __forceinline__ int64_t e8m0_pos(int64_t b) {
+// Byte offset of row m's block b in the MXFP4 scale layout: run-major
+// [K/256][rows][8] with run stride ld_run, the 8 blocks of a run ordered
+// 0, 2, 4, 6, 1, 3, 5, 7 (the order the GEMM's lanes consume them).
+__device__ __forceinline__ int64_t e8m0_off(int64_t m, int64_t b, int64_t ld_run) {
   const int j = (int)(b & 7);
-  return (b & ~(int64_t)7) | ((j & 1) ? 4 + (j >> 1) : (j >> 1));
+  return (b >> 3) * ld_run + m * 8 + ((j & 1) ? 4 + (j >> 1) : (j >> 1));
 }
 
 // Max of the four lanes of a quad (DPP xor 1, xor 2).

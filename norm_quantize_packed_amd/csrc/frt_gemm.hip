@@ -121,10 +121,12 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // row), with one E8M0 scale per 32 K-elements in sa [M, ld_sa] and sb
 // [N, K/32]. A 128-byte stage row holds 256 K-elements, i.e. four 64-deep
 // MFMA steps, each reading one 16-byte chunk per operand (lane l: row l % 32,
-// K half l / 32 = exactly one scale block). The scales are stored in the
-// MFMA order: within each run of 8 blocks (256 K-elements) the bytes are
-// blocks 0, 2, 4, 6, 1, 3, 5, 7, so the lanes of K half h load one dword
-// holding their blocks h, 2 + h, 4 + h, 6 + h and step s selects byte s.
+// K half l / 32 = exactly one scale block). The scales are stored run-major,
+// [K/256][rows][8] (run stride ld_sa for x, 8 N for W), each run of 8 blocks
+// (256 K-elements) in the order 0, 2, 4, 6, 1, 3, 5, 7: the lanes of K half
+// h load one dword holding their blocks h, 2 + h, 4 + h, 6 + h (a 32-row
+// block's dwords for one run are 256 contiguous bytes) and step s selects
+// byte s.
 // The scales of a stage are loaded into registers by the same issue call
 // as its tiles (so the wait counts cover them); alpha is 1.
 template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB, int AE = BM,
@@ -190,11 +192,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   if constexpr (FP4) {
     const int h4 = (lane >> 5) * 4;  // this K half's dword of a run
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
-      sa_row[i] = a.sa + (int64_t)min(m0 + wm0 + i * 32 + (lane & 31), a.M - 1) * a.ld_sa + h4;
+    for (int i = 0; i < MI; ++i) sa_row[i] = a.sa + (int64_t)min(m0 + wm0 + i * 32 + (lane & 31), a.M - 1) * 8 + h4;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      sb_row[j] = a.sb + (int64_t)min(n0 + wn0 + j * 32 + (lane & 31), a.N - 1) * (a.K / 32) + h4;
+    for (int j = 0; j < NJ; ++j) sb_row[j] = a.sb + (int64_t)min(n0 + wn0 + j * 32 + (lane & 31), a.N - 1) * 8 + h4;
   }
   // slot SL (= step mod NS) is a compile-time constant in every use, so all
   // LDS addresses are one lane base plus immediates
@@ -230,12 +230,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
           __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
       }
       if constexpr (FP4) {
-        // this lane's 4 block scales of the sub-buffer (256 K-elements)
-        const int blk = (kt * NSUB + q) * 8;
+        // this lane's 4 block scales of the sub-buffer (run kt * NSUB + q)
+        const int64_t run = kt * NSUB + q;
 #pragma unroll
-        for (int i = 0; i < MI; ++i) scA[SL][q][i] = *reinterpret_cast<const unsigned*>(sa_row[i] + blk);
+        for (int i = 0; i < MI; ++i)
+          scA[SL][q][i] = *reinterpret_cast<const unsigned*>(sa_row[i] + run * a.ld_sa);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) scB[SL][q][j] = *reinterpret_cast<const unsigned*>(sb_row[j] + blk);
+        for (int j = 0; j < NJ; ++j)
+          scB[SL][q][j] = *reinterpret_cast<const unsigned*>(sb_row[j] + run * ((int64_t)a.N * 8));
       }
     }
   };

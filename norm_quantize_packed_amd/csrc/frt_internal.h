@@ -22,7 +22,8 @@ struct AdaArgs {
   float* amax;
   int64_t M; int D;
   // MXFP4 output (launch_ada_norm_mxfp4): e2m1 codes in out ([M, ld_out]
-  // bytes, two per byte) and E8M0 block scales in sc [M, ld_sc]
+  // bytes, two per byte) and E8M0 block scales in sc, run-major
+  // [D/256][rows][8] with run stride ld_sc
   uint8_t* sc; int64_t ld_sc;
 };
 
@@ -52,7 +53,7 @@ struct PackSib {
 
 hipError_t launch_pack(const PackSib* sibs, int n_sib, int64_t K, uint8_t* w8,
                        float* w_scale, uint16_t* bias_cat, hipStream_t st);
-// MXFP4 pack: codes [sum N, K/2], E8M0 scales [sum N, K/32] (GEMM order)
+// MXFP4 pack: codes [sum N, K/2], E8M0 scales run-major [K/256][sum N][8]
 hipError_t launch_pack_mxfp4(const PackSib* sibs, int n_sib, int64_t K, uint8_t* w4, uint8_t* s4,
                              uint16_t* bias_cat, hipStream_t st);
 
@@ -84,7 +85,8 @@ struct GemmArgs {
   int64_t P;
   uint16_t* q_out; uint16_t* k_cache; uint16_t* v_cache;
   // MXFP4 operands (launch_gemm_mxfp4): x, w hold e2m1 codes (K/2 bytes a
-  // row, ld_x in bytes); E8M0 block scales sa [M, ld_sa], sb [N, K/32]
+  // row, ld_x in bytes); E8M0 block scales run-major [K/256][rows][8]: sa
+  // with run stride ld_sa, sb with run stride 8 N
   const uint8_t* sa; int64_t ld_sa;
   const uint8_t* sb;
 };

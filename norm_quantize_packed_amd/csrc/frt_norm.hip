@@ -113,7 +113,8 @@ __device__ __forceinline__ void amax_commit(float* amax, float m) {
 // MX: MXFP4 output instead of static FP8 (vector path, D % 256 == 0): the
 // four lanes of a quad hold 32 consecutive columns, one block; its max
 // comes from two DPP steps, then each lane writes its 8 codes (4 bytes) and
-// the quad's first lane the block's scale byte.
+// the quad's first lane the block's scale byte (run-major layout, run
+// stride ld_sc).
 template <int WPR, int NV, int VEC, bool MX = false>
 __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ada_norm_kernel(AdaArgs a) {
   constexpr int RPB = WPR <= 4 ? 4 / WPR : 1;
@@ -212,7 +213,7 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ada_norm_kernel(Ada
           for (int e = 0; e < VEC; ++e) am = max(am, __float_as_uint(fabsf(y[e])));
           const uint32_t sbyte = e8m0_of_amax(quad_umax(am));
           *reinterpret_cast<uint32_t*>(a.out + row * a.ld_out + c / 2) = mxfp4_pack8(y, sbyte);
-          if ((lane & 3) == 0) a.sc[row * a.ld_sc + e8m0_pos(c / 32)] = (uint8_t)sbyte;
+          if ((lane & 3) == 0) a.sc[e8m0_off(row, c / 32, a.ld_sc)] = (uint8_t)sbyte;
         } else if (a.out != nullptr) {
           float q[VEC];
 #pragma unroll

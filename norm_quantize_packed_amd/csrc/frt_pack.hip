@@ -129,8 +129,10 @@ unsigned grid_for(int64_t work, int64_t cap = 4096) {
 // elements of a row (16-byte load), the four threads of a quad one block of
 // 32; rows follow each other, so a quad never straddles a row. Threads past
 // the end still take part in the quad max (with zeros) and store nothing.
+// scales: the packed matrix's run-major scale array offset to this
+// sibling's first row (run stride = 8 x all packed rows).
 __global__ __launch_bounds__(kThreads) void pack_mx_kernel(const uint16_t* w, int64_t rows, int64_t K,
-                                                           uint8_t* codes, uint8_t* scales) {
+                                                           uint8_t* codes, uint8_t* scales, int64_t rows_total) {
   const int64_t nv = K / 8;
   const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const bool ok = t < rows * nv;
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void pack_mx_kernel(const uint16_t* w, in
   const uint32_t sbyte = e8m0_of_amax(quad_umax(am));
   if (ok) {
     *reinterpret_cast<uint32_t*>(codes + row * (K / 2) + vv * 4) = mxfp4_pack8(v, sbyte);
-    if ((threadIdx.x & 3) == 0) scales[row * (K / 32) + e8m0_pos(vv / 4)] = (uint8_t)sbyte;
+    if ((threadIdx.x & 3) == 0) scales[e8m0_off(row, vv / 4, rows_total * 8)] = (uint8_t)sbyte;
   }
 }
 
@@ -156,14 +158,15 @@ __global__ __launch_bounds__(kThreads) void pack_mx_kernel(const uint16_t* w, in
 
 hipError_t launch_pack_mxfp4(const PackSib* sibs, int n_sib, int64_t K, uint8_t* w4, uint8_t* s4,
                              uint16_t* bias_cat, hipStream_t st) {
+  const int64_t rows_total = sibs[n_sib - 1].row_off + sibs[n_sib - 1].rows;
   for (int i = 0; i < n_sib; ++i) {
     if (bias_cat != nullptr)
       hipLaunchKernelGGL(pack_prep_kernel, dim3(grid_for(sibs[i].rows)), dim3(kThreads), 0, st, nullptr,
                          bias_cat, sibs[i].b, sibs[i].rows, sibs[i].row_off, 0);
     const int64_t threads = sibs[i].rows * (K / 8);
     hipLaunchKernelGGL(pack_mx_kernel, dim3((unsigned)((threads + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       st, sibs[i].w, sibs[i].rows, K, w4 + sibs[i].row_off * (K / 2),
-                       s4 + sibs[i].row_off * (K / 32));
+                       st, sibs[i].w, sibs[i].rows, K, w4 + sibs[i].row_off * (K / 2), s4 + sibs[i].row_off * 8,
+                       rows_total);
   }
   return hipGetLastError();
 }

@@ -28,9 +28,10 @@ Readings where the pages and the specification leave a step open:
 - a block whose maximum is 0 gets the smallest scale (byte 0) and zero
   codes; a NaN in a block makes its scale byte 0xFF;
 - codes are stored two per byte, the lower-indexed element in the low
-  nibble; scales one byte per block, each run of 8 blocks stored in the
-  order 0, 2, 4, 6, 1, 3, 5, 7 (``scales_to_gemm_order``: the library's
-  layout, in which the GEMM's lanes read their blocks);
+  nibble; scales one byte per block, stored run-major ``[K/256, rows, 8]``
+  with each run of 8 blocks in the order 0, 2, 4, 6, 1, 3, 5, 7
+  (``scales_to_gemm_order``: the library's layout, in which the GEMM reads
+  a whole row block's scales for one K range as one contiguous piece);
 - a NaN or an infinity in a block makes its scale byte 0xFF.
 """
 
@@ -130,19 +131,22 @@ _RUN = np.array([0, 2, 4, 6, 1, 3, 5, 7])
 
 
 def scales_to_gemm_order(scales):
-    """Reorder each run of 8 block scales of a row to blocks 0, 2, 4, 6, 1,
-    3, 5, 7 (the layout the library stores; K/32 a multiple of 8)."""
+    """The library's scale layout: ``[K/256, rows, 8]`` (run-major: the 8
+    block scales of each run of 256 elements of a row sit together, and the
+    runs of all rows for one K range are contiguous), each run reordered to
+    blocks 0, 2, 4, 6, 1, 3, 5, 7. ``scales`` is ``[rows, K/32]``."""
     s = np.asarray(scales)
     r, nb = s.shape
-    return s.reshape(r, nb // 8, 8)[:, :, _RUN].reshape(r, nb)
+    return np.ascontiguousarray(s.reshape(r, nb // 8, 8)[:, :, _RUN].transpose(1, 0, 2))
 
 
 def scales_from_gemm_order(stored):
-    s = np.asarray(stored)
-    r, nb = s.shape
-    out = np.empty_like(s.reshape(r, nb // 8, 8))
-    out[:, :, _RUN] = s.reshape(r, nb // 8, 8)
-    return out.reshape(r, nb)
+    """Inverse of ``scales_to_gemm_order``: ``[K/256, rows, 8]`` -> ``[rows, K/32]``."""
+    g = np.asarray(stored)
+    runs, r, _ = g.shape
+    out = np.empty((r, runs, 8), dtype=g.dtype)
+    out[:, :, _RUN] = g.transpose(1, 0, 2)
+    return out.reshape(r, runs * 8)
 
 
 def gemm_mxfp4(a_codes, a_scales, b_codes, b_scales):

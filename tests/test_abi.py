@@ -315,7 +315,7 @@ def test_mxfp4_refusals(lib):
     def norm(D=512, **kw):
         a = dict(stream=None, M=4, D=D, residual=FAKE, ld_res=D, x=None, ld_x=0, gate=None, ld_gate=0,
                  weight=None, mod=FAKE + MB, ld_mod=0, eps=1e-6, residual_out=None, ld_rout=0,
-                 out_fp4=FAKE + 2 * MB, ld_out=D // 2, out_scale=FAKE + 3 * MB, ld_sc=D // 32,
+                 out_fp4=FAKE + 2 * MB, ld_out=D // 2, out_scale=FAKE + 3 * MB, ld_sc=8 * 4,
                  gate_out=None, ld_gout=0)
         a.update(kw)
         return lib.frt_ada_norm_quant_mxfp4(*a.values())
@@ -326,7 +326,7 @@ def test_mxfp4_refusals(lib):
     assert norm(M=0) == frt.FRT_OK
 
     def gemm(K=512, **kw):
-        a = dict(stream=None, M=16, K=K, x4=FAKE, ld_x4=K // 2, xs=FAKE + MB, ld_xs=K // 32,
+        a = dict(stream=None, M=16, K=K, x4=FAKE, ld_x4=K // 2, xs=FAKE + MB, ld_xs=8 * 16,
                  W4=FAKE + 2 * MB, S4=FAKE + 3 * MB, N=768, bias=None, n_split=1,
                  split_n=(ctypes.c_int64 * 1)(768), out=(ctypes.c_void_p * 1)(FAKE + 40 * MB),
                  ld_out=(ctypes.c_int64 * 1)(768), out_dtype=0)
@@ -335,6 +335,6 @@ def test_mxfp4_refusals(lib):
     assert gemm(K=1000) == frt.FRT_E_INVALID
     assert gemm(ld_x4=200) == frt.FRT_E_INVALID
     assert gemm(xs=None) == frt.FRT_E_INVALID
-    assert gemm(ld_xs=10) == frt.FRT_E_INVALID
+    assert gemm(ld_xs=100) == frt.FRT_E_INVALID           # run stride < 8*M
     assert gemm(out=(ctypes.c_void_p * 1)(FAKE + 3 * MB)) == frt.FRT_E_INVALID   # over S4
     assert gemm(M=0) == frt.FRT_OK

@@ -25,7 +25,7 @@ def _gpu_pack(Ws, bs=None):
     K = Ws[0].shape[1]
     N = sum(w.shape[0] for w in Ws)
     W4 = Guarded(N, K // 2, torch.uint8)
-    S4 = Guarded(N, K // 32, torch.uint8)
+    S4 = Guarded(K // 256, 8 * N, torch.uint8)      # [K/256][N][8]
     bc = torch.empty(N, dtype=torch.bfloat16, device="cuda") if bs is not None else None
     frt.frt_pack_weights_mxfp4([dev_bf16(w) for w in Ws],
                                None if bs is None else [dev_bf16(b) for b in bs],
@@ -33,7 +33,8 @@ def _gpu_pack(Ws, bs=None):
     torch.cuda.synchronize()
     W4.check_guards()
     S4.check_guards()
-    return host_u8(W4.view), host_u8(S4.view), (host_bf16(bc) if bc is not None else None)
+    return (host_u8(W4.view), host_u8(S4.view).reshape(K // 256, N, 8),
+            (host_bf16(bc) if bc is not None else None))
 
 
 def _oracle_pack(Ws):
@@ -70,7 +71,7 @@ def test_ada_norm_mxfp4_vs_oracle(M, D):
     ref = producers.ada_norm_quant_fp8(res, x, gate, mod, None, 1e-6)
     rc, rs = mxfp4.quantize_mxfp4(ref["y"])
     out4 = Guarded(M, D // 2, torch.uint8)
-    sc = Guarded(M, D // 32, torch.uint8)
+    sc = Guarded(D // 256, 8 * M, torch.uint8)      # [D/256][M][8]
     rout = torch.empty((M, D), dtype=torch.bfloat16, device="cuda")
     frt.frt_ada_norm_quant_mxfp4(dev_bf16(res), dev_bf16(mod), out4.view, sc.view, x=dev_bf16(x),
                                  gate=dev_bf16(gate), eps=1e-6, residual_out=rout)
@@ -78,7 +79,7 @@ def test_ada_norm_mxfp4_vs_oracle(M, D):
     out4.check_guards()
     sc.check_guards()
     assert np.array_equal(host_bf16(rout), ref["residual_out"])
-    gs = mxfp4.scales_from_gemm_order(host_u8(sc.view))
+    gs = mxfp4.scales_from_gemm_order(host_u8(sc.view).reshape(D // 256, M, 8))
     gc = mxfp4.unpack_nibbles(host_u8(out4.view))
     same = gs == rs
     assert same.mean() >= 0.999, f"{(~same).sum()} of {same.size} block scales differ"

@@ -123,8 +123,10 @@ def test_gemm_brute_force():
 def test_scale_order_round_trip():
     s = np.arange(2 * 16, dtype=np.uint8).reshape(2, 16)
     g = mxfp4.scales_to_gemm_order(s)
-    assert g[0, :8].tolist() == [0, 2, 4, 6, 1, 3, 5, 7]
-    assert g[1, 8:].tolist() == [24, 26, 28, 30, 25, 27, 29, 31]
+    assert g.shape == (2, 2, 8)
+    assert g[0, 0].tolist() == [0, 2, 4, 6, 1, 3, 5, 7]       # run 0 of row 0
+    assert g[0, 1].tolist() == [16, 18, 20, 22, 17, 19, 21, 23]  # run 0 of row 1
+    assert g[1, 1].tolist() == [24, 26, 28, 30, 25, 27, 29, 31]
     assert np.array_equal(mxfp4.scales_from_gemm_order(g), s)
 
 
