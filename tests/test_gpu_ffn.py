@@ -144,7 +144,7 @@ def _run_unfused(x8, s_a, w8, s_w, bias, s_o, H, M=None):
     (64, 1040, 320, False),   # K tail (K % 128 != 0)
     (65, 2048, 1024, False),  # mid-M plan with too few tiles -> 64x64
     (256, 2048, 8192, False), # the decoder layer's gate/up (128x128 plan)
-    (600, 1536, 704, True),   # large-M plan (256x256), ragged M and H
+    (600, 1536, 704, True),   # M >= 512 (64x64 plan: least per-CU load), ragged M and H
 ])
 def test_gemm_geglu_vs_oracle_and_unfused(M, K, H, bias):
     x8, s_a, w8, s_w, bc = _operands(M, K, H, 500 + M, bias)

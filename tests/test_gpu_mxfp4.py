@@ -96,7 +96,8 @@ def test_ada_norm_mxfp4_vs_oracle(M, D):
     (64, 2560, 2048, False),
     (256, 2560, 2048, True),    # the decoder layer's QKV (64x64 plan)
     (256, 16384, 2048, False),  # the decoder layer's gate/up (128x128 plan)
-    (600, 1024, 1024, False),   # ragged M
+    (600, 1024, 1024, False),   # ragged M (64x64 plan)
+    (256, 2048, 4096, False),   # 64x32 plan above the small-M band
 ])
 def test_gemm_mxfp4_vs_oracle(M, N, K, bias):
     a = wl.random_bf16(1400 + M, (M, K), 1.0)

@@ -90,8 +90,9 @@ def _qkv_operands(M, K, nh, kv, hd, seed, bias=False):
     (16, 2048, 8, 1, 256, 0, True),       # small M, rows past M not loaded
     (40, 1040, 4, 2, 64, 5, False),       # K tail, two KV heads
     (600, 1024, 4, 2, 128, 100, False),   # ragged M > 512 (64x64 plan)
-    (256, 512, 32, 8, 128, 7, False),     # 128x128 plan
-    (1024, 512, 32, 8, 128, 0, True),     # 256x256 plan
+    (256, 512, 32, 8, 128, 7, False),     # 64x64 plan (ties with 128x128)
+    (1024, 512, 32, 8, 128, 0, True),     # 128x128 plan (ties with 256x256)
+    (2048, 512, 32, 8, 128, 3, False),    # 256x256 plan
 ])
 def test_gemm_rope_vs_oracle_and_unfused(M, K, nh, kv, hd, P, bias):
     x8, s_a, w8, s_w, bc = _qkv_operands(M, K, nh, kv, hd, 700 + M, bias)
