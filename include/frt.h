@@ -402,7 +402,7 @@ int frt_packed_gemm_bf16in_split(void* stream, int64_t M, int64_t K,
  *
  *   n_sib, N_i [host], W_i [host], b_i [host]   as in frt_pack_weights_fp8;
  *                 every W_i 16-byte aligned.
- *   K             multiple of 512 in [512, 16384].
+ *   K             multiple of 256 in [512, 16384].
  *   W4            [sum N_i, K/2] code bytes (4-byte aligned).
  *   S4            scale bytes, [K/256][sum N_i][8] (run stride 8 * sum N_i).
  *   bias_cat      bf16 [sum N_i] or NULL.
@@ -444,7 +444,8 @@ int frt_ada_norm_quant_mxfp4(void* stream, int64_t M, int64_t D,
  *               the matrix cores' fp32 accumulation)
  *   out_s[m, n - off_s] = bf16_rne(acc[m, n] + bias_cat[n])   (or fp32)
  *
- *   M, K          rows; K a multiple of 512 in [512, 16384].
+ *   M, K          rows; K a multiple of 256 in [512, 16384] (the
+ *                 producer's D).
  *   x4, ld_x4     [M, ld_x4] code bytes (16-byte aligned, ld_x4 >= K/2, a
  *                 multiple of 16).
  *   xs, ld_xs     scale bytes [K/256][rows][8], ld_xs the run stride

@@ -470,8 +470,8 @@ int frt_pack_weights_mxfp4(void* stream, int n_sib, const int64_t* N_i, int64_t 
     return refuse(FRT_E_INVALID, "pack_mxfp4: n_sib=%d outside [1, %d]", n_sib, FRT_MAX_SPLITS);
   if (N_i == nullptr || W_i == nullptr || W4 == nullptr || S4 == nullptr)
     return refuse(FRT_E_INVALID, "pack_mxfp4: N_i, W_i, W4 and S4 are required");
-  if (K < 512 || K > 16384 || K % 512)
-    return refuse(FRT_E_INVALID, "pack_mxfp4: K=%lld must be a multiple of 512 in [512, 16384]", (long long)K);
+  if (K < 512 || K > 16384 || K % 256)
+    return refuse(FRT_E_INVALID, "pack_mxfp4: K=%lld must be a multiple of 256 in [512, 16384]", (long long)K);
   if (!aligned(W4, 4)) return refuse(FRT_E_INVALID, "pack_mxfp4: W4 must be 4-byte aligned");
   frt::PackSib sibs[FRT_MAX_SPLITS];
   int64_t rows = 0;
@@ -556,8 +556,8 @@ int frt_packed_gemm_mxfp4_split(void* stream, int64_t M, int64_t K, const uint8_
                                 int64_t N_total, const uint16_t* bias_cat, int n_split, const int64_t* split_n,
                                 void* const* out, const int64_t* ld_out, int out_dtype) {
   if (M < 0) return refuse(FRT_E_INVALID, "gemm_mxfp4: M=%lld < 0", (long long)M);
-  if (K < 512 || K > 16384 || K % 512)
-    return refuse(FRT_E_INVALID, "gemm_mxfp4: K=%lld must be a multiple of 512 in [512, 16384]", (long long)K);
+  if (K < 512 || K > 16384 || K % 256)
+    return refuse(FRT_E_INVALID, "gemm_mxfp4: K=%lld must be a multiple of 256 in [512, 16384]", (long long)K);
   if (xs == nullptr || S4 == nullptr) return refuse(FRT_E_INVALID, "gemm_mxfp4: xs and S4 are required");
   if (ld_xs < 8 * M || !aligned(xs, 4) || ld_xs % 4 || !aligned(S4, 4))
     return refuse(FRT_E_INVALID, "gemm_mxfp4: scales 4-byte aligned, ld_xs (run stride) >= 8*M and a multiple of 4");

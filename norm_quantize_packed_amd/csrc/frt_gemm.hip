@@ -504,7 +504,7 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   // (GLU: N = 2H, so this is also ceil(H / (BN / 2)) column tiles)
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
-  if constexpr (FP4) {  // K % 512 == 0 (whole stages) is part of the contract
+  if constexpr (FP4) {  // whole stages (K a multiple of 256 * NSUB) is checked by the caller
     hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, false, false, true>), dim3(tiles),
                        dim3(threads), 0, st, a);
     return hipGetLastError();
@@ -591,11 +591,19 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) { return launch_planne
 // adjacent lanes).
 hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st) { return launch_planned<true>(a, st); }
 
-// MXFP4 plans (K % 512 == 0: whole 256- or 512-element stages): the
-// small-M plan for M <= 64; above, the least per-CU load among 128x128 of
-// eight 32x64 waves (the sixteen-wave form exceeds its 128 registers with
-// the scale ring), 64x64 and 64x32. Half the bytes per row as FP8 move the
-// balance toward larger tiles only through plan_cost's row counts.
+// MXFP4 plans (K % 256 == 0: whole 256-element stages): the small-M plan
+// for M <= 64; above, the least per-CU load among 128x128 of eight 32x64
+// waves (the sixteen-wave form exceeds its 128 registers with the scale
+// ring), 64x64 and 64x32. Half the bytes per row as FP8 move the balance
+// toward larger tiles only through plan_cost's row counts. The 64x32 plans
+// stage 512 K-elements (two runs) when K allows it, else one run in a ring
+// twice as deep (the same K in flight).
+template <int AE>
+hipError_t launch_mx_narrow(const GemmArgs& a, hipStream_t st) {
+  if (a.K % 512 == 0) return launch_tiles<64, 32, 32, 32, 4, 1, 2, AE, false, false, true>(a, st);
+  return launch_tiles<64, 32, 32, 32, 7, 1, 1, AE, false, false, true>(a, st);
+}
+
 hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st) {
   if (a.M > 64) {
     const int cus = device_cus();
@@ -603,11 +611,11 @@ hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st) {
                   c32 = plan_cost(a, 64, 32, cus);
     if (c128 < c64 && c128 < c32) return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, false, false, true>(a, st);
     if (c64 < c32) return launch_tiles<64, 64, 32, 32, 4, 1, 1, 64, false, false, true>(a, st);
-    return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, false, true>(a, st);
+    return launch_mx_narrow<64>(a, st);
   }
-  if (a.M <= 16) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 16, false, false, true>(a, st);
-  if (a.M <= 32) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 32, false, false, true>(a, st);
-  return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, false, true>(a, st);
+  if (a.M <= 16) return launch_mx_narrow<16>(a, st);
+  if (a.M <= 32) return launch_mx_narrow<32>(a, st);
+  return launch_mx_narrow<64>(a, st);
 }
 
 // GEGLU plans: the same tiles with 64-column wave tiles (a gate/up pair per

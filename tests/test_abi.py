@@ -307,7 +307,7 @@ def test_mxfp4_refusals(lib):
     def pack(K=512, W=FAKE, W4=FAKE + 10 * MB, S4=FAKE + 11 * MB):
         return lib.frt_pack_weights_mxfp4(None, 1, (ctypes.c_int64 * 1)(64), K,
                                           (ctypes.c_void_p * 1)(W), None, W4, S4, None)
-    assert pack(K=768) == frt.FRT_E_INVALID            # not a multiple of 512
+    assert pack(K=640) == frt.FRT_E_INVALID            # not a multiple of 256
     assert pack(W=FAKE + 8) == frt.FRT_E_INVALID       # 16-byte weights
     assert pack(S4=FAKE + 10 * MB + 100) == frt.FRT_E_INVALID   # S4 over W4
     assert "overlap" in frt.frt_last_error()
@@ -333,6 +333,7 @@ def test_mxfp4_refusals(lib):
         a.update(kw)
         return lib.frt_packed_gemm_mxfp4_split(*a.values())
     assert gemm(K=1000) == frt.FRT_E_INVALID
+    assert gemm(K=640) == frt.FRT_E_INVALID               # K % 256
     assert gemm(ld_x4=200) == frt.FRT_E_INVALID
     assert gemm(xs=None) == frt.FRT_E_INVALID
     assert gemm(ld_xs=100) == frt.FRT_E_INVALID           # run stride < 8*M

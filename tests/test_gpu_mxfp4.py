@@ -45,7 +45,8 @@ def _oracle_pack(Ws):
 
 @pytest.mark.parametrize("shapes,K,std", [(((2048, 256, 256)), 2048, 0.02),
                                           (((96, 32)), 512, 1.0),
-                                          (((64,)), 4096, 1e-30)])
+                                          (((64,)), 4096, 1e-30),
+                                          (((40, 24)), 1280, 1.0)])   # K an odd number of 256-runs
 def test_pack_bit_exact(shapes, K, std):
     Ws = [wl.random_bf16(900 + i, (n, K), std) for i, n in enumerate(shapes)]
     bs = [wl.random_bf16(950 + i, (n,), 0.02) for i, n in enumerate(shapes)]
@@ -61,7 +62,7 @@ def _e2m1_ordinal(codes):
     return np.where(c & 8, -(c & 7), c & 7)
 
 
-@pytest.mark.parametrize("M,D", [(256, 2048), (7, 4096), (64, 512)])
+@pytest.mark.parametrize("M,D", [(256, 2048), (7, 4096), (64, 512), (33, 768)])
 def test_ada_norm_mxfp4_vs_oracle(M, D):
     rng = np.random.default_rng(M + D)
     res = wl.random_bf16(1300 + D, (M, D), 1.0)
@@ -98,6 +99,13 @@ def test_ada_norm_mxfp4_vs_oracle(M, D):
     (256, 16384, 2048, False),  # the decoder layer's gate/up (128x128 plan)
     (600, 1024, 1024, False),   # ragged M (64x64 plan)
     (256, 2048, 4096, False),   # 64x32 plan above the small-M band
+    # K an odd number of 256-element runs: the 64x32 plans take one run per
+    # stage in a deeper ring
+    (1, 1024, 768, True),
+    (24, 640, 1280, False),
+    (40, 512, 1280, False),
+    (200, 512, 768, False),
+    (256, 2560, 1280, False),   # 64x64 plan
 ])
 def test_gemm_mxfp4_vs_oracle(M, N, K, bias):
     a = wl.random_bf16(1400 + M, (M, K), 1.0)
