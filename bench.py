@@ -37,6 +37,14 @@ producers emit OCP MX FP4 (dynamic per-32 block scales) and the norm-fed
 GEMMs take MXFP4 weights packed at bind; metric and roofline are the same,
 with the FP4 matrix-core peak.
 
+``--tp T`` (workloads 3 and 5) measures one GPU's share of a
+tensor-parallel job over T GPUs: the producer over every row (its output is
+replicated across the ranks) and the packed GEMM on rank 0's slice of every
+sibling (N_i / T output columns, whole heads). The joint weight scale of a
+real T-way job is the all-reduced maximum over the ranks, taken once at
+bind; the slice here is packed with its own scale, which changes no
+kernel's work.
+
 ``--oproj`` (workload 2) adds the O projection of a seeded attention output:
 the static FP8 quantiser and the packed GEMM. With ``--rope --oproj --ffn``
 a step is the whole decoder layer around the attention core.
@@ -85,6 +93,8 @@ def parse():
     p.add_argument("--rope", action="store_true",
                    help="workload 2: the QKV GEMM writes RoPE'd q and the KV "
                         "caches through its epilogue")
+    p.add_argument("--tp", type=int, default=1,
+                   help="workloads 3, 5: time one rank's share of a T-way column-parallel GEMM")
     p.add_argument("--kernel-reps", type=int, default=20)
     p.add_argument("--hbm-calibration", action="store_true",
                    help="time a plain device copy of known size (HBM ceiling, "
@@ -119,7 +129,7 @@ class Step:
     """Device buffers of one rotation set and the launches of one step."""
 
 
-def build_sets(wid, rows, frt, torch, rope=False, mx=False):
+def build_sets(wid, rows, frt, torch, rope=False, mx=False, tp=1):
     import workloads as wl
     w = wl.WORKLOADS[wid]
     inp = wl.producer_inputs(wid, rows=rows)
@@ -177,6 +187,8 @@ def build_sets(wid, rows, frt, torch, rope=False, mx=False):
     pack_ms = []
     for site in range(len(w.gemms)):
         ww = wl.weights(wid, site)
+        if tp > 1:
+            ww = wl.tp_shard(ww, tp, 0, wl.TP_UNIT[wid])
         Ws = [bf16_dev(x) for x in ww["W"]]
         if rope and site == 0:
             # q and k rows pair-interleaved before packing (bind time)
@@ -751,7 +763,11 @@ def main():
     if a.mxfp4 and (wl.WORKLOADS[a.workload].form != "adarms" or a.ffn or a.rope or a.oproj):
         raise SystemExit("--mxfp4: the MXFP4 band covers the AdaRMS workloads' producer + packed "
                          "GEMM step (1, 2, 4), alone")
-    w, dev, act, packs, pack_ms = build_sets(a.workload, rows, frt, torch, rope=a.rope, mx=a.mxfp4)
+    if a.tp < 1 or (a.tp > 1 and (a.workload not in wl.TP_UNIT or a.ffn or a.rope or a.oproj or a.mxfp4)):
+        raise SystemExit(f"--tp: one rank's share of the packed GEMM, for workloads {sorted(wl.TP_UNIT)} "
+                         "alone")
+    w, dev, act, packs, pack_ms = build_sets(a.workload, rows, frt, torch, rope=a.rope, mx=a.mxfp4,
+                                             tp=a.tp)
     ffn = None
     if a.ffn:
         if a.workload not in wl.FFN_HIDDEN:
@@ -882,9 +898,10 @@ def main():
         "config": {"workload": w.name + ("+mxfp4" if a.mxfp4 else "")
                                + ("+qkv_rope_kvcache" if rp is not None else "")
                                + ("+o_proj" if op is not None else "")
-                               + ("+ffn_geglu_down" if ffn is not None else ""),
+                               + ("+ffn_geglu_down" if ffn is not None else "")
+                               + (f"+tp{a.tp}_rank0" if a.tp > 1 else ""),
                    "rows": rows, "D": w.D,
-                   "gemms": [list(g) for g in w.gemms], "bias": w.bias,
+                   "gemms": [list(p["splits"]) for p in packs], "bias": w.bias,
                    "rotation_sets": nset, "rotation_mib": round(nset * per_set / 2**20, 1),
                    "step_gemm_gflop": round(gemm_flops / 1e9, 3)},
         "norm_gbps": round(norm_bytes / (norm_us * 1e3), 1) if norm_us else None,
@@ -899,7 +916,10 @@ def main():
         res["config"]["ffn"] = {"H": ffn["H"], "down": [w.D, ffn["H"]]}
     if rp is not None:
         res["config"]["rope"] = {k: rp[k] for k in ("nh", "kv", "hd", "P", "T")}
-    if not a.no_cpu_baseline and ffn is None and rp is None and op is None and not a.mxfp4:
+    if a.tp > 1:
+        res["config"]["tp"] = {"ranks": a.tp, "rank": 0, "full_gemms": [list(g) for g in w.gemms]}
+    if (not a.no_cpu_baseline and ffn is None and rp is None and op is None and not a.mxfp4
+            and a.tp == 1):
         res["cpu_baseline"] = cpu_baseline(w, rows)
     print(json.dumps(res), flush=True)
 

@@ -157,6 +157,35 @@ def test_gemm_full_size_sampled(cid):
     assert_gemm_bf16(full[rows, cols], ref, f"workload {cid} sampled")
 
 
+@pytest.mark.parametrize("cid,tp", [(3, 8), (5, 8)])
+def test_gemm_tensor_parallel_shard_sampled(cid, tp):
+    """One GPU's share of a column-parallel packed GEMM at its real shape
+    (rank 0 of 8: 8192 x 3*384 x 3072 with bias, from the workload's own
+    weights; 2048 x 2*2048 x 16384 on random codes of that shape): every
+    sibling keeps its first N_i / tp rows, and sampled outputs are checked
+    one by one against the oracle."""
+    wk = wl.WORKLOADS[cid]
+    M, K = wk.rows, wk.D
+    if cid == 5:
+        splits = [n // tp for n in wk.gemms[0]]
+        w8 = wl.random_codes(4200 + tp, (sum(splits), K))
+        s_w, bias = np.float32(0.004), None
+    else:
+        ws = wl.tp_shard(wl.weights(cid, 0), tp, 0, wl.TP_UNIT[cid])
+        w8, s_w, bias, splits = pack.pack_weights(ws["W"], ws["b"])
+    x8 = wl.random_codes(4300 + cid, (M, K))
+    s_a = np.float32(0.01)
+    outs = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
+    full = np.concatenate(outs, axis=1)
+    N = w8.shape[0]
+    rng = np.random.default_rng(cid + tp)
+    rows = np.concatenate([rng.integers(0, M, 2000), [M - 1, 0]])
+    cols = np.concatenate([rng.integers(0, N, 2000), [N - 1, 0]])
+    acc = gemm.gemm_exact_at(x8, w8, rows, cols)
+    ref = gemm.epilogue(acc, s_a, s_w, None if bias is None else bias[cols])
+    assert_gemm_bf16(full[rows, cols], ref, f"workload {cid} rank 0 of {tp}")
+
+
 def test_gemm_edges_k_tail_strides_unaligned_splits():
     rng = np.random.default_rng(9)
     for (M, K, splits) in [(33, 528, (100, 28, 200)), (257, 1040, (96, 160)),

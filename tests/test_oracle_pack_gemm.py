@@ -14,6 +14,7 @@ import pytest
 import torch
 
 from oracle import codecs, gemm, pack
+import workloads as wl
 from workloads import random_codes, to_bf16_bits
 
 
@@ -173,3 +174,26 @@ def test_epilogue_alpha_and_bias():
     out = gemm.epilogue(acc, np.float32(3.0), np.float32(0.5), b)
     assert np.array_equal(out, [[2.0, -2.75]])
     assert gemm.to_bf16_ref(out)[0, 0] == 0x4000
+
+
+def test_column_parallel_shards_keep_the_joint_scale():
+    """Column-parallel sharding of a packed GEMM (each rank keeps N_i / tp
+    rows of every sibling): the maximum of the ranks' own scales, which a
+    4-byte all-reduce(MAX) at bind gives, is the single-GPU joint scale
+    (amax / 448 and the 1e-8 floor are monotone in amax), and a rank whose
+    slice holds the global maximum packs exactly its rows of the
+    single-GPU pack."""
+    ws = wl.weights(1, 0)
+    tp = 2
+    w8, s, _, splits = pack.pack_weights(ws["W"], ws["b"])
+    shards = [wl.tp_shard(ws, tp, r, 64) for r in range(tp)]
+    local = [pack.pack_weights(sh["W"], sh["b"]) for sh in shards]
+    assert [list(sh["splits"]) for sh in shards] == [[n // tp for n in splits]] * tp
+    assert max(lp[1] for lp in local) == s
+    r = int(np.argmax([lp[1] for lp in local]))
+    offs = np.cumsum([0] + list(splits))
+    rows = np.concatenate([np.arange(o + r * n // tp, o + (r + 1) * n // tp)
+                           for o, n in zip(offs[:-1], splits)])
+    assert np.array_equal(local[r][0], w8[rows])
+    with pytest.raises(ValueError):
+        wl.tp_shard(ws, 3, 0, 64)

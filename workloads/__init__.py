@@ -223,6 +223,28 @@ def down_weights(cid: int) -> np.ndarray:
 # 8 query heads and one KV head of 256), and the KV-cache geometry of the
 # suffix pass: P prefix rows already cached, the 256 suffix tokens written
 # behind them (T = P + S rows).
+# Tensor parallelism over the GEMM's output columns: the column group a
+# rank's share of every sibling must keep whole (one 128-wide attention head
+# of the QKV projection; a 128-column group of the FFN hidden size).
+TP_UNIT: Dict[int, int] = {3: 128, 5: 128}
+
+
+def tp_shard(ws: dict, tp: int, rank: int = 0, unit: int = 128) -> dict:
+    """Rank ``rank``'s share of ``weights()`` when the packed GEMM is split
+    over ``tp`` GPUs by output columns: rows ``[rank*n/tp, (rank+1)*n/tp)``
+    of every sibling ``W_i`` (``[n, K]``) and of its bias. Every ``n`` must
+    be a multiple of ``tp * unit``."""
+    Ws, bs, widths = [], [], []
+    for W, b, n in zip(ws["W"], ws["b"], ws["splits"]):
+        if n % (tp * unit):
+            raise ValueError(f"sibling width {n} does not split into {tp} groups of {unit}-column units")
+        m = n // tp
+        Ws.append(np.ascontiguousarray(W[rank * m:(rank + 1) * m]))
+        bs.append(None if b is None else np.ascontiguousarray(b[rank * m:(rank + 1) * m]))
+        widths.append(m)
+    return {"W": Ws, "b": bs, "splits": tuple(widths)}
+
+
 QKV_HEADS: Dict[int, Tuple[int, int, int]] = {2: (8, 1, 256)}
 ROPE_PREFIX: Dict[int, int] = {2: 768}
 
