@@ -12,7 +12,7 @@ import torch
 import norm_quantize_packed_amd as frt
 import workloads as wl
 from oracle import gemm, pack, producers
-from gpu_util import assert_gemm_f32, dev_bf16, dev_f32, host_u8, scalar
+from gpu_util import assert_gemm_f32, dev_bf16, dev_f32, scalar
 
 pytestmark = pytest.mark.gpu
 EPS = wl.EPS

@@ -9,7 +9,6 @@ and to torch's CPU float8_e4m3fn cast.
 import os
 
 import numpy as np
-import pytest
 import torch
 
 from oracle import codecs
