@@ -468,6 +468,36 @@ int frt_packed_gemm_mxfp4_split(void* stream, int64_t M, int64_t K,
                                 int out_dtype);
 
 /*
+ * frt_packed_gemm_mxfp4_geglu_quant — the merged gate/up GEMM on MXFP4
+ * operands with the GEGLU quantiser as its epilogue: the FFN tail of the
+ * 4-bit band (fp8_chain.py `BANDS`: the norm-fed gate/up projection in the
+ * block-scaled 4-bit format, the down projection kept in static FP8, so the
+ * GEGLU output is quantised to e4m3fn for it). For m < M, j < H, with acc
+ * as in frt_packed_gemm_mxfp4_split over W4 rows j (gate) and H + j (up):
+ *   g = bf16_rne(acc[m, j] + bias_cat[j]),  u = bf16_rne(acc[m, H + j] + bias_cat[H + j])
+ *   out_fp8[m, j] = e4m3_rne(clamp(fl32(gelu_tanh(g) * u / out_scale), +-448))
+ * i.e. exactly frt_packed_gemm_mxfp4_split (bf16 out) followed by
+ * frt_geglu_quant_fp8 on its output.
+ *
+ *   M, K, x4, ld_x4, xs, ld_xs   as in frt_packed_gemm_mxfp4_split.
+ *   W4, S4        [2H, K/2] codes and [K/256][2H][8] scales: the H gate
+ *                 rows, then the H up rows (frt_pack_weights_mxfp4 of the
+ *                 siblings {gate, up}).
+ *   H             width of each half (1 <= H, 2H <= 2^24).
+ *   bias_cat      bf16 [2H] or NULL.
+ *   out_scale     fp32 [1] (> 0): the down projection's static input scale.
+ *   out_fp8       e4m3fn [M, ld_out], ld_out >= H; must not overlap an
+ *                 input.
+ */
+int frt_packed_gemm_mxfp4_geglu_quant(void* stream, int64_t M, int64_t K,
+                                      const uint8_t* x4, int64_t ld_x4,
+                                      const uint8_t* xs, int64_t ld_xs,
+                                      const uint8_t* W4, const uint8_t* S4,
+                                      int64_t H, const uint16_t* bias_cat,
+                                      const float* out_scale, uint8_t* out_fp8,
+                                      int64_t ld_out);
+
+/*
  * frt_interleave_pairs_bf16 — the pack-time permutation of q or k
  * projection rows that turns the host's rotate-half rotary pairs
  * (i, i + hd/2) into adjacent pairs (2i, 2i + 1).

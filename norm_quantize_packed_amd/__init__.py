@@ -28,7 +28,7 @@ __all__ = [
     "frt_packed_gemm_fp8_geglu_quant", "frt_interleave_pairs_bf16",
     "frt_quantize_fp8_static", "frt_packed_gemm_bf16in_split",
     "frt_pack_weights_mxfp4", "frt_ada_norm_quant_mxfp4",
-    "frt_packed_gemm_mxfp4_split",
+    "frt_packed_gemm_mxfp4_split", "frt_packed_gemm_mxfp4_geglu_quant",
     "frt_qkv_split_rope_kvcache", "frt_packed_gemm_fp8_qkv_rope",
     "frt_last_error", "frt_abi_version",
     "FRT_OK", "FRT_E_INVALID", "FRT_E_UNSUPPORTED", "FRT_E_HIP",
@@ -78,6 +78,8 @@ _SIGNATURES = {
     "frt_packed_gemm_mxfp4_split": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _i32,
         ctypes.POINTER(_i64), ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32]),
+    "frt_packed_gemm_mxfp4_geglu_quant": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _p, _p, _i64]),
     "frt_packed_gemm_bf16in_split": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i32,
         ctypes.POINTER(_i64), ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32,
@@ -540,3 +542,22 @@ def frt_packed_gemm_mxfp4_split(x4, xs, W4, S4, outs: Sequence,
         _ptr(S4), int(W4.shape[0]), _ptr(bias_cat), n,
         (_i64 * n)(*[int(v) for v in split_n]), (_p * n)(*[_ptr(o) for o in outs]),
         (_i64 * n)(*[_ld(o) for o in outs]), out_dtype))
+
+
+def frt_packed_gemm_mxfp4_geglu_quant(x4, xs, W4, S4, out_scale, out_fp8,
+                                      bias_cat=None, *, M: Optional[int] = None,
+                                      stream=None) -> None:
+    """Merged gate/up GEMM on MXFP4 operands (``W4`` = ``[2H, K/2]``, gate
+    rows first, ``S4`` its ``[K/256, 2H, 8]`` scales) with the GEGLU
+    quantiser as epilogue; ``out_fp8`` is ``[>= M, >= H]`` e4m3fn codes."""
+    for t, nme in ((x4, "x4"), (xs, "xs"), (W4, "W4"), (S4, "S4"), (out_fp8, "out_fp8")):
+        _u8_like(t, nme)
+    _f32_like(out_scale, "out_scale")
+    _bf16_like(bias_cat, "bias_cat")
+    if W4.shape[0] % 2:
+        raise ValueError("frt: W4 must hold 2H rows (gate, then up)")
+    Mv = x4.shape[0] if M is None else int(M)
+    _check(load_library().frt_packed_gemm_mxfp4_geglu_quant(
+        _stream(stream), Mv, int(W4.shape[1]) * 2, _ptr(x4), _ld(x4), _ptr(xs), _ld(xs),
+        _ptr(W4), _ptr(S4), int(W4.shape[0] // 2), _ptr(bias_cat), _ptr(out_scale),
+        _ptr(out_fp8), _ld(out_fp8)))

@@ -584,6 +584,52 @@ int frt_packed_gemm_mxfp4_split(void* stream, int64_t M, int64_t K, const uint8_
   return hip_status(frt::launch_gemm_mxfp4(a, (hipStream_t)stream), "gemm_mxfp4 launch");
 }
 
+int frt_packed_gemm_mxfp4_geglu_quant(void* stream, int64_t M, int64_t K, const uint8_t* x4, int64_t ld_x4,
+                                      const uint8_t* xs, int64_t ld_xs, const uint8_t* W4, const uint8_t* S4,
+                                      int64_t H, const uint16_t* bias_cat, const float* out_scale, uint8_t* out_fp8,
+                                      int64_t ld_out) {
+  if (M < 0) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: M=%lld < 0", (long long)M);
+  if (K < 512 || K > 16384 || K % 256)
+    return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: K=%lld must be a multiple of 256 in [512, 16384]", (long long)K);
+  if (H < 1) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: H < 1");
+  if (M > (1 << 24) || 2 * H > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "gemm_mxfp4_geglu: M or 2H too large");
+  if (x4 == nullptr || xs == nullptr || W4 == nullptr || S4 == nullptr || out_scale == nullptr || out_fp8 == nullptr)
+    return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: x4, xs, W4, S4, out_scale and out_fp8 are required");
+  const int64_t kb = K / 2;
+  if (ld_x4 < kb || ld_x4 % 16) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: ld_x4 must be >= K/2 and a multiple of 16");
+  if (!aligned(x4, 16) || !aligned(W4, 16))
+    return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: x4 and W4 must be 16-byte aligned");
+  if (ld_xs < 8 * M || !aligned(xs, 4) || ld_xs % 4 || !aligned(S4, 4))
+    return refuse(FRT_E_INVALID,
+                  "gemm_mxfp4_geglu: scales 4-byte aligned, ld_xs (run stride) >= 8*M and a multiple of 4");
+  if ((M - 1) * ld_x4 + kb > (int64_t)0x7fffffff || 2 * H * kb > (int64_t)0x7fffffff)
+    return refuse(FRT_E_UNSUPPORTED, "gemm_mxfp4_geglu: operand larger than 2 GiB");
+  if (ld_out < H) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: ld_out < H");
+  if (M == 0) return ok();
+  const Range o = span(out_fp8, M, H, ld_out, 1);
+  const Range in[] = {span(x4, M, kb, ld_x4, 1),           span(W4, 2 * H, kb, kb, 1),
+                      span(bias_cat, 1, 2 * H, 2 * H, 2),  span(out_scale, 1, 1, 1, 4),
+                      span(xs, K / 256, 8 * M, ld_xs, 1),  span(S4, K / 256, 16 * H, 16 * H, 1)};
+  for (int i = 0; i < 6; ++i)
+    if (overlap(o, in[i])) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: out_fp8 overlaps input %d", i);
+  frt::GemmArgs a{};
+  a.x = x4;
+  a.ld_x = ld_x4;
+  a.w = W4;
+  a.bias = bias_cat;
+  a.M = (int)M;
+  a.N = (int)(2 * H);
+  a.K = (int)K;
+  a.H = (int)H;
+  a.q8 = out_fp8;
+  a.ld_q8 = ld_out;
+  a.q_scale = out_scale;
+  a.sa = xs;
+  a.ld_sa = ld_xs;
+  a.sb = S4;
+  return hip_status(frt::launch_gemm_mxfp4_geglu(a, (hipStream_t)stream), "gemm_mxfp4_geglu launch");
+}
+
 int frt_interleave_pairs_bf16(void* stream, int nheads, int hd, int64_t K, const uint16_t* src, uint16_t* dst) {
   if (nheads < 1 || hd < 2 || hd % 2) return refuse(FRT_E_INVALID, "interleave: nheads >= 1 and an even hd >= 2");
   if (K < 1) return refuse(FRT_E_INVALID, "interleave: K < 1");

@@ -107,7 +107,8 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // 2q and up column c in 2q + 1 of the same lane, and the epilogue writes
 // e4m3(gelu_tanh(bf16(gate)) * bf16(up) / q_scale) for H columns. Gate rows
 // past H (a ragged last tile) read up rows, whose results are never stored;
-// up rows past 2H read zeros.
+// up rows past 2H read zeros. With FP4 the same rows are loaded (K/2 bytes
+// a row) and each lane takes the block scales of the row it multiplies.
 //
 // ROPE: the QKV split + RoPE + KV-cache form. Columns [0, nh hd) are q,
 // the next kv hd are k, the last kv hd are v, with the q and k rows
@@ -144,7 +145,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   constexpr int SUBB = ROWS * 128;     // one 128-deep sub-buffer
   constexpr int STAGE = NSUB * SUBB;   // one stage = NSUB sub-buffers
   constexpr int KST = 128 * NSUB;      // K bytes per stage
-  static_assert(!FP4 || (!KTAIL && !GLU && !ROPE), "MXFP4 form: whole stages, split epilogue");
+  static_assert(!FP4 || (!KTAIL && !ROPE), "MXFP4 form: whole stages, split or GEGLU epilogue");
   constexpr int SCL = FP4 ? MI + NJ : 0;  // scale loads per sub-buffer
   static_assert(NS >= 2 && NSUB * (LPW + SCL) * (NS - 2) <= 63, "ring depth vs vmcnt range");
   static_assert(NS * STAGE <= 160 * 1024, "ring exceeds LDS");
@@ -178,7 +179,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   static_assert(NW % 2 == 0, "row swizzle assumes an even wave count");
   const int cch = (lane & 7) ^ (((wave & 1) << 2) | (lrow >> 1));
   const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
-  const uint32_t offB = GLU ? (uint32_t)(lrow * a.K + cch * 16)
+  const uint32_t offB = GLU ? (uint32_t)(lrow * Kb + cch * 16)
                             : (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * Kb) + cch * 16;
   const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
   const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)Kb;
@@ -194,7 +195,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 #pragma unroll
     for (int i = 0; i < MI; ++i) sa_row[i] = a.sa + (int64_t)min(m0 + wm0 + i * 32 + (lane & 31), a.M - 1) * 8 + h4;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) sb_row[j] = a.sb + (int64_t)min(n0 + wn0 + j * 32 + (lane & 31), a.N - 1) * 8 + h4;
+    for (int j = 0; j < NJ; ++j) {
+      // tile-local B row t; under GLU the gate or up row it was loaded from
+      const int t = wn0 + j * 32 + (lane & 31);
+      const int row = GLU ? ((t >> 5) & 1) * a.H + n0 + (t >> 6) * 32 + (t & 31) : n0 + t;
+      sb_row[j] = a.sb + (int64_t)min(row, a.N - 1) * 8 + h4;
+    }
   }
   // slot SL (= step mod NS) is a compile-time constant in every use, so all
   // LDS addresses are one lane base plus immediates
@@ -217,7 +223,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
           // (ub / 4) % 2, 32-column pair ub / 8, 8-row group ub % 4
           const int ub = wave + (j - LPA) * NW;
           const int row = ((ub >> 2) & 1) * a.H + n0 + (ub >> 3) * 32 + (ub & 3) * 8;
-          o = offB + (uint32_t)row * (uint32_t)a.K + k0;
+          o = offB + (uint32_t)row * (uint32_t)Kb + k0;
         } else {
           o = offB + (j - LPA) * stepB + k0;
         }
@@ -505,7 +511,7 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
   if constexpr (FP4) {  // whole stages (K a multiple of 256 * NSUB) is checked by the caller
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, false, false, true>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, false, true>), dim3(tiles),
                        dim3(threads), 0, st, a);
     return hipGetLastError();
   }
@@ -616,6 +622,20 @@ hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st) {
   if (a.M <= 16) return launch_mx_narrow<16>(a, st);
   if (a.M <= 32) return launch_mx_narrow<32>(a, st);
   return launch_mx_narrow<64>(a, st);
+}
+
+// MXFP4 GEGLU plans: the MXFP4 128x128 plan (its waves are already 32x64)
+// where it has the least per-CU load, else 64x64 of two 32x64 waves; like
+// the split plans they alternate two accumulator sets over the 64-deep
+// steps, so the fused codes equal the split GEMM's bf16 output quantised by
+// the standalone GEGLU kernel.
+hipError_t launch_gemm_mxfp4_geglu(const GemmArgs& a, hipStream_t st) {
+  if (a.M > 64) {
+    const int cus = device_cus();
+    if (plan_cost(a, 128, 128, cus) < plan_cost(a, 64, 64, cus))
+      return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, true, false, true>(a, st);
+  }
+  return launch_tiles<64, 64, 32, 64, 4, 1, 1, 64, true, false, true>(a, st);
 }
 
 // GEGLU plans: the same tiles with 64-column wave tiles (a gate/up pair per

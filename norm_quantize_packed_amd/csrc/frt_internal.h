@@ -110,6 +110,7 @@ hipError_t launch_quant(const GegluArgs& a, int vec, hipStream_t st);
 
 hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_mxfp4_geglu(const GemmArgs& a, hipStream_t st);
 
 struct RopeArgs {
   const uint16_t* qkv; int64_t ld_qkv;

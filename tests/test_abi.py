@@ -339,3 +339,18 @@ def test_mxfp4_refusals(lib):
     assert gemm(ld_xs=100) == frt.FRT_E_INVALID           # run stride < 8*M
     assert gemm(out=(ctypes.c_void_p * 1)(FAKE + 3 * MB)) == frt.FRT_E_INVALID   # over S4
     assert gemm(M=0) == frt.FRT_OK
+
+    def geglu(K=512, **kw):
+        a = dict(stream=None, M=16, K=K, x4=FAKE, ld_x4=K // 2, xs=FAKE + MB, ld_xs=8 * 16,
+                 W4=FAKE + 2 * MB, S4=FAKE + 3 * MB, H=384, bias=None, out_scale=FAKE + 4 * MB,
+                 out=FAKE + 40 * MB, ld_out=384)
+        a.update(kw)
+        return lib.frt_packed_gemm_mxfp4_geglu_quant(*a.values())
+    assert geglu(K=640) == frt.FRT_E_INVALID              # K % 256
+    assert geglu(H=0) == frt.FRT_E_INVALID
+    assert geglu(xs=None) == frt.FRT_E_INVALID
+    assert geglu(out_scale=None) == frt.FRT_E_INVALID
+    assert geglu(ld_xs=100) == frt.FRT_E_INVALID          # run stride < 8*M
+    assert geglu(ld_out=300) == frt.FRT_E_INVALID         # ld_out < H
+    assert geglu(out=FAKE + 3 * MB) == frt.FRT_E_INVALID  # over S4
+    assert geglu(M=0) == frt.FRT_OK

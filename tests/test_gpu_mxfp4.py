@@ -14,9 +14,9 @@ import torch
 
 import norm_quantize_packed_amd as frt
 import workloads as wl
-from oracle import codecs, mxfp4, producers
-from gpu_util import (Guarded, assert_gemm_bf16, assert_gemm_f32, dev_bf16, dev_u8,
-                      host_bf16, host_u8)
+from oracle import codecs, ffn, mxfp4, producers
+from gpu_util import (Guarded, assert_codes_close, assert_gemm_bf16, assert_gemm_f32, dev_bf16,
+                      dev_u8, host_bf16, host_u8, scalar)
 
 pytestmark = pytest.mark.gpu
 
@@ -131,3 +131,47 @@ def test_gemm_mxfp4_vs_oracle(M, N, K, bias):
     assert_gemm_f32(got32, ref, f"mxfp4 {M}x{N}x{K} fp32")
     got16 = np.concatenate([host_bf16(o) for o in outs16], 1)
     assert_gemm_bf16(got16, ref, f"mxfp4 {M}x{N}x{K} bf16")
+
+
+@pytest.mark.parametrize("M,K,H,bias", [
+    (256, 2048, 8192, False),   # the decoder layer's gate/up (128x128 plan)
+    (600, 512, 4000, True),     # 128x128 plan, ragged M and H (last tile half gate columns)
+    (600, 1024, 704, False),    # 64x64 plan, ragged M and H
+    (40, 1280, 320, True),      # small M; K an odd number of 256-element runs
+    (1, 512, 64, False),        # one row, one tile
+])
+def test_gemm_mxfp4_geglu_vs_unfused_and_oracle(M, K, H, bias):
+    """The MXFP4 gate/up GEMM with the GEGLU quantiser as its epilogue: its
+    codes equal the split MXFP4 GEMM's bf16 output quantised by the
+    standalone GEGLU kernel bit for bit; that bf16 output is within the GEMM
+    tolerance of the exact oracle GEMM, and the codes match the oracle's
+    GEGLU quantiser on it."""
+    a = wl.random_bf16(1500 + M, (M, K), 1.0)
+    ac, as_ = mxfp4.quantize_mxfp4(codecs.bf16_to_f32(a))
+    Wg = wl.random_bf16(1501 + H, (H, K), 0.02)
+    Wu = wl.random_bf16(1502 + H, (H, K), 0.02)
+    bs = [wl.random_bf16(1503, (H,), 0.02), wl.random_bf16(1504, (H,), 0.02)] if bias else None
+    w4, ws4, bc = _gpu_pack([Wg, Wu], bs)
+    x4, xs = dev_u8(mxfp4.pack_nibbles(ac)), dev_u8(mxfp4.scales_to_gemm_order(as_))
+    dw4, dws4 = dev_u8(w4), dev_u8(ws4)
+    db = None if bc is None else dev_bf16(bc)
+    # unfused: bf16 gate|up, then the standalone quantiser
+    gu = torch.empty((M, 2 * H), dtype=torch.bfloat16, device="cuda")
+    frt.frt_packed_gemm_mxfp4_split(x4, xs, dw4, dws4, [gu], [2 * H], db)
+    torch.cuda.synchronize()
+    gu_bits = host_bf16(gu)
+    s_o = producers.calibrate_act_scale(ffn.geglu(gu_bits, H))
+    unf = torch.empty((M, H), dtype=torch.uint8, device="cuda")
+    frt.frt_geglu_quant_fp8(gu, H, scalar(s_o), out_fp8=unf)
+    # fused, into a guarded buffer with a wider row stride
+    out = Guarded(M, H, torch.uint8, ld=H + 16)
+    frt.frt_packed_gemm_mxfp4_geglu_quant(x4, xs, dw4, dws4, scalar(s_o), out.view, db)
+    torch.cuda.synchronize()
+    out.check_guards()
+    got = host_u8(out.view)
+    assert np.array_equal(got, host_u8(unf)), "fused codes differ from the unfused chain"
+    ref = mxfp4.gemm_mxfp4(ac, as_, mxfp4.unpack_nibbles(w4), mxfp4.scales_from_gemm_order(ws4))
+    if bc is not None:
+        ref = ref + codecs.bf16_to_f32(bc).astype(np.float64)[None, :]
+    assert_gemm_bf16(gu_bits, ref, f"mxfp4 gate|up {M}x{2 * H}x{K}")
+    assert_codes_close(got, ffn.geglu_quant_fp8(gu_bits, H, s_o)["codes"], what=f"mxfp4 geglu {M}x{H}")
