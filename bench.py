@@ -35,7 +35,9 @@ RoPE + cache kernel) is timed beside it.
 ``--mxfp4`` (AdaRMS workloads 1, 2, 4) runs the MXFP4 band instead: the
 producers emit OCP MX FP4 (dynamic per-32 block scales) and the norm-fed
 GEMMs take MXFP4 weights packed at bind; metric and roofline are the same,
-with the FP4 matrix-core peak.
+with the FP4 matrix-core peak. With ``--ffn`` (workload 2) the MXFP4
+gate/up GEMM carries the GEGLU quantiser and the down projection stays in
+static FP8.
 
 ``--tp T`` (workloads 3 and 5) measures one GPU's share of a
 tensor-parallel job over T GPUs: the producer over every row (its output is
@@ -222,10 +224,11 @@ def build_sets(wid, rows, frt, torch, rope=False, mx=False, tp=1):
     return w, dev, act, packs, pack_ms
 
 
-def build_ffn(w, rows, act, packs, frt, torch):
+def build_ffn(w, rows, act, packs, frt, torch, mx=False):
     """The FFN tail's bind: pack the down projection and calibrate the
     GEGLU output scale on the calibration batch (its producer codes through
-    the bf16 gate/up GEMM and the standalone quantiser's amax)."""
+    the bf16 gate/up GEMM and the standalone quantiser's amax; with `mx` the
+    MXFP4 producers and gate/up GEMM)."""
     import workloads as wl
     H = wl.FFN_HIDDEN[w.cid]
     Wd = bf16_dev(wl.down_weights(w.cid))
@@ -235,7 +238,21 @@ def build_ffn(w, rows, act, packs, frt, torch):
     del Wd
     cal = wl.producer_inputs(w.cid, calib=True, rows=rows)
     x8 = torch.empty(rows, w.D, dtype=torch.uint8, device="cuda")
-    if w.form == "adarms":
+    H2 = 2 * H
+    gu = torch.empty(rows, H2, dtype=torch.bfloat16, device="cuda")
+    p = packs[-1]
+    if mx:
+        D = w.D
+        x4 = torch.empty(rows, D // 2, dtype=torch.uint8, device="cuda")
+        xs = torch.empty(D // 256, rows, 8, dtype=torch.uint8, device="cuda")
+        rout = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
+        cm = bf16_dev(cal["mod"])
+        frt.frt_ada_norm_quant_mxfp4(bf16_dev(cal["residual"]), cm, x4, xs, x=bf16_dev(cal["x"]),
+                                     gate=bf16_dev(cal["gate"]), eps=wl.EPS, residual_out=rout)
+        frt.frt_ada_norm_quant_mxfp4(rout, bf16_dev(cal["mod2"]), x4, xs, x=bf16_dev(cal["x2"]),
+                                     gate=cm[0, 2 * D:3 * D], eps=wl.EPS)
+        frt.frt_packed_gemm_mxfp4_split(x4, xs, p["W8"], p["ws"], [gu], [H2])
+    elif w.form == "adarms":
         D = w.D
         rout = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
         cm = bf16_dev(cal["mod"])
@@ -248,9 +265,8 @@ def build_ffn(w, rows, act, packs, frt, torch):
             bf16_dev(cal["x"]), bf16_dev(cal["temb"].reshape(rows, -1)),
             torch.from_numpy(cal["table"]).cuda(), act[0], cal["shift_idx"],
             cal["scale_idx"], eps=wl.EPS, out_fp8=x8)
-    p = packs[-1]
-    gu = torch.empty(rows, 2 * H, dtype=torch.bfloat16, device="cuda")
-    frt.frt_packed_gemm_fp8_split(x8, p["W8"], act[-1], p["ws"], [gu], [2 * H])
+    if not mx:
+        frt.frt_packed_gemm_fp8_split(x8, p["W8"], act[-1], p["ws"], [gu], [H2])
     amax = torch.zeros(1, dtype=torch.float32, device="cuda")
     frt.frt_geglu_quant_fp8(gu, H, None, amax_out=amax)
     torch.cuda.synchronize()
@@ -342,7 +358,9 @@ def make_outputs(w, rows, packs, torch, ffn=None):
 
 def step_launches_mx(w, s, outs, rows, frt, eps):
     """The MXFP4 band's step: the AdaRMS producers emit MXFP4, the packed
-    GEMMs take MXFP4 operands."""
+    GEMMs take MXFP4 operands. With the FFN tail the gate/up GEMM carries
+    the GEGLU quantiser (FP8 codes) and the static-FP8 down projection
+    follows."""
     d = s["dev"]
     D = w.D
     o4 = outs["x4"]
@@ -360,6 +378,13 @@ def step_launches_mx(w, s, outs, rows, frt, eps):
         L.append(("gemm2_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
             o4[1][0], o4[1][1], p1["W8"], p1["ws"], outs["gemm"][1], p1["splits"],
             bias_cat=p1["bias"])))
+        f = s.get("ffn")
+        if f is not None:
+            L[-1] = ("gemm2_mx_geglu", lambda: frt.frt_packed_gemm_mxfp4_geglu_quant(
+                o4[1][0], o4[1][1], p1["W8"], p1["ws"], f["scale"], outs["hid8"],
+                bias_cat=p1["bias"]))
+            L.append(("gemm_down", lambda: frt.frt_packed_gemm_fp8_split(
+                outs["hid8"], f["W8"], f["scale"], f["ws"], [outs["dn"]], [w.D])))
     return L
 
 
@@ -413,20 +438,26 @@ def step_launches(w, s, act, outs, rows, frt, eps):
     return L
 
 
-def unfused_launches(w, s, act, outs, frt):
+def unfused_launches(w, s, act, outs, frt, mx=False):
     """The unfused forms of the fused launches (timed for comparison only):
-    the bf16 gate|up GEMM and the standalone GEGLU quantiser; the bf16 QKV
-    GEMM and the standalone split + RoPE + cache kernel."""
+    the bf16 gate|up GEMM (FP8 or, with `mx`, MXFP4) and the standalone
+    GEGLU quantiser; the bf16 QKV GEMM and the standalone split + RoPE +
+    cache kernel."""
     L = []
     f = s.get("ffn")
     if f is not None:
         pl = s["packs"][-1]
         H = f["H"]
-        L += [("gateup_bf16", lambda: frt.frt_packed_gemm_fp8_split(
-                  outs["x8"][-1], pl["W8"], act[-1], pl["ws"], [outs["gu"]], [2 * H],
-                  bias_cat=pl["bias"])),
-              ("geglu", lambda: frt.frt_geglu_quant_fp8(
-                  outs["gu"], H, f["scale"], out_fp8=outs["hid8_unfused"]))]
+        if mx:
+            x4, xs = outs["x4"][-1]
+            L.append(("gateup_bf16_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
+                x4, xs, pl["W8"], pl["ws"], [outs["gu"]], [2 * H], bias_cat=pl["bias"])))
+        else:
+            L.append(("gateup_bf16", lambda: frt.frt_packed_gemm_fp8_split(
+                outs["x8"][-1], pl["W8"], act[-1], pl["ws"], [outs["gu"]], [2 * H],
+                bias_cat=pl["bias"])))
+        L.append(("geglu", lambda: frt.frt_geglu_quant_fp8(
+            outs["gu"], H, f["scale"], out_fp8=outs["hid8_unfused"])))
     r = s.get("rope")
     if r is not None:
         p0 = s["packs"][0]
@@ -443,6 +474,12 @@ def unfused_launches(w, s, act, outs, frt):
 def kernel_work(w, kind, rows, packs, ffn=None, rope=None, oproj=None):
     """Algorithmic bytes and FLOPs of one launch."""
     D = w.D
+    if ffn is not None and kind in ("gemm2_mx_geglu", "gateup_bf16_mx"):
+        H = ffn["H"]
+        bias = 2 * H * 2 if packs[-1]["bias"] is not None else 0
+        out = rows * H if kind == "gemm2_mx_geglu" else rows * 2 * H * 2
+        return (rows * (D // 2 + D // 32) + 2 * H * (D // 2 + D // 32) + out + bias,
+                2.0 * rows * 2 * H * D)
     if kind.endswith("_mx"):
         if kind.startswith("norm"):     # res, x, rout bf16; codes D/2; scales D/32
             gate = rows * D * 2 if (w.cid == 4 and kind == "norm1_mx") else D * 2
@@ -760,9 +797,9 @@ def main():
     rows = a.rows if a.rows is not None else w0.rows
     if (a.rope or a.oproj) and a.workload not in wl.QKV_HEADS:
         raise SystemExit(f"--rope: the attention head is defined for workloads {sorted(wl.QKV_HEADS)}")
-    if a.mxfp4 and (wl.WORKLOADS[a.workload].form != "adarms" or a.ffn or a.rope or a.oproj):
+    if a.mxfp4 and (wl.WORKLOADS[a.workload].form != "adarms" or a.rope or a.oproj):
         raise SystemExit("--mxfp4: the MXFP4 band covers the AdaRMS workloads' producer + packed "
-                         "GEMM step (1, 2, 4), alone")
+                         "GEMM step (1, 2, 4), with --ffn its FFN tail (2)")
     if a.tp < 1 or (a.tp > 1 and (a.workload not in wl.TP_UNIT or a.ffn or a.rope or a.oproj or a.mxfp4)):
         raise SystemExit(f"--tp: one rank's share of the packed GEMM, for workloads {sorted(wl.TP_UNIT)} "
                          "alone")
@@ -773,7 +810,7 @@ def main():
         if a.workload not in wl.FFN_HIDDEN:
             raise SystemExit("--ffn: the FFN tail follows the gate/up GEMM of "
                              f"workloads {sorted(wl.FFN_HIDDEN)}")
-        ffn = build_ffn(w, rows, act, packs, frt, torch)
+        ffn = build_ffn(w, rows, act, packs, frt, torch, mx=a.mxfp4)
     sets, per_set = make_rotation(w, dev, packs, rows, torch, ffn)
     outs = make_outputs(w, rows, packs, torch, ffn)
     if a.mxfp4:
@@ -849,7 +886,7 @@ def main():
     timed = [[fn for _, fn in st] for st in steps_fns]
     all_kinds = list(kinds)
     if ffn is not None or rp is not None:
-        extra = [unfused_launches(w, s, act, outs, frt) for s in sets]
+        extra = [unfused_launches(w, s, act, outs, frt, mx=a.mxfp4) for s in sets]
         all_kinds += [k for k, _ in extra[0]]
         timed = [t + [fn for _, fn in e] for t, e in zip(timed, extra)]
     table = []
@@ -861,7 +898,7 @@ def main():
         row = {"kernel": kind, "us": round(us, 3), "bytes": int(b),
                "GB/s": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
         if f:
-            peak = FP4_PEAK_TFLOPS if kind.endswith("_mx") else FP8_PEAK_TFLOPS
+            peak = FP4_PEAK_TFLOPS if "_mx" in kind else FP8_PEAK_TFLOPS
             row["TFLOP/s"] = round(f / us / 1e6, 2)
             row["mfma_frac"] = round(f / us / 1e6 / peak, 4)
             row["bound"] = "mfma" if f / b > peak * 1e12 / (HBM_PEAK_GBS * 1e9) else "hbm"
@@ -879,7 +916,7 @@ def main():
     traffic = load_traffic(a.workload, dom["kernel"]) if a.rows is None else None
     if dom["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dom["TFLOP/s"],
-                "peak": FP4_PEAK_TFLOPS if dom["kernel"].endswith("_mx") else FP8_PEAK_TFLOPS,
+                "peak": FP4_PEAK_TFLOPS if "_mx" in dom["kernel"] else FP8_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": dom["mfma_frac"], "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS,
