@@ -498,6 +498,51 @@ int frt_packed_gemm_mxfp4_geglu_quant(void* stream, int64_t M, int64_t K,
                                       int64_t ld_out);
 
 /*
+ * frt_quantize_mxfp4 — dynamic MXFP4 quantiser of a bf16 tensor: the 4-bit
+ * band's quantize-from-bf16 entry (fp8_chain.py `BANDS`, the `fp4` row's
+ * GEMM package; `PackedLinearNvfp4` quantises a bf16 input it does not get
+ * from a producer), for GEMM inputs that no norm producer writes, such as
+ * the attention output before the O projection. Per row m < M, block
+ * b < D/32 of 32 columns:
+ *   s = 2^(floor(log2 max_k |x[m, 32b + k]|) - 2)   (E8M0 byte; 0 for an
+ *       all-zero block, 0xFF when the block holds a NaN or an infinity)
+ *   code[m, 32b + k] = e2m1_rne(x[m, 32b + k] / s)  (saturating at +-6)
+ * i.e. the OCP MX conversion of the bf16 values; both the scale and the
+ * codes are decided on those exact values.
+ *
+ *   M, D          rows; D a multiple of 256 (1 <= D/256, D <= 2^24).
+ *   x, ld_x       bf16 [M, ld_x], 16-byte aligned, ld_x >= D, ld_x % 8 == 0.
+ *   out_fp4, ld_out   [M, ld_out] code bytes (element 2j in the low nibble),
+ *                 4-byte aligned, ld_out >= D/2, ld_out % 4 == 0.
+ *   out_scale, ld_sc  scale bytes [D/256][rows][8] (run stride ld_sc >= 8M),
+ *                 each run's blocks in the order 0, 2, 4, 6, 1, 3, 5, 7 (the
+ *                 layout frt_packed_gemm_mxfp4_split reads).
+ * Outputs must not overlap the input or each other.
+ */
+int frt_quantize_mxfp4(void* stream, int64_t M, int64_t D,
+                       const uint16_t* x, int64_t ld_x,
+                       uint8_t* out_fp4, int64_t ld_out,
+                       uint8_t* out_scale, int64_t ld_sc);
+
+/*
+ * frt_geglu_quant_mxfp4 — the GEGLU of a bf16 gate|up buffer quantised to
+ * MXFP4: the 4-bit band's GELU-mul that emits packed 4-bit codes for a 4-bit
+ * down projection (fp8_chain.py `BANDS`, the `fp4_full` row). For m < M,
+ * j < H: y = gelu_tanh(gu[m, j]) * gu[m, H + j] (fp32, as
+ * frt_geglu_quant_fp8 forms it), then y is quantised as frt_quantize_mxfp4
+ * quantises x (blocks of 32 along H).
+ *
+ *   M, H          rows; width of each half, a multiple of 256 (2H <= 2^24).
+ *   gu, ld_gu     bf16 [M, ld_gu]: gate in [0, H), up in [H, 2H); 16-byte
+ *                 aligned, ld_gu >= 2H, ld_gu % 8 == 0.
+ *   out_fp4, ld_out, out_scale, ld_sc   as in frt_quantize_mxfp4 (D = H).
+ */
+int frt_geglu_quant_mxfp4(void* stream, int64_t M, int64_t H,
+                          const uint16_t* gu, int64_t ld_gu,
+                          uint8_t* out_fp4, int64_t ld_out,
+                          uint8_t* out_scale, int64_t ld_sc);
+
+/*
  * frt_interleave_pairs_bf16 — the pack-time permutation of q or k
  * projection rows that turns the host's rotate-half rotary pairs
  * (i, i + hd/2) into adjacent pairs (2i, 2i + 1).

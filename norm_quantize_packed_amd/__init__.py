@@ -29,6 +29,7 @@ __all__ = [
     "frt_quantize_fp8_static", "frt_packed_gemm_bf16in_split",
     "frt_pack_weights_mxfp4", "frt_ada_norm_quant_mxfp4",
     "frt_packed_gemm_mxfp4_split", "frt_packed_gemm_mxfp4_geglu_quant",
+    "frt_quantize_mxfp4", "frt_geglu_quant_mxfp4",
     "frt_qkv_split_rope_kvcache", "frt_packed_gemm_fp8_qkv_rope",
     "frt_last_error", "frt_abi_version",
     "FRT_OK", "FRT_E_INVALID", "FRT_E_UNSUPPORTED", "FRT_E_HIP",
@@ -80,6 +81,8 @@ _SIGNATURES = {
         ctypes.POINTER(_i64), ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32]),
     "frt_packed_gemm_mxfp4_geglu_quant": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _p, _p, _i64]),
+    "frt_quantize_mxfp4": (_i32, [_p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]),
+    "frt_geglu_quant_mxfp4": (_i32, [_p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]),
     "frt_packed_gemm_bf16in_split": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i32,
         ctypes.POINTER(_i64), ctypes.POINTER(_p), ctypes.POINTER(_i64), _i32,
@@ -561,3 +564,29 @@ def frt_packed_gemm_mxfp4_geglu_quant(x4, xs, W4, S4, out_scale, out_fp8,
         _stream(stream), Mv, int(W4.shape[1]) * 2, _ptr(x4), _ld(x4), _ptr(xs), _ld(xs),
         _ptr(W4), _ptr(S4), int(W4.shape[0] // 2), _ptr(bias_cat), _ptr(out_scale),
         _ptr(out_fp8), _ld(out_fp8)))
+
+
+def frt_quantize_mxfp4(x, out_fp4, out_scale, *, M: Optional[int] = None,
+                       stream=None) -> None:
+    """Dynamic MXFP4 of a bf16 ``x [M, D]``: codes into ``out_fp4
+    [M, D/2]``, scales into ``out_scale [D/256, rows, 8]``."""
+    _bf16_like(x, "x")
+    _u8_like(out_fp4, "out_fp4")
+    _u8_like(out_scale, "out_scale")
+    Mv = x.shape[0] if M is None else int(M)
+    _check(load_library().frt_quantize_mxfp4(
+        _stream(stream), Mv, int(x.shape[1]), _ptr(x), _ld(x), _ptr(out_fp4), _ld(out_fp4),
+        _ptr(out_scale), _ld(out_scale)))
+
+
+def frt_geglu_quant_mxfp4(gu, H: int, out_fp4, out_scale, *,
+                          M: Optional[int] = None, stream=None) -> None:
+    """GEGLU of a bf16 gate|up buffer ``gu [M, >= 2H]`` quantised to MXFP4:
+    codes into ``out_fp4 [M, H/2]``, scales into ``out_scale [H/256, rows, 8]``."""
+    _bf16_like(gu, "gu")
+    _u8_like(out_fp4, "out_fp4")
+    _u8_like(out_scale, "out_scale")
+    Mv = gu.shape[0] if M is None else int(M)
+    _check(load_library().frt_geglu_quant_mxfp4(
+        _stream(stream), Mv, int(H), _ptr(gu), _ld(gu), _ptr(out_fp4), _ld(out_fp4),
+        _ptr(out_scale), _ld(out_scale)))

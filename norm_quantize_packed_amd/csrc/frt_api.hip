@@ -371,6 +371,53 @@ int frt_geglu_quant_fp8(void* stream, int64_t M, int64_t H, const uint16_t* gu, 
   return hip_status(frt::launch_geglu(a, vec8 ? 8 : 1, (hipStream_t)stream), "geglu launch");
 }
 
+namespace {
+
+// Shared contract of the two MXFP4 quantisers from bf16: `cols` input
+// columns per row (2H for the GEGLU form), H output columns.
+int mx_quant(const char* who, void* stream, int64_t M, int64_t H, int64_t cols, const uint16_t* x, int64_t ld_x,
+             uint8_t* out_fp4, int64_t ld_out, uint8_t* out_scale, int64_t ld_sc, bool glu) {
+  if (M < 0) return refuse(FRT_E_INVALID, "%s: M=%lld < 0", who, (long long)M);
+  if (H < 256 || cols > (1 << 24) || H % 256)
+    return refuse(FRT_E_INVALID, "%s: width %lld must be a multiple of 256 (at most 2^24 input columns)", who,
+                  (long long)H);
+  if (x == nullptr || out_fp4 == nullptr || out_scale == nullptr)
+    return refuse(FRT_E_INVALID, "%s: input, out_fp4 and out_scale are required", who);
+  if (ld_x < cols || ld_x % 8 || !aligned(x, 16))
+    return refuse(FRT_E_INVALID, "%s: input 16-byte aligned with a row stride >= its columns and a multiple of 8",
+                  who);
+  if (ld_out < H / 2 || ld_out % 4 || !aligned(out_fp4, 4))
+    return refuse(FRT_E_INVALID, "%s: out_fp4 4-byte aligned, ld_out >= H/2 and a multiple of 4", who);
+  if (ld_sc < 8 * M) return refuse(FRT_E_INVALID, "%s: ld_sc (the scale run stride) < 8*M", who);
+  if (M == 0) return ok();
+  const Range in = span(x, M, cols, ld_x, 2), o = span(out_fp4, M, H / 2, ld_out, 1),
+              sc = span(out_scale, H / 256, 8 * M, ld_sc, 1);
+  if (overlap(o, in) || overlap(sc, in) || overlap(o, sc))
+    return refuse(FRT_E_INVALID, "%s: outputs overlap the input or each other", who);
+  frt::GegluArgs a{};
+  a.gu = x;
+  a.ld_gu = ld_x;
+  a.out = out_fp4;
+  a.ld_out = ld_out;
+  a.M = M;
+  a.H = (int)H;
+  a.sc = out_scale;
+  a.ld_sc = ld_sc;
+  return hip_status(frt::launch_mx_quant(a, glu, (hipStream_t)stream), who);
+}
+
+}  // namespace
+
+int frt_quantize_mxfp4(void* stream, int64_t M, int64_t D, const uint16_t* x, int64_t ld_x, uint8_t* out_fp4,
+                       int64_t ld_out, uint8_t* out_scale, int64_t ld_sc) {
+  return mx_quant("quantize_mxfp4", stream, M, D, D, x, ld_x, out_fp4, ld_out, out_scale, ld_sc, false);
+}
+
+int frt_geglu_quant_mxfp4(void* stream, int64_t M, int64_t H, const uint16_t* gu, int64_t ld_gu, uint8_t* out_fp4,
+                          int64_t ld_out, uint8_t* out_scale, int64_t ld_sc) {
+  return mx_quant("geglu_mxfp4", stream, M, H, 2 * H, gu, ld_gu, out_fp4, ld_out, out_scale, ld_sc, true);
+}
+
 int frt_packed_gemm_fp8_geglu_quant(void* stream, int64_t M, int64_t K, const uint8_t* x8, int64_t ld_x,
                                     const uint8_t* W8, int64_t H, const float* act_scale,
                                     const float* w_scale, const uint16_t* bias_cat,

@@ -15,6 +15,15 @@
 // The same epilogue also runs inside the gate/up GEMM (frt_gemm.hip), which
 // skips the bf16 round trip through HBM.
 //
+// mx_quant_kernel: the 4-bit band's quantisers from bf16 (fp8_chain.py
+// `BANDS`: the `fp4` row's quantize-from-bf16 entry, for a GEMM input that no
+// norm producer writes, such as the attention output before the O
+// projection; the `fp4_full` row's GELU-mul that emits packed 4-bit codes
+// for a 4-bit down projection), in the OCP MXFP4 format: per row, blocks of
+// 32 columns, one E8M0 scale 2^(floor(log2 max|v|) - 2) per block and the
+// e2m1 codes of v / scale (nearest, ties to even, saturating at 6), two per
+// byte; scales run-major [H/256][rows][8] as the MXFP4 GEMM reads them.
+//
 // quant_kernel: the plain static quantiser of a bf16 tensor (fp8_chain.py
 // `_band_elements`, `out_project`: `quantize_fp8_static_bf16` of the
 // attention output before the O projection; impls/linear_proj/
@@ -142,7 +151,53 @@ __global__ __launch_bounds__(256) void quant_kernel(GegluArgs a) {
   }
 }
 
+// One thread per 8 columns; the four lanes of a quad hold one 32-column
+// block (H % 32 == 0, so a quad is either wholly inside the row or wholly
+// past its end).
+template <bool GLU>
+__global__ __launch_bounds__(256) void mx_quant_kernel(GegluArgs a) {
+  const int nv = a.H / 8;
+  const int v = blockIdx.x * 256 + threadIdx.x;
+  if (v >= nv) return;
+  for (int64_t m = blockIdx.y; m < a.M; m += gridDim.y) {
+    const uint16_t* row = a.gu + m * a.ld_gu;
+    const int64_t c = (int64_t)v * 8;
+    const uint4 g = *reinterpret_cast<const uint4*>(row + c);
+    const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+    float y[8];
+    if constexpr (GLU) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + a.H + c);
+      const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gv = (e & 1) ? bf16hi(gw[e >> 1]) : bf16lo(gw[e >> 1]);
+        const float uv = (e & 1) ? bf16hi(uw[e >> 1]) : bf16lo(uw[e >> 1]);
+        y[e] = gelu_tanh(gv) * uv;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = (e & 1) ? bf16hi(gw[e >> 1]) : bf16lo(gw[e >> 1]);
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(fabsf(y[e])));
+    const uint32_t sbyte = e8m0_of_amax(quad_umax(am));
+    *reinterpret_cast<uint32_t*>(a.out + m * a.ld_out + c / 2) = mxfp4_pack8(y, sbyte);
+    if ((threadIdx.x & 3) == 0) a.sc[e8m0_off(m, c / 32, a.ld_sc)] = (uint8_t)sbyte;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_mx_quant(const GegluArgs& a, bool glu, hipStream_t st) {
+  const int64_t nv = a.H / 8;
+  const dim3 grid((unsigned)((nv + 255) / 256), (unsigned)(a.M < 65535 ? a.M : 65535));
+  if (glu)
+    hipLaunchKernelGGL((mx_quant_kernel<true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((mx_quant_kernel<false>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant(const GegluArgs& a, int vec, hipStream_t st) {
   const int64_t nv = a.H / vec;

@@ -102,11 +102,15 @@ struct GegluArgs {
   float* y; int64_t ld_y;
   float* amax;
   int64_t M; int H;
+  uint8_t* sc; int64_t ld_sc;   // MXFP4 block scales (launch_mx_quant)
 };
 
 hipError_t launch_geglu(const GegluArgs& a, int vec, hipStream_t st);
 // static FP8 of a bf16 [M, H] tensor (GegluArgs with gu = x, no up half)
 hipError_t launch_quant(const GegluArgs& a, int vec, hipStream_t st);
+// MXFP4 of a bf16 [M, H] tensor (glu = false) or of the GEGLU of a bf16
+// gate|up [M, 2H] buffer (glu = true): codes into out, scales into sc
+hipError_t launch_mx_quant(const GegluArgs& a, bool glu, hipStream_t st);
 
 hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st);

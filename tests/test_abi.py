@@ -354,3 +354,17 @@ def test_mxfp4_refusals(lib):
     assert geglu(ld_out=300) == frt.FRT_E_INVALID         # ld_out < H
     assert geglu(out=FAKE + 3 * MB) == frt.FRT_E_INVALID  # over S4
     assert geglu(M=0) == frt.FRT_OK
+
+    def q4(fn, W=512, **kw):
+        a = dict(stream=None, M=16, W=W, x=FAKE, ld_x=(2 if fn.endswith("geglu_quant_mxfp4") else 1) * W,
+                 out=FAKE + 2 * MB, ld_out=W // 2, sc=FAKE + 3 * MB, ld_sc=8 * 16)
+        a.update(kw)
+        return getattr(lib, fn)(*a.values())
+    for fn in ("frt_quantize_mxfp4", "frt_geglu_quant_mxfp4"):
+        assert q4(fn, W=384) == frt.FRT_E_INVALID         # width % 256
+        assert q4(fn, x=None) == frt.FRT_E_INVALID
+        assert q4(fn, x=FAKE + 8) == frt.FRT_E_INVALID    # 16-byte input
+        assert q4(fn, ld_out=200) == frt.FRT_E_INVALID    # ld_out < W/2
+        assert q4(fn, ld_sc=100) == frt.FRT_E_INVALID     # run stride < 8*M
+        assert q4(fn, out=FAKE + 64) == frt.FRT_E_INVALID  # over the input
+        assert q4(fn, M=0) == frt.FRT_OK
