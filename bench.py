@@ -37,7 +37,10 @@ producers emit OCP MX FP4 (dynamic per-32 block scales) and the norm-fed
 GEMMs take MXFP4 weights packed at bind; metric and roofline are the same,
 with the FP4 matrix-core peak. With ``--ffn`` (workload 2) the MXFP4
 gate/up GEMM carries the GEGLU quantiser and the down projection stays in
-static FP8.
+static FP8; ``--fp4-full`` runs the down projection in MXFP4 as well (the
+bf16 gate|up output, the GEGLU quantised to MXFP4, the MXFP4 down GEMM).
+``--oproj`` quantises the attention output to MXFP4 for an MXFP4 O
+projection.
 
 ``--tp T`` (workloads 3 and 5) measures one GPU's share of a
 tensor-parallel job over T GPUs: the producer over every row (its output is
@@ -89,6 +92,8 @@ def parse():
                         "GEMM and append the down projection")
     p.add_argument("--mxfp4", action="store_true",
                    help="AdaRMS workloads: MXFP4 producers and GEMMs (the FP4 band)")
+    p.add_argument("--fp4-full", action="store_true",
+                   help="with --mxfp4 --ffn: the down projection in MXFP4 too (GEGLU emits MXFP4)")
     p.add_argument("--oproj", action="store_true",
                    help="workload 2: quantise a seeded attention output and "
                         "run the O projection")
@@ -224,7 +229,7 @@ def build_sets(wid, rows, frt, torch, rope=False, mx=False, tp=1):
     return w, dev, act, packs, pack_ms
 
 
-def build_ffn(w, rows, act, packs, frt, torch, mx=False):
+def build_ffn(w, rows, act, packs, frt, torch, mx=False, full=False):
     """The FFN tail's bind: pack the down projection and calibrate the
     GEGLU output scale on the calibration batch (its producer codes through
     the bf16 gate/up GEMM and the standalone quantiser's amax; with `mx` the
@@ -232,6 +237,11 @@ def build_ffn(w, rows, act, packs, frt, torch, mx=False):
     import workloads as wl
     H = wl.FFN_HIDDEN[w.cid]
     Wd = bf16_dev(wl.down_weights(w.cid))
+    if full:        # MXFP4 down projection: dynamic block scales, no calibration
+        Wd4 = torch.empty(w.D, H // 2, dtype=torch.uint8, device="cuda")
+        Sd4 = torch.empty(H // 256, w.D, 8, dtype=torch.uint8, device="cuda")
+        frt.frt_pack_weights_mxfp4([Wd], None, Wd4, Sd4)
+        return {"H": H, "W8": Wd4, "ws": Sd4, "scale": None, "full": True}
     Wd8 = torch.empty(w.D, H, dtype=torch.uint8, device="cuda")
     wsd = torch.empty(1, dtype=torch.float32, device="cuda")
     frt.frt_pack_weights_fp8([Wd], None, Wd8, wsd)
@@ -271,7 +281,7 @@ def build_ffn(w, rows, act, packs, frt, torch, mx=False):
     frt.frt_geglu_quant_fp8(gu, H, None, amax_out=amax)
     torch.cuda.synchronize()
     s_h = np.float32(amax.item()) / np.float32(448.0)
-    return {"H": H, "W8": Wd8, "ws": wsd,
+    return {"H": H, "W8": Wd8, "ws": wsd, "full": False,
             "scale": torch.tensor([float(s_h)], dtype=torch.float32, device="cuda")}
 
 
@@ -301,16 +311,29 @@ def make_rotation(w, dev, packs, rows, torch, ffn=None):
             s["ffn"] = dict(ffn)
             if i > 0:
                 s["ffn"]["W8"] = ffn["W8"].clone()
+                if ffn["ws"].numel() > 1:
+                    s["ffn"]["ws"] = ffn["ws"].clone()
         sets.append(s)
     return sets, per
 
 
-def make_oproj(w, rows, frt, torch):
+def make_oproj(w, rows, frt, torch, mx=False):
     """O projection: packed W_o, the attention output and its calibrated
-    static scale, the FP8 input and the bf16 output buffers."""
+    static scale, the FP8 input and the bf16 output buffers (with `mx`: the
+    MXFP4 pack of W_o and the MXFP4 input buffers)."""
     import workloads as wl
     inp, cal = wl.o_proj_inputs(w.cid), wl.o_proj_inputs(w.cid, calib=True)
     Wo = bf16_dev(inp["W_o"])
+    if mx:
+        Ko = Wo.shape[1]
+        W4 = torch.empty(w.D, Ko // 2, dtype=torch.uint8, device="cuda")
+        S4 = torch.empty(Ko // 256, w.D, 8, dtype=torch.uint8, device="cuda")
+        frt.frt_pack_weights_mxfp4([Wo], None, W4, S4)
+        att = bf16_dev(inp["att"])
+        return {"W8": W4, "ws": S4, "att": att, "scale": None,
+                "o4": (torch.empty(rows, Ko // 2, dtype=torch.uint8, device="cuda"),
+                       torch.empty(Ko // 256, rows, 8, dtype=torch.uint8, device="cuda")),
+                "out": torch.empty(rows, w.D, dtype=torch.bfloat16, device="cuda")}
     W8 = torch.empty(Wo.shape, dtype=torch.uint8, device="cuda")
     ws = torch.empty(1, dtype=torch.float32, device="cuda")
     frt.frt_pack_weights_fp8([Wo], None, W8, ws)
@@ -353,6 +376,9 @@ def make_outputs(w, rows, packs, torch, ffn=None):
         o["dn"] = torch.empty(rows, D, dtype=torch.bfloat16, device="cuda")
         o["gu"] = torch.empty(rows, 2 * H, dtype=torch.bfloat16, device="cuda")
         o["hid8_unfused"] = torch.empty(rows, H, dtype=torch.uint8, device="cuda")
+        if ffn["full"]:
+            o["hid4"] = (torch.empty(rows, H // 2, dtype=torch.uint8, device="cuda"),
+                         torch.empty(H // 256, rows, 8, dtype=torch.uint8, device="cuda"))
     return o
 
 
@@ -379,12 +405,24 @@ def step_launches_mx(w, s, outs, rows, frt, eps):
             o4[1][0], o4[1][1], p1["W8"], p1["ws"], outs["gemm"][1], p1["splits"],
             bias_cat=p1["bias"])))
         f = s.get("ffn")
-        if f is not None:
+        if f is not None and f["full"]:
+            H, h4 = f["H"], outs["hid4"]
+            L[-1] = ("gemm2_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
+                o4[1][0], o4[1][1], p1["W8"], p1["ws"], [outs["gu"]], [2 * H], bias_cat=p1["bias"]))
+            L.append(("geglu_mx", lambda: frt.frt_geglu_quant_mxfp4(outs["gu"], H, h4[0], h4[1])))
+            L.append(("gemm_down_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
+                h4[0], h4[1], f["W8"], f["ws"], [outs["dn"]], [w.D])))
+        elif f is not None:
             L[-1] = ("gemm2_mx_geglu", lambda: frt.frt_packed_gemm_mxfp4_geglu_quant(
                 o4[1][0], o4[1][1], p1["W8"], p1["ws"], f["scale"], outs["hid8"],
                 bias_cat=p1["bias"]))
             L.append(("gemm_down", lambda: frt.frt_packed_gemm_fp8_split(
                 outs["hid8"], f["W8"], f["scale"], f["ws"], [outs["dn"]], [w.D])))
+    o = s.get("oproj")
+    if o is not None:
+        L.insert(2, ("quant_o_mx", lambda: frt.frt_quantize_mxfp4(o["att"], o["o4"][0], o["o4"][1])))
+        L.insert(3, ("gemm_o_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
+            o["o4"][0], o["o4"][1], o["W8"], o["ws"], [o["out"]], [w.D])))
     return L
 
 
@@ -445,7 +483,7 @@ def unfused_launches(w, s, act, outs, frt, mx=False):
     cache kernel."""
     L = []
     f = s.get("ffn")
-    if f is not None:
+    if f is not None and not f["full"]:
         pl = s["packs"][-1]
         H = f["H"]
         if mx:
@@ -474,6 +512,16 @@ def unfused_launches(w, s, act, outs, frt, mx=False):
 def kernel_work(w, kind, rows, packs, ffn=None, rope=None, oproj=None):
     """Algorithmic bytes and FLOPs of one launch."""
     D = w.D
+    if oproj is not None and kind in ("quant_o_mx", "gemm_o_mx"):
+        Ko = oproj["att"].shape[1]
+        if kind == "quant_o_mx":        # bf16 in, codes + scales out
+            return rows * Ko * 2 + rows * (Ko // 2 + Ko // 32), 0.0
+        return rows * (Ko // 2 + Ko // 32) + D * (Ko // 2 + Ko // 32) + rows * D * 2, 2.0 * rows * D * Ko
+    if ffn is not None and kind in ("geglu_mx", "gemm_down_mx"):
+        H = ffn["H"]
+        if kind == "geglu_mx":          # bf16 [M, 2H] in, codes + scales out
+            return rows * 2 * H * 2 + rows * (H // 2 + H // 32), 0.0
+        return rows * (H // 2 + H // 32) + D * (H // 2 + H // 32) + rows * D * 2, 2.0 * rows * D * H
     if ffn is not None and kind in ("gemm2_mx_geglu", "gateup_bf16_mx"):
         H = ffn["H"]
         bias = 2 * H * 2 if packs[-1]["bias"] is not None else 0
@@ -797,9 +845,12 @@ def main():
     rows = a.rows if a.rows is not None else w0.rows
     if (a.rope or a.oproj) and a.workload not in wl.QKV_HEADS:
         raise SystemExit(f"--rope: the attention head is defined for workloads {sorted(wl.QKV_HEADS)}")
-    if a.mxfp4 and (wl.WORKLOADS[a.workload].form != "adarms" or a.rope or a.oproj):
+    if a.mxfp4 and (wl.WORKLOADS[a.workload].form != "adarms" or a.rope):
         raise SystemExit("--mxfp4: the MXFP4 band covers the AdaRMS workloads' producer + packed "
-                         "GEMM step (1, 2, 4), with --ffn its FFN tail (2)")
+                         "GEMM step (1, 2, 4), with --ffn / --oproj the FFN tail and O projection (2)")
+    if a.fp4_full and not (a.mxfp4 and a.ffn):
+        raise SystemExit("--fp4-full: the MXFP4 band's FFN tail with an MXFP4 down projection "
+                         "(needs --mxfp4 --ffn)")
     if a.tp < 1 or (a.tp > 1 and (a.workload not in wl.TP_UNIT or a.ffn or a.rope or a.oproj or a.mxfp4)):
         raise SystemExit(f"--tp: one rank's share of the packed GEMM, for workloads {sorted(wl.TP_UNIT)} "
                          "alone")
@@ -810,19 +861,21 @@ def main():
         if a.workload not in wl.FFN_HIDDEN:
             raise SystemExit("--ffn: the FFN tail follows the gate/up GEMM of "
                              f"workloads {sorted(wl.FFN_HIDDEN)}")
-        ffn = build_ffn(w, rows, act, packs, frt, torch, mx=a.mxfp4)
+        ffn = build_ffn(w, rows, act, packs, frt, torch, mx=a.mxfp4, full=a.fp4_full)
     sets, per_set = make_rotation(w, dev, packs, rows, torch, ffn)
     outs = make_outputs(w, rows, packs, torch, ffn)
     if a.mxfp4:
         outs["x4"] = [(torch.empty(rows, w.D // 2, dtype=torch.uint8, device="cuda"),
                        torch.empty(w.D // 256, rows, 8, dtype=torch.uint8, device="cuda")) for _ in packs]
     rp = make_rope(w, rows, torch) if a.rope else None
-    op = make_oproj(w, rows, frt, torch) if a.oproj else None
+    op = make_oproj(w, rows, frt, torch, mx=a.mxfp4) if a.oproj else None
     for i, st in enumerate(sets):
         if rp is not None:
             st["rope"] = rp
         if op is not None:   # each rotation set streams its own W_o copy
             st["oproj"] = dict(op, W8=op["W8"] if i == 0 else op["W8"].clone())
+            if a.mxfp4 and i > 0:
+                st["oproj"]["ws"] = op["ws"].clone()
     nset = len(sets)
 
     steps_fns = [step_launches_mx(w, s, outs, rows, frt, wl.EPS) if a.mxfp4 else
@@ -936,6 +989,7 @@ def main():
                                + ("+qkv_rope_kvcache" if rp is not None else "")
                                + ("+o_proj" if op is not None else "")
                                + ("+ffn_geglu_down" if ffn is not None else "")
+                               + ("+fp4_down" if a.fp4_full else "")
                                + (f"+tp{a.tp}_rank0" if a.tp > 1 else ""),
                    "rows": rows, "D": w.D,
                    "gemms": [list(p["splits"]) for p in packs], "bias": w.bias,
