@@ -631,6 +631,35 @@ int frt_packed_gemm_fp8_qkv_rope(void* stream, int64_t M, int64_t K,
                                  uint16_t* q_out, uint16_t* k_cache,
                                  uint16_t* v_cache);
 
+/*
+ * frt_packed_gemm_mxfp4_qkv_rope — the merged QKV GEMM on MXFP4 operands
+ * with the split + RoPE + KV-cache write as its epilogue: the 4-bit band's
+ * QKV projection feeding the attention head. For m < M and column n of the
+ * [M, (nh + 2kv) hd] product:
+ *   v = bf16_rne(acc[m, n] + bias_cat[n])   (acc as in
+ *       frt_packed_gemm_mxfp4_split)
+ * then exactly frt_qkv_split_rope_kvcache on those values, i.e. the same
+ * results as frt_packed_gemm_mxfp4_split (bf16 out) followed by
+ * frt_qkv_split_rope_kvcache.
+ *
+ *   M, K, x4, ld_x4, xs, ld_xs   as in frt_packed_gemm_mxfp4_split.
+ *   W4, S4        [(nh + 2kv) hd, K/2] codes and [K/256][(nh + 2kv) hd][8]
+ *                 scales: q rows, k rows (both pair-interleaved before
+ *                 packing, frt_interleave_pairs_bf16), v rows.
+ *   bias_cat      bf16 [(nh + 2kv) hd] or NULL.
+ *   nh, kv, hd, rope, P, T, q_out, k_cache, v_cache   as in
+ *                 frt_qkv_split_rope_kvcache (S = M).
+ */
+int frt_packed_gemm_mxfp4_qkv_rope(void* stream, int64_t M, int64_t K,
+                                   const uint8_t* x4, int64_t ld_x4,
+                                   const uint8_t* xs, int64_t ld_xs,
+                                   const uint8_t* W4, const uint8_t* S4,
+                                   int nh, int kv, int hd,
+                                   const uint16_t* bias_cat,
+                                   const uint16_t* rope, int64_t P, int64_t T,
+                                   uint16_t* q_out, uint16_t* k_cache,
+                                   uint16_t* v_cache);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ __all__ = [
     "frt_quantize_fp8_static", "frt_packed_gemm_bf16in_split",
     "frt_pack_weights_mxfp4", "frt_ada_norm_quant_mxfp4",
     "frt_packed_gemm_mxfp4_split", "frt_packed_gemm_mxfp4_geglu_quant",
-    "frt_quantize_mxfp4", "frt_geglu_quant_mxfp4",
+    "frt_quantize_mxfp4", "frt_geglu_quant_mxfp4", "frt_packed_gemm_mxfp4_qkv_rope",
     "frt_qkv_split_rope_kvcache", "frt_packed_gemm_fp8_qkv_rope",
     "frt_last_error", "frt_abi_version",
     "FRT_OK", "FRT_E_INVALID", "FRT_E_UNSUPPORTED", "FRT_E_HIP",
@@ -82,6 +82,9 @@ _SIGNATURES = {
     "frt_packed_gemm_mxfp4_geglu_quant": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _p, _p, _i64]),
     "frt_quantize_mxfp4": (_i32, [_p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]),
+    "frt_packed_gemm_mxfp4_qkv_rope": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i32, _i32, _i32, _p, _p, _i64, _i64,
+        _p, _p, _p]),
     "frt_geglu_quant_mxfp4": (_i32, [_p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]),
     "frt_packed_gemm_bf16in_split": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p, _p, _p, _i32,
@@ -590,3 +593,20 @@ def frt_geglu_quant_mxfp4(gu, H: int, out_fp4, out_scale, *,
     _check(load_library().frt_geglu_quant_mxfp4(
         _stream(stream), Mv, int(H), _ptr(gu), _ld(gu), _ptr(out_fp4), _ld(out_fp4),
         _ptr(out_scale), _ld(out_scale)))
+
+
+def frt_packed_gemm_mxfp4_qkv_rope(x4, xs, W4, S4, nh: int, kv: int, hd: int, rope,
+                                   P: int, q_out, k_cache, v_cache, bias_cat=None, *,
+                                   M: Optional[int] = None, stream=None) -> None:
+    """Merged QKV GEMM on MXFP4 operands with the split + RoPE + KV-cache
+    epilogue (q and k weight rows pair-interleaved before packing)."""
+    for t, nme in ((x4, "x4"), (xs, "xs"), (W4, "W4"), (S4, "S4")):
+        _u8_like(t, nme)
+    _bf16_like(bias_cat, "bias_cat")
+    _cache_args(rope, q_out, k_cache, v_cache)
+    Mv = x4.shape[0] if M is None else int(M)
+    T = k_cache.numel() // (kv * hd)
+    _check(load_library().frt_packed_gemm_mxfp4_qkv_rope(
+        _stream(stream), Mv, int(W4.shape[1]) * 2, _ptr(x4), _ld(x4), _ptr(xs), _ld(xs),
+        _ptr(W4), _ptr(S4), int(nh), int(kv), int(hd), _ptr(bias_cat), _ptr(rope), int(P),
+        int(T), _ptr(q_out), _ptr(k_cache), _ptr(v_cache)))

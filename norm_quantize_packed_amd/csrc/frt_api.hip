@@ -782,4 +782,52 @@ int frt_packed_gemm_fp8_qkv_rope(void* stream, int64_t M, int64_t K, const uint8
   return hip_status(frt::launch_gemm_rope(a, (hipStream_t)stream), "gemm_rope launch");
 }
 
+int frt_packed_gemm_mxfp4_qkv_rope(void* stream, int64_t M, int64_t K, const uint8_t* x4, int64_t ld_x4,
+                                   const uint8_t* xs, int64_t ld_xs, const uint8_t* W4, const uint8_t* S4, int nh,
+                                   int kv, int hd, const uint16_t* bias_cat, const uint16_t* rope, int64_t P,
+                                   int64_t T, uint16_t* q_out, uint16_t* k_cache, uint16_t* v_cache) {
+  if (M < 0) return refuse(FRT_E_INVALID, "gemm_mxfp4_rope: M=%lld < 0", (long long)M);
+  if (K < 512 || K > 16384 || K % 256)
+    return refuse(FRT_E_INVALID, "gemm_mxfp4_rope: K=%lld must be a multiple of 256 in [512, 16384]", (long long)K);
+  if (M > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "gemm_mxfp4_rope: M too large");
+  if (x4 == nullptr || xs == nullptr || W4 == nullptr || S4 == nullptr)
+    return refuse(FRT_E_INVALID, "gemm_mxfp4_rope: x4, xs, W4 and S4 are required");
+  const int64_t kb = K / 2;
+  if (ld_x4 < kb || ld_x4 % 16)
+    return refuse(FRT_E_INVALID, "gemm_mxfp4_rope: ld_x4 must be >= K/2 and a multiple of 16");
+  if (!aligned(x4, 16) || !aligned(W4, 16))
+    return refuse(FRT_E_INVALID, "gemm_mxfp4_rope: x4 and W4 must be 16-byte aligned");
+  if (ld_xs < 8 * M || !aligned(xs, 4) || ld_xs % 4 || !aligned(S4, 4))
+    return refuse(FRT_E_INVALID,
+                  "gemm_mxfp4_rope: scales 4-byte aligned, ld_xs (run stride) >= 8*M and a multiple of 4");
+  const int64_t N = (nh >= 1 && kv >= 1 && hd >= 2) ? (int64_t)(nh + 2 * kv) * hd : 0;
+  if ((M - 1) * ld_x4 + kb > (int64_t)0x7fffffff || N * kb > (int64_t)0x7fffffff)
+    return refuse(FRT_E_UNSUPPORTED, "gemm_mxfp4_rope: operand larger than 2 GiB");
+  const Range in[5] = {span(x4, M, kb, ld_x4, 1), span(W4, N, kb, kb, 1), span(bias_cat, 1, N, N, 2),
+                       span(xs, K / 256, 8 * M, ld_xs, 1), span(S4, K / 256, 8 * N, 8 * N, 1)};
+  const int rc = check_rope_outputs("gemm_mxfp4_rope", M, nh, kv, hd, rope, P, T, q_out, k_cache, v_cache, in, 5);
+  if (rc != FRT_OK) return rc;
+  if (M == 0) return ok();
+  frt::GemmArgs a{};
+  a.x = x4;
+  a.ld_x = ld_x4;
+  a.w = W4;
+  a.bias = bias_cat;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.sa = xs;
+  a.ld_sa = ld_xs;
+  a.sb = S4;
+  a.rope = rope;
+  a.nh = nh;
+  a.kv = kv;
+  a.hd = hd;
+  a.P = P;
+  a.q_out = q_out;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  return hip_status(frt::launch_gemm_mxfp4_rope(a, (hipStream_t)stream), "gemm_mxfp4_rope launch");
+}
+
 }  // extern "C"

@@ -145,7 +145,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   constexpr int SUBB = ROWS * 128;     // one 128-deep sub-buffer
   constexpr int STAGE = NSUB * SUBB;   // one stage = NSUB sub-buffers
   constexpr int KST = 128 * NSUB;      // K bytes per stage
-  static_assert(!FP4 || (!KTAIL && !ROPE), "MXFP4 form: whole stages, split or GEGLU epilogue");
+  static_assert(!FP4 || !KTAIL, "MXFP4 form: whole stages");
   constexpr int SCL = FP4 ? MI + NJ : 0;  // scale loads per sub-buffer
   static_assert(NS >= 2 && NSUB * (LPW + SCL) * (NS - 2) <= 63, "ring depth vs vmcnt range");
   static_assert(NS * STAGE <= 160 * 1024, "ring exceeds LDS");
@@ -511,7 +511,7 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
   if constexpr (FP4) {  // whole stages (K a multiple of 256 * NSUB) is checked by the caller
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, false, true>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE, true>), dim3(tiles),
                        dim3(threads), 0, st, a);
     return hipGetLastError();
   }
@@ -604,25 +604,32 @@ hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st) { return launch_p
 // toward larger tiles only through plan_cost's row counts. The 64x32 plans
 // stage 512 K-elements (two runs) when K allows it, else one run in a ring
 // twice as deep (the same K in flight).
-template <int AE>
+template <int AE, bool ROPE>
 hipError_t launch_mx_narrow(const GemmArgs& a, hipStream_t st) {
-  if (a.K % 512 == 0) return launch_tiles<64, 32, 32, 32, 4, 1, 2, AE, false, false, true>(a, st);
-  return launch_tiles<64, 32, 32, 32, 7, 1, 1, AE, false, false, true>(a, st);
+  if (a.K % 512 == 0) return launch_tiles<64, 32, 32, 32, 4, 1, 2, AE, false, ROPE, true>(a, st);
+  return launch_tiles<64, 32, 32, 32, 7, 1, 1, AE, false, ROPE, true>(a, st);
 }
 
-hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st) {
+// The split plans; the RoPE form (the QKV split + RoPE + KV-cache epilogue)
+// runs on the same tiles, so its results equal the split GEMM's bf16 output
+// passed through the standalone consumer.
+template <bool ROPE>
+hipError_t launch_mx_planned(const GemmArgs& a, hipStream_t st) {
   if (a.M > 64) {
     const int cus = device_cus();
     const int64_t c128 = plan_cost(a, 128, 128, cus), c64 = plan_cost(a, 64, 64, cus),
                   c32 = plan_cost(a, 64, 32, cus);
-    if (c128 < c64 && c128 < c32) return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, false, false, true>(a, st);
-    if (c64 < c32) return launch_tiles<64, 64, 32, 32, 4, 1, 1, 64, false, false, true>(a, st);
-    return launch_mx_narrow<64>(a, st);
+    if (c128 < c64 && c128 < c32) return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, false, ROPE, true>(a, st);
+    if (c64 < c32) return launch_tiles<64, 64, 32, 32, 4, 1, 1, 64, false, ROPE, true>(a, st);
+    return launch_mx_narrow<64, ROPE>(a, st);
   }
-  if (a.M <= 16) return launch_mx_narrow<16>(a, st);
-  if (a.M <= 32) return launch_mx_narrow<32>(a, st);
-  return launch_mx_narrow<64>(a, st);
+  if (a.M <= 16) return launch_mx_narrow<16, ROPE>(a, st);
+  if (a.M <= 32) return launch_mx_narrow<32, ROPE>(a, st);
+  return launch_mx_narrow<64, ROPE>(a, st);
 }
+
+hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st) { return launch_mx_planned<false>(a, st); }
+hipError_t launch_gemm_mxfp4_rope(const GemmArgs& a, hipStream_t st) { return launch_mx_planned<true>(a, st); }
 
 // MXFP4 GEGLU plans: the MXFP4 128x128 plan (its waves are already 32x64)
 // where it has the least per-CU load, else 64x64 of two 32x64 waves; like

@@ -115,6 +115,7 @@ hipError_t launch_mx_quant(const GegluArgs& a, bool glu, hipStream_t st);
 hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_mxfp4_geglu(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm_mxfp4_rope(const GemmArgs& a, hipStream_t st);
 
 struct RopeArgs {
   const uint16_t* qkv; int64_t ld_qkv;

@@ -368,3 +368,17 @@ def test_mxfp4_refusals(lib):
         assert q4(fn, ld_sc=100) == frt.FRT_E_INVALID     # run stride < 8*M
         assert q4(fn, out=FAKE + 64) == frt.FRT_E_INVALID  # over the input
         assert q4(fn, M=0) == frt.FRT_OK
+
+    def mrope(K=512, **kw):
+        a = dict(stream=None, M=16, K=K, x4=FAKE, ld_x4=K // 2, xs=FAKE + MB, ld_xs=8 * 16,
+                 W4=FAKE + 2 * MB, S4=FAKE + 3 * MB, nh=4, kv=2, hd=64, bias=None,
+                 rope=FAKE + 4 * MB, P=0, T=16, q=FAKE + 40 * MB, kc=FAKE + 41 * MB, vc=FAKE + 42 * MB)
+        a.update(kw)
+        return lib.frt_packed_gemm_mxfp4_qkv_rope(*a.values())
+    assert mrope(K=640) == frt.FRT_E_INVALID              # K % 256
+    assert mrope(xs=None) == frt.FRT_E_INVALID
+    assert mrope(ld_xs=100) == frt.FRT_E_INVALID          # run stride < 8*M
+    assert mrope(hd=63) == frt.FRT_E_INVALID              # odd head dim
+    assert mrope(P=1) == frt.FRT_E_INVALID                # P + M > T
+    assert mrope(q=FAKE + 3 * MB) == frt.FRT_E_INVALID    # q over S4
+    assert mrope(M=0) == frt.FRT_OK

@@ -14,7 +14,7 @@ import torch
 
 import norm_quantize_packed_amd as frt
 import workloads as wl
-from oracle import codecs, ffn, mxfp4, producers
+from oracle import codecs, ffn, mxfp4, producers, rope
 from gpu_util import (Guarded, assert_codes_close, assert_gemm_bf16, assert_gemm_f32, dev_bf16,
                       dev_u8, host_bf16, host_u8, scalar)
 
@@ -246,3 +246,63 @@ def test_geglu_quant_mxfp4(M, H):
     d = np.abs(_e2m1_ordinal(gc) - _e2m1_ordinal(rc))[np.repeat(same, 32, axis=1)]
     assert d.max(initial=0) <= 1
     assert (d > 0).mean() <= 0.001, f"{(d > 0).sum()} of {d.size} codes differ"
+
+
+_FILL = 0x3C01   # bf16 pattern pre-filled into the caches (rows not written keep it)
+
+
+def _caches(T, kv, hd):
+    k = torch.full((T, kv, hd), _FILL, dtype=torch.int16, device="cuda")
+    return k.view(torch.bfloat16), k.clone().view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,K,nh,kv,hd,P,bias", [
+    (256, 2048, 8, 1, 256, 768, False),   # the decoder layer's heads (64x64 plan)
+    (1024, 512, 32, 8, 128, 0, True),     # 128x128 plan
+    (16, 512, 4, 2, 64, 5, True),         # small M: rows past M not loaded
+    (40, 768, 2, 1, 128, 0, False),       # K an odd number of 256-element runs
+    (600, 1024, 4, 2, 128, 100, False),   # ragged M
+])
+def test_gemm_mxfp4_rope_vs_unfused_and_oracle(M, K, nh, kv, hd, P, bias):
+    """The MXFP4 QKV GEMM with the split + RoPE + KV-cache epilogue: q and
+    the cache rows equal the split MXFP4 GEMM's bf16 output passed through
+    the standalone consumer bit for bit; that bf16 output is within the GEMM
+    tolerance of the exact oracle, and the consumer on it equals the
+    oracle's."""
+    a = wl.random_bf16(1800 + M, (M, K), 1.0)
+    ac, as_ = mxfp4.quantize_mxfp4(codecs.bf16_to_f32(a))
+    Wq = rope.interleave_rows(wl.random_bf16(1801 + hd, (nh * hd, K), 0.02), nh, hd)
+    Wk = rope.interleave_rows(wl.random_bf16(1802 + hd, (kv * hd, K), 0.02), kv, hd)
+    Wv = wl.random_bf16(1803 + hd, (kv * hd, K), 0.02)
+    bs = [wl.random_bf16(1804 + i, (n,), 0.02) for i, n in enumerate((nh * hd, kv * hd, kv * hd))] \
+        if bias else None
+    w4, ws4, bc = _gpu_pack([Wq, Wk, Wv], bs)
+    width = (nh + 2 * kv) * hd
+    T = P + M + 3
+    table = wl.rope_table(M, hd, P)
+    dtab = dev_bf16(table)
+    x4, xs = dev_u8(mxfp4.pack_nibbles(ac)), dev_u8(mxfp4.scales_to_gemm_order(as_))
+    dw4, dws4 = dev_u8(w4), dev_u8(ws4)
+    db = None if bc is None else dev_bf16(bc)
+    q = torch.empty((M, nh, hd), dtype=torch.bfloat16, device="cuda")
+    kc, vc = _caches(T, kv, hd)
+    frt.frt_packed_gemm_mxfp4_qkv_rope(x4, xs, dw4, dws4, nh, kv, hd, dtab, P, q, kc, vc, db)
+    qkv = torch.empty((M, width), dtype=torch.bfloat16, device="cuda")
+    frt.frt_packed_gemm_mxfp4_split(x4, xs, dw4, dws4, [qkv], [width], db)
+    q2 = torch.empty_like(q)
+    kc2, vc2 = _caches(T, kv, hd)
+    frt.frt_qkv_split_rope_kvcache(qkv, dtab, nh, kv, hd, P, q2, kc2, vc2)
+    torch.cuda.synchronize()
+    assert torch.equal(q.view(torch.int16), q2.view(torch.int16))
+    assert torch.equal(kc.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), vc2.view(torch.int16))
+    qkv_bits = host_bf16(qkv)
+    ref = mxfp4.gemm_mxfp4(ac, as_, mxfp4.unpack_nibbles(w4), mxfp4.scales_from_gemm_order(ws4))
+    if bc is not None:
+        ref = ref + codecs.bf16_to_f32(bc).astype(np.float64)[None, :]
+    assert_gemm_bf16(qkv_bits, ref, f"mxfp4 qkv {M}x{width}x{K}")
+    fill = np.full((T, kv, hd), _FILL, np.uint16)
+    rq, rk, rv = rope.qkv_split_rope_kvcache(qkv_bits, table, nh, kv, hd, P, fill, fill)
+    assert np.array_equal(host_bf16(q).reshape(rq.shape), rq)
+    assert np.array_equal(host_bf16(kc), rk)
+    assert np.array_equal(host_bf16(vc), rv)
