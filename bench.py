@@ -40,7 +40,8 @@ gate/up GEMM carries the GEGLU quantiser and the down projection stays in
 static FP8; ``--fp4-full`` runs the down projection in MXFP4 as well (the
 bf16 gate|up output, the GEGLU quantised to MXFP4, the MXFP4 down GEMM).
 ``--oproj`` quantises the attention output to MXFP4 for an MXFP4 O
-projection.
+projection, and ``--rope`` gives the MXFP4 QKV GEMM the split + RoPE +
+KV-cache epilogue.
 
 ``--tp T`` (workloads 3 and 5) measures one GPU's share of a
 tensor-parallel job over T GPUs: the producer over every row (its output is
@@ -418,6 +419,11 @@ def step_launches_mx(w, s, outs, rows, frt, eps):
                 bias_cat=p1["bias"]))
             L.append(("gemm_down", lambda: frt.frt_packed_gemm_fp8_split(
                 outs["hid8"], f["W8"], f["scale"], f["ws"], [outs["dn"]], [w.D])))
+    r = s.get("rope")
+    if r is not None:
+        L[1] = ("gemm1_mx_rope", lambda: frt.frt_packed_gemm_mxfp4_qkv_rope(
+            o4[0][0], o4[0][1], p0["W8"], p0["ws"], r["nh"], r["kv"], r["hd"], r["table"], r["P"],
+            r["q"], r["kc"], r["vc"], bias_cat=p0["bias"]))
     o = s.get("oproj")
     if o is not None:
         L.insert(2, ("quant_o_mx", lambda: frt.frt_quantize_mxfp4(o["att"], o["o4"][0], o["o4"][1])))
@@ -500,12 +506,16 @@ def unfused_launches(w, s, act, outs, frt, mx=False):
     if r is not None:
         p0 = s["packs"][0]
         width = (r["nh"] + 2 * r["kv"]) * r["hd"]
-        L += [("qkv_bf16", lambda: frt.frt_packed_gemm_fp8_split(
-                  outs["x8"][0], p0["W8"], act[0], p0["ws"], [r["qkv"]], [width],
-                  bias_cat=p0["bias"])),
-              ("rope_split", lambda: frt.frt_qkv_split_rope_kvcache(
-                  r["qkv"], r["table"], r["nh"], r["kv"], r["hd"], r["P"],
-                  r["q"], r["kc"], r["vc"]))]
+        if mx:
+            qx4, qxs = outs["x4"][0]
+            L.append(("qkv_bf16_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
+                qx4, qxs, p0["W8"], p0["ws"], [r["qkv"]], [width], bias_cat=p0["bias"])))
+        else:
+            L.append(("qkv_bf16", lambda: frt.frt_packed_gemm_fp8_split(
+                outs["x8"][0], p0["W8"], act[0], p0["ws"], [r["qkv"]], [width],
+                bias_cat=p0["bias"])))
+        L.append(("rope_split", lambda: frt.frt_qkv_split_rope_kvcache(
+            r["qkv"], r["table"], r["nh"], r["kv"], r["hd"], r["P"], r["q"], r["kc"], r["vc"])))
     return L
 
 
@@ -517,6 +527,10 @@ def kernel_work(w, kind, rows, packs, ffn=None, rope=None, oproj=None):
         if kind == "quant_o_mx":        # bf16 in, codes + scales out
             return rows * Ko * 2 + rows * (Ko // 2 + Ko // 32), 0.0
         return rows * (Ko // 2 + Ko // 32) + D * (Ko // 2 + Ko // 32) + rows * D * 2, 2.0 * rows * D * Ko
+    if rope is not None and kind in ("gemm1_mx_rope", "qkv_bf16_mx"):
+        N = (rope["nh"] + 2 * rope["kv"]) * rope["hd"]
+        out = rows * N * 2 + (rows * rope["hd"] * 2 if kind == "gemm1_mx_rope" else 0)
+        return rows * (D // 2 + D // 32) + N * (D // 2 + D // 32) + out, 2.0 * rows * N * D
     if ffn is not None and kind in ("geglu_mx", "gemm_down_mx"):
         H = ffn["H"]
         if kind == "geglu_mx":          # bf16 [M, 2H] in, codes + scales out
@@ -845,9 +859,9 @@ def main():
     rows = a.rows if a.rows is not None else w0.rows
     if (a.rope or a.oproj) and a.workload not in wl.QKV_HEADS:
         raise SystemExit(f"--rope: the attention head is defined for workloads {sorted(wl.QKV_HEADS)}")
-    if a.mxfp4 and (wl.WORKLOADS[a.workload].form != "adarms" or a.rope):
+    if a.mxfp4 and wl.WORKLOADS[a.workload].form != "adarms":
         raise SystemExit("--mxfp4: the MXFP4 band covers the AdaRMS workloads' producer + packed "
-                         "GEMM step (1, 2, 4), with --ffn / --oproj the FFN tail and O projection (2)")
+                         "GEMM step (1, 2, 4), with --rope / --oproj / --ffn the rest of the layer (2)")
     if a.fp4_full and not (a.mxfp4 and a.ffn):
         raise SystemExit("--fp4-full: the MXFP4 band's FFN tail with an MXFP4 down projection "
                          "(needs --mxfp4 --ffn)")
