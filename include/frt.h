@@ -498,6 +498,29 @@ int frt_packed_gemm_mxfp4_geglu_quant(void* stream, int64_t M, int64_t K,
                                       int64_t ld_out);
 
 /*
+ * frt_packed_gemm_mxfp4_geglu_mxfp4 — the MXFP4 gate/up GEMM with the GEGLU
+ * quantised to MXFP4 in its epilogue: the 4-bit band's `fp4_full` row
+ * (fp8_chain.py `BANDS`: the GELU-mul emits packed 4-bit codes and the down
+ * projection runs in 4-bit), fused. For m < M, j < H, with g and u as in
+ * frt_packed_gemm_mxfp4_geglu_quant and y = gelu_tanh(g) * u (fp32), y is
+ * quantised as frt_geglu_quant_mxfp4 quantises it, i.e. the result equals
+ * frt_packed_gemm_mxfp4_split (bf16 out) followed by frt_geglu_quant_mxfp4.
+ *
+ *   M, K, x4, ld_x4, xs, ld_xs, W4, S4, bias_cat   as in
+ *                 frt_packed_gemm_mxfp4_geglu_quant.
+ *   H             width of each half, a multiple of 256 (2H <= 2^24).
+ *   out_fp4, ld_out, out_scale, ld_sc   as in frt_geglu_quant_mxfp4; must
+ *                 not overlap an input or each other.
+ */
+int frt_packed_gemm_mxfp4_geglu_mxfp4(void* stream, int64_t M, int64_t K,
+                                      const uint8_t* x4, int64_t ld_x4,
+                                      const uint8_t* xs, int64_t ld_xs,
+                                      const uint8_t* W4, const uint8_t* S4,
+                                      int64_t H, const uint16_t* bias_cat,
+                                      uint8_t* out_fp4, int64_t ld_out,
+                                      uint8_t* out_scale, int64_t ld_sc);
+
+/*
  * frt_quantize_mxfp4 — dynamic MXFP4 quantiser of a bf16 tensor: the 4-bit
  * band's quantize-from-bf16 entry (fp8_chain.py `BANDS`, the `fp4` row's
  * GEMM package; `PackedLinearNvfp4` quantises a bf16 input it does not get

@@ -30,6 +30,7 @@ __all__ = [
     "frt_pack_weights_mxfp4", "frt_ada_norm_quant_mxfp4",
     "frt_packed_gemm_mxfp4_split", "frt_packed_gemm_mxfp4_geglu_quant",
     "frt_quantize_mxfp4", "frt_geglu_quant_mxfp4", "frt_packed_gemm_mxfp4_qkv_rope",
+    "frt_packed_gemm_mxfp4_geglu_mxfp4",
     "frt_qkv_split_rope_kvcache", "frt_packed_gemm_fp8_qkv_rope",
     "frt_last_error", "frt_abi_version",
     "FRT_OK", "FRT_E_INVALID", "FRT_E_UNSUPPORTED", "FRT_E_HIP",
@@ -82,6 +83,8 @@ _SIGNATURES = {
     "frt_packed_gemm_mxfp4_geglu_quant": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _p, _p, _i64]),
     "frt_quantize_mxfp4": (_i32, [_p, _i64, _i64, _p, _i64, _p, _i64, _p, _i64]),
+    "frt_packed_gemm_mxfp4_geglu_mxfp4": (_i32, [
+        _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i64, _p, _p, _i64, _p, _i64]),
     "frt_packed_gemm_mxfp4_qkv_rope": (_i32, [
         _p, _i64, _i64, _p, _i64, _p, _i64, _p, _p, _i32, _i32, _i32, _p, _p, _i64, _i64,
         _p, _p, _p]),
@@ -610,3 +613,21 @@ def frt_packed_gemm_mxfp4_qkv_rope(x4, xs, W4, S4, nh: int, kv: int, hd: int, ro
         _stream(stream), Mv, int(W4.shape[1]) * 2, _ptr(x4), _ld(x4), _ptr(xs), _ld(xs),
         _ptr(W4), _ptr(S4), int(nh), int(kv), int(hd), _ptr(bias_cat), _ptr(rope), int(P),
         int(T), _ptr(q_out), _ptr(k_cache), _ptr(v_cache)))
+
+
+def frt_packed_gemm_mxfp4_geglu_mxfp4(x4, xs, W4, S4, out_fp4, out_scale, bias_cat=None, *,
+                                      M: Optional[int] = None, stream=None) -> None:
+    """Merged gate/up GEMM on MXFP4 operands with the GEGLU quantised to
+    MXFP4 in its epilogue: codes into ``out_fp4 [M, H/2]``, scales into
+    ``out_scale [H/256, rows, 8]``."""
+    for t, nme in ((x4, "x4"), (xs, "xs"), (W4, "W4"), (S4, "S4"), (out_fp4, "out_fp4"),
+                   (out_scale, "out_scale")):
+        _u8_like(t, nme)
+    _bf16_like(bias_cat, "bias_cat")
+    if W4.shape[0] % 2:
+        raise ValueError("frt: W4 must hold 2H rows (gate, then up)")
+    Mv = x4.shape[0] if M is None else int(M)
+    _check(load_library().frt_packed_gemm_mxfp4_geglu_mxfp4(
+        _stream(stream), Mv, int(W4.shape[1]) * 2, _ptr(x4), _ld(x4), _ptr(xs), _ld(xs),
+        _ptr(W4), _ptr(S4), int(W4.shape[0] // 2), _ptr(bias_cat), _ptr(out_fp4), _ld(out_fp4),
+        _ptr(out_scale), _ld(out_scale)))

@@ -631,34 +631,44 @@ int frt_packed_gemm_mxfp4_split(void* stream, int64_t M, int64_t K, const uint8_
   return hip_status(frt::launch_gemm_mxfp4(a, (hipStream_t)stream), "gemm_mxfp4 launch");
 }
 
-int frt_packed_gemm_mxfp4_geglu_quant(void* stream, int64_t M, int64_t K, const uint8_t* x4, int64_t ld_x4,
-                                      const uint8_t* xs, int64_t ld_xs, const uint8_t* W4, const uint8_t* S4,
-                                      int64_t H, const uint16_t* bias_cat, const float* out_scale, uint8_t* out_fp8,
-                                      int64_t ld_out) {
-  if (M < 0) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: M=%lld < 0", (long long)M);
+namespace {
+
+// The MXFP4 gate/up GEMM with the GEGLU epilogue: FP8 codes at out_scale
+// (out_fp8) or MXFP4 codes + block scales (out_fp4, out_sc).
+int mx_geglu(const char* who, void* stream, int64_t M, int64_t K, const uint8_t* x4, int64_t ld_x4,
+             const uint8_t* xs, int64_t ld_xs, const uint8_t* W4, const uint8_t* S4, int64_t H,
+             const uint16_t* bias_cat, const float* out_scale, uint8_t* out_fp8, uint8_t* out_fp4, int64_t ld_out,
+             uint8_t* out_sc, int64_t ld_sc) {
+  const bool mxo = out_fp4 != nullptr;
+  if (M < 0) return refuse(FRT_E_INVALID, "%s: M=%lld < 0", who, (long long)M);
   if (K < 512 || K > 16384 || K % 256)
-    return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: K=%lld must be a multiple of 256 in [512, 16384]", (long long)K);
-  if (H < 1) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: H < 1");
-  if (M > (1 << 24) || 2 * H > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "gemm_mxfp4_geglu: M or 2H too large");
-  if (x4 == nullptr || xs == nullptr || W4 == nullptr || S4 == nullptr || out_scale == nullptr || out_fp8 == nullptr)
-    return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: x4, xs, W4, S4, out_scale and out_fp8 are required");
+    return refuse(FRT_E_INVALID, "%s: K=%lld must be a multiple of 256 in [512, 16384]", who, (long long)K);
+  if (H < 1 || (mxo && H % 256))
+    return refuse(FRT_E_INVALID, "%s: H=%lld must be >= 1%s", who, (long long)H, mxo ? " and a multiple of 256" : "");
+  if (M > (1 << 24) || 2 * H > (1 << 24)) return refuse(FRT_E_UNSUPPORTED, "%s: M or 2H too large", who);
+  if (x4 == nullptr || xs == nullptr || W4 == nullptr || S4 == nullptr ||
+      (mxo ? out_sc == nullptr : (out_scale == nullptr || out_fp8 == nullptr)))
+    return refuse(FRT_E_INVALID, "%s: x4, xs, W4, S4 and the outputs%s are required", who,
+                  mxo ? "" : " (with out_scale)");
   const int64_t kb = K / 2;
-  if (ld_x4 < kb || ld_x4 % 16) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: ld_x4 must be >= K/2 and a multiple of 16");
-  if (!aligned(x4, 16) || !aligned(W4, 16))
-    return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: x4 and W4 must be 16-byte aligned");
+  if (ld_x4 < kb || ld_x4 % 16) return refuse(FRT_E_INVALID, "%s: ld_x4 must be >= K/2 and a multiple of 16", who);
+  if (!aligned(x4, 16) || !aligned(W4, 16)) return refuse(FRT_E_INVALID, "%s: x4 and W4 must be 16-byte aligned", who);
   if (ld_xs < 8 * M || !aligned(xs, 4) || ld_xs % 4 || !aligned(S4, 4))
-    return refuse(FRT_E_INVALID,
-                  "gemm_mxfp4_geglu: scales 4-byte aligned, ld_xs (run stride) >= 8*M and a multiple of 4");
+    return refuse(FRT_E_INVALID, "%s: scales 4-byte aligned, ld_xs (run stride) >= 8*M and a multiple of 4", who);
   if ((M - 1) * ld_x4 + kb > (int64_t)0x7fffffff || 2 * H * kb > (int64_t)0x7fffffff)
-    return refuse(FRT_E_UNSUPPORTED, "gemm_mxfp4_geglu: operand larger than 2 GiB");
-  if (ld_out < H) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: ld_out < H");
+    return refuse(FRT_E_UNSUPPORTED, "%s: operand larger than 2 GiB", who);
+  if (mxo && (ld_out < H / 2 || ld_out % 4 || !aligned(out_fp4, 4) || ld_sc < 8 * M))
+    return refuse(FRT_E_INVALID, "%s: out_fp4 4-byte aligned, ld_out >= H/2 and a multiple of 4, ld_sc >= 8*M", who);
+  if (!mxo && ld_out < H) return refuse(FRT_E_INVALID, "%s: ld_out < H", who);
   if (M == 0) return ok();
-  const Range o = span(out_fp8, M, H, ld_out, 1);
   const Range in[] = {span(x4, M, kb, ld_x4, 1),           span(W4, 2 * H, kb, kb, 1),
                       span(bias_cat, 1, 2 * H, 2 * H, 2),  span(out_scale, 1, 1, 1, 4),
                       span(xs, K / 256, 8 * M, ld_xs, 1),  span(S4, K / 256, 16 * H, 16 * H, 1)};
+  const Range o = mxo ? span(out_fp4, M, H / 2, ld_out, 1) : span(out_fp8, M, H, ld_out, 1);
+  const Range so = span(out_sc, H / 256, 8 * M, ld_sc, 1);
   for (int i = 0; i < 6; ++i)
-    if (overlap(o, in[i])) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu: out_fp8 overlaps input %d", i);
+    if (overlap(o, in[i]) || overlap(so, in[i])) return refuse(FRT_E_INVALID, "%s: an output overlaps input %d", who, i);
+  if (overlap(o, so)) return refuse(FRT_E_INVALID, "%s: the codes overlap the scales", who);
   frt::GemmArgs a{};
   a.x = x4;
   a.ld_x = ld_x4;
@@ -668,13 +678,39 @@ int frt_packed_gemm_mxfp4_geglu_quant(void* stream, int64_t M, int64_t K, const 
   a.N = (int)(2 * H);
   a.K = (int)K;
   a.H = (int)H;
-  a.q8 = out_fp8;
-  a.ld_q8 = ld_out;
-  a.q_scale = out_scale;
+  if (mxo) {
+    a.q4 = out_fp4;
+    a.ld_q4 = ld_out;
+    a.sc4 = out_sc;
+    a.ld_sc4 = ld_sc;
+  } else {
+    a.q8 = out_fp8;
+    a.ld_q8 = ld_out;
+    a.q_scale = out_scale;
+  }
   a.sa = xs;
   a.ld_sa = ld_xs;
   a.sb = S4;
-  return hip_status(frt::launch_gemm_mxfp4_geglu(a, (hipStream_t)stream), "gemm_mxfp4_geglu launch");
+  return hip_status(frt::launch_gemm_mxfp4_geglu(a, (hipStream_t)stream), who);
+}
+
+}  // namespace
+
+int frt_packed_gemm_mxfp4_geglu_quant(void* stream, int64_t M, int64_t K, const uint8_t* x4, int64_t ld_x4,
+                                      const uint8_t* xs, int64_t ld_xs, const uint8_t* W4, const uint8_t* S4,
+                                      int64_t H, const uint16_t* bias_cat, const float* out_scale, uint8_t* out_fp8,
+                                      int64_t ld_out) {
+  return mx_geglu("gemm_mxfp4_geglu", stream, M, K, x4, ld_x4, xs, ld_xs, W4, S4, H, bias_cat, out_scale, out_fp8,
+                  nullptr, ld_out, nullptr, 0);
+}
+
+int frt_packed_gemm_mxfp4_geglu_mxfp4(void* stream, int64_t M, int64_t K, const uint8_t* x4, int64_t ld_x4,
+                                      const uint8_t* xs, int64_t ld_xs, const uint8_t* W4, const uint8_t* S4,
+                                      int64_t H, const uint16_t* bias_cat, uint8_t* out_fp4, int64_t ld_out,
+                                      uint8_t* out_scale, int64_t ld_sc) {
+  if (out_fp4 == nullptr) return refuse(FRT_E_INVALID, "gemm_mxfp4_geglu_mxfp4: out_fp4 is required");
+  return mx_geglu("gemm_mxfp4_geglu_mxfp4", stream, M, K, x4, ld_x4, xs, ld_xs, W4, S4, H, bias_cat, nullptr, nullptr,
+                  out_fp4, ld_out, out_scale, ld_sc);
 }
 
 int frt_interleave_pairs_bf16(void* stream, int nheads, int hd, int64_t K, const uint16_t* src, uint16_t* dst) {

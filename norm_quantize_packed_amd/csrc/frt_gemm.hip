@@ -445,6 +445,52 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
     return;
   }
   if constexpr (GLU) {
+    if (a.q4 != nullptr) {
+      // GEGLU to MXFP4: a block scale needs the maximum over 32 consecutive
+      // columns, which the MFMA layout spreads over 32 lanes, so the wave's
+      // y tile goes through LDS (the stage ring, free once every wave is past
+      // its last fragment read) and comes back row-wise: 8 consecutive
+      // columns per lane, one 32-column block per quad, quantised as the
+      // standalone GEGLU -> MXFP4 kernel quantises them
+      static_assert(NJ == 2, "one 32-column gate block per wave");
+      constexpr int YR = MI * 32;  // rows of the wave's y tile (32 columns)
+      __syncthreads();
+      float* ys = reinterpret_cast<float*>(smem) + wave * YR * 32;
+      const int gc0 = n0 + (wn0 >> 1);  // the wave's first gate column
+      const float bg = (a.bias != nullptr && gc0 < a.H) ? bf16f(a.bias[gc0 + (lane & 31)]) : 0.0f;
+      const float bu = (a.bias != nullptr && gc0 < a.H) ? bf16f(a.bias[a.H + gc0 + (lane & 31)]) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const float vg = alpha * acc[i][0][r] + bg;
+          const float vu = alpha * acc[i][1][r] + bu;
+          ys[rl * 32 + (lane & 31)] =
+              gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < YR * 4 / 64; ++k) {
+        const int t = lane + 64 * k, rl = t >> 2, v = t & 3;
+        const float4 y0 = *reinterpret_cast<const float4*>(ys + rl * 32 + v * 8);
+        const float4 y1 = *reinterpret_cast<const float4*>(ys + rl * 32 + v * 8 + 4);
+        const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+        uint32_t am = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(fabsf(y[e])));
+        const uint32_t sbyte = e8m0_of_amax(quad_umax(am));
+        const uint32_t codes = mxfp4_pack8(y, sbyte);
+        const int m = m0 + wm0 + rl;
+        if (m < a.M && gc0 < a.H) {
+          const int64_t c = gc0 + v * 8;
+          *reinterpret_cast<uint32_t*>(a.q4 + (int64_t)m * a.ld_q4 + c / 2) = codes;
+          if (v == 0) a.sc4[e8m0_off(m, c / 32, a.ld_sc4)] = (uint8_t)sbyte;
+        }
+      }
+      return;
+    }
     // gate and up rounded to bf16 as the unfused GEMM output would be,
     // then the GEGLU quantiser of frt_ffn.hip
     const float qs = *a.q_scale, qr = 1.0f / qs;

@@ -89,6 +89,11 @@ struct GemmArgs {
   // with run stride ld_sa, sb with run stride 8 N
   const uint8_t* sa; int64_t ld_sa;
   const uint8_t* sb;
+  // GEGLU form with an MXFP4 output (q4 non-null, instead of q8): codes
+  // [M, ld_q4] two per byte, scales run-major [H/256][rows][8] with run
+  // stride ld_sc4; H % 256 == 0
+  uint8_t* q4; int64_t ld_q4;
+  uint8_t* sc4; int64_t ld_sc4;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

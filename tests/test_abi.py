@@ -355,6 +355,20 @@ def test_mxfp4_refusals(lib):
     assert geglu(out=FAKE + 3 * MB) == frt.FRT_E_INVALID  # over S4
     assert geglu(M=0) == frt.FRT_OK
 
+    def geglu4(K=512, **kw):
+        a = dict(stream=None, M=16, K=K, x4=FAKE, ld_x4=K // 2, xs=FAKE + MB, ld_xs=8 * 16,
+                 W4=FAKE + 2 * MB, S4=FAKE + 3 * MB, H=512, bias=None, out=FAKE + 40 * MB,
+                 ld_out=256, sc=FAKE + 41 * MB, ld_sc=8 * 16)
+        a.update(kw)
+        return lib.frt_packed_gemm_mxfp4_geglu_mxfp4(*a.values())
+    assert geglu4(H=384) == frt.FRT_E_INVALID              # H % 256
+    assert geglu4(out=None) == frt.FRT_E_INVALID
+    assert geglu4(sc=None) == frt.FRT_E_INVALID
+    assert geglu4(ld_out=200) == frt.FRT_E_INVALID         # ld_out < H/2
+    assert geglu4(ld_sc=100) == frt.FRT_E_INVALID          # run stride < 8*M
+    assert geglu4(sc=FAKE + 40 * MB + 64) == frt.FRT_E_INVALID   # scales over the codes
+    assert geglu4(M=0) == frt.FRT_OK
+
     def q4(fn, W=512, **kw):
         a = dict(stream=None, M=16, W=W, x=FAKE, ld_x=(2 if fn.endswith("geglu_quant_mxfp4") else 1) * W,
                  out=FAKE + 2 * MB, ld_out=W // 2, sc=FAKE + 3 * MB, ld_sc=8 * 16)

@@ -306,3 +306,36 @@ def test_gemm_mxfp4_rope_vs_unfused_and_oracle(M, K, nh, kv, hd, P, bias):
     assert np.array_equal(host_bf16(q).reshape(rq.shape), rq)
     assert np.array_equal(host_bf16(kc), rk)
     assert np.array_equal(host_bf16(vc), rv)
+
+
+@pytest.mark.parametrize("M,K,H,bias", [
+    (256, 2048, 8192, False),   # the decoder layer's gate/up (128x128 plan)
+    (600, 1024, 768, True),     # 64x64 plan, ragged M
+    (40, 1280, 256, True),      # small M, K an odd number of runs
+    (1, 512, 512, False),
+])
+def test_gemm_mxfp4_geglu_to_mxfp4_vs_unfused(M, K, H, bias):
+    """The MXFP4 gate/up GEMM with the GEGLU quantised to MXFP4 in its
+    epilogue: codes and scales equal the split MXFP4 GEMM's bf16 output
+    passed through the standalone GEGLU -> MXFP4 kernel bit for bit (whose
+    agreement with the oracle the GEGLU -> MXFP4 test checks)."""
+    a = wl.random_bf16(1900 + M, (M, K), 1.0)
+    ac, as_ = mxfp4.quantize_mxfp4(codecs.bf16_to_f32(a))
+    Wg = wl.random_bf16(1901 + H, (H, K), 0.02)
+    Wu = wl.random_bf16(1902 + H, (H, K), 0.02)
+    bs = [wl.random_bf16(1903, (H,), 0.02), wl.random_bf16(1904, (H,), 0.02)] if bias else None
+    w4, ws4, bc = _gpu_pack([Wg, Wu], bs)
+    x4, xs = dev_u8(mxfp4.pack_nibbles(ac)), dev_u8(mxfp4.scales_to_gemm_order(as_))
+    dw4, dws4 = dev_u8(w4), dev_u8(ws4)
+    db = None if bc is None else dev_bf16(bc)
+    gu = torch.empty((M, 2 * H), dtype=torch.bfloat16, device="cuda")
+    frt.frt_packed_gemm_mxfp4_split(x4, xs, dw4, dws4, [gu], [2 * H], db)
+    u4, us = _mx_out(M, H)
+    frt.frt_geglu_quant_mxfp4(gu, H, u4.view, us.view)
+    f4, fs = _mx_out(M, H)
+    frt.frt_packed_gemm_mxfp4_geglu_mxfp4(x4, xs, dw4, dws4, f4.view, fs.view, db)
+    torch.cuda.synchronize()
+    for g in (u4, us, f4, fs):
+        g.check_guards()
+    assert np.array_equal(host_u8(fs.view), host_u8(us.view)), "block scales differ"
+    assert np.array_equal(host_u8(f4.view), host_u8(u4.view)), "codes differ"
