@@ -38,7 +38,9 @@ GEMMs take MXFP4 weights packed at bind; metric and roofline are the same,
 with the FP4 matrix-core peak. With ``--ffn`` (workload 2) the MXFP4
 gate/up GEMM carries the GEGLU quantiser and the down projection stays in
 static FP8; ``--fp4-full`` runs the down projection in MXFP4 as well (the
-bf16 gate|up output, the GEGLU quantised to MXFP4, the MXFP4 down GEMM).
+gate/up GEMM's epilogue quantises the GEGLU to MXFP4 for the MXFP4 down
+GEMM; the unfused bf16 gate|up GEMM + GEGLU -> MXFP4 kernel is timed beside
+it).
 ``--oproj`` quantises the attention output to MXFP4 for an MXFP4 O
 projection, and ``--rope`` gives the MXFP4 QKV GEMM the split + RoPE +
 KV-cache epilogue.
@@ -378,8 +380,9 @@ def make_outputs(w, rows, packs, torch, ffn=None):
         o["gu"] = torch.empty(rows, 2 * H, dtype=torch.bfloat16, device="cuda")
         o["hid8_unfused"] = torch.empty(rows, H, dtype=torch.uint8, device="cuda")
         if ffn["full"]:
-            o["hid4"] = (torch.empty(rows, H // 2, dtype=torch.uint8, device="cuda"),
-                         torch.empty(H // 256, rows, 8, dtype=torch.uint8, device="cuda"))
+            for k in ("hid4", "hid4_unfused"):
+                o[k] = (torch.empty(rows, H // 2, dtype=torch.uint8, device="cuda"),
+                        torch.empty(H // 256, rows, 8, dtype=torch.uint8, device="cuda"))
     return o
 
 
@@ -407,10 +410,9 @@ def step_launches_mx(w, s, outs, rows, frt, eps):
             bias_cat=p1["bias"])))
         f = s.get("ffn")
         if f is not None and f["full"]:
-            H, h4 = f["H"], outs["hid4"]
-            L[-1] = ("gemm2_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
-                o4[1][0], o4[1][1], p1["W8"], p1["ws"], [outs["gu"]], [2 * H], bias_cat=p1["bias"]))
-            L.append(("geglu_mx", lambda: frt.frt_geglu_quant_mxfp4(outs["gu"], H, h4[0], h4[1])))
+            h4 = outs["hid4"]
+            L[-1] = ("gemm2_mx_geglu4", lambda: frt.frt_packed_gemm_mxfp4_geglu_mxfp4(
+                o4[1][0], o4[1][1], p1["W8"], p1["ws"], h4[0], h4[1], bias_cat=p1["bias"]))
             L.append(("gemm_down_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
                 h4[0], h4[1], f["W8"], f["ws"], [outs["dn"]], [w.D])))
         elif f is not None:
@@ -489,7 +491,14 @@ def unfused_launches(w, s, act, outs, frt, mx=False):
     cache kernel."""
     L = []
     f = s.get("ffn")
-    if f is not None and not f["full"]:
+    if f is not None and f["full"]:
+        pl = s["packs"][-1]
+        H, h4 = f["H"], outs["hid4_unfused"]
+        gx4, gxs = outs["x4"][-1]
+        L.append(("gateup_bf16_mx", lambda: frt.frt_packed_gemm_mxfp4_split(
+            gx4, gxs, pl["W8"], pl["ws"], [outs["gu"]], [2 * H], bias_cat=pl["bias"])))
+        L.append(("geglu_mx", lambda: frt.frt_geglu_quant_mxfp4(outs["gu"], H, h4[0], h4[1])))
+    elif f is not None:
         pl = s["packs"][-1]
         H = f["H"]
         if mx:
@@ -536,10 +545,11 @@ def kernel_work(w, kind, rows, packs, ffn=None, rope=None, oproj=None):
         if kind == "geglu_mx":          # bf16 [M, 2H] in, codes + scales out
             return rows * 2 * H * 2 + rows * (H // 2 + H // 32), 0.0
         return rows * (H // 2 + H // 32) + D * (H // 2 + H // 32) + rows * D * 2, 2.0 * rows * D * H
-    if ffn is not None and kind in ("gemm2_mx_geglu", "gateup_bf16_mx"):
+    if ffn is not None and kind in ("gemm2_mx_geglu", "gemm2_mx_geglu4", "gateup_bf16_mx"):
         H = ffn["H"]
         bias = 2 * H * 2 if packs[-1]["bias"] is not None else 0
-        out = rows * H if kind == "gemm2_mx_geglu" else rows * 2 * H * 2
+        out = {"gemm2_mx_geglu": rows * H, "gemm2_mx_geglu4": rows * (H // 2 + H // 32)}.get(
+            kind, rows * 2 * H * 2)
         return (rows * (D // 2 + D // 32) + 2 * H * (D // 2 + D // 32) + out + bias,
                 2.0 * rows * 2 * H * D)
     if kind.endswith("_mx"):
