@@ -448,14 +448,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
     if (a.q4 != nullptr) {
       // GEGLU to MXFP4: a block scale needs the maximum over 32 consecutive
       // columns, which the MFMA layout spreads over 32 lanes, so the wave's
-      // y tile goes through LDS (the stage ring, free once every wave is past
-      // its last fragment read) and comes back row-wise: 8 consecutive
+      // y tile goes through LDS and comes back row-wise: 8 consecutive
       // columns per lane, one 32-column block per quad, quantised as the
-      // standalone GEGLU -> MXFP4 kernel quantises them
+      // standalone GEGLU -> MXFP4 kernel quantises them. The tiles go to
+      // ring slot KT % NS, whose last stage (KT - NS) every wave finished
+      // reading before a later barrier, when they fit in it; else to the
+      // whole ring after a barrier. Each wave reads back only what it wrote.
       static_assert(NJ == 2, "one 32-column gate block per wave");
       constexpr int YR = MI * 32;  // rows of the wave's y tile (32 columns)
-      __syncthreads();
-      float* ys = reinterpret_cast<float*>(smem) + wave * YR * 32;
+      constexpr bool ONE_SLOT = NW * YR * 32 * 4 <= STAGE;
+      uint8_t* ybase = smem;
+      if constexpr (ONE_SLOT)
+        ybase = smem + (KT % NS) * STAGE;
+      else
+        __syncthreads();
+      float* ys = reinterpret_cast<float*>(ybase) + wave * YR * 32;
       const int gc0 = n0 + (wn0 >> 1);  // the wave's first gate column
       const float bg = (a.bias != nullptr && gc0 < a.H) ? bf16f(a.bias[gc0 + (lane & 31)]) : 0.0f;
       const float bu = (a.bias != nullptr && gc0 < a.H) ? bf16f(a.bias[a.H + gc0 + (lane & 31)]) : 0.0f;
@@ -470,7 +477,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
               gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
         }
       }
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));  // this wave's LDS writes done
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int k = 0; k < YR * 4 / 64; ++k) {
         const int t = lane + 64 * k, rl = t >> 2, v = t & 3;
