@@ -639,7 +639,10 @@ hipError_t launch_planned(const GemmArgs& a, hipStream_t st) {
   }
   // rows past M are not loaded (at M <= 16, 8 of every 12 load
   // instructions would only fetch zeros): M = 1 9.3 -> 8.8 us, M = 16
-  // 9.8 -> 9.3 us for 6144 x 4096 weights
+  // 9.8 -> 9.3 us for 6144 x 4096 weights. At M <= 16 a three-deep ring of
+  // 512-deep stages keeps more of the weight stream in flight (M = 1
+  // 8.75 -> 8.50 us, M = 16 9.23 -> 9.05 us; it loses at M = 32 and 64)
+  if (a.M <= 16 && a.K % 512 == 0) return launch_tiles<64, 32, 32, 32, 3, 1, 4, 16, false, ROPE>(a, st);
   if (a.M <= 16) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 16, false, ROPE>(a, st);
   if (a.M <= 32) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 32, false, ROPE>(a, st);
   return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, ROPE>(a, st);
@@ -656,10 +659,12 @@ hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st) { return launch_p
 // waves (the sixteen-wave form exceeds its 128 registers with the scale
 // ring), 64x64 and 64x32. Half the bytes per row as FP8 move the balance
 // toward larger tiles only through plan_cost's row counts. The 64x32 plans
-// stage 512 K-elements (two runs) when K allows it, else one run in a ring
-// twice as deep (the same K in flight).
+// stage 1024 K-elements (four runs) in a three-deep ring when K allows it
+// (6144 x 4096 weights: M = 1 7.7 -> 6.9 us, M = 16 8.2 -> 7.3 us, M = 64
+// level), else 512 in a four-deep ring, else one run in a seven-deep ring.
 template <int AE, bool ROPE>
 hipError_t launch_mx_narrow(const GemmArgs& a, hipStream_t st) {
+  if (a.K % 1024 == 0) return launch_tiles<64, 32, 32, 32, 3, 1, 4, AE, false, ROPE, true>(a, st);
   if (a.K % 512 == 0) return launch_tiles<64, 32, 32, 32, 4, 1, 2, AE, false, ROPE, true>(a, st);
   return launch_tiles<64, 32, 32, 32, 7, 1, 1, AE, false, ROPE, true>(a, st);
 }
