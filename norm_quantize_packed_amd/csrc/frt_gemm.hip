@@ -125,11 +125,15 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // K half l / 32 = exactly one scale block). The scales are stored run-major,
 // [K/256][rows][8] (run stride ld_sa for x, 8 N for W), each run of 8 blocks
 // (256 K-elements) in the order 0, 2, 4, 6, 1, 3, 5, 7: the lanes of K half
-// h load one dword holding their blocks h, 2 + h, 4 + h, 6 + h (a 32-row
+// h take one dword holding their blocks h, 2 + h, 4 + h, 6 + h (a 32-row
 // block's dwords for one run are 256 contiguous bytes) and step s selects
-// byte s.
-// The scales of a stage are loaded into registers by the same issue call
-// as its tiles (so the wait counts cover them); alpha is 1.
+// byte s. Each run's scales of the tile's rows are staged in LDS beside the
+// tiles: one direct dword load per 32-row block (A rows, then the B rows in
+// tile order), issued by the same call as the tiles and spread over the
+// waves (the wait counts cover them), and read back with the fragments, so
+// a block's scales are fetched once per block, not once per wave using them. Rows past M or N
+// fetch zeros (each run has its own record count); their results are never
+// stored. alpha is 1.
 template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB, int AE = BM,
           bool GLU = false, bool ROPE = false, bool FP4 = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a) {
@@ -146,10 +150,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   constexpr int STAGE = NSUB * SUBB;   // one stage = NSUB sub-buffers
   constexpr int KST = 128 * NSUB;      // K bytes per stage
   static_assert(!FP4 || !KTAIL, "MXFP4 form: whole stages");
-  constexpr int SCL = FP4 ? MI + NJ : 0;  // scale loads per sub-buffer
+  // MXFP4 scale staging: AER A rows (AE rounded up to 32) and BN B rows of
+  // 8 bytes per run, SLT 32-row loads per sub-buffer; every wave issues SCL
+  // of them, wave w load k being block min(w + k NW, SLT - 1) (a repeated
+  // block writes the same bytes to the same place)
+  constexpr int AER = (AE + 31) / 32 * 32;
+  constexpr int SLT = FP4 ? AER / 32 + BN / 32 : 0;
+  constexpr int SCB = FP4 ? (AER + BN) * 8 : 0;  // scale bytes per sub-buffer
+  constexpr int SCL = (SLT + NW - 1) / NW;
+  static_assert(BN % 32 == 0, "32-row scale loads");
   static_assert(NS >= 2 && NSUB * (LPW + SCL) * (NS - 2) <= 63, "ring depth vs vmcnt range");
-  static_assert(NS * STAGE <= 160 * 1024, "ring exceeds LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  constexpr int SCBASE = NS * STAGE;  // the scale area follows the ring
+  static_assert(NS * (STAGE + NSUB * SCB) <= 160 * 1024, "ring exceeds LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * (STAGE + NSUB * SCB)];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -184,22 +197,29 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
   const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)Kb;
   const int KT = (Kb + KST - 1) / KST;
-  // MXFP4 scales: this lane's MFMA rows (rows past M or N read the last
-  // row: their results are never stored), a ring slot per stage
-  constexpr int SNS = FP4 ? NS : 1, SNB = FP4 ? NSUB : 1;
-  unsigned scA[SNS][SNB][FP4 ? MI : 1], scB[SNS][SNB][FP4 ? NJ : 1];
-  const uint8_t* sa_row[FP4 ? MI : 1];
-  const uint8_t* sb_row[FP4 ? NJ : 1];
+  // MXFP4 scales of the stage being multiplied, read from LDS with the
+  // fragments: sub-buffer q, this lane's A (B) row block i (j)
+  unsigned sA[FP4 ? NSUB : 1][FP4 ? MI : 1], sB[FP4 ? NSUB : 1][FP4 ? NJ : 1];
+  // this wave's scale loads, chosen once by uniform selects: source buffer,
+  // run stride, per-run record count, byte offset of the block's first row
+  // and LDS offset; under GLU B block g is gate (g even) or up rows of the
+  // 32-column pair g / 2
+  constexpr int SCK = FP4 ? SCL : 1;
+  const uint8_t* sc_src[SCK];
+  int64_t sc_run[SCK];
+  uint32_t sc_rec[SCK], sc_off[SCK], sc_lds[SCK];
   if constexpr (FP4) {
-    const int h4 = (lane >> 5) * 4;  // this K half's dword of a run
 #pragma unroll
-    for (int i = 0; i < MI; ++i) sa_row[i] = a.sa + (int64_t)min(m0 + wm0 + i * 32 + (lane & 31), a.M - 1) * 8 + h4;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      // tile-local B row t; under GLU the gate or up row it was loaded from
-      const int t = wn0 + j * 32 + (lane & 31);
-      const int row = GLU ? ((t >> 5) & 1) * a.H + n0 + (t >> 6) * 32 + (t & 31) : n0 + t;
-      sb_row[j] = a.sb + (int64_t)min(row, a.N - 1) * 8 + h4;
+    for (int k = 0; k < SCL; ++k) {
+      const int s = min(wave + k * NW, SLT - 1);
+      const bool isA = s < AER / 32;
+      const int g = s - AER / 32;
+      const int row = isA ? m0 + s * 32 : GLU ? (g & 1) * a.H + n0 + (g >> 1) * 32 : n0 + g * 32;
+      sc_src[k] = isA ? a.sa : a.sb;
+      sc_run[k] = isA ? a.ld_sa : (int64_t)a.N * 8;
+      sc_rec[k] = (uint32_t)(isA ? a.M : a.N) * 8u;
+      sc_off[k] = (uint32_t)row * 8u;
+      sc_lds[k] = isA ? s * 256 : AER * 8 + g * 256;
     }
   }
   // slot SL (= step mod NS) is a compile-time constant in every use, so all
@@ -236,14 +256,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
           __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
       }
       if constexpr (FP4) {
-        // this lane's 4 block scales of the sub-buffer (run kt * NSUB + q)
+        // the scales of run kt * NSUB + q: 32 rows (256 bytes) per load
         const int64_t run = kt * NSUB + q;
+        uint8_t* sdst = smem + SCBASE + (SL * NSUB + q) * SCB;
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-          scA[SL][q][i] = *reinterpret_cast<const unsigned*>(sa_row[i] + run * a.ld_sa);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          scB[SL][q][j] = *reinterpret_cast<const unsigned*>(sb_row[j] + run * ((int64_t)a.N * 8));
+        for (int k = 0; k < SCL; ++k) {
+          const __amdgpu_buffer_rsrc_t r = make_rsrc(sc_src[k] + run * sc_run[k], sc_rec[k]);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(sdst + sc_lds[k]), 4, lane * 4, sc_off[k], 0, 0);
+        }
       }
     }
   };
@@ -252,6 +272,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const int sw = (lrow32 >> 1) & 7;  // (row >> 1) & 7 for rows 32k + lrow32
   const uint8_t* lbase0 = smem + lrow32 * 128 + ((((lane >> 5) * 2) ^ sw) * 16);
   const uint8_t* lbase1 = smem + lrow32 * 128 + ((((lane >> 5) * 2 + 4) ^ sw) * 16);
+  // this lane's scale dword within a 32-row block: row lrow32, K half l / 32
+  const uint8_t* sbase = smem + SCBASE + lrow32 * 8 + (lane >> 5) * 4;
   auto read_frags = [&](auto SLC, auto SUBC, auto* af, auto* bf) {
     constexpr int SL = decltype(SLC)::value, SUB = decltype(SUBC)::value;
     if constexpr (FP4) {
@@ -262,6 +284,18 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const v4i*>(lb + (BM + wn0 + j * 32) * 128);
 #pragma unroll
       for (int i = 0; i < MI; ++i) af[i] = *reinterpret_cast<const v4i*>(lb + (wm0 + i * 32) * 128);
+      if constexpr ((SUB & 3) == 0) {
+        // the sub-buffer's scales; A blocks past the AER staged rows (rows
+        // past M) take the last staged block
+        constexpr int Q = SUB >> 2;
+        const uint8_t* sp = sbase + (SL * NSUB + Q) * SCB;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+          sA[Q][i] = *reinterpret_cast<const unsigned*>(sp + min(wm0 + i * 32, AER - 32) * 8);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          sB[Q][j] = *reinterpret_cast<const unsigned*>(sp + (AER + wn0 + j * 32) * 8);
+      }
       return;
     } else {
     const uint8_t* lb = ((SUB & 1) ? lbase1 : lbase0) + SL * STAGE + (SUB >> 1) * SUBB;
@@ -326,7 +360,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
         for (int r = 0; r < 16; ++r) acc2[i][j][r] = 0.0f;
   }
   auto mfmas = [&](const frag_t* af, const frag_t* bf, auto ACC, auto SLC, auto SUBC) {
-    constexpr int SL = decltype(SLC)::value, SUB = decltype(SUBC)::value;
+    constexpr int SUB = decltype(SUBC)::value;
 #pragma unroll
     for (int q = 0; q < MI * NJ; ++q) {
       const int i = q / NJ, j = q % NJ;
@@ -336,8 +370,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
         constexpr int s = SUB & 3, sb = SUB >> 2;
         const v8i a8 = {af[i][0], af[i][1], af[i][2], af[i][3], 0, 0, 0, 0};
         const v8i b8 = {bf[j][0], bf[j][1], bf[j][2], bf[j][3], 0, 0, 0, 0};
-        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, s, (int)scA[SL][sb][i], s,
-                                                           (int)scB[SL][sb][j]);
+        c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, s, (int)sA[sb][i], s,
+                                                           (int)sB[sb][j]);
       } else {
         c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], c, 0, 0, 0, 0, 0, 0);
       }
@@ -656,8 +690,7 @@ hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st) { return launch_p
 
 // MXFP4 plans (K % 256 == 0: whole 256-element stages): the small-M plan
 // for M <= 64; above, the least per-CU load among 128x128 of eight 32x64
-// waves (the sixteen-wave form exceeds its 128 registers with the scale
-// ring), 64x64 and 64x32. Half the bytes per row as FP8 move the balance
+// waves, 64x64 and 64x32. Half the bytes per row as FP8 move the balance
 // toward larger tiles only through plan_cost's row counts. The 64x32 plans
 // stage 1024 K-elements (four runs) in a three-deep ring when K allows it
 // (6144 x 4096 weights: M = 1 7.7 -> 6.9 us, M = 16 8.2 -> 7.3 us, M = 64
