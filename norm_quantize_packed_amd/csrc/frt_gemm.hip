@@ -131,9 +131,9 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // tiles: one direct dword load per 32-row block (A rows, then the B rows in
 // tile order), issued by the same call as the tiles and spread over the
 // waves (the wait counts cover them), and read back with the fragments, so
-// a block's scales are fetched once per block, not once per wave using them. Rows past M or N
-// fetch zeros (each run has its own record count); their results are never
-// stored. alpha is 1.
+// a block's scales are fetched once, not once per wave that uses them. Rows
+// past M or N fetch zeros (each run has its own record count); their results
+// are never stored. alpha is 1.
 template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB, int AE = BM,
           bool GLU = false, bool ROPE = false, bool FP4 = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a) {
@@ -208,6 +208,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const uint8_t* sc_src[SCK];
   int64_t sc_run[SCK];
   uint32_t sc_rec[SCK], sc_off[SCK], sc_lds[SCK];
+  // a block lands K-half-major (LDS dword l holds row l % 32, half l / 32),
+  // so the lanes of the MFMA layout read consecutive dwords
+  const uint32_t sc_lane = (uint32_t)((lane & 31) * 8 + (lane >> 5) * 4);
   if constexpr (FP4) {
 #pragma unroll
     for (int k = 0; k < SCL; ++k) {
@@ -262,7 +265,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 #pragma unroll
         for (int k = 0; k < SCL; ++k) {
           const __amdgpu_buffer_rsrc_t r = make_rsrc(sc_src[k] + run * sc_run[k], sc_rec[k]);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(sdst + sc_lds[k]), 4, lane * 4, sc_off[k], 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(sdst + sc_lds[k]), 4, sc_lane, sc_off[k], 0, 0);
         }
       }
     }
@@ -273,7 +276,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const uint8_t* lbase0 = smem + lrow32 * 128 + ((((lane >> 5) * 2) ^ sw) * 16);
   const uint8_t* lbase1 = smem + lrow32 * 128 + ((((lane >> 5) * 2 + 4) ^ sw) * 16);
   // this lane's scale dword within a 32-row block: row lrow32, K half l / 32
-  const uint8_t* sbase = smem + SCBASE + lrow32 * 8 + (lane >> 5) * 4;
+  const uint8_t* sbase = smem + SCBASE + lane * 4;
   auto read_frags = [&](auto SLC, auto SUBC, auto* af, auto* bf) {
     constexpr int SL = decltype(SLC)::value, SUB = decltype(SUBC)::value;
     if constexpr (FP4) {
