@@ -990,7 +990,8 @@ def main():
     norm_bytes = sum(kernel_work(w, k, rows, packs, ffn, rp, op)[0] for k in kinds if k.startswith("norm"))
     norm_us = sum(r["us"] for r in table if r["kernel"].startswith("norm"))
     dom = max((r for r in table if r["kernel"] in kinds), key=lambda r: r["us"])
-    traffic = load_traffic(a.workload, dom["kernel"]) if a.rows is None else None
+    # (records cover the full workload shapes: not a --rows or --tp variant)
+    traffic = load_traffic(a.workload, dom["kernel"]) if a.rows is None and a.tp == 1 else None
     if dom["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dom["TFLOP/s"],
                 "peak": FP4_PEAK_TFLOPS if "_mx" in dom["kernel"] else FP8_PEAK_TFLOPS,
