@@ -106,6 +106,12 @@ def test_ada_norm_mxfp4_vs_oracle(M, D):
     (40, 512, 1280, False),
     (200, 512, 768, False),
     (256, 2560, 1280, False),   # 64x64 plan
+    # N not a multiple of 32: the last 32-row block of B scales is partial
+    # (rows past N fetch zeros); one case per plan
+    (300, 16300, 512, True),    # 128x128 plan
+    (600, 1000, 1024, False),   # 64x64 plan
+    (333, 1000, 512, True),     # 64x32 plan
+    (5, 1000, 768, False),      # small-M plan
 ])
 def test_gemm_mxfp4_vs_oracle(M, N, K, bias):
     a = wl.random_bf16(1400 + M, (M, K), 1.0)
@@ -139,6 +145,8 @@ def test_gemm_mxfp4_vs_oracle(M, N, K, bias):
     (600, 1024, 704, False),    # 64x64 plan, ragged M and H
     (40, 1280, 320, True),      # small M; K an odd number of 256-element runs
     (1, 512, 64, False),        # one row, one tile
+    (300, 512, 8100, False),    # 128x128 plan, H not a multiple of 32
+    (300, 512, 1000, True),     # 64x64 plan, H not a multiple of 32
 ])
 def test_gemm_mxfp4_geglu_vs_unfused_and_oracle(M, K, H, bias):
     """The MXFP4 gate/up GEMM with the GEGLU quantiser as its epilogue: its
