@@ -14,7 +14,8 @@ Python binding is larger than a step's GPU time) and replayed; the timed
 region is bracketed by device synchronisation. Each step reads a different
 copy of the weights and activations, rotating through enough copies that the
 working set is at least 512 MiB, so the 256 MiB Infinity Cache cannot serve
-repeated weight streams. Per-kernel durations come from HIP events around
+repeated weight streams (``--warm`` drops the rotation and labels the line:
+the cache-served figure). Per-kernel durations come from HIP events around
 graph replays of that kernel alone on the launch stream (same rotation).
 
 Output: one JSON line on stdout (metric, value, roofline of the dominant
@@ -78,6 +79,7 @@ FP8_PEAK_TFLOPS = 5000.0       # dense FP8 MFMA (datasheet 5.0 PFLOP/s)
 FP4_PEAK_TFLOPS = 10100.0      # dense FP4 MFMA (datasheet 10.1 PFLOP/s)
 RIDGE = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 ROTATE_BYTES = 512 << 20
+WARM_REPEATS = 16   # --warm: the one buffer set repeated this often per graph
 METRIC = "packed FP8 GEMM TFLOP/s (%MFMA peak) + norm-quant GB/s (%HBM peak)"
 
 
@@ -105,6 +107,9 @@ def parse():
                         "caches through its epilogue")
     p.add_argument("--tp", type=int, default=1,
                    help="workloads 3, 5: time one rank's share of a T-way column-parallel GEMM")
+    p.add_argument("--warm", action="store_true",
+                   help="one set of buffers, no rotation: repeats may be served from the "
+                        "Infinity Cache (a labelled warm figure, not the rotated one)")
     p.add_argument("--kernel-reps", type=int, default=20)
     p.add_argument("--hbm-calibration", action="store_true",
                    help="time a plain device copy of known size (HBM ceiling, "
@@ -288,15 +293,17 @@ def build_ffn(w, rows, act, packs, frt, torch, mx=False, full=False):
             "scale": torch.tensor([float(s_h)], dtype=torch.float32, device="cuda")}
 
 
-def make_rotation(w, dev, packs, rows, torch, ffn=None):
+def make_rotation(w, dev, packs, rows, torch, ffn=None, warm=False):
     """Copies of activations and weights so one pass over the sets moves at
-    least ROTATE_BYTES."""
+    least ROTATE_BYTES. Warm: one set, listed WARM_REPEATS times, so that a
+    graph still holds many launches (the host's replay calls are slower than
+    one short launch)."""
     per = sum(t.numel() * t.element_size() for t in dev.values()
               if t.dim() > 1 and t.shape[0] == rows)
     per += sum(p["W8"].numel() for p in packs)
     if ffn is not None:
         per += ffn["W8"].numel()
-    n = max(1, math.ceil(ROTATE_BYTES / max(per, 1)))
+    n = 1 if warm else max(1, math.ceil(ROTATE_BYTES / max(per, 1)))
     sets = []
     for i in range(n):
         s = {"dev": {}, "packs": []}
@@ -317,6 +324,8 @@ def make_rotation(w, dev, packs, rows, torch, ffn=None):
                 if ffn["ws"].numel() > 1:
                     s["ffn"]["ws"] = ffn["ws"].clone()
         sets.append(s)
+    if warm:
+        sets = sets * WARM_REPEATS
     return sets, per
 
 
@@ -886,7 +895,7 @@ def main():
             raise SystemExit("--ffn: the FFN tail follows the gate/up GEMM of "
                              f"workloads {sorted(wl.FFN_HIDDEN)}")
         ffn = build_ffn(w, rows, act, packs, frt, torch, mx=a.mxfp4, full=a.fp4_full)
-    sets, per_set = make_rotation(w, dev, packs, rows, torch, ffn)
+    sets, per_set = make_rotation(w, dev, packs, rows, torch, ffn, warm=a.warm)
     outs = make_outputs(w, rows, packs, torch, ffn)
     if a.mxfp4:
         outs["x4"] = [(torch.empty(rows, w.D // 2, dtype=torch.uint8, device="cuda"),
@@ -897,8 +906,9 @@ def main():
         if rp is not None:
             st["rope"] = rp
         if op is not None:   # each rotation set streams its own W_o copy
-            st["oproj"] = dict(op, W8=op["W8"] if i == 0 else op["W8"].clone())
-            if a.mxfp4 and i > 0:
+            fresh = i > 0 and not a.warm
+            st["oproj"] = dict(op, W8=op["W8"].clone() if fresh else op["W8"])
+            if a.mxfp4 and fresh:
                 st["oproj"]["ws"] = op["ws"].clone()
     nset = len(sets)
 
@@ -991,7 +1001,8 @@ def main():
     norm_us = sum(r["us"] for r in table if r["kernel"].startswith("norm"))
     dom = max((r for r in table if r["kernel"] in kinds), key=lambda r: r["us"])
     # (records cover the full workload shapes: not a --rows or --tp variant)
-    traffic = load_traffic(a.workload, dom["kernel"]) if a.rows is None and a.tp == 1 else None
+    traffic = (load_traffic(a.workload, dom["kernel"])
+               if a.rows is None and a.tp == 1 and not a.warm else None)
     if dom["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dom["TFLOP/s"],
                 "peak": FP4_PEAK_TFLOPS if "_mx" in dom["kernel"] else FP8_PEAK_TFLOPS,
@@ -1015,10 +1026,14 @@ def main():
                                + ("+o_proj" if op is not None else "")
                                + ("+ffn_geglu_down" if ffn is not None else "")
                                + ("+fp4_down" if a.fp4_full else "")
-                               + (f"+tp{a.tp}_rank0" if a.tp > 1 else ""),
+                               + (f"+tp{a.tp}_rank0" if a.tp > 1 else "")
+                               + ("+warm" if a.warm else ""),
                    "rows": rows, "D": w.D,
                    "gemms": [list(p["splits"]) for p in packs], "bias": w.bias,
-                   "rotation_sets": nset, "rotation_mib": round(nset * per_set / 2**20, 1),
+                   "rotation_sets": 1 if a.warm else nset,
+                   "rotation_mib": round((1 if a.warm else nset) * per_set / 2**20, 1),
+                   "cache": "warm: one buffer set, repeats may hit the Infinity Cache" if a.warm
+                            else "rotated: each pass moves >= 512 MiB of distinct buffers",
                    "step_gemm_gflop": round(gemm_flops / 1e9, 3)},
         "norm_gbps": round(norm_bytes / (norm_us * 1e3), 1) if norm_us else None,
         "norm_hbm_frac": round(norm_bytes / (norm_us * 1e3) / HBM_PEAK_GBS, 4) if norm_us else None,
@@ -1035,7 +1050,7 @@ def main():
     if a.tp > 1:
         res["config"]["tp"] = {"ranks": a.tp, "rank": 0, "full_gemms": [list(g) for g in w.gemms]}
     if (not a.no_cpu_baseline and ffn is None and rp is None and op is None and not a.mxfp4
-            and a.tp == 1):
+            and a.tp == 1 and not a.warm):
         res["cpu_baseline"] = cpu_baseline(w, rows)
     print(json.dumps(res), flush=True)
 
