@@ -321,6 +321,9 @@ int gemm_prepare(int64_t M, int64_t K, int64_t kb, const uint8_t* x8, int64_t ld
   a.N = (int)N_total;
   a.K = (int)K;
   a.out_f32 = out_dtype;
+  a.vec_out = out_dtype == 0;
+  for (int s = 0; s < n_split; ++s)
+    if (split_n[s] % 8 || ld_out[s] % 8 || !aligned(out[s], 16)) a.vec_out = 0;
   return FRT_OK;
 }
 

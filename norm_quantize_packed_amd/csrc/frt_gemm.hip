@@ -561,6 +561,70 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
     }
     return;
   }
+  // Waves of 128 x 64 (the 256x256 plan) hold whole 128-byte row segments
+  // of the bf16 output. With vec_out they pass them through LDS, 64 rows at
+  // a time, and store 16 bytes a lane (8 rows x 128 bytes an instruction)
+  // instead of the 64-byte halves the MFMA layout gives. Each wave uses its
+  // own 8 KB of ring slot KT % NS, whose last stage every wave finished
+  // reading before an earlier barrier and into which no load is pending, so
+  // no block barrier is needed. Within the 64 x 128-byte buffer, 16-byte
+  // chunk c of row r sits at position c ^ (r & 7).
+  constexpr bool WIDE = !GLU && !ROPE && !FP4 && WN == 64 && NJ == 2 && MI % 2 == 0 &&
+                        NW * 64 * 128 <= STAGE;
+  if constexpr (WIDE) {
+    if (a.vec_out) {
+      uint8_t* wb = smem + (KT % NS) * STAGE + wave * (64 * 128);
+      float bj[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int n = n0 + wn0 + j * 32 + (lane & 31);
+        bj[j] = (a.bias != nullptr && n < a.N) ? bf16f(a.bias[n]) : 0.0f;
+      }
+#pragma unroll
+      for (int h = 0; h < MI / 2; ++h) {
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int rr = i2 * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // row in the half
+              const int c = j * 32 + (lane & 31);                                  // column in the wave
+              const float v = alpha * acc[2 * h + i2][j][r] + bj[j];
+              *reinterpret_cast<uint16_t*>(wb + rr * 128 + (((c >> 3) ^ (rr & 7)) << 4) + (c & 7) * 2) =
+                  (uint16_t)f2bf(v);
+            }
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int t = lane + 64 * k;
+          const int rr = t >> 3, cc = t & 7;
+          const uint4 v = *reinterpret_cast<const uint4*>(wb + rr * 128 + ((cc ^ (rr & 7)) << 4));
+          const int m = m0 + wm0 + h * 64 + rr;
+          const int n = n0 + wn0 + cc * 8;
+          if (m < a.M && n < a.N) {
+            // split widths are multiples of 8: the chunk lies in one split
+            uint8_t* base = reinterpret_cast<uint8_t*>(a.sp.ptr[0]);
+            int64_t ld = a.sp.ld[0];
+            int off0 = 0;
+#pragma unroll
+            for (int s = 1; s < FRT_MAX_SPLITS; ++s) {
+              if (s < a.sp.n && n >= a.sp.off[s]) {
+                base = reinterpret_cast<uint8_t*>(a.sp.ptr[s]);
+                ld = a.sp.ld[s];
+                off0 = a.sp.off[s];
+              }
+            }
+            *reinterpret_cast<uint4*>(base + ((int64_t)m * ld + (n - off0)) * 2) = v;
+          }
+        }
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
+        __builtin_amdgcn_wave_barrier();
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int n = n0 + wn0 + j * 32 + (lane & 31);

@@ -72,6 +72,10 @@ struct GemmArgs {
   int M, N, K;
   int out_f32;
   SplitTab sp;
+  // bf16 outputs whose split widths and row strides are multiples of 8
+  // elements and whose pointers are 16-byte aligned: the 256x256 plan then
+  // stores whole 128-byte row segments (16 bytes a lane)
+  int vec_out;
   // gate/up GEGLU epilogue (launch_gemm_geglu): W8 holds 2H rows, gate
   // first; codes of gelu_tanh(gate) * up go to q8 [M, ld_q8] at q_scale
   int H;
