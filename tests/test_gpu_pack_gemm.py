@@ -268,3 +268,25 @@ def test_gemm_large_full_grid(K):
             first = out
         else:
             assert np.array_equal(out, first), f"{M}x{N}x{K} rep {rep}"
+
+
+def test_gemm_large_staged_epilogue_matches_per_lane_stores():
+    """The 256x256 plan (2000 x 5000 x 528 takes it: 160 tiles, one round)
+    stages bf16 results in LDS and stores whole 128-byte row segments when
+    every split width and row stride is a multiple of 8 elements; a padded
+    stride (ld = n + 6) takes the per-lane stores. Ragged M, N and K, a
+    bias, and a split boundary inside a tile: both layouts give the same
+    bits, match the oracle, and write nothing outside their outputs."""
+    rng = np.random.default_rng(31)
+    M, K, splits = 2000, 528, [3000, 2000]
+    N = sum(splits)
+    x8 = wl.random_codes(5101, (M, K))
+    w8 = wl.random_codes(5102, (N, K))
+    bias = wl.to_bf16_bits(0.05 * rng.standard_normal(N).astype(np.float32))
+    s_a, s_w = np.float32(0.003), np.float32(0.002)
+    ref = gemm.packed_gemm_split(x8, w8, s_a, s_w, bias, splits)
+    staged = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
+    lane = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False, ld_pad=6)
+    for i, (a, b, r) in enumerate(zip(staged, lane, ref)):
+        assert np.array_equal(a, b), f"split {i}: staged and per-lane stores differ"
+        assert_gemm_bf16(a, r, f"2000x5000x528 split {i}")
