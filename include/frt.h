@@ -239,6 +239,11 @@ size_t frt_packed_gemm_fp8_workspace_size(int64_t M, int64_t N_total,
  *   workspace, ws_bytes   at least frt_packed_gemm_fp8_workspace_size
  *                 bytes (NULL/0 allowed when that is 0, as it is for every
  *                 shape today); a smaller one is refused before any launch.
+ *
+ * Layout and speed: with bf16 outputs whose split widths and row strides are
+ * multiples of 8 elements and whose pointers are 16-byte aligned, the
+ * large-M plan (256 x 256 tiles) stores whole 128-byte row segments; any
+ * other accepted layout gives the same bits through per-element stores.
  */
 int frt_packed_gemm_fp8_split(void* stream, int64_t M, int64_t K,
                               const uint8_t* x8, int64_t ld_x,
