@@ -5,8 +5,13 @@
 A step is one pass of the whole path over one batch: every producer site of
 the workload (gated-residual AdaRMS or per-token-table LayerNorm, static FP8
 out) followed by its packed sibling GEMM (dequant + bias + column split,
-bf16 out). The default workload is the AdaRMS decoder layer (256 tokens,
-D = 2048; QKV 2048|256|256 from site 1, gate|up 8192|8192 from site 2).
+bf16 out). The default workload is the widest configuration: the
+per-token-table adaLN FFN site over 2048 tokens at D = 16384 (chunks 3-5)
+feeding the merged gate|up GEMM 2048 x 32768 x 16384, whose FP8 matrix-core
+bound GEMM is the dominant kernel. ``--workload 2`` is the AdaRMS decoder
+step (256 tokens, D = 2048; QKV 2048|256|256 from site 1, gate|up
+8192|8192 from site 2), ``--workload 3`` the video-DiT QKV step and
+``--workload 4`` the small-M latency band.
 
 Timing. Inputs and packed weights are resident in HBM before the timed
 region. Steps are captured into HIP graphs (the per-call host cost of the
@@ -88,7 +93,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
     p.add_argument("--rows", type=int, default=None,
                    help="override the producer row count (e.g. the small-M sweep)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -712,17 +717,36 @@ COPY_BYTES = 256 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_sources_sha():
-    """sha256 over the HIP sources and headers: a counter record is used only
-    while the kernels it measured are unchanged."""
+# the sources a kernel kind is built from: its own file plus the shared
+# headers and the ABI layer that fills its arguments
+_SHARED_SOURCES = ("frt_api.hip", "frt_device.h", "frt_internal.h")
+
+
+def _kernel_files(kind):
+    csrc = os.path.join(ROOT, "norm_quantize_packed_amd", "csrc")
+    every = sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".h")))
+    if kind is None:
+        return csrc, every
+    if kind.startswith("norm"):
+        own = "frt_norm.hip"
+    elif kind.startswith("gemm") or kind.startswith(("gateup", "qkv")):
+        own = "frt_gemm.hip"
+    else:
+        return csrc, every
+    return csrc, sorted(set(_SHARED_SOURCES) | {own})
+
+
+def kernel_sources_sha(kind=None):
+    """sha256 over the HIP sources a kernel kind is built from (every source
+    when `kind` is None): a counter record is used only while the kernel it
+    measured is unchanged."""
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "norm_quantize_packed_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(f.read())
+    csrc, names = _kernel_files(kind)
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()
 
 
@@ -784,7 +808,7 @@ def summarize_pmc(a):
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
            "traffic_bytes": round(fetch_b + write_b),
-           "sources_sha256": kernel_sources_sha()}
+           "sources_sha256": kernel_sources_sha(kind)}
     os.makedirs(PROFILES, exist_ok=True)
     out = os.path.join(PROFILES, f"traffic_w{a.workload}_{kind}.json")
     with open(out, "w") as fh:
@@ -802,7 +826,7 @@ def load_traffic(wid, kind):
             rec = json.load(fh)
     except (OSError, ValueError):
         return None
-    if rec.get("sources_sha256") != kernel_sources_sha():
+    if rec.get("sources_sha256") != kernel_sources_sha(kind):
         return None
     return int(rec["traffic_bytes"])
 

@@ -291,24 +291,6 @@ def frt_packed_gemm_fp8_workspace_size(M: int, N_total: int, K: int) -> int:
     return int(load_library().frt_packed_gemm_fp8_workspace_size(M, N_total, K))
 
 
-_WORKSPACES: dict = {}
-
-
-def default_workspace(nbytes: int, device=None):
-    """A zero-initialised workspace of at least `nbytes` on `device`, cached
-    per device (the library leaves its counter region zero after every
-    call, so the buffer is reused as is; it is reallocated, zero-filled,
-    only when a larger one is needed). Calls sharing it must be
-    stream-ordered."""
-    import torch
-    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
-    ws = _WORKSPACES.get(dev)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
-        _WORKSPACES[dev] = ws
-    return ws
-
-
 def frt_packed_gemm_fp8_split(x8, W8, act_scale, w_scale, outs: Sequence,
                               split_n: Sequence[int], bias_cat=None, *,
                               M: Optional[int] = None, workspace=None,
@@ -340,8 +322,11 @@ def frt_packed_gemm_fp8_split(x8, W8, act_scale, w_scale, outs: Sequence,
     ws_need = frt_packed_gemm_fp8_workspace_size(Mv, N, K)
     ws_ptr, ws_bytes = 0, 0
     if ws_need:
+        # the caller owns every buffer: a plan that needs a workspace is
+        # refused here rather than allocated behind the caller's back
         if workspace is None:
-            workspace = default_workspace(ws_need, x8.device)
+            raise ValueError(f"frt: this GEMM needs a device workspace of {ws_need} bytes "
+                             "(frt_packed_gemm_fp8_workspace_size); pass workspace=")
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     lib = load_library()
     _check(lib.frt_packed_gemm_fp8_split(

@@ -23,6 +23,7 @@
 // the logical tile index gives each XCD a contiguous run of tiles, and runs
 // are rastered in groups of GM tile-rows so that the tiles resident on one
 // XCD share A and B panels in that XCD's L2.
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 #include <utility>
@@ -131,9 +132,10 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // tiles: one direct dword load per 32-row block (A rows, then the B rows in
 // tile order), issued by the same call as the tiles and spread over the
 // waves (the wait counts cover them), and read back with the fragments, so
-// a block's scales are fetched once, not once per wave that uses them. Rows
-// past M or N fetch zeros (each run has its own record count); their results
-// are never stored. alpha is 1.
+// a block's scales are fetched once, not once per wave that uses them. Each
+// run has its own record count (rows x 8 bytes) and a lane's whole offset
+// (block row and lane) is range-checked against it, so rows past M or N
+// fetch zeros, per lane; their results are never stored. alpha is 1.
 template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB, int AE = BM,
           bool GLU = false, bool ROPE = false, bool FP4 = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a) {
@@ -265,7 +267,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
 #pragma unroll
         for (int k = 0; k < SCL; ++k) {
           const __amdgpu_buffer_rsrc_t r = make_rsrc(sc_src[k] + run * sc_run[k], sc_rec[k]);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(sdst + sc_lds[k]), 4, sc_lane, sc_off[k], 0, 0);
+          // the block's row offset rides in the lane offset, which the raw
+          // buffer range check covers (the scalar offset is not checked):
+          // rows past M or N fetch zeros and nothing past the run is read
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(sdst + sc_lds[k]), 4, sc_lane + sc_off[k], 0, 0, 0);
         }
       }
     }
@@ -684,18 +689,20 @@ hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
 // The current plans use no workspace (the argument is kept in the ABI).
 size_t gemm_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device, cached per device. Threads that race
+// on a device's first query each store the same count; the relaxed atomic
+// makes those concurrent stores and loads well defined.
 int device_cus() {
-  static int cus[64] = {0};
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
+  int c = cus[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     int n = 0;
-    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-                   ? n
-                   : 256;
+    c = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+    cus[dev].store(c, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return c;
 }
 
 // Operand bytes (per K byte) that the busiest CU loads under a BM x BN tile

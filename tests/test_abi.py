@@ -396,3 +396,46 @@ def test_mxfp4_refusals(lib):
     assert mrope(P=1) == frt.FRT_E_INVALID                # P + M > T
     assert mrope(q=FAKE + 3 * MB) == frt.FRT_E_INVALID    # q over S4
     assert mrope(M=0) == frt.FRT_OK
+
+
+class _FakeDev:
+    """Stands in for a device tensor in the binding's argument checks (its
+    address is never dereferenced: the call below is refused first)."""
+
+    def __init__(self, shape, dtype, addr):
+        self.shape, self.dtype, self.is_cuda, self._addr = tuple(shape), dtype, True, addr
+        self.device = "cuda:0"
+
+    def data_ptr(self):
+        return self._addr
+
+    def dim(self):
+        return len(self.shape)
+
+    def stride(self, d=None):
+        st = [1] * len(self.shape)
+        for i in range(len(self.shape) - 2, -1, -1):
+            st[i] = st[i + 1] * self.shape[i + 1]
+        return tuple(st) if d is None else st[d]
+
+    def numel(self):
+        n = 1
+        for s in self.shape:
+            n *= s
+        return n
+
+    def element_size(self):
+        return 1
+
+
+def test_binding_refuses_to_allocate_a_workspace(lib, monkeypatch):
+    """A plan that needs a workspace is refused by the binding when the
+    caller passes none: the binding never allocates one behind the call."""
+    import torch
+    monkeypatch.setattr(frt, "frt_packed_gemm_fp8_workspace_size", lambda M, N, K: 4096)
+    x8 = _FakeDev((16, 512), torch.uint8, FAKE)
+    W8 = _FakeDev((768, 512), torch.uint8, FAKE + MB)
+    sc = _FakeDev((1,), torch.float32, FAKE + 2 * MB)
+    out = _FakeDev((16, 768), torch.bfloat16, FAKE + 3 * MB)
+    with pytest.raises(ValueError, match="workspace"):
+        frt.frt_packed_gemm_fp8_split(x8, W8, sc, sc, [out], [768])

@@ -93,17 +93,28 @@ def test_summarize_pmc_scales_by_the_copy(tmp_path, monkeypatch):
     assert rec["fetch_bytes"] == 1000 * 1024 * 2
     assert rec["write_bytes"] == 400 * 1024
     assert rec["traffic_bytes"] == 1000 * 1024 * 2 + 400 * 1024
-    assert rec["sources_sha256"] == bench.kernel_sources_sha()
+    assert rec["sources_sha256"] == bench.kernel_sources_sha("gemm2")
 
 
 def test_traffic_record_needs_the_current_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     assert bench.load_traffic(2, "gemm2") is None            # no record
-    rec = {"traffic_bytes": 123, "sources_sha256": bench.kernel_sources_sha()}
+    rec = {"traffic_bytes": 123, "sources_sha256": bench.kernel_sources_sha("gemm2")}
     (tmp_path / "traffic_w2_gemm2.json").write_text(json.dumps(rec))
     assert bench.load_traffic(2, "gemm2") == 123
-    monkeypatch.setattr(bench, "kernel_sources_sha", lambda: "0" * 64)
+    monkeypatch.setattr(bench, "kernel_sources_sha", lambda kind=None: "0" * 64)
     assert bench.load_traffic(2, "gemm2") is None            # kernels changed
+
+
+def test_traffic_record_follows_its_own_kernel_sources():
+    """A GEMM record covers the GEMM's sources, a producer record the
+    producer's: a change to one kernel file leaves the other's hash alone."""
+    g = set(bench._kernel_files("gemm1")[1])
+    n = set(bench._kernel_files("norm1")[1])
+    assert "frt_gemm.hip" in g and "frt_norm.hip" not in g
+    assert "frt_norm.hip" in n and "frt_gemm.hip" not in n
+    assert {"frt_api.hip", "frt_device.h", "frt_internal.h"} <= g & n
+    assert bench.kernel_sources_sha("gemm1") != bench.kernel_sources_sha("norm1")
 
 
 def test_more_than_one_gpu_is_refused():
