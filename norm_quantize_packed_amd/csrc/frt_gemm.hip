@@ -53,6 +53,11 @@ __device__ __forceinline__ constexpr int vm_lgkm0_imm(int n) {
   return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4);
 }
 
+// s_waitcnt immediate: vmcnt(n) alone (lgkmcnt and expcnt at their maxima)
+__device__ __forceinline__ constexpr int vm_imm(int n) {
+  return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
 struct TileXY {
   int tm, tn;
 };
@@ -71,6 +76,245 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
   return TileXY{first + within % rows, within / rows};
 }
 
+
+// Epilogue shared by the tile kernels: alpha * acc + bias, then the split,
+// GEGLU or RoPE form of the output. `slot` is SLOT bytes of LDS that no wave
+// of the block reads any more and that no load still targets (each wave
+// stages only in its own part of it, so no block barrier is needed); `lds` is
+// the whole allocation (TOTAL bytes), used after a block barrier when the
+// staging needs more than the slot.
+template <int MI, int NJ, int WN, int NW, bool GLU, bool ROPE, bool FP4, int SLOT, int TOTAL>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, v16f (&acc)[MI][NJ], int m0, int n0, int wm0,
+                                              int wn0, int wave, int lane, uint8_t* slot, uint8_t* lds) {
+  const float alpha = FP4 ? 1.0f : (*a.act_scale) * (*a.w_scale);
+  if constexpr (ROPE) {
+    const int nq = a.nh * a.hd, nk = a.kv * a.hd;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int n = n0 + wn0 + j * 32 + (lane & 31);
+      const bool nok = n < a.N;
+      const bool rot = n < nq + nk;
+      const int d = n % a.hd;
+      const float b = (a.bias != nullptr && nok) ? bf16f(a.bias[n]) : 0.0f;
+      uint16_t* dst;
+      int64_t ld;
+      if (n < nq) {
+        dst = a.q_out + n;
+        ld = nq;
+      } else if (rot) {
+        dst = a.k_cache + a.P * nk + (n - nq);
+        ld = nk;
+      } else {
+        dst = a.v_cache + a.P * nk + (n - nq - nk);
+        ld = nk;
+      }
+      // a' = a c - b s on the even column, b' = b c + a s on the odd one
+      const float sgn = (n & 1) ? 1.0f : -1.0f;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        // the (cos, sin) words of this lane's 16 rows, loaded together (rows
+        // past M read row M - 1 and are not stored)
+        uint32_t cs[16];
+        const uint16_t* rp = a.rope + (d & ~1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = min(m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), a.M - 1);
+          cs[r] = rot ? *reinterpret_cast<const uint32_t*>(rp + (int64_t)m * a.hd) : 0u;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const float v = __uint_as_float(f2bf(alpha * acc[i][j][r] + b) << 16);
+          const float p = lane_xor1(v);
+          const float o = rot ? __builtin_fmaf(v, bf16lo(cs[r]), sgn * (p * bf16hi(cs[r]))) : v;
+          if (nok && m < a.M) dst[(int64_t)m * ld] = (uint16_t)f2bf(o);
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (GLU) {
+    if constexpr (FP4) {
+    if (a.q4 != nullptr) {
+      // GEGLU to MXFP4: a block scale needs the maximum over 32 consecutive
+      // columns, which the MFMA layout spreads over 32 lanes, so the wave's
+      // y tile goes through LDS and comes back row-wise: 8 consecutive
+      // columns per lane, one 32-column block per quad, quantised as the
+      // standalone GEGLU -> MXFP4 kernel quantises them. The tiles go to
+      // ring slot KT % NS, whose last stage (KT - NS) every wave finished
+      // reading before a later barrier, when they fit in it; else to the
+      // whole ring after a barrier. Each wave reads back only what it wrote.
+      static_assert(NJ == 2, "one 32-column gate block per wave");
+      constexpr int YR = MI * 32;  // rows of the wave's y tile (32 columns)
+      constexpr bool ONE_SLOT = NW * YR * 32 * 4 <= SLOT;
+      static_assert(ONE_SLOT || NW * YR * 32 * 4 <= TOTAL, "y tiles exceed the LDS");
+      uint8_t* ybase = lds;
+      if constexpr (ONE_SLOT)
+        ybase = slot;
+      else
+        __syncthreads();
+      float* ys = reinterpret_cast<float*>(ybase) + wave * YR * 32;
+      const int gc0 = n0 + (wn0 >> 1);  // the wave's first gate column
+      const float bg = (a.bias != nullptr && gc0 < a.H) ? bf16f(a.bias[gc0 + (lane & 31)]) : 0.0f;
+      const float bu = (a.bias != nullptr && gc0 < a.H) ? bf16f(a.bias[a.H + gc0 + (lane & 31)]) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const float vg = alpha * acc[i][0][r] + bg;
+          const float vu = alpha * acc[i][1][r] + bu;
+          ys[rl * 32 + (lane & 31)] =
+              gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));  // this wave's LDS writes done
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = 0; k < YR * 4 / 64; ++k) {
+        const int t = lane + 64 * k, rl = t >> 2, v = t & 3;
+        const float4 y0 = *reinterpret_cast<const float4*>(ys + rl * 32 + v * 8);
+        const float4 y1 = *reinterpret_cast<const float4*>(ys + rl * 32 + v * 8 + 4);
+        const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+        uint32_t am = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(fabsf(y[e])));
+        const uint32_t sbyte = e8m0_of_amax(quad_umax(am));
+        const uint32_t codes = mxfp4_pack8(y, sbyte);
+        const int m = m0 + wm0 + rl;
+        if (m < a.M && gc0 < a.H) {
+          const int64_t c = gc0 + v * 8;
+          *reinterpret_cast<uint32_t*>(a.q4 + (int64_t)m * a.ld_q4 + c / 2) = codes;
+          if (v == 0) a.sc4[e8m0_off(m, c / 32, a.ld_sc4)] = (uint8_t)sbyte;
+        }
+      }
+      return;
+    }
+    }
+    // gate and up rounded to bf16 as the unfused GEMM output would be,
+    // then the GEGLU quantiser of frt_ffn.hip
+    const float qs = *a.q_scale, qr = 1.0f / qs;
+#pragma unroll
+    for (int q = 0; q < NJ / 2; ++q) {
+      const int gc = n0 + (wn0 >> 1) + q * 32 + (lane & 31);
+      if (gc >= a.H) continue;
+      const float bg = a.bias != nullptr ? bf16f(a.bias[gc]) : 0.0f;
+      const float bu = a.bias != nullptr ? bf16f(a.bias[a.H + gc]) : 0.0f;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          if (m < a.M) {
+            const float vg = alpha * acc[i][2 * q][r] + bg;
+            const float vu = alpha * acc[i][2 * q + 1][r] + bu;
+            const float y = gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
+            a.q8[(int64_t)m * a.ld_q8 + gc] = (uint8_t)cvt2_fp8(clamp_fp8(div_rn(y, qs, qr)), 0.0f);
+          }
+        }
+      }
+    }
+    return;
+  }
+  // Waves of 128 x 64 (the 256x256 plan) hold whole 128-byte row segments
+  // of the bf16 output. With vec_out they pass them through LDS, 64 rows at
+  // a time, and store 16 bytes a lane (8 rows x 128 bytes an instruction)
+  // instead of the 64-byte halves the MFMA layout gives. Each wave uses its
+  // own 8 KB of ring slot KT % NS, whose last stage every wave finished
+  // reading before an earlier barrier and into which no load is pending, so
+  // no block barrier is needed. Within the 64 x 128-byte buffer, 16-byte
+  // chunk c of row r sits at position c ^ (r & 7).
+  constexpr bool WIDE = !GLU && !ROPE && !FP4 && WN % 64 == 0 && MI % 2 == 0 && NW * 64 * 128 <= SLOT;
+  if constexpr (WIDE) {
+    if (a.vec_out) {
+      uint8_t* wb = slot + wave * (64 * 128);
+      float bj[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int n = n0 + wn0 + j * 32 + (lane & 31);
+        bj[j] = (a.bias != nullptr && n < a.N) ? bf16f(a.bias[n]) : 0.0f;
+      }
+      // 64-column halves of the wave tile, then 64-row halves
+#pragma unroll
+      for (int jh = 0; jh < NJ / 2; ++jh) {
+      // this lane stores 8-column chunk lane % 8 of the half in every row it
+      // writes; split widths are multiples of 8, so the chunk lies in one
+      // split, found once per half
+      const int nc = n0 + wn0 + jh * 64 + (lane & 7) * 8;
+      const bool nok = nc < a.N;
+      uint8_t* colp = reinterpret_cast<uint8_t*>(a.sp.ptr[0]) + (int64_t)nc * 2;
+      int64_t ldb = a.sp.ld[0] * 2;
+#pragma unroll
+      for (int s = 1; s < FRT_MAX_SPLITS; ++s) {
+        if (s < a.sp.n && nc >= a.sp.off[s]) {
+          colp = reinterpret_cast<uint8_t*>(a.sp.ptr[s]) + (int64_t)(nc - a.sp.off[s]) * 2;
+          ldb = a.sp.ld[s] * 2;
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < MI / 2; ++h) {
+#pragma unroll
+        for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+          for (int j2 = 0; j2 < 2; ++j2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = 2 * jh + j2;
+              const int rr = i2 * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // row in the half
+              const int c = j2 * 32 + (lane & 31);                                 // column in the half
+              const float v = alpha * acc[2 * h + i2][j][r] + bj[j];
+              *reinterpret_cast<uint16_t*>(wb + rr * 128 + (((c >> 3) ^ (rr & 7)) << 4) + (c & 7) * 2) =
+                  (uint16_t)f2bf(v);
+            }
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int rr = (lane >> 3) + 8 * k, cc = lane & 7;
+          const uint4 v = *reinterpret_cast<const uint4*>(wb + rr * 128 + ((cc ^ (rr & 7)) << 4));
+          const int m = m0 + wm0 + h * 64 + rr;
+          if (nok && m < a.M) *reinterpret_cast<uint4*>(colp + (int64_t)m * ldb) = v;
+        }
+        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
+        __builtin_amdgcn_wave_barrier();
+      }
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn0 + j * 32 + (lane & 31);
+    if (n >= a.N) continue;
+    uint8_t* base = reinterpret_cast<uint8_t*>(a.sp.ptr[0]);
+    int64_t ld = a.sp.ld[0];
+    int off0 = 0;
+#pragma unroll
+    for (int s = 1; s < FRT_MAX_SPLITS; ++s) {
+      if (s < a.sp.n && n >= a.sp.off[s]) {
+        base = reinterpret_cast<uint8_t*>(a.sp.ptr[s]);
+        ld = a.sp.ld[s];
+        off0 = a.sp.off[s];
+      }
+    }
+    const float b = a.bias != nullptr ? bf16f(a.bias[n]) : 0.0f;
+    const int col = n - off0;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        if (m < a.M) {
+          const float v = alpha * acc[i][j][r] + b;
+          if (a.out_f32)
+            reinterpret_cast<float*>(base)[(int64_t)m * ld + col] = v;
+          else
+            reinterpret_cast<uint16_t*>(base)[(int64_t)m * ld + col] = (uint16_t)f2bf(v);
+        }
+      }
+    }
+  }
+}
 
 // Tiled kernel: BM x BN block tile, WM x WN per wave, 128-deep K staging.
 //
@@ -438,230 +682,328 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       for (int j = 0; j < NJ; ++j) acc[i][j] += acc2[i][j];
   }
 
-  // ---- epilogue: alpha * acc + bias, column split, bf16 (or fp32) ----
-  const float alpha = FP4 ? 1.0f : (*a.act_scale) * (*a.w_scale);
-  if constexpr (ROPE) {
-    const int nq = a.nh * a.hd, nk = a.kv * a.hd;
+  gemm_epilogue<MI, NJ, WN, NW, GLU, ROPE, FP4, STAGE, NS * STAGE>(a, acc, m0, n0, wm0, wn0, wave, lane,
+                                                                 smem + (KT % NS) * STAGE, smem);
+}
+
+// The split table in LDS: the 256 x 256 kernel's epilogue looks a column's
+// split up there (lane by lane) instead of keeping the table's 80 scalar
+// registers live next to 256 accumulator registers.
+struct LdsSplits {
+  uint64_t ptr[FRT_MAX_SPLITS];
+  int64_t ld[FRT_MAX_SPLITS];
+  int off[FRT_MAX_SPLITS];
+  int n;
+};
+
+// Output pointer of column n (in its split) and its row stride, in bytes
+// of `esize`-byte elements.
+__device__ __forceinline__ void split_of(const LdsSplits* t, int n, int esize, uint8_t*& colp, int64_t& ldb) {
+  const int ns = t->n;
+  int idx = 0;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int n = n0 + wn0 + j * 32 + (lane & 31);
-      const bool nok = n < a.N;
-      const bool rot = n < nq + nk;
-      const int d = n % a.hd;
-      const float b = (a.bias != nullptr && nok) ? bf16f(a.bias[n]) : 0.0f;
-      uint16_t* dst;
-      int64_t ld;
-      if (n < nq) {
-        dst = a.q_out + n;
-        ld = nq;
-      } else if (rot) {
-        dst = a.k_cache + a.P * nk + (n - nq);
-        ld = nk;
-      } else {
-        dst = a.v_cache + a.P * nk + (n - nq - nk);
-        ld = nk;
-      }
-      // a' = a c - b s on the even column, b' = b c + a s on the odd one
-      const float sgn = (n & 1) ? 1.0f : -1.0f;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        // the (cos, sin) words of this lane's 16 rows, loaded together (rows
-        // past M read row M - 1 and are not stored)
-        uint32_t cs[16];
-        const uint16_t* rp = a.rope + (d & ~1);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = min(m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), a.M - 1);
-          cs[r] = rot ? *reinterpret_cast<const uint32_t*>(rp + (int64_t)m * a.hd) : 0u;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const float v = __uint_as_float(f2bf(alpha * acc[i][j][r] + b) << 16);
-          const float p = lane_xor1(v);
-          const float o = rot ? __builtin_fmaf(v, bf16lo(cs[r]), sgn * (p * bf16hi(cs[r]))) : v;
-          if (nok && m < a.M) dst[(int64_t)m * ld] = (uint16_t)f2bf(o);
-        }
-      }
-    }
-    return;
+  for (int s = 1; s < FRT_MAX_SPLITS; ++s)
+    if (s < ns && n >= t->off[s]) idx = s;
+  colp = reinterpret_cast<uint8_t*>(t->ptr[idx]) + (int64_t)(n - t->off[idx]) * esize;
+  ldb = t->ld[idx] * esize;
+}
+
+// Split epilogue of the 256 x 256 kernel (bf16 or fp32 out, optional bias):
+// out = alpha * acc + bias into the split owning each column. With vec_out
+// each 64 x 64 quarter of the wave tile goes through the wave's own 8 KB of
+// LDS and leaves as whole 128-byte row segments (16 bytes a lane); else each
+// lane stores its elements. Called after a block barrier that ended every
+// use of the ring; `tab` must not overlap the waves' staging (32 KB).
+__device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v16f (&acc)[4][4], int m0, int n0, int wm0,
+                                                       int wn0, int wave, int lane, uint8_t* smem, LdsSplits* tab) {
+  constexpr int MI = 4, NJ = 4;
+  if (threadIdx.x < FRT_MAX_SPLITS) {
+    tab->ptr[threadIdx.x] = reinterpret_cast<uint64_t>(a.sp.ptr[threadIdx.x]);
+    tab->ld[threadIdx.x] = a.sp.ld[threadIdx.x];
+    tab->off[threadIdx.x] = a.sp.off[threadIdx.x];
+    if (threadIdx.x == 0) tab->n = a.sp.n;
   }
-  if constexpr (GLU) {
-    if (a.q4 != nullptr) {
-      // GEGLU to MXFP4: a block scale needs the maximum over 32 consecutive
-      // columns, which the MFMA layout spreads over 32 lanes, so the wave's
-      // y tile goes through LDS and comes back row-wise: 8 consecutive
-      // columns per lane, one 32-column block per quad, quantised as the
-      // standalone GEGLU -> MXFP4 kernel quantises them. The tiles go to
-      // ring slot KT % NS, whose last stage (KT - NS) every wave finished
-      // reading before a later barrier, when they fit in it; else to the
-      // whole ring after a barrier. Each wave reads back only what it wrote.
-      static_assert(NJ == 2, "one 32-column gate block per wave");
-      constexpr int YR = MI * 32;  // rows of the wave's y tile (32 columns)
-      constexpr bool ONE_SLOT = NW * YR * 32 * 4 <= STAGE;
-      uint8_t* ybase = smem;
-      if constexpr (ONE_SLOT)
-        ybase = smem + (KT % NS) * STAGE;
-      else
-        __syncthreads();
-      float* ys = reinterpret_cast<float*>(ybase) + wave * YR * 32;
-      const int gc0 = n0 + (wn0 >> 1);  // the wave's first gate column
-      const float bg = (a.bias != nullptr && gc0 < a.H) ? bf16f(a.bias[gc0 + (lane & 31)]) : 0.0f;
-      const float bu = (a.bias != nullptr && gc0 < a.H) ? bf16f(a.bias[a.H + gc0 + (lane & 31)]) : 0.0f;
+  __syncthreads();
+  const float alpha = (*a.act_scale) * (*a.w_scale);
+  float bj[NJ];
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const float vg = alpha * acc[i][0][r] + bg;
-          const float vu = alpha * acc[i][1][r] + bu;
-          ys[rl * 32 + (lane & 31)] =
-              gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));  // this wave's LDS writes done
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int k = 0; k < YR * 4 / 64; ++k) {
-        const int t = lane + 64 * k, rl = t >> 2, v = t & 3;
-        const float4 y0 = *reinterpret_cast<const float4*>(ys + rl * 32 + v * 8);
-        const float4 y1 = *reinterpret_cast<const float4*>(ys + rl * 32 + v * 8 + 4);
-        const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-        uint32_t am = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(fabsf(y[e])));
-        const uint32_t sbyte = e8m0_of_amax(quad_umax(am));
-        const uint32_t codes = mxfp4_pack8(y, sbyte);
-        const int m = m0 + wm0 + rl;
-        if (m < a.M && gc0 < a.H) {
-          const int64_t c = gc0 + v * 8;
-          *reinterpret_cast<uint32_t*>(a.q4 + (int64_t)m * a.ld_q4 + c / 2) = codes;
-          if (v == 0) a.sc4[e8m0_off(m, c / 32, a.ld_sc4)] = (uint8_t)sbyte;
-        }
-      }
-      return;
-    }
-    // gate and up rounded to bf16 as the unfused GEMM output would be,
-    // then the GEGLU quantiser of frt_ffn.hip
-    const float qs = *a.q_scale, qr = 1.0f / qs;
-#pragma unroll
-    for (int q = 0; q < NJ / 2; ++q) {
-      const int gc = n0 + (wn0 >> 1) + q * 32 + (lane & 31);
-      if (gc >= a.H) continue;
-      const float bg = a.bias != nullptr ? bf16f(a.bias[gc]) : 0.0f;
-      const float bu = a.bias != nullptr ? bf16f(a.bias[a.H + gc]) : 0.0f;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          if (m < a.M) {
-            const float vg = alpha * acc[i][2 * q][r] + bg;
-            const float vu = alpha * acc[i][2 * q + 1][r] + bu;
-            const float y = gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
-            a.q8[(int64_t)m * a.ld_q8 + gc] = (uint8_t)cvt2_fp8(clamp_fp8(div_rn(y, qs, qr)), 0.0f);
-          }
-        }
-      }
-    }
-    return;
+  for (int j = 0; j < NJ; ++j) {
+    const int n = n0 + wn0 + j * 32 + (lane & 31);
+    bj[j] = (a.bias != nullptr && n < a.N) ? bf16f(a.bias[n]) : 0.0f;
   }
-  // Waves of 128 x 64 (the 256x256 plan) hold whole 128-byte row segments
-  // of the bf16 output. With vec_out they pass them through LDS, 64 rows at
-  // a time, and store 16 bytes a lane (8 rows x 128 bytes an instruction)
-  // instead of the 64-byte halves the MFMA layout gives. Each wave uses its
-  // own 8 KB of ring slot KT % NS, whose last stage every wave finished
-  // reading before an earlier barrier and into which no load is pending, so
-  // no block barrier is needed. Within the 64 x 128-byte buffer, 16-byte
-  // chunk c of row r sits at position c ^ (r & 7).
-  constexpr bool WIDE = !GLU && !ROPE && !FP4 && WN == 64 && NJ == 2 && MI % 2 == 0 &&
-                        NW * 64 * 128 <= STAGE;
-  if constexpr (WIDE) {
-    if (a.vec_out) {
-      uint8_t* wb = smem + (KT % NS) * STAGE + wave * (64 * 128);
-      float bj[NJ];
+  // whole wave tile inside M (every tile but the last row of tiles)
+  const bool rows_in = m0 + wm0 + 128 <= a.M;
+  if (a.vec_out) {
+    uint8_t* wb = smem + wave * (64 * 128);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int n = n0 + wn0 + j * 32 + (lane & 31);
-        bj[j] = (a.bias != nullptr && n < a.N) ? bf16f(a.bias[n]) : 0.0f;
-      }
+    for (int jh = 0; jh < 2; ++jh) {
+      // this lane stores 8-column chunk lane % 8 of the half in each of its
+      // rows; split widths are multiples of 8, so the chunk lies in one split
+      const int nc = n0 + wn0 + jh * 64 + (lane & 7) * 8;
+      const bool nok = nc < a.N;
+      uint8_t* colp;
+      int64_t ldb;
+      split_of(tab, nok ? nc : 0, 2, colp, ldb);
 #pragma unroll
-      for (int h = 0; h < MI / 2; ++h) {
+      for (int h = 0; h < 2; ++h) {
+        // quarter (h, jh) into LDS: 16-byte chunk c of row r at c ^ (r & 7)
 #pragma unroll
         for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-          for (int j = 0; j < NJ; ++j)
+          for (int j2 = 0; j2 < 2; ++j2)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int rr = i2 * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // row in the half
-              const int c = j * 32 + (lane & 31);                                  // column in the wave
-              const float v = alpha * acc[2 * h + i2][j][r] + bj[j];
+              const int rr = i2 * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+              const int c = j2 * 32 + (lane & 31);
+              const float v = alpha * acc[2 * h + i2][2 * jh + j2][r] + bj[2 * jh + j2];
               *reinterpret_cast<uint16_t*>(wb + rr * 128 + (((c >> 3) ^ (rr & 7)) << 4) + (c & 7) * 2) =
                   (uint16_t)f2bf(v);
             }
         __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
         __builtin_amdgcn_wave_barrier();
+        const int mb = m0 + wm0 + h * 64;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const int t = lane + 64 * k;
-          const int rr = t >> 3, cc = t & 7;
-          const uint4 v = *reinterpret_cast<const uint4*>(wb + rr * 128 + ((cc ^ (rr & 7)) << 4));
-          const int m = m0 + wm0 + h * 64 + rr;
-          const int n = n0 + wn0 + cc * 8;
-          if (m < a.M && n < a.N) {
-            // split widths are multiples of 8: the chunk lies in one split
-            uint8_t* base = reinterpret_cast<uint8_t*>(a.sp.ptr[0]);
-            int64_t ld = a.sp.ld[0];
-            int off0 = 0;
-#pragma unroll
-            for (int s = 1; s < FRT_MAX_SPLITS; ++s) {
-              if (s < a.sp.n && n >= a.sp.off[s]) {
-                base = reinterpret_cast<uint8_t*>(a.sp.ptr[s]);
-                ld = a.sp.ld[s];
-                off0 = a.sp.off[s];
-              }
-            }
-            *reinterpret_cast<uint4*>(base + ((int64_t)m * ld + (n - off0)) * 2) = v;
-          }
+          const int rr = (lane >> 3) + 8 * k;
+          const uint4 v = *reinterpret_cast<const uint4*>(wb + rr * 128 + (((lane & 7) ^ (rr & 7)) << 4));
+          if (nok && (rows_in || mb + rr < a.M)) *reinterpret_cast<uint4*>(colp + (int64_t)(mb + rr) * ldb) = v;
         }
         __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
         __builtin_amdgcn_wave_barrier();
       }
-      return;
     }
+    return;
   }
+  // per-lane stores; rows past M exist only in the last row of tiles
+  auto store_all = [&](auto F32C) {
+    constexpr bool F32 = decltype(F32C)::value;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int n = n0 + wn0 + j * 32 + (lane & 31);
-    if (n >= a.N) continue;
-    uint8_t* base = reinterpret_cast<uint8_t*>(a.sp.ptr[0]);
-    int64_t ld = a.sp.ld[0];
-    int off0 = 0;
+    for (int j = 0; j < NJ; ++j) {
+      const int n = n0 + wn0 + j * 32 + (lane & 31);
+      if (n >= a.N) continue;
+      uint8_t* colp;
+      int64_t ldb;
+      split_of(tab, n, F32 ? 4 : 2, colp, ldb);
 #pragma unroll
-    for (int s = 1; s < FRT_MAX_SPLITS; ++s) {
-      if (s < a.sp.n && n >= a.sp.off[s]) {
-        base = reinterpret_cast<uint8_t*>(a.sp.ptr[s]);
-        ld = a.sp.ld[s];
-        off0 = a.sp.off[s];
-      }
-    }
-    const float b = a.bias != nullptr ? bf16f(a.bias[n]) : 0.0f;
-    const int col = n - off0;
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < a.M) {
-          const float v = alpha * acc[i][j][r] + b;
-          if (a.out_f32)
-            reinterpret_cast<float*>(base)[(int64_t)m * ld + col] = v;
-          else
-            reinterpret_cast<uint16_t*>(base)[(int64_t)m * ld + col] = (uint16_t)f2bf(v);
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const float v = alpha * acc[i][j][r] + bj[j];
+          if (rows_in || m < a.M) {
+            if constexpr (F32)
+              *reinterpret_cast<float*>(colp + (int64_t)m * ldb) = v;
+            else
+              *reinterpret_cast<uint16_t*>(colp + (int64_t)m * ldb) = (uint16_t)f2bf(v);
+          }
         }
+    }
+  };
+  if (a.out_f32)
+    store_all(std::true_type{});
+  else
+    store_all(std::false_type{});
+}
+
+// Large-M FP8 kernel: a 256 x 256 block tile of four 128 x 128 wave tiles
+// (one wave per SIMD, accumulators in the matrix-core registers).
+//
+// The LDS is a ring of five 32 KB units; a unit holds the A rows or the B
+// rows of one 128-deep stage (256 rows x 128 bytes, the same swizzled row
+// layout as gemm_kernel). Stage kt reads units 2kt (A) and 2kt + 1 (B);
+// while it runs, unit 2kt + 2 is still in flight and units 2kt + 3 and
+// 2kt + 4 are issued into the slots of stage kt - 1, so up to three units
+// (96 KB) load behind the compute instead of one 64 KB stage (the load path
+// keeps more lines in flight this way; half-line row segments, the other way
+// to deepen a ring within 160 KB, fetch each line twice and are slower).
+//
+// Each wave double-buffers its fragments across the two 64-deep sub-steps
+// of a stage and issues its work in a fixed order (no compiler reordering):
+// sub-step 0 interleaves its 16 MFMAs with the 16 loads of the two new units
+// and the 16 half-reads of sub-step 1's fragments; sub-step 1 runs 9 MFMAs,
+// waits for units up to 2kt + 3 and takes the stage barrier, then issues
+// the next stage's first fragments two half-reads per MFMA over its last 7.
+// Each accumulator takes its MFMAs in K order, as in gemm_kernel, so both
+// produce the same bits. Past the last stage the loads fetch zeros into free
+// slots (branch-free); the block drains them before the epilogue.
+//
+// GLU and ROPE select the epilogue forms described at gemm_kernel; KTAIL
+// zero-fills the 16-byte chunks past K.
+template <bool GLU, bool ROPE, bool KTAIL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm256_kernel(GemmArgs a) {
+  constexpr int BM = 256, BN = 256, GM = 4, NW = 4, MI = 4, NJ = 4;
+  constexpr int UNIT = 256 * 128, RU = 5, LPU = 256 / 8 / NW;  // 8 loads a wave per unit
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[RU * UNIT];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = (a.N + BN - 1) / BN;
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + a.K);
+  const uint32_t w_bytes = (uint32_t)((int64_t)a.N * a.K);
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, w_bytes);
+  // load j of a unit covers tile rows 8g .. 8g + 7, g = wave + 4j; with g's
+  // parity that of the wave, (row >> 1) & 7 = ((wave & 1) << 2) | (lrow >> 1)
+  const int lrow = lane >> 3;
+  const int cch = (lane & 7) ^ (((wave & 1) << 2) | (lrow >> 1));
+  const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
+  const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)a.K;
+  const int KT = (a.K + 127) / 128, NU = 2 * KT;
+  // the tile being loaded: first output row and column (GLU: first gate
+  // column) and this lane's base offsets
+  int m0 = 0, n0 = 0;
+  uint32_t offA = 0, offB = 0;
+  auto set_tile = [&](int tl) {
+    const TileXY t = tile_of(tl, tiles_m, tiles_n, GM);
+    m0 = t.tm * BM;
+    n0 = t.tn * (GLU ? BN / 2 : BN);
+    offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
+    offB = GLU ? (uint32_t)(lrow * a.K + cch * 16) : (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
+  };
+  auto ld = [&](int u, int j) {
+    uint8_t* dst = smem + (u % RU) * UNIT + (wave + j * NW) * 1024;
+    const int k0 = (u >> 1) * 128;
+    uint32_t o;
+    if (u & 1) {
+      if constexpr (GLU) {
+        // B unit g: gate or up half by (g / 4) % 2, 32-column pair g / 8,
+        // 8-row group g % 4
+        const int g = wave + j * NW;
+        const int row = ((g >> 2) & 1) * a.H + n0 + (g >> 3) * 32 + (g & 3) * 8;
+        o = offB + (uint32_t)row * (uint32_t)a.K + k0;
+      } else {
+        o = offB + j * stepB + k0;
       }
+    } else {
+      o = offA + j * stepA + k0;
+    }
+    if constexpr (KTAIL) {
+      if (k0 + cch * 16 >= a.K) o = kOOB;
+    }
+    if (u >= NU) o = kOOB;
+    if (u & 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
+  };
+  auto prologue_loads = [&]() {
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+#pragma unroll
+      for (int j = 0; j < LPU; ++j) ld(u, j);
+  };
+  const int lrow32 = lane & 31;
+  const int sw = (lrow32 >> 1) & 7;
+  const int lo0 = lrow32 * 128 + ((((lane >> 5) * 2) ^ sw) * 16);      // sub-step 0 chunk
+  const int lo1 = lrow32 * 128 + ((((lane >> 5) * 2 + 4) ^ sw) * 16);  // sub-step 1 chunk
+  // the fragment's second chunk sits at position ^ 1, i.e. +16 or -16 bytes
+  const int d1 = (sw & 1) ? -16 : 16;
+  v8i fa[2][MI], fb[2][NJ];
+  v16f acc[MI][NJ];
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto mf = [&](auto FC, int i, int j) {
+    constexpr int F = decltype(FC)::value;
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[F][i], fb[F][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+  };
+  // 16-byte half h (0..15) of a fragment set: fragment f = h / 2 (A_k for
+  // even f, B_k for odd, k = f / 2), part h % 2
+  auto half_read = [&](auto FC, const uint8_t* la, const uint8_t* lb, int h) {
+    constexpr int F = decltype(FC)::value;
+    const int f = h >> 1, k = f >> 1;
+    const uint8_t* rowp = ((f & 1) ? lb + (wn0 + k * 32) * 128 : la + (wm0 + k * 32) * 128) + ((h & 1) ? d1 : 0);
+    const v4i v = *reinterpret_cast<const v4i*>(rowp);
+    if (f & 1) {
+      if (h & 1) fb[F][k].hi = v; else fb[F][k].lo = v;
+    } else {
+      if (h & 1) fa[F][k].hi = v; else fa[F][k].lo = v;
+    }
+  };
+  // MFMA order: shells k = 0..3 ((k, 0..k) then (0..k-1, k)), so the first
+  // MFMAs need the fragments read first
+  constexpr int OI[16] = {0, 1, 1, 0, 2, 2, 2, 0, 1, 3, 3, 3, 3, 0, 1, 2};
+  constexpr int OJ[16] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2, 3, 3, 3, 3};
+
+  // One tile per block: a block that ends leaves its stores draining while
+  // the CU's next block loads (a loop over tiles inside one block would
+  // have to wait for them: loads and stores share the wait counter).
+  set_tile(blockIdx.x);
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // prologue: units 0..2; units 0 and 1 landed; stage 0's first fragments
+  prologue_loads();
+  {
+    __builtin_amdgcn_s_waitcnt(vm_imm(LPU));
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int h = 0; h < 16; ++h) half_read(I0{}, smem + lo0, smem + UNIT + lo0, h);
+    for (int kt = 0; kt < KT; ++kt) {
+      const uint8_t* la1 = smem + ((2 * kt) % RU) * UNIT + lo1;
+      const uint8_t* lb1 = smem + ((2 * kt + 1) % RU) * UNIT + lo1;
+      const uint8_t* la0n = smem + ((2 * kt + 2) % RU) * UNIT + lo0;
+      const uint8_t* lb0n = smem + ((2 * kt + 3) % RU) * UNIT + lo0;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        mf(I0{}, OI[q], OJ[q]);
+        ld(2 * kt + 3 + (q >> 3), q & 7);
+        half_read(I1{}, la1, lb1, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int q = 0; q < 9; ++q) {
+        mf(I1{}, OI[q], OJ[q]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // units up to 2kt + 3 landed (this wave's last LPU loads are unit 2kt + 4)
+      __builtin_amdgcn_s_waitcnt(vm_imm(LPU));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < 7; ++q) {
+        half_read(I0{}, la0n, lb0n, 2 * q);
+        half_read(I0{}, la0n, lb0n, 2 * q + 1);
+        mf(I1{}, OI[9 + q], OJ[9 + q]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      half_read(I0{}, la0n, lb0n, 14);
+      half_read(I0{}, la0n, lb0n, 15);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
+  // drain the zero-fill loads past the last stage; then every wave is done
+  // with the ring and the epilogue may stage in any of it
+  __builtin_amdgcn_s_waitcnt(vm_imm(0));
+  __syncthreads();
+  if constexpr (!GLU && !ROPE)
+    gemm256_split_epilogue(a, acc, m0, n0, wm0, wn0, wave, lane, smem,
+                           reinterpret_cast<LdsSplits*>(smem + NW * 64 * 128));
+  else
+    gemm_epilogue<MI, NJ, 128, NW, GLU, ROPE, false, RU * UNIT, RU * UNIT>(a, acc, m0, n0, wm0, wn0, wave, lane, smem,
+                                                                         smem);
+}
+
+// K from which the 256 x 256 plan runs on gemm256_kernel rather than on
+// gemm_kernel's eight 128 x 64 waves (measured, rotated operands: 2048 x
+// 32768 x 16384 868 -> 822 us, 2048 x 16384 x 16384 451 -> 420 us, 8192 x
+// 9216 x 12288 800 -> 773 us, x 6144 444 -> 439 us; at K = 3072-4096 the
+// single wave per SIMD exposes the tile's prologue and epilogue: 8192 x 9216
+// x 3072 240 -> 250 us, 2048 x 32768 x 4096 272 -> 278 us)
+constexpr int kDeepK = 6144;
+
+template <bool GLU, bool ROPE>
+hipError_t launch_256(const GemmArgs& a, hipStream_t st) {
+  const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  if (a.K % 128 == 0)
+    hipLaunchKernelGGL((gemm256_kernel<GLU, ROPE, false>), dim3(tiles), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((gemm256_kernel<GLU, ROPE, true>), dim3(tiles), dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1, int AE = BM, bool GLU = false,
@@ -720,8 +1062,9 @@ int64_t plan_cost(const GemmArgs& a, int BM, int BN, int cus) {
 
 // Tile plans (measured on MI355X, graph-replayed launches with HBM-resident
 // weights):
-//  M > 64: the plan of least per-CU load (plan_cost) among 256x256 tiles of
-//    eight 128x64 waves (M >= 512 only: the MFMA-bound shapes), 128x128 of
+//  M > 64: the plan of least per-CU load (plan_cost) among 256x256 tiles
+//    (M >= 512 only: the MFMA-bound shapes; gemm256_kernel's four 128x128
+//    waves from K = kDeepK, else eight 128x64 waves), 128x128 of
 //    sixteen 32x32 waves, 64x64 of four 32x32 waves and 64x32 with 256-deep
 //    stages. E.g. 256 x 16384 -> 128x128; 256 x 2560 -> 64x64 (160 tiles);
 //    256 x 2048 over K = 8192 -> 64x32 (256 tiles: 17 us against 22 us for
@@ -739,7 +1082,9 @@ hipError_t launch_planned(const GemmArgs& a, hipStream_t st) {
     for (int p = 0; p < 4; ++p)  // ordered large to small: ties go to the smaller tile
       if (cost[p] <= c) c = cost[p], best = p;
     switch (best) {
-      case 0: return launch_tiles<256, 256, 128, 64, 2, 4, 1, 256, false, ROPE>(a, st);
+      case 0:
+        return a.K >= kDeepK ? launch_256<false, ROPE>(a, st)
+                             : launch_tiles<256, 256, 128, 64, 2, 4, 1, 256, false, ROPE>(a, st);
       case 1: return launch_tiles<128, 128, 32, 32, 3, 2, 1, 128, false, ROPE>(a, st);
       case 2: return launch_tiles<64, 64, 32, 32, 4, 1, 1, 64, false, ROPE>(a, st);
       default: return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, ROPE>(a, st);
@@ -819,7 +1164,8 @@ hipError_t launch_gemm_geglu(const GemmArgs& a, hipStream_t st) {
     const int cus = device_cus();
     const int64_t c256 = a.M >= 512 ? plan_cost(a, 256, 256, cus) : INT64_MAX;
     const int64_t c128 = plan_cost(a, 128, 128, cus), c64 = plan_cost(a, 64, 64, cus);
-    if (c256 < c128 && c256 < c64) return launch_tiles<256, 256, 128, 64, 2, 4, 1, 256, true>(a, st);
+    if (c256 < c128 && c256 < c64)
+      return a.K >= kDeepK ? launch_256<true, false>(a, st) : launch_tiles<256, 256, 128, 64, 2, 4, 1, 256, true>(a, st);
     if (c128 < c64) return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, true>(a, st);
   }
   return launch_tiles<64, 64, 32, 64, 4, 1, 1, 64, true>(a, st);

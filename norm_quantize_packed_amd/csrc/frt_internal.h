@@ -101,6 +101,8 @@ struct GemmArgs {
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// compute units of the current device (cached per device)
+int device_cus();
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm_geglu(const GemmArgs& a, hipStream_t st);
 

@@ -12,7 +12,8 @@ import torch
 import norm_quantize_packed_amd as frt
 import workloads as wl
 from oracle import gemm, pack, producers
-from gpu_util import assert_gemm_f32, dev_bf16, dev_f32, scalar
+from gpu_util import (assert_codes_close, assert_gemm_f32, assert_rows_close, dev_bf16,
+                      dev_f32, host_bf16, host_u8, scalar)
 
 pytestmark = pytest.mark.gpu
 EPS = wl.EPS
@@ -80,3 +81,104 @@ def test_chain_ptok_workload3_slice():
     torch.cuda.synchronize()
     got = np.concatenate([o.cpu().numpy() for o in outs], 1)
     assert_gemm_f32(got, ref, "chain 3")
+
+
+def test_chain_adarms_workload2():
+    """Workload 2's decoder step on the GPU (the chained sites of the
+    AdaRMS stack): site 1 (broadcast prev_gate, mod_1) writes its residual
+    output in place and feeds the QKV GEMM; site 2 runs in place on that
+    residual with x_2, prev_gate = mod_1's gate chunk and mod_2, and feeds
+    the gate|up GEMM. Against the oracle's same chain: the residual after
+    both sites bit-exact, codes within one step on <= 0.1 %, both GEMMs
+    within the GEMM tolerance of the oracle chain and of the exact GEMM of
+    the GPU's own codes."""
+    D = wl.WORKLOADS[2].D
+    cal = wl.producer_inputs(2, calib=True)
+    c1 = producers.ada_norm_quant_fp8(cal["residual"], cal["x"], cal["gate"], cal["mod"], None, EPS)
+    s1 = producers.calibrate_act_scale(c1["y"])
+    c2 = producers.ada_norm_quant_fp8(c1["residual_out"], cal["x2"], cal["mod"][0, 2 * D:3 * D],
+                                      cal["mod2"], None, EPS)
+    s2 = producers.calibrate_act_scale(c2["y"])
+    inp = wl.producer_inputs(2)
+    M = inp["rows"]
+    r1 = producers.ada_norm_quant_fp8(inp["residual"], inp["x"], inp["gate"], inp["mod"], s1, EPS)
+    r2 = producers.ada_norm_quant_fp8(r1["residual_out"], inp["x2"], inp["mod"][0, 2 * D:3 * D],
+                                      inp["mod2"], s2, EPS)
+    ws = [wl.weights(2, 0), wl.weights(2, 1)]
+    packed = [pack.pack_weights(w["W"], w["b"]) for w in ws]
+
+    res = dev_bf16(inp["residual"])
+    mod1 = dev_bf16(inp["mod"])
+    x8 = [torch.empty(M, D, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    gpu_w = [_packed_gpu(w) for w in ws]
+    outs = [[torch.empty(M, n, dtype=torch.float32, device="cuda") for n in p[3]] for p in packed]
+    frt.frt_ada_norm_quant_fp8(res, mod1, scalar(s1), x=dev_bf16(inp["x"]), gate=dev_bf16(inp["gate"]),
+                               eps=EPS, residual_out=res, out_fp8=x8[0])
+    frt.frt_packed_gemm_fp8_split(x8[0], gpu_w[0][0], scalar(s1), gpu_w[0][1], outs[0], packed[0][3])
+    frt.frt_ada_norm_quant_fp8(res, dev_bf16(inp["mod2"]), scalar(s2), x=dev_bf16(inp["x2"]),
+                               gate=mod1[0, 2 * D:3 * D], eps=EPS, residual_out=res, out_fp8=x8[1])
+    frt.frt_packed_gemm_fp8_split(x8[1], gpu_w[1][0], scalar(s2), gpu_w[1][1], outs[1], packed[1][3])
+    torch.cuda.synchronize()
+
+    assert np.array_equal(host_bf16(res), r2["residual_out"]), "residual after both sites"
+    for site, (r, s, p, gw, o) in enumerate(zip((r1, r2), (s1, s2), packed, gpu_w, outs)):
+        codes = host_u8(x8[site])
+        assert_codes_close(codes, r["codes"], what=f"site {site + 1} codes")
+        w8, s_w, _, splits = p
+        assert np.array_equal(host_u8(gw[0]), w8) and np.float32(gw[1].item()) == s_w
+        got = np.concatenate([t.cpu().numpy() for t in o], 1)
+        chain = np.concatenate(gemm.packed_gemm_split(r["codes"], w8, s, s_w, None, splits), 1)
+        assert_gemm_f32(got, chain, f"workload 2 site {site + 1} GEMM vs the oracle chain")
+        own = gemm.epilogue(gemm.gemm_exact(codes, w8), s, s_w)
+        assert_gemm_f32(got, own, f"workload 2 site {site + 1} GEMM vs its own codes")
+
+
+@pytest.mark.parametrize("cid", [3, 5])
+def test_chain_ptok_full_size(cid):
+    """The per-token-table site at full size, all on the GPU: producer over
+    every row (codes within one step on <= 0.1 % of the oracle's, y within
+    1e-5 per row), the packer on the workload's own weights, and the packed
+    GEMM in the bench's launch with fp32 out; every GEMM output is checked
+    against the exact oracle GEMM of the GPU's own codes and packed weights
+    (identical operands). (A comparison with the oracle chain's GEMM adds
+    nothing: it differs from that by exactly alpha times the allowed code
+    differences times W, and at 25 M codes a row can hold several of them.)"""
+    wk = wl.WORKLOADS[cid]
+    R, D = wk.rows, wk.D
+    cal = wl.producer_inputs(cid, calib=True)
+    s = producers.calibrate_act_scale(producers.ptok_norm_quant_fp8(
+        cal["x"], cal["temb"], cal["table"], None, wk.shift_idx, wk.scale_idx, EPS)["y"])
+    del cal
+    inp = wl.producer_inputs(cid)
+    r = producers.ptok_norm_quant_fp8(inp["x"], inp["temb"], inp["table"], s,
+                                      wk.shift_idx, wk.scale_idx, EPS)
+    x8 = torch.empty(R, D, dtype=torch.uint8, device="cuda")
+    y = torch.empty(R, D, dtype=torch.float32, device="cuda")
+    frt.frt_ptok_table_norm_quant_fp8(dev_bf16(inp["x"]), dev_bf16(inp["temb"].reshape(R, -1)),
+                                      dev_f32(inp["table"]), scalar(s), wk.shift_idx, wk.scale_idx,
+                                      eps=EPS, out_fp8=x8, y_f32=y)
+    torch.cuda.synchronize()
+    del inp
+    codes = host_u8(x8)
+    assert_codes_close(codes, r["codes"], what=f"workload {cid} codes")
+    assert_rows_close(y.cpu().numpy(), r["y"], what=f"workload {cid} y")
+    del y
+    w = wl.weights(cid, 0)
+    W8, ws, bc = _packed_gpu(w)
+    splits = list(w["splits"])
+    bias = host_bf16(bc) if wk.bias else None
+    if cid == 3:   # the packer bit-exact at this size (workload 5's is sampled elsewhere)
+        w8r, s_wr, br, _ = pack.pack_weights(w["W"], w["b"])
+        assert np.array_equal(host_u8(W8), w8r) and np.float32(ws.item()) == s_wr
+        assert np.array_equal(bias, br)
+    del w
+    outs = [torch.empty(R, n, dtype=torch.float32, device="cuda") for n in splits]
+    frt.frt_packed_gemm_fp8_split(x8, W8, scalar(s), ws, outs, splits,
+                                  bias_cat=bc if wk.bias else None)
+    torch.cuda.synchronize()
+    got = np.concatenate([o.cpu().numpy() for o in outs], 1)
+    del outs
+    w8 = host_u8(W8)
+    s_w = np.float32(ws.item())
+    own = gemm.epilogue(gemm.gemm_exact(codes, w8), s, s_w, bias)
+    assert_gemm_f32(got, own, f"workload {cid} full GEMM vs its own operands")

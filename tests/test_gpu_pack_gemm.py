@@ -290,3 +290,47 @@ def test_gemm_large_staged_epilogue_matches_per_lane_stores():
     for i, (a, b, r) in enumerate(zip(staged, lane, ref)):
         assert np.array_equal(a, b), f"split {i}: staged and per-lane stores differ"
         assert_gemm_bf16(a, r, f"2000x5000x528 split {i}")
+
+
+@pytest.mark.parametrize("K", [6144, 6160])
+def test_gemm_deep_k_plan_full_grid(K):
+    """The 256x256 plan at K >= 6144 (four 128x128 waves, five-unit ring):
+    2000 x 5000 takes it (160 tiles, one round; ragged M and N), with a bias,
+    three splits whose boundaries fall inside tiles and, at K = 6160, a K
+    tail. Every fp32 output is checked against the oracle; the staged bf16
+    stores (whole 128-byte row segments) and the per-lane stores of a padded
+    stride give the same bits, match the oracle and write nothing outside
+    their outputs; a second call repeats the bits."""
+    rng = np.random.default_rng(K)
+    M, splits = 2000, [3000, 1200, 800]
+    N = sum(splits)
+    x8 = wl.random_codes(6101 + K, (M, K))
+    w8 = wl.random_codes(6102 + K, (N, K))
+    bias = wl.to_bf16_bits(0.05 * rng.standard_normal(N).astype(np.float32))
+    s_a, s_w = np.float32(0.003), np.float32(0.002)
+    ref = gemm.packed_gemm_split(x8, w8, s_a, s_w, bias, splits)
+    f32 = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=True)
+    for i, (g, r) in enumerate(zip(f32, ref)):
+        assert_gemm_f32(g, r, f"2000x5000x{K} fp32 split {i}")
+    staged = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
+    lane = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False, ld_pad=6)
+    again = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
+    for i, (a, b, c, r) in enumerate(zip(staged, lane, again, ref)):
+        assert np.array_equal(a, b), f"split {i}: staged and per-lane stores differ"
+        assert np.array_equal(a, c), f"split {i}: repeated call differs"
+        assert_gemm_bf16(a, r, f"2000x5000x{K} split {i}")
+
+
+def test_gemm_deep_k_plan_row_capacity():
+    """M below the buffers' rows on the deep-K 256x256 plan (the last row of
+    tiles is partial): rows past M are neither written nor read."""
+    M, K, N = 1900, 6144, 5120
+    x8 = wl.random_codes(6301, (2048, K))
+    w8 = wl.random_codes(6302, (N, K))
+    out = torch.full((2048, N), 1.5, dtype=torch.bfloat16, device="cuda")
+    frt.frt_packed_gemm_fp8_split(dev_u8(x8), dev_u8(w8), scalar(0.01), scalar(0.002),
+                                  [out], [N], M=M)
+    torch.cuda.synchronize()
+    assert (out[M:].float() == 1.5).all()
+    ref = gemm.packed_gemm_split(x8[:M], w8, np.float32(0.01), np.float32(0.002), None, [N])[0]
+    assert_gemm_bf16(host_bf16(out[:M]), ref, "deep-K M=1900")
