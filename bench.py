@@ -724,16 +724,16 @@ _SHARED_SOURCES = ("frt_api.hip", "frt_device.h", "frt_internal.h")
 
 def _kernel_files(kind):
     csrc = os.path.join(ROOT, "norm_quantize_packed_amd", "csrc")
-    every = sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".h")))
+    every = sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".h", ".inc")))
     if kind is None:
         return csrc, every
     if kind.startswith("norm"):
-        own = "frt_norm.hip"
+        own = {"frt_norm.hip"}
     elif kind.startswith("gemm") or kind.startswith(("gateup", "qkv")):
-        own = "frt_gemm.hip"
+        own = {"frt_gemm.hip", "frt_gemm_epilogue.inc"}
     else:
         return csrc, every
-    return csrc, sorted(set(_SHARED_SOURCES) | {own})
+    return csrc, sorted(set(_SHARED_SOURCES) | own)
 
 
 def kernel_sources_sha(kind=None):

@@ -77,243 +77,16 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 }
 
 
-// Epilogue shared by the tile kernels: alpha * acc + bias, then the split,
-// GEGLU or RoPE form of the output. `slot` is SLOT bytes of LDS that no wave
-// of the block reads any more and that no load still targets (each wave
-// stages only in its own part of it, so no block barrier is needed); `lds` is
-// the whole allocation (TOTAL bytes), used after a block barrier when the
-// staging needs more than the slot.
+// The tile kernels' epilogue (frt_gemm_epilogue.inc) as a function, for the
+// GEGLU and RoPE forms of gemm256_kernel (gemm_kernel includes the same
+// source in its own body, where the compiler schedules the argument loads
+// of the split table lazily, as a function boundary does not let it).
+// `slot` is SLOT bytes of LDS that no wave of the block reads any more and
+// that no load still targets; `lds` is the whole allocation (TOTAL bytes).
 template <int MI, int NJ, int WN, int NW, bool GLU, bool ROPE, bool FP4, int SLOT, int TOTAL>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, v16f (&acc)[MI][NJ], int m0, int n0, int wm0,
+__device__ __forceinline__ void gemm_epilogue(GemmArgs a, v16f (&acc)[MI][NJ], int m0, int n0, int wm0,
                                               int wn0, int wave, int lane, uint8_t* slot, uint8_t* lds) {
-  const float alpha = FP4 ? 1.0f : (*a.act_scale) * (*a.w_scale);
-  if constexpr (ROPE) {
-    const int nq = a.nh * a.hd, nk = a.kv * a.hd;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int n = n0 + wn0 + j * 32 + (lane & 31);
-      const bool nok = n < a.N;
-      const bool rot = n < nq + nk;
-      const int d = n % a.hd;
-      const float b = (a.bias != nullptr && nok) ? bf16f(a.bias[n]) : 0.0f;
-      uint16_t* dst;
-      int64_t ld;
-      if (n < nq) {
-        dst = a.q_out + n;
-        ld = nq;
-      } else if (rot) {
-        dst = a.k_cache + a.P * nk + (n - nq);
-        ld = nk;
-      } else {
-        dst = a.v_cache + a.P * nk + (n - nq - nk);
-        ld = nk;
-      }
-      // a' = a c - b s on the even column, b' = b c + a s on the odd one
-      const float sgn = (n & 1) ? 1.0f : -1.0f;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        // the (cos, sin) words of this lane's 16 rows, loaded together (rows
-        // past M read row M - 1 and are not stored)
-        uint32_t cs[16];
-        const uint16_t* rp = a.rope + (d & ~1);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = min(m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), a.M - 1);
-          cs[r] = rot ? *reinterpret_cast<const uint32_t*>(rp + (int64_t)m * a.hd) : 0u;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const float v = __uint_as_float(f2bf(alpha * acc[i][j][r] + b) << 16);
-          const float p = lane_xor1(v);
-          const float o = rot ? __builtin_fmaf(v, bf16lo(cs[r]), sgn * (p * bf16hi(cs[r]))) : v;
-          if (nok && m < a.M) dst[(int64_t)m * ld] = (uint16_t)f2bf(o);
-        }
-      }
-    }
-    return;
-  }
-  if constexpr (GLU) {
-    if constexpr (FP4) {
-    if (a.q4 != nullptr) {
-      // GEGLU to MXFP4: a block scale needs the maximum over 32 consecutive
-      // columns, which the MFMA layout spreads over 32 lanes, so the wave's
-      // y tile goes through LDS and comes back row-wise: 8 consecutive
-      // columns per lane, one 32-column block per quad, quantised as the
-      // standalone GEGLU -> MXFP4 kernel quantises them. The tiles go to
-      // ring slot KT % NS, whose last stage (KT - NS) every wave finished
-      // reading before a later barrier, when they fit in it; else to the
-      // whole ring after a barrier. Each wave reads back only what it wrote.
-      static_assert(NJ == 2, "one 32-column gate block per wave");
-      constexpr int YR = MI * 32;  // rows of the wave's y tile (32 columns)
-      constexpr bool ONE_SLOT = NW * YR * 32 * 4 <= SLOT;
-      static_assert(ONE_SLOT || NW * YR * 32 * 4 <= TOTAL, "y tiles exceed the LDS");
-      uint8_t* ybase = lds;
-      if constexpr (ONE_SLOT)
-        ybase = slot;
-      else
-        __syncthreads();
-      float* ys = reinterpret_cast<float*>(ybase) + wave * YR * 32;
-      const int gc0 = n0 + (wn0 >> 1);  // the wave's first gate column
-      const float bg = (a.bias != nullptr && gc0 < a.H) ? bf16f(a.bias[gc0 + (lane & 31)]) : 0.0f;
-      const float bu = (a.bias != nullptr && gc0 < a.H) ? bf16f(a.bias[a.H + gc0 + (lane & 31)]) : 0.0f;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const float vg = alpha * acc[i][0][r] + bg;
-          const float vu = alpha * acc[i][1][r] + bu;
-          ys[rl * 32 + (lane & 31)] =
-              gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));  // this wave's LDS writes done
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int k = 0; k < YR * 4 / 64; ++k) {
-        const int t = lane + 64 * k, rl = t >> 2, v = t & 3;
-        const float4 y0 = *reinterpret_cast<const float4*>(ys + rl * 32 + v * 8);
-        const float4 y1 = *reinterpret_cast<const float4*>(ys + rl * 32 + v * 8 + 4);
-        const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-        uint32_t am = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) am = max(am, __float_as_uint(fabsf(y[e])));
-        const uint32_t sbyte = e8m0_of_amax(quad_umax(am));
-        const uint32_t codes = mxfp4_pack8(y, sbyte);
-        const int m = m0 + wm0 + rl;
-        if (m < a.M && gc0 < a.H) {
-          const int64_t c = gc0 + v * 8;
-          *reinterpret_cast<uint32_t*>(a.q4 + (int64_t)m * a.ld_q4 + c / 2) = codes;
-          if (v == 0) a.sc4[e8m0_off(m, c / 32, a.ld_sc4)] = (uint8_t)sbyte;
-        }
-      }
-      return;
-    }
-    }
-    // gate and up rounded to bf16 as the unfused GEMM output would be,
-    // then the GEGLU quantiser of frt_ffn.hip
-    const float qs = *a.q_scale, qr = 1.0f / qs;
-#pragma unroll
-    for (int q = 0; q < NJ / 2; ++q) {
-      const int gc = n0 + (wn0 >> 1) + q * 32 + (lane & 31);
-      if (gc >= a.H) continue;
-      const float bg = a.bias != nullptr ? bf16f(a.bias[gc]) : 0.0f;
-      const float bu = a.bias != nullptr ? bf16f(a.bias[a.H + gc]) : 0.0f;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          if (m < a.M) {
-            const float vg = alpha * acc[i][2 * q][r] + bg;
-            const float vu = alpha * acc[i][2 * q + 1][r] + bu;
-            const float y = gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
-            a.q8[(int64_t)m * a.ld_q8 + gc] = (uint8_t)cvt2_fp8(clamp_fp8(div_rn(y, qs, qr)), 0.0f);
-          }
-        }
-      }
-    }
-    return;
-  }
-  // Waves of 128 x 64 (the 256x256 plan) hold whole 128-byte row segments
-  // of the bf16 output. With vec_out they pass them through LDS, 64 rows at
-  // a time, and store 16 bytes a lane (8 rows x 128 bytes an instruction)
-  // instead of the 64-byte halves the MFMA layout gives. Each wave uses its
-  // own 8 KB of ring slot KT % NS, whose last stage every wave finished
-  // reading before an earlier barrier and into which no load is pending, so
-  // no block barrier is needed. Within the 64 x 128-byte buffer, 16-byte
-  // chunk c of row r sits at position c ^ (r & 7).
-  constexpr bool WIDE = !GLU && !ROPE && !FP4 && WN % 64 == 0 && MI % 2 == 0 && NW * 64 * 128 <= SLOT;
-  if constexpr (WIDE) {
-    if (a.vec_out) {
-      uint8_t* wb = slot + wave * (64 * 128);
-      float bj[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int n = n0 + wn0 + j * 32 + (lane & 31);
-        bj[j] = (a.bias != nullptr && n < a.N) ? bf16f(a.bias[n]) : 0.0f;
-      }
-      // 64-column halves of the wave tile, then 64-row halves
-#pragma unroll
-      for (int jh = 0; jh < NJ / 2; ++jh) {
-      // this lane stores 8-column chunk lane % 8 of the half in every row it
-      // writes; split widths are multiples of 8, so the chunk lies in one
-      // split, found once per half
-      const int nc = n0 + wn0 + jh * 64 + (lane & 7) * 8;
-      const bool nok = nc < a.N;
-      uint8_t* colp = reinterpret_cast<uint8_t*>(a.sp.ptr[0]) + (int64_t)nc * 2;
-      int64_t ldb = a.sp.ld[0] * 2;
-#pragma unroll
-      for (int s = 1; s < FRT_MAX_SPLITS; ++s) {
-        if (s < a.sp.n && nc >= a.sp.off[s]) {
-          colp = reinterpret_cast<uint8_t*>(a.sp.ptr[s]) + (int64_t)(nc - a.sp.off[s]) * 2;
-          ldb = a.sp.ld[s] * 2;
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < MI / 2; ++h) {
-#pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-          for (int j2 = 0; j2 < 2; ++j2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int j = 2 * jh + j2;
-              const int rr = i2 * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);  // row in the half
-              const int c = j2 * 32 + (lane & 31);                                 // column in the half
-              const float v = alpha * acc[2 * h + i2][j][r] + bj[j];
-              *reinterpret_cast<uint16_t*>(wb + rr * 128 + (((c >> 3) ^ (rr & 7)) << 4) + (c & 7) * 2) =
-                  (uint16_t)f2bf(v);
-            }
-        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int rr = (lane >> 3) + 8 * k, cc = lane & 7;
-          const uint4 v = *reinterpret_cast<const uint4*>(wb + rr * 128 + ((cc ^ (rr & 7)) << 4));
-          const int m = m0 + wm0 + h * 64 + rr;
-          if (nok && m < a.M) *reinterpret_cast<uint4*>(colp + (int64_t)m * ldb) = v;
-        }
-        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
-        __builtin_amdgcn_wave_barrier();
-      }
-      }
-      return;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int n = n0 + wn0 + j * 32 + (lane & 31);
-    if (n >= a.N) continue;
-    uint8_t* base = reinterpret_cast<uint8_t*>(a.sp.ptr[0]);
-    int64_t ld = a.sp.ld[0];
-    int off0 = 0;
-#pragma unroll
-    for (int s = 1; s < FRT_MAX_SPLITS; ++s) {
-      if (s < a.sp.n && n >= a.sp.off[s]) {
-        base = reinterpret_cast<uint8_t*>(a.sp.ptr[s]);
-        ld = a.sp.ld[s];
-        off0 = a.sp.off[s];
-      }
-    }
-    const float b = a.bias != nullptr ? bf16f(a.bias[n]) : 0.0f;
-    const int col = n - off0;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (m < a.M) {
-          const float v = alpha * acc[i][j][r] + b;
-          if (a.out_f32)
-            reinterpret_cast<float*>(base)[(int64_t)m * ld + col] = v;
-          else
-            reinterpret_cast<uint16_t*>(base)[(int64_t)m * ld + col] = (uint16_t)f2bf(v);
-        }
-      }
-    }
-  }
+#include "frt_gemm_epilogue.inc"
 }
 
 // Tiled kernel: BM x BN block tile, WM x WN per wave, 128-deep K staging.
@@ -339,10 +112,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, v16f (&acc)[MI]
 // alternate between two accumulator sets (independent MFMAs back to back);
 // large wave tiles (two waves per SIMD) reuse one fragment set and rely on
 // the other wave of the SIMD to cover the fragment reads.
-// AE (<= BM): A rows actually loaded. A call with M <= AE leaves tile rows
-// [AE, BM) unloaded: their MFMA results only reach output rows >= M, which
-// the epilogue never stores, and every wave still issues the same number of
-// loads per stage, so the vmcnt counts stay exact.
+// AE (<= BM): A rows actually loaded, and the A rows a stage holds in LDS
+// (the B rows follow them). A call with M <= AE needs no tile rows past AE:
+// fragment reads of those rows take row 0 instead (in-bounds reads whose
+// MFMA results only reach output rows >= M, which the epilogue never
+// stores), and every wave still issues the same number of loads per stage,
+// so the vmcnt counts stay exact.
 //
 // GLU: the gate/up GEGLU form. W8 holds 2H rows (gate rows, then up rows)
 // and a tile covers BN/2 gate columns [g0, g0 + BN/2) together with the
@@ -386,7 +161,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   constexpr int WAVES_N = BN / WN;
   constexpr int NW = (BM / WM) * WAVES_N;
   constexpr int MI = WM / 32, NJ = WN / 32;
-  constexpr int ROWS = BM + BN;
+  constexpr int ROWS = AE + BN;  // LDS rows of a 128-deep sub-buffer: A, then B
   static_assert(AE <= BM && AE % 16 == 0, "A rows loaded");
   static_assert(!GLU || (NJ % 2 == 0 && WN % 64 == 0), "GEGLU pairs need 64-column wave tiles");
   constexpr int LOADS = (AE + BN) / 8;  // 1 KiB load instructions per stage
@@ -482,7 +257,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       for (int j = 0; j < LPW; ++j) {
         const bool A = j < LPA;
         // A rows 8u.., B rows BM + 8u.. (u counts this operand's loads)
-        const int u = wave + (A ? j : j - LPA) * NW + (A ? 0 : BM / 8);
+        const int u = wave + (A ? j : j - LPA) * NW + (A ? 0 : AE / 8);
         uint8_t* dst = smem + SL * STAGE + q * SUBB + u * 1024;
         uint32_t o;
         if (A) {
@@ -526,6 +301,8 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const uint8_t* lbase1 = smem + lrow32 * 128 + ((((lane >> 5) * 2 + 4) ^ sw) * 16);
   // this lane's scale dword within a 32-row block: row lrow32, K half l / 32
   const uint8_t* sbase = smem + SCBASE + lane * 4;
+  // first LDS row of A fragment i of this wave (row 0 past the loaded rows)
+  auto arow = [&](int i) { return (AE == BM || wm0 + i * 32 < AE) ? wm0 + i * 32 : 0; };
   auto read_frags = [&](auto SLC, auto SUBC, auto* af, auto* bf) {
     constexpr int SL = decltype(SLC)::value, SUB = decltype(SUBC)::value;
     if constexpr (FP4) {
@@ -533,9 +310,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       const uint8_t* lb = smem + lrow32 * 128 + ((((SUB & 3) * 2 + (lane >> 5)) ^ sw) * 16) + SL * STAGE +
                           (SUB >> 2) * SUBB;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const v4i*>(lb + (BM + wn0 + j * 32) * 128);
+      for (int j = 0; j < NJ; ++j) bf[j] = *reinterpret_cast<const v4i*>(lb + (AE + wn0 + j * 32) * 128);
 #pragma unroll
-      for (int i = 0; i < MI; ++i) af[i] = *reinterpret_cast<const v4i*>(lb + (wm0 + i * 32) * 128);
+      for (int i = 0; i < MI; ++i) af[i] = *reinterpret_cast<const v4i*>(lb + arow(i) * 128);
       if constexpr ((SUB & 3) == 0) {
         // the sub-buffer's scales; A blocks past the AER staged rows (rows
         // past M) take the last staged block
@@ -555,14 +332,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
     const int d1 = (sw & 1) ? -16 : 16;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const uint8_t* rowp = lb + (BM + wn0 + j * 32) * 128;
+      const uint8_t* rowp = lb + (AE + wn0 + j * 32) * 128;
       const v4i lo = *reinterpret_cast<const v4i*>(rowp);
       const v4i hi = *reinterpret_cast<const v4i*>(rowp + d1);
       bf[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const uint8_t* rowp = lb + (wm0 + i * 32) * 128;
+      const uint8_t* rowp = lb + arow(i) * 128;
       const v4i lo = *reinterpret_cast<const v4i*>(rowp);
       const v4i hi = *reinterpret_cast<const v4i*>(rowp + d1);
       af[i] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -682,8 +459,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       for (int j = 0; j < NJ; ++j) acc[i][j] += acc2[i][j];
   }
 
-  gemm_epilogue<MI, NJ, WN, NW, GLU, ROPE, FP4, STAGE, NS * STAGE>(a, acc, m0, n0, wm0, wn0, wave, lane,
-                                                                 smem + (KT % NS) * STAGE, smem);
+  {
+    constexpr int SLOT = STAGE, TOTAL = NS * STAGE;
+    uint8_t* slot = smem + (KT % NS) * STAGE;
+    uint8_t* lds = smem;
+#include "frt_gemm_epilogue.inc"
+  }
 }
 
 // The split table in LDS: the 256 x 256 kernel's epilogue looks a column's

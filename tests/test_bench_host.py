@@ -111,7 +111,7 @@ def test_traffic_record_follows_its_own_kernel_sources():
     producer's: a change to one kernel file leaves the other's hash alone."""
     g = set(bench._kernel_files("gemm1")[1])
     n = set(bench._kernel_files("norm1")[1])
-    assert "frt_gemm.hip" in g and "frt_norm.hip" not in g
+    assert {"frt_gemm.hip", "frt_gemm_epilogue.inc"} <= g and "frt_norm.hip" not in g
     assert "frt_norm.hip" in n and "frt_gemm.hip" not in n
     assert {"frt_api.hip", "frt_device.h", "frt_internal.h"} <= g & n
     assert bench.kernel_sources_sha("gemm1") != bench.kernel_sources_sha("norm1")
