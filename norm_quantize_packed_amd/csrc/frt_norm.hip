@@ -248,7 +248,9 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ptok_norm_kernel(Pt
   const float* tab_s = a.table + (int64_t)a.shift_idx * a.D;
   const float* tab_c = a.table + (int64_t)a.scale_idx * a.D;
 
-  float x[NV][VEC];
+  // x stays in its packed bf16 form (16 bytes a vector) and is widened
+  // where it is used, which keeps more rows in flight per CU
+  Vec<VEC> xv[NV];
   Vec<VEC> tsh[NV], tsc[NV];
   float ts[EARLY ? NV : 1][VEC], tc[EARLY ? NV : 1][VEC];
   float sum = 0.0f;
@@ -258,8 +260,7 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ptok_norm_kernel(Pt
     const int v = sub * 64 + lane + i * 64 * WPR;
     if (row_ok && v < nvec) {
       const int64_t c = (int64_t)v * VEC;
-      Vec<VEC> xv;
-      xv.load(a.x + row * a.ld_x + c);
+      xv[i].load(a.x + row * a.ld_x + c);
       tsh[i].load(trow + (int64_t)a.shift_idx * a.D + c);
       tsc[i].load(trow + (int64_t)a.scale_idx * a.D + c);
       if constexpr (EARLY) {
@@ -267,13 +268,7 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ptok_norm_kernel(Pt
         load_f32<VEC>(tab_c + c, tc[i]);
       }
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        x[i][e] = xv.f(e);
-        sum += x[i][e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) x[i][e] = 0.0f;
+      for (int e = 0; e < VEC; ++e) sum += xv[i].f(e);
     }
   }
   const float inv_d = 1.0f / (float)a.D;
@@ -285,7 +280,7 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ptok_norm_kernel(Pt
     if (row_ok && v < nvec) {
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        const float d = x[i][e] - mu;
+        const float d = xv[i].f(e) - mu;
         sq = __builtin_fmaf(d, d, sq);
       }
     }
@@ -320,7 +315,7 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ptok_norm_kernel(Pt
         for (int e = 0; e < VEC; ++e) {
           const float shift = tsv[e] + tsh[i].f(e);
           const float scale = tcv[e] + tsc[i].f(e);
-          const float n = (x[i][e] - mu) * rstd;
+          const float n = (xv[i].f(e) - mu) * rstd;
           y[e] = __builtin_fmaf(n, scale, n) + shift;
         }
         if (a.y != nullptr) store_f32<VEC>(a.y + row * a.ld_y + c, y);
