@@ -7,7 +7,9 @@
 //
 // Both operands are K-contiguous ("TN"). The main loop runs on the CDNA4
 // FP8 matrix cores, v_mfma_f32_32x32x64_f8f6f4 (A = 32 rows of x8, B = 32
-// rows of W8, 64-deep K step, fp32 accumulate).
+// rows of W8, 64-deep K step, fp32 accumulate) in the tile kernels, and
+// v_mfma_f32_16x16x128_f8f6f4 (16 rows each, 128-deep) in the deep-K
+// 256 x 256 kernel.
 //
 // Tiles are staged through LDS with direct buffer->LDS loads, in 128-deep K
 // stages (a stage may hold NSUB of them), row-major with one 128-byte
@@ -38,6 +40,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr uint32_t kOOB = 0x80000000u;  // offset past any record count
@@ -56,6 +59,11 @@ __device__ __forceinline__ constexpr int vm_lgkm0_imm(int n) {
 // s_waitcnt immediate: vmcnt(n) alone (lgkmcnt and expcnt at their maxima)
 __device__ __forceinline__ constexpr int vm_imm(int n) {
   return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+
+// s_waitcnt immediate: lgkmcnt(n) alone (vmcnt and expcnt at their maxima)
+__device__ __forceinline__ constexpr int lgkm_imm(int n) {
+  return 0xF | (0x3 << 14) | (0x7 << 4) | ((n & 0xF) << 8);
 }
 
 struct TileXY {
@@ -83,8 +91,8 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // of the split table lazily, as a function boundary does not let it).
 // `slot` is SLOT bytes of LDS that no wave of the block reads any more and
 // that no load still targets; `lds` is the whole allocation (TOTAL bytes).
-template <int MI, int NJ, int WN, int NW, bool GLU, bool ROPE, bool FP4, int SLOT, int TOTAL>
-__device__ __forceinline__ void gemm_epilogue(GemmArgs a, v16f (&acc)[MI][NJ], int m0, int n0, int wm0,
+template <int MI, int NJ, int WN, int NW, bool GLU, bool ROPE, bool FP4, int SLOT, int TOTAL, typename ACC>
+__device__ __forceinline__ void gemm_epilogue(GemmArgs a, ACC (&acc)[MI][NJ], int m0, int n0, int wm0,
                                               int wn0, int wave, int lane, uint8_t* slot, uint8_t* lds) {
 #include "frt_gemm_epilogue.inc"
 }
@@ -490,14 +498,16 @@ __device__ __forceinline__ void split_of(const LdsSplits* t, int n, int esize, u
 }
 
 // Split epilogue of the 256 x 256 kernel (bf16 or fp32 out, optional bias):
-// out = alpha * acc + bias into the split owning each column. With vec_out
-// each 64 x 64 quarter of the wave tile goes through the wave's own 8 KB of
-// LDS and leaves as whole 128-byte row segments (16 bytes a lane); else each
-// lane stores its elements. Called after a block barrier that ended every
-// use of the ring; `tab` must not overlap the waves' staging (32 KB).
-__device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v16f (&acc)[4][4], int m0, int n0, int wm0,
+// out = alpha * acc + bias into the split owning each column. The
+// accumulators are 16 x 16 fragments: lane l holds column l % 16 of
+// fragment (i, j), rows 4 (l / 16) + r, r = 0..3. With vec_out each 64 x 64
+// quarter of the wave tile goes through the wave's own 8 KB of LDS and leaves
+// as whole 128-byte row segments (16 bytes a lane); else each lane stores its
+// elements. Called after a block barrier that ended every use of the ring;
+// `tab` must not overlap the waves' staging (32 KB).
+__device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v4f (&acc)[8][8], int m0, int n0, int wm0,
                                                        int wn0, int wave, int lane, uint8_t* smem, LdsSplits* tab) {
-  constexpr int MI = 4, NJ = 4;
+  constexpr int MI = 8, NJ = 8;
   if (threadIdx.x < FRT_MAX_SPLITS) {
     tab->ptr[threadIdx.x] = reinterpret_cast<uint64_t>(a.sp.ptr[threadIdx.x]);
     tab->ld[threadIdx.x] = a.sp.ld[threadIdx.x];
@@ -506,15 +516,20 @@ __device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v16f (
   }
   __syncthreads();
   const float alpha = (*a.act_scale) * (*a.w_scale);
+  const int c16 = lane & 15, r4 = (lane >> 4) * 4;
   float bj[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    const int n = n0 + wn0 + j * 32 + (lane & 31);
+    const int n = n0 + wn0 + j * 16 + c16;
     bj[j] = (a.bias != nullptr && n < a.N) ? bf16f(a.bias[n]) : 0.0f;
   }
   // whole wave tile inside M (every tile but the last row of tiles)
   const bool rows_in = m0 + wm0 + 128 <= a.M;
   if (a.vec_out) {
+    // 16-byte chunk c of staging row r sits at c ^ key(r); the key's bit 1
+    // from row bit 3 keeps the four rows one store instruction writes
+    // (r, r + 4, r + 8, r + 12) on distinct banks
+    auto key = [](int r) { return (r & 7) ^ ((r >> 2) & 2); };
     uint8_t* wb = smem + wave * (64 * 128);
 #pragma unroll
     for (int jh = 0; jh < 2; ++jh) {
@@ -527,17 +542,16 @@ __device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v16f (
       split_of(tab, nok ? nc : 0, 2, colp, ldb);
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        // quarter (h, jh) into LDS: 16-byte chunk c of row r at c ^ (r & 7)
 #pragma unroll
-        for (int i2 = 0; i2 < 2; ++i2)
+        for (int i2 = 0; i2 < 4; ++i2)
 #pragma unroll
-          for (int j2 = 0; j2 < 2; ++j2)
+          for (int j2 = 0; j2 < 4; ++j2)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int rr = i2 * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-              const int c = j2 * 32 + (lane & 31);
-              const float v = alpha * acc[2 * h + i2][2 * jh + j2][r] + bj[2 * jh + j2];
-              *reinterpret_cast<uint16_t*>(wb + rr * 128 + (((c >> 3) ^ (rr & 7)) << 4) + (c & 7) * 2) =
+            for (int r = 0; r < 4; ++r) {
+              const int rr = i2 * 16 + r4 + r;
+              const int c = j2 * 16 + c16;
+              const float v = alpha * acc[4 * h + i2][4 * jh + j2][r] + bj[4 * jh + j2];
+              *reinterpret_cast<uint16_t*>(wb + rr * 128 + (((c >> 3) ^ key(rr)) << 4) + (c & 7) * 2) =
                   (uint16_t)f2bf(v);
             }
         __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
@@ -546,7 +560,7 @@ __device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v16f (
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int rr = (lane >> 3) + 8 * k;
-          const uint4 v = *reinterpret_cast<const uint4*>(wb + rr * 128 + (((lane & 7) ^ (rr & 7)) << 4));
+          const uint4 v = *reinterpret_cast<const uint4*>(wb + rr * 128 + (((lane & 7) ^ key(rr)) << 4));
           if (nok && (rows_in || mb + rr < a.M)) *reinterpret_cast<uint4*>(colp + (int64_t)(mb + rr) * ldb) = v;
         }
         __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
@@ -560,7 +574,7 @@ __device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v16f (
     constexpr bool F32 = decltype(F32C)::value;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int n = n0 + wn0 + j * 32 + (lane & 31);
+      const int n = n0 + wn0 + j * 16 + c16;
       if (n >= a.N) continue;
       uint8_t* colp;
       int64_t ldb;
@@ -568,8 +582,8 @@ __device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v16f (
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = m0 + wm0 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm0 + i * 16 + r4 + r;
           const float v = alpha * acc[i][j][r] + bj[j];
           if (rows_in || m < a.M) {
             if constexpr (F32)
@@ -587,7 +601,12 @@ __device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v16f (
 }
 
 // Large-M FP8 kernel: a 256 x 256 block tile of four 128 x 128 wave tiles
-// (one wave per SIMD, accumulators in the matrix-core registers).
+// (one wave per SIMD, accumulators in the matrix-core registers), on
+// v_mfma_f32_16x16x128_f8f6f4: each MFMA takes a whole 128-deep stage of a
+// 16-row A fragment and a 16-row B fragment. Under sustained load the board
+// holds an FP8 MFMA loop of this shape at a higher engine clock than one of
+// 32x32x64 MFMAs doing the same work (measured: 2.05 against 1.86 GHz), and
+// this kernel's time follows the clock.
 //
 // The LDS is a ring of five 32 KB units; a unit holds the A rows or the B
 // rows of one 128-deep stage (256 rows x 128 bytes, the same swizzled row
@@ -598,21 +617,25 @@ __device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v16f (
 // keeps more lines in flight this way; half-line row segments, the other way
 // to deepen a ring within 160 KB, fetch each line twice and are slower).
 //
-// Each wave double-buffers its fragments across the two 64-deep sub-steps
-// of a stage and issues its work in a fixed order (no compiler reordering):
-// sub-step 0 interleaves its 16 MFMAs with the 16 loads of the two new units
-// and the 16 half-reads of sub-step 1's fragments; sub-step 1 runs 9 MFMAs,
-// waits for units up to 2kt + 3 and takes the stage barrier, then issues
-// the next stage's first fragments two half-reads per MFMA over its last 7.
-// Each accumulator takes its MFMAs in K order, as in gemm_kernel, so both
-// produce the same bits. Past the last stage the loads fetch zeros into free
-// slots (branch-free); the block drains them before the epilogue.
+// A wave's 128 x 128 tile is four 64 x 64 blocks over quarters of its
+// fragments (A lo / A hi: fragment rows 0-63 / 64-127; B lo / B hi likewise),
+// 16 MFMAs each, in the order (A lo, B lo), (A hi, B lo), (A lo, B hi),
+// (A hi, B hi), four register quarters (128 VGPRs) in all: during the first
+// block the wave issues the stage's 16 loads and reads the stage's A hi and
+// B hi; after the third it waits for the next stage's units and takes the
+// stage barrier, and during the last, which needs neither, it reads the next
+// stage's A lo and B lo. Work is issued in a fixed order (no compiler
+// reordering). Each accumulator takes one MFMA per stage, in K order. Past
+// the last stage the loads fetch zeros into free slots (branch-free); the
+// block drains them before the epilogue.
 //
-// GLU and ROPE select the epilogue forms described at gemm_kernel; KTAIL
-// zero-fills the 16-byte chunks past K.
+// GLU and ROPE select the epilogue forms described at gemm_kernel; for GLU
+// the B tile interleaves 16 gate rows and the 16 matching up rows, so each
+// lane holds a gate column and its up column. KTAIL zero-fills the 16-byte
+// chunks past K.
 template <bool GLU, bool ROPE, bool KTAIL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm256_kernel(GemmArgs a) {
-  constexpr int BM = 256, BN = 256, GM = 4, NW = 4, MI = 4, NJ = 4;
+  constexpr int BM = 256, BN = 256, GM = 4, NW = 4, MI = 8, NJ = 8;
   constexpr int UNIT = 256 * 128, RU = 5, LPU = 256 / 8 / NW;  // 8 loads a wave per unit
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RU * UNIT];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -631,27 +654,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
   const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)a.K;
   const int KT = (a.K + 127) / 128, NU = 2 * KT;
-  // the tile being loaded: first output row and column (GLU: first gate
-  // column) and this lane's base offsets
-  int m0 = 0, n0 = 0;
-  uint32_t offA = 0, offB = 0;
-  auto set_tile = [&](int tl) {
-    const TileXY t = tile_of(tl, tiles_m, tiles_n, GM);
-    m0 = t.tm * BM;
-    n0 = t.tn * (GLU ? BN / 2 : BN);
-    offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
-    offB = GLU ? (uint32_t)(lrow * a.K + cch * 16) : (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
-  };
+  // One tile per block: a block that ends leaves its stores draining while
+  // the CU's next block loads (a loop over tiles inside one block would
+  // have to wait for them: loads and stores share the wait counter).
+  // m0, n0: the tile's first output row and column (GLU: first gate column)
+  const TileXY t = tile_of(blockIdx.x, tiles_m, tiles_n, GM);
+  const int m0 = t.tm * BM, n0 = t.tn * (GLU ? BN / 2 : BN);
+  const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
+  const uint32_t offB =
+      GLU ? (uint32_t)(lrow * a.K + cch * 16) : (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
   auto ld = [&](int u, int j) {
     uint8_t* dst = smem + (u % RU) * UNIT + (wave + j * NW) * 1024;
     const int k0 = (u >> 1) * 128;
     uint32_t o;
     if (u & 1) {
       if constexpr (GLU) {
-        // B unit g: gate or up half by (g / 4) % 2, 32-column pair g / 8,
-        // 8-row group g % 4
+        // B unit g: 16-column group g / 4, gate or up half by (g / 2) % 2,
+        // 8-row group g % 2
         const int g = wave + j * NW;
-        const int row = ((g >> 2) & 1) * a.H + n0 + (g >> 3) * 32 + (g & 3) * 8;
+        const int row = ((g >> 1) & 1) * a.H + n0 + (g >> 2) * 16 + (g & 1) * 8;
         o = offB + (uint32_t)row * (uint32_t)a.K + k0;
       } else {
         o = offB + j * stepB + k0;
@@ -668,95 +689,120 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
   };
-  auto prologue_loads = [&]() {
-#pragma unroll
-    for (int u = 0; u < 3; ++u)
-#pragma unroll
-      for (int j = 0; j < LPU; ++j) ld(u, j);
-  };
-  const int lrow32 = lane & 31;
-  const int sw = (lrow32 >> 1) & 7;
-  const int lo0 = lrow32 * 128 + ((((lane >> 5) * 2) ^ sw) * 16);      // sub-step 0 chunk
-  const int lo1 = lrow32 * 128 + ((((lane >> 5) * 2 + 4) ^ sw) * 16);  // sub-step 1 chunk
+  // fragment lanes: row lane % 16 of a 16-row fragment, 32-byte K group
+  // lane / 16 (chunks 2g and 2g + 1 of the 128-byte row); the row's swizzle
+  // key (row >> 1) & 7 is (lane % 16) / 2 for every fragment
+  const int r16 = lane & 15, sw = r16 >> 1;
+  const int lo = r16 * 128 + ((((lane >> 4) * 2) ^ sw) * 16);
   // the fragment's second chunk sits at position ^ 1, i.e. +16 or -16 bytes
   const int d1 = (sw & 1) ? -16 : 16;
-  v8i fa[2][MI], fb[2][NJ];
-  v16f acc[MI][NJ];
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  auto mf = [&](auto FC, int i, int j) {
-    constexpr int F = decltype(FC)::value;
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[F][i], fb[F][j], acc[i][j], 0, 0, 0, 0, 0, 0);
+  v8i R[4][4];  // four quarters of four fragments
+  v4f acc[MI][NJ];
+  // 16-byte half h (0..7) of quarter Q: fragment h / 2 of the 64 rows from
+  // row0 of `unit` (which includes this lane's offset), part h % 2
+  auto rd = [&](auto QC, const uint8_t* unit, int row0, int h) {
+    constexpr int Q = decltype(QC)::value;
+    const int k = h >> 1;
+    const v4i v = *reinterpret_cast<const v4i*>(unit + (row0 + k * 16) * 128 + ((h & 1) ? d1 : 0));
+    if (h & 1)
+      R[Q][k].hi = v;
+    else
+      R[Q][k].lo = v;
   };
-  // 16-byte half h (0..15) of a fragment set: fragment f = h / 2 (A_k for
-  // even f, B_k for odd, k = f / 2), part h % 2
-  auto half_read = [&](auto FC, const uint8_t* la, const uint8_t* lb, int h) {
-    constexpr int F = decltype(FC)::value;
-    const int f = h >> 1, k = f >> 1;
-    const uint8_t* rowp = ((f & 1) ? lb + (wn0 + k * 32) * 128 : la + (wm0 + k * 32) * 128) + ((h & 1) ? d1 : 0);
-    const v4i v = *reinterpret_cast<const v4i*>(rowp);
-    if (f & 1) {
-      if (h & 1) fb[F][k].hi = v; else fb[F][k].lo = v;
-    } else {
-      if (h & 1) fa[F][k].hi = v; else fa[F][k].lo = v;
-    }
+  // MFMA of accumulator (i0 + i, j0 + j) on fragment i of quarter QA and
+  // fragment j of quarter QB
+  auto mf = [&](auto QAC, auto QBC, int i0, int j0, int i, int j) {
+    constexpr int QA = decltype(QAC)::value, QB = decltype(QBC)::value;
+    acc[i0 + i][j0 + j] =
+        __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(R[QA][i], R[QB][j], acc[i0 + i][j0 + j], 0, 0, 0, 0, 0, 0);
   };
-  // MFMA order: shells k = 0..3 ((k, 0..k) then (0..k-1, k)), so the first
-  // MFMAs need the fragments read first
+  // MFMA order within a block: shells k = 0..3 ((k, 0..k) then (0..k-1, k)),
+  // so the first MFMAs need the fragments read first
   constexpr int OI[16] = {0, 1, 1, 0, 2, 2, 2, 0, 1, 3, 3, 3, 3, 0, 1, 2};
   constexpr int OJ[16] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2, 3, 3, 3, 3};
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  // stage kt: quarter 0 holds A lo, 1 B lo, 2 A hi, 3 B hi
+  auto stage = [&](int kt) {
+    const uint8_t* ua = smem + ((2 * kt) % RU) * UNIT + lo;
+    const uint8_t* ub = smem + ((2 * kt + 1) % RU) * UNIT + lo;
+    const uint8_t* una = smem + ((2 * kt + 2) % RU) * UNIT + lo;
+    const uint8_t* unb = smem + ((2 * kt + 3) % RU) * UNIT + lo;
+    __builtin_amdgcn_sched_barrier(0);
+    // (A lo, B lo); the loads of unit 2kt + 4 (its slot, unit 2kt - 1's,
+    // was freed at the previous stage's first barrier); this stage's A hi
+    // and B hi, which finish the reads of units 2kt and 2kt + 1
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mf(I0{}, I1{}, 0, 0, OI[q], OJ[q]);
+      if ((q & 1) == 0) ld(2 * kt + 4, q >> 1);
+      if (q < 8)
+        rd(I2{}, ua, wm0 + 64, q);
+      else
+        rd(I3{}, ub, wn0 + 64, q - 8);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // every wave done with units 2kt and 2kt + 1
+    __builtin_amdgcn_s_waitcnt(lgkm_imm(0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // (A hi, B lo) with the loads of unit 2kt + 5 (into unit 2kt's slot),
+    // then (A lo, B hi)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mf(I2{}, I1{}, 4, 0, OI[q], OJ[q]);
+      if ((q & 1) == 0) ld(2 * kt + 5, q >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mf(I0{}, I3{}, 0, 4, OI[q], OJ[q]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // units up to 2kt + 3 landed (this wave's last 2 LPU loads are units
+    // 2kt + 4 and 2kt + 5)
+    __builtin_amdgcn_s_waitcnt(vm_imm(2 * LPU));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // (A hi, B hi); the next stage's A lo and B lo into their quarters, in
+    // the order A0 B0 A1 B1 ... the next first block needs
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mf(I2{}, I3{}, 4, 4, OI[q], OJ[q]);
+      const int f = q >> 1, h = 2 * (f >> 1) + (q & 1);
+      if ((f & 1) == 0)
+        rd(I0{}, una, wm0, h);
+      else
+        rd(I1{}, unb, wn0, h);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
-  // One tile per block: a block that ends leaves its stores draining while
-  // the CU's next block loads (a loop over tiles inside one block would
-  // have to wait for them: loads and stores share the wait counter).
-  set_tile(blockIdx.x);
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  // prologue: units 0..2; units 0 and 1 landed; stage 0's first fragments
-  prologue_loads();
-  {
-    __builtin_amdgcn_s_waitcnt(vm_imm(LPU));
-    __builtin_amdgcn_s_barrier();
+      for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+  // prologue: units 0..3 in flight; once units 0 and 1 landed, stage 0's
+  // A lo and B lo
 #pragma unroll
-    for (int h = 0; h < 16; ++h) half_read(I0{}, smem + lo0, smem + UNIT + lo0, h);
-    for (int kt = 0; kt < KT; ++kt) {
-      const uint8_t* la1 = smem + ((2 * kt) % RU) * UNIT + lo1;
-      const uint8_t* lb1 = smem + ((2 * kt + 1) % RU) * UNIT + lo1;
-      const uint8_t* la0n = smem + ((2 * kt + 2) % RU) * UNIT + lo0;
-      const uint8_t* lb0n = smem + ((2 * kt + 3) % RU) * UNIT + lo0;
-      __builtin_amdgcn_sched_barrier(0);
+  for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        mf(I0{}, OI[q], OJ[q]);
-        ld(2 * kt + 3 + (q >> 3), q & 7);
-        half_read(I1{}, la1, lb1, q);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int j = 0; j < LPU; ++j) ld(u, j);
+  __builtin_amdgcn_s_waitcnt(vm_imm(2 * LPU));
+  __builtin_amdgcn_s_barrier();
 #pragma unroll
-      for (int q = 0; q < 9; ++q) {
-        mf(I1{}, OI[q], OJ[q]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // units up to 2kt + 3 landed (this wave's last LPU loads are unit 2kt + 4)
-      __builtin_amdgcn_s_waitcnt(vm_imm(LPU));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < 7; ++q) {
-        half_read(I0{}, la0n, lb0n, 2 * q);
-        half_read(I0{}, la0n, lb0n, 2 * q + 1);
-        mf(I1{}, OI[9 + q], OJ[9 + q]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      half_read(I0{}, la0n, lb0n, 14);
-      half_read(I0{}, la0n, lb0n, 15);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+  for (int q = 0; q < 16; ++q) {
+    const int f = q >> 1, h = 2 * (f >> 1) + (q & 1);
+    if ((f & 1) == 0)
+      rd(I0{}, smem + lo, wm0, h);
+    else
+      rd(I1{}, smem + UNIT + lo, wn0, h);
   }
+  for (int kt = 0; kt < KT; ++kt) stage(kt);
   // drain the zero-fill loads past the last stage; then every wave is done
   // with the ring and the epilogue may stage in any of it
   __builtin_amdgcn_s_waitcnt(vm_imm(0));
