@@ -653,7 +653,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int cch = (lane & 7) ^ (((wave & 1) << 2) | (lrow >> 1));
   const uint32_t stepA = (uint32_t)(8 * NW) * (uint32_t)a.ld_x;
   const uint32_t stepB = (uint32_t)(8 * NW) * (uint32_t)a.K;
-  const int KT = (a.K + 127) / 128, NU = 2 * KT;
+  const int KT = (a.K + 127) / 128;
   // One tile per block: a block that ends leaves its stores draining while
   // the CU's next block loads (a loop over tiles inside one block would
   // have to wait for them: loads and stores share the wait counter).
@@ -663,11 +663,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
   const uint32_t offB =
       GLU ? (uint32_t)(lrow * a.K + cch * 16) : (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
-  auto ld = [&](int u, int j) {
-    uint8_t* dst = smem + (u % RU) * UNIT + (wave + j * NW) * 1024;
-    const int k0 = (u >> 1) * 128;
+  // load j (of LPU) of the A (B = false) or B unit of stage ks into the
+  // ring slot at byte offset `so`; units past the last stage fetch zeros
+  auto ld = [&](int so, auto BC, int ks, int j) {
+    constexpr bool B = decltype(BC)::value;
+    uint8_t* dst = smem + so + (wave + j * NW) * 1024;
+    const int k0 = ks * 128;
     uint32_t o;
-    if (u & 1) {
+    if constexpr (B) {
       if constexpr (GLU) {
         // B unit g: 16-column group g / 4, gate or up half by (g / 2) % 2,
         // 8-row group g % 2
@@ -683,8 +686,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     if constexpr (KTAIL) {
       if (k0 + cch * 16 >= a.K) o = kOOB;
     }
-    if (u >= NU) o = kOOB;
-    if (u & 1)
+    if (ks >= KT) o = kOOB;
+    if constexpr (B)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
@@ -724,12 +727,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-  // stage kt: quarter 0 holds A lo, 1 B lo, 2 A hi, 3 B hi
-  auto stage = [&](int kt) {
-    const uint8_t* ua = smem + ((2 * kt) % RU) * UNIT + lo;
-    const uint8_t* ub = smem + ((2 * kt + 1) % RU) * UNIT + lo;
-    const uint8_t* una = smem + ((2 * kt + 2) % RU) * UNIT + lo;
-    const uint8_t* unb = smem + ((2 * kt + 3) % RU) * UNIT + lo;
+  using BA = std::false_type;
+  using BB = std::true_type;
+  // unit u sits in ring slot u % RU; slot offsets in bytes, advanced by
+  // one unit with a wrap (no division in the loop)
+  auto nx = [](int so) { return so + UNIT == RU * UNIT ? 0 : so + UNIT; };
+  // stage kt, whose A unit 2kt sits at slot offset sa: quarter 0 holds A
+  // lo, 1 B lo, 2 A hi, 3 B hi
+  auto stage = [&](int kt, int sa) {
+    const int sb = nx(sa), sna = nx(sb), snb = nx(sna), s4 = nx(snb);
+    const uint8_t* ua = smem + sa + lo;
+    const uint8_t* ub = smem + sb + lo;
+    const uint8_t* una = smem + sna + lo;
+    const uint8_t* unb = smem + snb + lo;
     __builtin_amdgcn_sched_barrier(0);
     // (A lo, B lo); the loads of unit 2kt + 4 (its slot, unit 2kt - 1's,
     // was freed at the previous stage's first barrier); this stage's A hi
@@ -737,7 +747,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       mf(I0{}, I1{}, 0, 0, OI[q], OJ[q]);
-      if ((q & 1) == 0) ld(2 * kt + 4, q >> 1);
+      if ((q & 1) == 0) ld(s4, BA{}, kt + 2, q >> 1);
       if (q < 8)
         rd(I2{}, ua, wm0 + 64, q);
       else
@@ -753,7 +763,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       mf(I2{}, I1{}, 4, 0, OI[q], OJ[q]);
-      if ((q & 1) == 0) ld(2 * kt + 5, q >> 1);
+      if ((q & 1) == 0) ld(sa, BB{}, kt + 2, q >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -789,9 +799,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // prologue: units 0..3 in flight; once units 0 and 1 landed, stage 0's
   // A lo and B lo
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int j = 0; j < LPU; ++j) ld(0, BA{}, 0, j);
 #pragma unroll
-    for (int j = 0; j < LPU; ++j) ld(u, j);
+  for (int j = 0; j < LPU; ++j) ld(UNIT, BB{}, 0, j);
+#pragma unroll
+  for (int j = 0; j < LPU; ++j) ld(2 * UNIT, BA{}, 1, j);
+#pragma unroll
+  for (int j = 0; j < LPU; ++j) ld(3 * UNIT, BB{}, 1, j);
   __builtin_amdgcn_s_waitcnt(vm_imm(2 * LPU));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -802,7 +816,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     else
       rd(I1{}, smem + UNIT + lo, wn0, h);
   }
-  for (int kt = 0; kt < KT; ++kt) stage(kt);
+  for (int kt = 0, sa = 0; kt < KT; ++kt, sa = nx(nx(sa))) stage(kt, sa);
   // drain the zero-fill loads past the last stage; then every wave is done
   // with the ring and the epilogue may stage in any of it
   __builtin_amdgcn_s_waitcnt(vm_imm(0));
