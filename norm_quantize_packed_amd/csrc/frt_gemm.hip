@@ -663,12 +663,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
   const uint32_t offB =
       GLU ? (uint32_t)(lrow * a.K + cch * 16) : (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
-  // load j (of LPU) of the A (B = false) or B unit of stage ks into the
-  // ring slot at byte offset `so`; units past the last stage fetch zeros
-  auto ld = [&](int so, auto BC, int ks, int j) {
+  // this lane's offset for load 0 of the A (B = false) or B unit of stage
+  // ks, or kOOB past the last stage (and, with KTAIL, past K). Load j adds
+  // a multiple of the row stride that leaves kOOB past any record count
+  // (the host bounds M (M >= 512 here), K and ld_x: under 2^31 - 224 row
+  // strides), so a unit's zero fill needs one select, not one per load.
+  auto ubase = [&](auto BC, int ks) {
+    constexpr bool B = decltype(BC)::value;
+    const int k0 = ks * 128;
+    uint32_t o = (B ? offB : offA) + k0;
+    if constexpr (KTAIL) {
+      if (k0 + cch * 16 >= a.K) o = kOOB;
+    }
+    return ks < KT ? o : kOOB;
+  };
+  // load j (of LPU) of a unit whose ubase is `ob` into the ring slot at
+  // byte offset `so`
+  auto ld = [&](int so, auto BC, uint32_t ob, int j) {
     constexpr bool B = decltype(BC)::value;
     uint8_t* dst = smem + so + (wave + j * NW) * 1024;
-    const int k0 = ks * 128;
     uint32_t o;
     if constexpr (B) {
       if constexpr (GLU) {
@@ -676,21 +689,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // 8-row group g % 2
         const int g = wave + j * NW;
         const int row = ((g >> 1) & 1) * a.H + n0 + (g >> 2) * 16 + (g & 1) * 8;
-        o = offB + (uint32_t)row * (uint32_t)a.K + k0;
+        o = ob + (uint32_t)row * (uint32_t)a.K;
       } else {
-        o = offB + j * stepB + k0;
+        o = ob + j * stepB;
       }
-    } else {
-      o = offA + j * stepA + k0;
-    }
-    if constexpr (KTAIL) {
-      if (k0 + cch * 16 >= a.K) o = kOOB;
-    }
-    if (ks >= KT) o = kOOB;
-    if constexpr (B)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
-    else
+    } else {
+      o = ob + j * stepA;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
+    }
   };
   // fragment lanes: row lane % 16 of a 16-row fragment, 32-byte K group
   // lane / 16 (chunks 2g and 2g + 1 of the 128-byte row); the row's swizzle
@@ -740,6 +747,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint8_t* ub = smem + sb + lo;
     const uint8_t* una = smem + sna + lo;
     const uint8_t* unb = smem + snb + lo;
+    const uint32_t oa2 = ubase(BA{}, kt + 2), ob2 = ubase(BB{}, kt + 2);
     __builtin_amdgcn_sched_barrier(0);
     // (A lo, B lo); the loads of unit 2kt + 4 (its slot, unit 2kt - 1's,
     // was freed at the previous stage's first barrier); this stage's A hi
@@ -747,7 +755,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       mf(I0{}, I1{}, 0, 0, OI[q], OJ[q]);
-      if ((q & 1) == 0) ld(s4, BA{}, kt + 2, q >> 1);
+      if ((q & 1) == 0) ld(s4, BA{}, oa2, q >> 1);
       if (q < 8)
         rd(I2{}, ua, wm0 + 64, q);
       else
@@ -763,7 +771,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       mf(I2{}, I1{}, 4, 0, OI[q], OJ[q]);
-      if ((q & 1) == 0) ld(sa, BB{}, kt + 2, q >> 1);
+      if ((q & 1) == 0) ld(sa, BB{}, ob2, q >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -799,13 +807,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // prologue: units 0..3 in flight; once units 0 and 1 landed, stage 0's
   // A lo and B lo
 #pragma unroll
-  for (int j = 0; j < LPU; ++j) ld(0, BA{}, 0, j);
+  for (int j = 0; j < LPU; ++j) ld(0, BA{}, ubase(BA{}, 0), j);
 #pragma unroll
-  for (int j = 0; j < LPU; ++j) ld(UNIT, BB{}, 0, j);
+  for (int j = 0; j < LPU; ++j) ld(UNIT, BB{}, ubase(BB{}, 0), j);
 #pragma unroll
-  for (int j = 0; j < LPU; ++j) ld(2 * UNIT, BA{}, 1, j);
+  for (int j = 0; j < LPU; ++j) ld(2 * UNIT, BA{}, ubase(BA{}, 1), j);
 #pragma unroll
-  for (int j = 0; j < LPU; ++j) ld(3 * UNIT, BB{}, 1, j);
+  for (int j = 0; j < LPU; ++j) ld(3 * UNIT, BB{}, ubase(BB{}, 1), j);
   __builtin_amdgcn_s_waitcnt(vm_imm(2 * LPU));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
