@@ -18,9 +18,12 @@ __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float(uint
 
 // fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  return ((u & 0x7fffffffu) > 0x7f800000u) ? (((u >> 16) & 0x8000u) | 0x7fc0u) : r;
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  // NaN -> the sign and the quiet NaN 0x7fc0, selected by a mask (all ones
+  // when |u| > 0x7f800000) rather than a branch
+  const uint32_t nan = (uint32_t)((int32_t)(0x7f800000u - (u & 0x7fffffffu)) >> 31);
+  return (r & ~nan) | ((((u >> 16) & 0x8000u) | 0x7fc0u) & nan);
 }
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return f2bf(lo) | (f2bf(hi) << 16);

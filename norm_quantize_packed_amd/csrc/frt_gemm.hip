@@ -91,8 +91,8 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // of the split table lazily, as a function boundary does not let it).
 // `slot` is SLOT bytes of LDS that no wave of the block reads any more and
 // that no load still targets; `lds` is the whole allocation (TOTAL bytes).
-template <int MI, int NJ, int WN, int NW, bool GLU, bool ROPE, bool FP4, int SLOT, int TOTAL, typename ACC>
-__device__ __forceinline__ void gemm_epilogue(GemmArgs a, ACC (&acc)[MI][NJ], int m0, int n0, int wm0,
+template <int MI, int NJ, int WN, int NW, bool GLU, bool ROPE, bool FP4, int SLOT, int TOTAL>
+__device__ __forceinline__ void gemm_epilogue(GemmArgs a, v16f (&acc)[MI][NJ], int m0, int n0, int wm0,
                                               int wn0, int wave, int lane, uint8_t* slot, uint8_t* lds) {
 #include "frt_gemm_epilogue.inc"
 }
@@ -497,17 +497,121 @@ __device__ __forceinline__ void split_of(const LdsSplits* t, int n, int esize, u
   ldb = t->ld[idx] * esize;
 }
 
-// Split epilogue of the 256 x 256 kernel (bf16 or fp32 out, optional bias):
-// out = alpha * acc + bias into the split owning each column. The
-// accumulators are 16 x 16 fragments: lane l holds column l % 16 of
-// fragment (i, j), rows 4 (l / 16) + r, r = 0..3. With vec_out each 64 x 64
-// quarter of the wave tile goes through the wave's own 8 KB of LDS and leaves
-// as whole 128-byte row segments (16 bytes a lane); else each lane stores its
-// elements. Called after a block barrier that ended every use of the ring;
-// `tab` must not overlap the waves' staging (32 KB).
-__device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v4f (&acc)[8][8], int m0, int n0, int wm0,
-                                                       int wn0, int wave, int lane, uint8_t* smem, LdsSplits* tab) {
+// Two floats as packed bf16, low half first, by the conversion instruction
+// (v_cvt_pk_bf16_f32): round to nearest even, the same bits as f2bf for
+// every non-NaN input (checked over all 2^32 patterns on the device); a
+// NaN stays a NaN but keeps its payload bits where f2bf returns 0x7fc0.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// Epilogue of the 256 x 256 kernel: out = alpha * acc + bias in the split,
+// GEGLU or RoPE form (the forms described at gemm_kernel). The kernel's
+// MFMAs take the B fragment as their first operand, so lane l holds output
+// row 16i + l % 16 of accumulator (i, j) and the four consecutive columns
+// 16j + 4 (l / 16) + r, r = 0..3, of it: each lane writes its values
+// straight to memory, four columns at a time, with no staging. Split form:
+// with vec_out (bf16, split widths, offsets and strides multiples of 8)
+// 8 bytes a store, else one store per element; `tab` is the split table in
+// LDS, filled here after a block barrier. Rows past M exist only in the
+// last row of tiles.
+template <bool GLU, bool ROPE>
+__device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8][8], int m0, int n0, int wm0,
+                                                 int wn0, int lane, LdsSplits* tab) {
   constexpr int MI = 8, NJ = 8;
+  const int c4 = (lane >> 4) * 4;            // first of the lane's columns in a fragment
+  const int mr = m0 + wm0 + (lane & 15);     // the lane's row in row block i = 0
+  const bool rows_in = m0 + wm0 + 128 <= a.M;
+  const float alpha = (*a.act_scale) * (*a.w_scale);
+  if constexpr (ROPE) {
+    const int nq = a.nh * a.hd, nk = a.kv * a.hd;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        // the rotary pair (n, n + 1): n even, both in one of q, k, v
+        const int n = n0 + wn0 + j * 16 + c4 + 2 * t;
+        if (n >= a.N) continue;
+        const bool rot = n < nq + nk;
+        const int d = n % a.hd;
+        const float be = a.bias != nullptr ? bf16f(a.bias[n]) : 0.0f;
+        const float bo = a.bias != nullptr ? bf16f(a.bias[n + 1]) : 0.0f;
+        uint16_t* dst;
+        int64_t ld;
+        if (n < nq) {
+          dst = a.q_out + n;
+          ld = nq;
+        } else if (rot) {
+          dst = a.k_cache + a.P * nk + (n - nq);
+          ld = nk;
+        } else {
+          dst = a.v_cache + a.P * nk + (n - nq - nk);
+          ld = nk;
+        }
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+          const int m = mr + i * 16;
+          if (!rows_in && m >= a.M) continue;
+          const float ve = __uint_as_float(f2bf(alpha * acc[i][j][2 * t] + be) << 16);
+          const float vo = __uint_as_float(f2bf(alpha * acc[i][j][2 * t + 1] + bo) << 16);
+          float oe = ve, oo = vo;
+          if (rot) {
+            // a' = a c - b s on the even column, b' = b c + a s on the odd one
+            const uint32_t cs = *reinterpret_cast<const uint32_t*>(a.rope + (int64_t)m * a.hd + d);
+            oe = __builtin_fmaf(ve, bf16lo(cs), -1.0f * (vo * bf16hi(cs)));
+            oo = __builtin_fmaf(vo, bf16lo(cs), 1.0f * (ve * bf16hi(cs)));
+          }
+          dst[(int64_t)m * ld] = (uint16_t)f2bf(oe);
+          dst[(int64_t)m * ld + 1] = (uint16_t)f2bf(oo);
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (GLU) {
+    // gate and up rounded to bf16 as the unfused GEMM output would be, then
+    // the GEGLU quantiser of frt_ffn.hip; accumulators 2p (gate) and 2p + 1
+    // (up) hold the same four gate columns
+    const float qs = *a.q_scale, qr = 1.0f / qs;
+    const bool vec4 = ((reinterpret_cast<uintptr_t>(a.q8) | (uintptr_t)a.ld_q8) & 3) == 0;
+#pragma unroll
+    for (int p = 0; p < NJ / 2; ++p) {
+      const int gc = n0 + (wn0 >> 1) + p * 16 + c4;
+      if (gc >= a.H) continue;
+      float bg[4], bu[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = a.bias != nullptr && gc + r < a.H;
+        bg[r] = ok ? bf16f(a.bias[gc + r]) : 0.0f;
+        bu[r] = ok ? bf16f(a.bias[a.H + gc + r]) : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int m = mr + i * 16;
+        if (!rows_in && m >= a.M) continue;
+        uint32_t codes = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float vg = alpha * acc[i][2 * p][r] + bg[r];
+          const float vu = alpha * acc[i][2 * p + 1][r] + bu[r];
+          const float y = gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
+          codes |= ((uint32_t)cvt2_fp8(clamp_fp8(div_rn(y, qs, qr)), 0.0f) & 0xFFu) << (8 * r);
+        }
+        uint8_t* q = a.q8 + (int64_t)m * a.ld_q8 + gc;
+        if (vec4 && gc + 4 <= a.H) {
+          *reinterpret_cast<uint32_t*>(q) = codes;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (gc + r < a.H) q[r] = (uint8_t)(codes >> (8 * r));
+        }
+      }
+    }
+    return;
+  }
   if (threadIdx.x < FRT_MAX_SPLITS) {
     tab->ptr[threadIdx.x] = reinterpret_cast<uint64_t>(a.sp.ptr[threadIdx.x]);
     tab->ld[threadIdx.x] = a.sp.ld[threadIdx.x];
@@ -515,84 +619,63 @@ __device__ __forceinline__ void gemm256_split_epilogue(const GemmArgs& a, v4f (&
     if (threadIdx.x == 0) tab->n = a.sp.n;
   }
   __syncthreads();
-  const float alpha = (*a.act_scale) * (*a.w_scale);
-  const int c16 = lane & 15, r4 = (lane >> 4) * 4;
-  float bj[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int n = n0 + wn0 + j * 16 + c16;
-    bj[j] = (a.bias != nullptr && n < a.N) ? bf16f(a.bias[n]) : 0.0f;
-  }
-  // whole wave tile inside M (every tile but the last row of tiles)
-  const bool rows_in = m0 + wm0 + 128 <= a.M;
   if (a.vec_out) {
-    // 16-byte chunk c of staging row r sits at c ^ key(r); the key's bit 1
-    // from row bit 3 keeps the four rows one store instruction writes
-    // (r, r + 4, r + 8, r + 12) on distinct banks
-    auto key = [](int r) { return (r & 7) ^ ((r >> 2) & 2); };
-    uint8_t* wb = smem + wave * (64 * 128);
+    // rows checked only in the last row of tiles (a uniform branch)
+    auto store_vec = [&](auto ALLC) {
+      constexpr bool ALL = decltype(ALLC)::value;
 #pragma unroll
-    for (int jh = 0; jh < 2; ++jh) {
-      // this lane stores 8-column chunk lane % 8 of the half in each of its
-      // rows; split widths are multiples of 8, so the chunk lies in one split
-      const int nc = n0 + wn0 + jh * 64 + (lane & 7) * 8;
-      const bool nok = nc < a.N;
-      uint8_t* colp;
-      int64_t ldb;
-      split_of(tab, nok ? nc : 0, 2, colp, ldb);
+      for (int j = 0; j < NJ; ++j) {
+        // columns n .. n + 3 lie in one split (its width and offset are
+        // multiples of 8)
+        const int n = n0 + wn0 + j * 16 + c4;
+        if (n >= a.N) continue;
+        uint8_t* colp;
+        int64_t ldb;
+        split_of(tab, n, 2, colp, ldb);
+        colp += (int64_t)mr * ldb;
+        float b[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+        for (int r = 0; r < 4; ++r) b[r] = a.bias != nullptr ? bf16f(a.bias[n + r]) : 0.0f;
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2)
-#pragma unroll
-          for (int j2 = 0; j2 < 4; ++j2)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int rr = i2 * 16 + r4 + r;
-              const int c = j2 * 16 + c16;
-              const float v = alpha * acc[4 * h + i2][4 * jh + j2][r] + bj[4 * jh + j2];
-              *reinterpret_cast<uint16_t*>(wb + rr * 128 + (((c >> 3) ^ key(rr)) << 4) + (c & 7) * 2) =
-                  (uint16_t)f2bf(v);
-            }
-        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
-        __builtin_amdgcn_wave_barrier();
-        const int mb = m0 + wm0 + h * 64;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int rr = (lane >> 3) + 8 * k;
-          const uint4 v = *reinterpret_cast<const uint4*>(wb + rr * 128 + (((lane & 7) ^ key(rr)) << 4));
-          if (nok && (rows_in || mb + rr < a.M)) *reinterpret_cast<uint4*>(colp + (int64_t)(mb + rr) * ldb) = v;
+        for (int i = 0; i < MI; ++i) {
+          if (!ALL && mr + i * 16 >= a.M) continue;
+          const u32x2_t v = {pk_bf16(alpha * acc[i][j][0] + b[0], alpha * acc[i][j][1] + b[1]),
+                             pk_bf16(alpha * acc[i][j][2] + b[2], alpha * acc[i][j][3] + b[3])};
+          // a global (not flat) store: the split table holds generic pointers
+          *(__attribute__((address_space(1))) u32x2_t*)(uintptr_t)(colp + (int64_t)(i * 16) * ldb) = v;
         }
-        __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(63));
-        __builtin_amdgcn_wave_barrier();
       }
-    }
+    };
+    if (rows_in)
+      store_vec(std::true_type{});
+    else
+      store_vec(std::false_type{});
     return;
   }
-  // per-lane stores; rows past M exist only in the last row of tiles
+  // one store per element (fp32 output, or splits not on 8-column bounds)
   auto store_all = [&](auto F32C) {
     constexpr bool F32 = decltype(F32C)::value;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int n = n0 + wn0 + j * 16 + c16;
-      if (n >= a.N) continue;
-      uint8_t* colp;
-      int64_t ldb;
-      split_of(tab, n, F32 ? 4 : 2, colp, ldb);
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int r = 0; r < 4; ++r) {
+        const int n = n0 + wn0 + j * 16 + c4 + r;
+        if (n >= a.N) continue;
+        uint8_t* colp;
+        int64_t ldb;
+        split_of(tab, n, F32 ? 4 : 2, colp, ldb);
+        const float b = a.bias != nullptr ? bf16f(a.bias[n]) : 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm0 + i * 16 + r4 + r;
-          const float v = alpha * acc[i][j][r] + bj[j];
-          if (rows_in || m < a.M) {
-            if constexpr (F32)
-              *reinterpret_cast<float*>(colp + (int64_t)m * ldb) = v;
-            else
-              *reinterpret_cast<uint16_t*>(colp + (int64_t)m * ldb) = (uint16_t)f2bf(v);
-          }
+        for (int i = 0; i < MI; ++i) {
+          const int m = mr + i * 16;
+          if (!rows_in && m >= a.M) continue;
+          const float v = alpha * acc[i][j][r] + b;
+          if constexpr (F32)
+            *reinterpret_cast<float*>(colp + (int64_t)m * ldb) = v;
+          else
+            *reinterpret_cast<uint16_t*>(colp + (int64_t)m * ldb) = (uint16_t)f2bf(v);
         }
-    }
+      }
   };
   if (a.out_f32)
     store_all(std::true_type{});
@@ -720,11 +803,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       R[Q][k].lo = v;
   };
   // MFMA of accumulator (i0 + i, j0 + j) on fragment i of quarter QA and
-  // fragment j of quarter QB
+  // fragment j of quarter QB, the B fragment first (so that a lane's
+  // results run along an output row)
   auto mf = [&](auto QAC, auto QBC, int i0, int j0, int i, int j) {
     constexpr int QA = decltype(QAC)::value, QB = decltype(QBC)::value;
     acc[i0 + i][j0 + j] =
-        __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(R[QA][i], R[QB][j], acc[i0 + i][j0 + j], 0, 0, 0, 0, 0, 0);
+        __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(R[QB][j], R[QA][i], acc[i0 + i][j0 + j], 0, 0, 0, 0, 0, 0);
   };
   // MFMA order within a block: shells k = 0..3 ((k, 0..k) then (0..k-1, k)),
   // so the first MFMAs need the fragments read first
@@ -829,12 +913,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // with the ring and the epilogue may stage in any of it
   __builtin_amdgcn_s_waitcnt(vm_imm(0));
   __syncthreads();
-  if constexpr (!GLU && !ROPE)
-    gemm256_split_epilogue(a, acc, m0, n0, wm0, wn0, wave, lane, smem,
-                           reinterpret_cast<LdsSplits*>(smem + NW * 64 * 128));
-  else
-    gemm_epilogue<MI, NJ, 128, NW, GLU, ROPE, false, RU * UNIT, RU * UNIT>(a, acc, m0, n0, wm0, wn0, wave, lane, smem,
-                                                                         smem);
+  gemm256_epilogue<GLU, ROPE>(a, acc, m0, n0, wm0, wn0, lane, reinterpret_cast<LdsSplits*>(smem));
 }
 
 // K from which the 256 x 256 plan runs on gemm256_kernel rather than on
