@@ -483,6 +483,7 @@ struct LdsSplits {
   int64_t ld[FRT_MAX_SPLITS];
   int off[FRT_MAX_SPLITS];
   int n;
+  uint8_t grp[32];  // the split of each 8-column group of a 256-column tile
 };
 
 // Output pointer of column n (in its split) and its row stride, in bytes
@@ -577,17 +578,22 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
     // (up) hold the same four gate columns
     const float qs = *a.q_scale, qr = 1.0f / qs;
     const bool vec4 = ((reinterpret_cast<uintptr_t>(a.q8) | (uintptr_t)a.ld_q8) & 3) == 0;
+    // the biases first (the compiler cannot move their loads above the
+    // code stores)
+    float bg[NJ / 2][4], bu[NJ / 2][4];
+#pragma unroll
+    for (int p = 0; p < NJ / 2; ++p)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int gc = n0 + (wn0 >> 1) + p * 16 + c4 + r;
+        const bool ok = a.bias != nullptr && gc < a.H;
+        bg[p][r] = ok ? bf16f(a.bias[gc]) : 0.0f;
+        bu[p][r] = ok ? bf16f(a.bias[a.H + gc]) : 0.0f;
+      }
 #pragma unroll
     for (int p = 0; p < NJ / 2; ++p) {
       const int gc = n0 + (wn0 >> 1) + p * 16 + c4;
       if (gc >= a.H) continue;
-      float bg[4], bu[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = a.bias != nullptr && gc + r < a.H;
-        bg[r] = ok ? bf16f(a.bias[gc + r]) : 0.0f;
-        bu[r] = ok ? bf16f(a.bias[a.H + gc + r]) : 0.0f;
-      }
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int m = mr + i * 16;
@@ -595,8 +601,8 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
         uint32_t codes = 0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float vg = alpha * acc[i][2 * p][r] + bg[r];
-          const float vu = alpha * acc[i][2 * p + 1][r] + bu[r];
+          const float vg = alpha * acc[i][2 * p][r] + bg[p][r];
+          const float vu = alpha * acc[i][2 * p + 1][r] + bu[p][r];
           const float y = gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
           codes |= ((uint32_t)cvt2_fp8(clamp_fp8(div_rn(y, qs, qr)), 0.0f) & 0xFFu) << (8 * r);
         }
@@ -617,32 +623,57 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
     tab->ld[threadIdx.x] = a.sp.ld[threadIdx.x];
     tab->off[threadIdx.x] = a.sp.off[threadIdx.x];
     if (threadIdx.x == 0) tab->n = a.sp.n;
+  } else if (threadIdx.x >= 64 && threadIdx.x < 96 && a.vec_out) {
+    // vec_out split widths are multiples of 8: an 8-column group lies in one
+    // split, found once here for the whole block
+    const int g = threadIdx.x - 64, n = n0 + 8 * g;
+    int idx = 0;
+#pragma unroll
+    for (int sp = 1; sp < FRT_MAX_SPLITS; ++sp)
+      if (sp < a.sp.n && n >= a.sp.off[sp]) idx = sp;
+    tab->grp[g] = (uint8_t)idx;
   }
   __syncthreads();
   if (a.vec_out) {
+    // every column chunk's split and bias first (the compiler cannot move
+    // these loads above the output stores, which might alias them)
+    uint8_t* colp[NJ];
+    int64_t ldb[NJ];
+    float b[NJ][4];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      // columns n .. n + 3 lie in the split of their 8-column group
+      const int n = n0 + wn0 + j * 16 + c4;
+      const int idx = tab->grp[(wn0 + j * 16 + c4) >> 3];
+      ldb[j] = tab->ld[idx] * 2;
+      colp[j] = reinterpret_cast<uint8_t*>(tab->ptr[idx]) + (int64_t)(n - tab->off[idx]) * 2 + (int64_t)mr * ldb[j];
+    }
+    if (a.bias != nullptr) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int n = n0 + wn0 + j * 16 + c4, nb = n < a.N ? n : 0;  // N >= 8
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[j][r] = bf16f(a.bias[nb + r]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[j][r] = 0.0f;
+    }
     // rows checked only in the last row of tiles (a uniform branch)
     auto store_vec = [&](auto ALLC) {
       constexpr bool ALL = decltype(ALLC)::value;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        // columns n .. n + 3 lie in one split (its width and offset are
-        // multiples of 8)
-        const int n = n0 + wn0 + j * 16 + c4;
-        if (n >= a.N) continue;
-        uint8_t* colp;
-        int64_t ldb;
-        split_of(tab, n, 2, colp, ldb);
-        colp += (int64_t)mr * ldb;
-        float b[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) b[r] = a.bias != nullptr ? bf16f(a.bias[n + r]) : 0.0f;
+        if (n0 + wn0 + j * 16 + c4 >= a.N) continue;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           if (!ALL && mr + i * 16 >= a.M) continue;
-          const u32x2_t v = {pk_bf16(alpha * acc[i][j][0] + b[0], alpha * acc[i][j][1] + b[1]),
-                             pk_bf16(alpha * acc[i][j][2] + b[2], alpha * acc[i][j][3] + b[3])};
+          const u32x2_t v = {pk_bf16(alpha * acc[i][j][0] + b[j][0], alpha * acc[i][j][1] + b[j][1]),
+                             pk_bf16(alpha * acc[i][j][2] + b[j][2], alpha * acc[i][j][3] + b[j][3])};
           // a global (not flat) store: the split table holds generic pointers
-          *(__attribute__((address_space(1))) u32x2_t*)(uintptr_t)(colp + (int64_t)(i * 16) * ldb) = v;
+          *(__attribute__((address_space(1))) u32x2_t*)(uintptr_t)(colp[j] + (int64_t)(i * 16) * ldb[j]) = v;
         }
       }
     };
@@ -917,12 +948,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // K from which the 256 x 256 plan runs on gemm256_kernel rather than on
-// gemm_kernel's eight 128 x 64 waves (measured, rotated operands: 2048 x
-// 32768 x 16384 868 -> 822 us, 2048 x 16384 x 16384 451 -> 420 us, 8192 x
-// 9216 x 12288 800 -> 773 us, x 6144 444 -> 439 us; at K = 3072-4096 the
-// single wave per SIMD exposes the tile's prologue and epilogue: 8192 x 9216
-// x 3072 240 -> 250 us, 2048 x 32768 x 4096 272 -> 278 us)
-constexpr int kDeepK = 6144;
+// gemm_kernel's eight 128 x 64 waves (measured, rotated operands, same box:
+// 8192 x 9216 x 3072 with bias and three splits 217 -> 214 us, 2048 x 32768
+// x 4096 255 -> 225 us, 2048 x 9216 x 4096 101 -> 98 us, 8192 x 9216 x 2048
+// level; at K = 1024 the single wave per SIMD exposes the tile's prologue
+// and epilogue: 8192 x 9216 x 1024 100 -> 111 us)
+constexpr int kDeepK = 2048;
 
 template <bool GLU, bool ROPE>
 hipError_t launch_256(const GemmArgs& a, hipStream_t st) {

@@ -145,7 +145,8 @@ def _run_unfused(x8, s_a, w8, s_w, bias, s_o, H, M=None):
     (65, 2048, 1024, False),  # mid-M plan with too few tiles -> 64x64
     (256, 2048, 8192, False), # the decoder layer's gate/up (128x128 plan)
     (600, 1536, 704, True),   # M >= 512 (64x64 plan: least per-CU load), ragged M and H
-    (2000, 6160, 2500, True), # 256x256 plan at K >= 6144 (four 128x128 waves), ragged M, H, K
+    (2000, 6160, 2500, True), # deep-K 256x256 plan (four 128x128 waves), ragged M, H, K
+    (2000, 2064, 2500, False), # deep-K plan near its K threshold, K tail
 ])
 def test_gemm_geglu_vs_oracle_and_unfused(M, K, H, bias):
     x8, s_a, w8, s_w, bc = _operands(M, K, H, 500 + M, bias)

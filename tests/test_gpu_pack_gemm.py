@@ -292,13 +292,13 @@ def test_gemm_large_staged_epilogue_matches_per_lane_stores():
         assert_gemm_bf16(a, r, f"2000x5000x528 split {i}")
 
 
-@pytest.mark.parametrize("K", [6144, 6160])
+@pytest.mark.parametrize("K", [2048, 3088, 6160])
 def test_gemm_deep_k_plan_full_grid(K):
-    """The 256x256 plan at K >= 6144 (four 128x128 waves, five-unit ring):
+    """The 256x256 plan at K >= 2048 (four 128x128 waves, five-unit ring):
     2000 x 5000 takes it (160 tiles, one round; ragged M and N), with a bias,
-    three splits whose boundaries fall inside tiles and, at K = 6160, a K
-    tail. Every fp32 output is checked against the oracle; the staged bf16
-    stores (whole 128-byte row segments) and the per-lane stores of a padded
+    three splits whose boundaries fall inside tiles and, at K = 3088 and
+    6160, a K tail. Every fp32 output is checked against the oracle; the
+    8-byte row-segment bf16 stores and the per-element stores of a padded
     stride give the same bits, match the oracle and write nothing outside
     their outputs; a second call repeats the bits."""
     rng = np.random.default_rng(K)
@@ -316,7 +316,7 @@ def test_gemm_deep_k_plan_full_grid(K):
     lane = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False, ld_pad=6)
     again = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
     for i, (a, b, c, r) in enumerate(zip(staged, lane, again, ref)):
-        assert np.array_equal(a, b), f"split {i}: staged and per-lane stores differ"
+        assert np.array_equal(a, b), f"split {i}: vector and per-element stores differ"
         assert np.array_equal(a, c), f"split {i}: repeated call differs"
         assert_gemm_bf16(a, r, f"2000x5000x{K} split {i}")
 

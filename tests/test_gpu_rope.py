@@ -93,7 +93,8 @@ def _qkv_operands(M, K, nh, kv, hd, seed, bias=False):
     (256, 512, 32, 8, 128, 7, False),     # 64x64 plan (ties with 128x128)
     (1024, 512, 32, 8, 128, 0, True),     # 128x128 plan (ties with 256x256)
     (2048, 512, 32, 8, 128, 3, False),    # 256x256 plan
-    (2000, 6144, 32, 8, 128, 9, True),    # 256x256 plan at K >= 6144, ragged M, bias
+    (2000, 6144, 32, 8, 128, 9, True),    # deep-K 256x256 plan, ragged M, bias
+    (2000, 2048, 32, 8, 128, 5, False),   # deep-K plan at its K threshold
 ])
 def test_gemm_rope_vs_oracle_and_unfused(M, K, nh, kv, hd, P, bias):
     x8, s_a, w8, s_w, bc = _qkv_operands(M, K, nh, kv, hd, 700 + M, bias)
