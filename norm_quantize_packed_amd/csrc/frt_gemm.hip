@@ -504,7 +504,7 @@ __device__ __forceinline__ void split_of(const LdsSplits* t, int n, int esize, u
 // NaN stays a NaN but keeps its payload bits where f2bf returns 0x7fc0.
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
@@ -512,21 +512,27 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 // Epilogue of the 256 x 256 kernel: out = alpha * acc + bias in the split,
 // GEGLU or RoPE form (the forms described at gemm_kernel). The kernel's
 // MFMAs take the B fragment as their first operand, so lane l holds output
-// row 16i + l % 16 of accumulator (i, j) and the four consecutive columns
-// 16j + 4 (l / 16) + r, r = 0..3, of it: each lane writes its values
-// straight to memory, four columns at a time, with no staging. Split form:
-// with vec_out (bf16, split widths, offsets and strides multiples of 8)
-// 8 bytes a store, else one store per element; `tab` is the split table in
-// LDS, filled here after a block barrier. Rows past M exist only in the
-// last row of tiles.
+// row 16i + l % 16 of accumulator (i, j) and four consecutive columns of
+// it: for the GEGLU form columns 16j + 4q + r (q = l / 16, r = 0..3); for
+// the split and RoPE forms the B tile's rows are loaded in an order (see
+// the kernel) that gives accumulators 2p and 2p + 1 the columns 32p + 8q +
+// r and 32p + 8q + 4 + r, eight consecutive columns a lane. Each lane
+// writes its values straight to memory with no staging. Split form: with
+// vec_out (bf16, split widths, offsets and strides multiples of 8) 16 bytes
+// a store, else one store per element; `tab` is the split table in LDS,
+// filled here after a block barrier. Rows past M exist only in the last row
+// of tiles.
 template <bool GLU, bool ROPE>
 __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8][8], int m0, int n0, int wm0,
                                                  int wn0, int lane, LdsSplits* tab) {
   constexpr int MI = 8, NJ = 8;
-  const int c4 = (lane >> 4) * 4;            // first of the lane's columns in a fragment
+  const int c4 = (lane >> 4) * 4;            // GEGLU: first of the lane's columns in a fragment
+  const int c8 = (lane >> 4) * 8;            // split, RoPE: first of its columns in a fragment pair
   const int mr = m0 + wm0 + (lane & 15);     // the lane's row in row block i = 0
   const bool rows_in = m0 + wm0 + 128 <= a.M;
   const float alpha = (*a.act_scale) * (*a.w_scale);
+  // split / RoPE column of value r of accumulator column block j
+  auto col = [&](int j, int r) { return n0 + wn0 + (j >> 1) * 32 + c8 + (j & 1) * 4 + r; };
   if constexpr (ROPE) {
     const int nq = a.nh * a.hd, nk = a.kv * a.hd;
 #pragma unroll
@@ -534,7 +540,7 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         // the rotary pair (n, n + 1): n even, both in one of q, k, v
-        const int n = n0 + wn0 + j * 16 + c4 + 2 * t;
+        const int n = col(j, 2 * t);
         if (n >= a.N) continue;
         const bool rot = n < nq + nk;
         const int d = n % a.hd;
@@ -635,45 +641,50 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
   }
   __syncthreads();
   if (a.vec_out) {
-    // every column chunk's split and bias first (the compiler cannot move
+    // every 8-column chunk's split and bias first (the compiler cannot move
     // these loads above the output stores, which might alias them)
-    uint8_t* colp[NJ];
-    int64_t ldb[NJ];
-    float b[NJ][4];
+    constexpr int NP = NJ / 2;
+    uint8_t* colp[NP];
+    int64_t ldb[NP];
+    float b[NP][8];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      // columns n .. n + 3 lie in the split of their 8-column group
-      const int n = n0 + wn0 + j * 16 + c4;
-      const int idx = tab->grp[(wn0 + j * 16 + c4) >> 3];
-      ldb[j] = tab->ld[idx] * 2;
-      colp[j] = reinterpret_cast<uint8_t*>(tab->ptr[idx]) + (int64_t)(n - tab->off[idx]) * 2 + (int64_t)mr * ldb[j];
+    for (int p = 0; p < NP; ++p) {
+      // columns n .. n + 7: one 8-column group, in one split
+      const int n = col(2 * p, 0);
+      const int idx = tab->grp[(n - n0) >> 3];
+      ldb[p] = tab->ld[idx] * 2;
+      colp[p] = reinterpret_cast<uint8_t*>(tab->ptr[idx]) + (int64_t)(n - tab->off[idx]) * 2 + (int64_t)mr * ldb[p];
     }
     if (a.bias != nullptr) {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int n = n0 + wn0 + j * 16 + c4, nb = n < a.N ? n : 0;  // N >= 8
+      for (int p = 0; p < NP; ++p) {
+        const int n = col(2 * p, 0), nb = n < a.N ? n : 0;  // N >= 8
 #pragma unroll
-        for (int r = 0; r < 4; ++r) b[j][r] = bf16f(a.bias[nb + r]);
+        for (int r = 0; r < 8; ++r) b[p][r] = bf16f(a.bias[nb + r]);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+      for (int p = 0; p < NP; ++p)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) b[j][r] = 0.0f;
+        for (int r = 0; r < 8; ++r) b[p][r] = 0.0f;
     }
     // rows checked only in the last row of tiles (a uniform branch)
     auto store_vec = [&](auto ALLC) {
       constexpr bool ALL = decltype(ALLC)::value;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if (n0 + wn0 + j * 16 + c4 >= a.N) continue;
+      for (int p = 0; p < NP; ++p) {
+        if (col(2 * p, 0) >= a.N) continue;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           if (!ALL && mr + i * 16 >= a.M) continue;
-          const u32x2_t v = {pk_bf16(alpha * acc[i][j][0] + b[j][0], alpha * acc[i][j][1] + b[j][1]),
-                             pk_bf16(alpha * acc[i][j][2] + b[j][2], alpha * acc[i][j][3] + b[j][3])};
+          const v4f& lo = acc[i][2 * p];
+          const v4f& hi = acc[i][2 * p + 1];
+          const u32x4_t v = {pk_bf16(alpha * lo[0] + b[p][0], alpha * lo[1] + b[p][1]),
+                             pk_bf16(alpha * lo[2] + b[p][2], alpha * lo[3] + b[p][3]),
+                             pk_bf16(alpha * hi[0] + b[p][4], alpha * hi[1] + b[p][5]),
+                             pk_bf16(alpha * hi[2] + b[p][6], alpha * hi[3] + b[p][7])};
           // a global (not flat) store: the split table holds generic pointers
-          *(__attribute__((address_space(1))) u32x2_t*)(uintptr_t)(colp[j] + (int64_t)(i * 16) * ldb[j]) = v;
+          *(__attribute__((address_space(1))) u32x4_t*)(uintptr_t)(colp[p] + (int64_t)(i * 16) * ldb[p]) = v;
         }
       }
     };
@@ -690,7 +701,7 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int n = n0 + wn0 + j * 16 + c4 + r;
+        const int n = col(j, r);
         if (n >= a.N) continue;
         uint8_t* colp;
         int64_t ldb;
@@ -775,8 +786,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const TileXY t = tile_of(blockIdx.x, tiles_m, tiles_n, GM);
   const int m0 = t.tm * BM, n0 = t.tn * (GLU ? BN / 2 : BN);
   const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
+  // B rows: GLU forms map each load's rows in ld below; the split and RoPE
+  // forms put W row 32j + 16 (wave % 2) + 8 (lrow / 4) + 4 (wave / 2) +
+  // lrow % 4 into tile row 32j + 8 wave + lrow (load j), so that fragment
+  // rows 4q..4q+3 of fragments 2p and 2p + 1 are columns 32p + 8q .. + 7
   const uint32_t offB =
-      GLU ? (uint32_t)(lrow * a.K + cch * 16) : (uint32_t)((int64_t)(n0 + wave * 8 + lrow) * a.K) + cch * 16;
+      GLU ? (uint32_t)(lrow * a.K + cch * 16)
+          : (uint32_t)((int64_t)(n0 + 16 * (wave & 1) + 8 * (lrow >> 2) + 4 * (wave >> 1) + (lrow & 3)) * a.K) +
+                cch * 16;
   // this lane's offset for load 0 of the A (B = false) or B unit of stage
   // ks, or kOOB past the last stage (and, with KTAIL, past K). Load j adds
   // a multiple of the row stride that leaves kOOB past any record count
