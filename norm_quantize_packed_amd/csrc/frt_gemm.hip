@@ -8,8 +8,8 @@
 // Both operands are K-contiguous ("TN"). The main loop runs on the CDNA4
 // FP8 matrix cores, v_mfma_f32_32x32x64_f8f6f4 (A = 32 rows of x8, B = 32
 // rows of W8, 64-deep K step, fp32 accumulate) in the tile kernels, and
-// v_mfma_f32_16x16x128_f8f6f4 (16 rows each, 128-deep) in the deep-K
-// 256 x 256 kernel.
+// v_mfma_f32_16x16x128_f8f6f4 (16 rows each, 128-deep) in the 256 x 256
+// kernel.
 //
 // Tiles are staged through LDS with direct buffer->LDS loads, in 128-deep K
 // stages (a stage may hold NSUB of them), row-major with one 128-byte
@@ -84,18 +84,6 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
   return TileXY{first + within % rows, within / rows};
 }
 
-
-// The tile kernels' epilogue (frt_gemm_epilogue.inc) as a function, for the
-// GEGLU and RoPE forms of gemm256_kernel (gemm_kernel includes the same
-// source in its own body, where the compiler schedules the argument loads
-// of the split table lazily, as a function boundary does not let it).
-// `slot` is SLOT bytes of LDS that no wave of the block reads any more and
-// that no load still targets; `lds` is the whole allocation (TOTAL bytes).
-template <int MI, int NJ, int WN, int NW, bool GLU, bool ROPE, bool FP4, int SLOT, int TOTAL>
-__device__ __forceinline__ void gemm_epilogue(GemmArgs a, v16f (&acc)[MI][NJ], int m0, int n0, int wm0,
-                                              int wn0, int wave, int lane, uint8_t* slot, uint8_t* lds) {
-#include "frt_gemm_epilogue.inc"
-}
 
 // Tiled kernel: BM x BN block tile, WM x WN per wave, 128-deep K staging.
 //
@@ -964,14 +952,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   gemm256_epilogue<GLU, ROPE>(a, acc, m0, n0, wm0, wn0, lane, reinterpret_cast<LdsSplits*>(smem));
 }
 
-// K from which the 256 x 256 plan runs on gemm256_kernel rather than on
-// gemm_kernel's eight 128 x 64 waves (measured, rotated operands, same box:
-// 8192 x 9216 x 3072 with bias and three splits 217 -> 214 us, 2048 x 32768
-// x 4096 255 -> 225 us, 2048 x 9216 x 4096 101 -> 98 us, 8192 x 9216 x 2048
-// level; at K = 1024 the single wave per SIMD exposes the tile's prologue
-// and epilogue: 8192 x 9216 x 1024 100 -> 111 us)
-constexpr int kDeepK = 2048;
-
+// The 256 x 256 plan runs on gemm256_kernel at every K the API admits: it
+// beat a 256 x 256 tile of eight 128 x 64 waves (32x32x64 MFMAs, the same
+// direct-store improvements to its epilogue) down to K = 512 (rotated
+// operands, same box: 8192 x 9216 x 512 / 1024: 72.6 -> 67.6, 102.0 -> 94.0
+// us; 2048 x 32768 x 512 / 1024: 62.2 -> 55.8, 87.0 -> 78.0 us).
 template <bool GLU, bool ROPE>
 hipError_t launch_256(const GemmArgs& a, hipStream_t st) {
   const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
@@ -1040,7 +1025,7 @@ int64_t plan_cost(const GemmArgs& a, int BM, int BN, int cus) {
 // weights):
 //  M > 64: the plan of least per-CU load (plan_cost) among 256x256 tiles
 //    (M >= 512 only: the MFMA-bound shapes; gemm256_kernel's four 128x128
-//    waves from K = kDeepK, else eight 128x64 waves), 128x128 of
+//    waves), 128x128 of
 //    sixteen 32x32 waves, 64x64 of four 32x32 waves and 64x32 with 256-deep
 //    stages. E.g. 256 x 16384 -> 128x128; 256 x 2560 -> 64x64 (160 tiles);
 //    256 x 2048 over K = 8192 -> 64x32 (256 tiles: 17 us against 22 us for
@@ -1058,9 +1043,7 @@ hipError_t launch_planned(const GemmArgs& a, hipStream_t st) {
     for (int p = 0; p < 4; ++p)  // ordered large to small: ties go to the smaller tile
       if (cost[p] <= c) c = cost[p], best = p;
     switch (best) {
-      case 0:
-        return a.K >= kDeepK ? launch_256<false, ROPE>(a, st)
-                             : launch_tiles<256, 256, 128, 64, 2, 4, 1, 256, false, ROPE>(a, st);
+      case 0: return launch_256<false, ROPE>(a, st);
       case 1: return launch_tiles<128, 128, 32, 32, 3, 2, 1, 128, false, ROPE>(a, st);
       case 2: return launch_tiles<64, 64, 32, 32, 4, 1, 1, 64, false, ROPE>(a, st);
       default: return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, ROPE>(a, st);
@@ -1132,16 +1115,16 @@ hipError_t launch_gemm_mxfp4_geglu(const GemmArgs& a, hipStream_t st) {
   return launch_tiles<64, 64, 32, 64, 4, 1, 1, 64, true, false, true>(a, st);
 }
 
-// GEGLU plans: the same tiles with 64-column wave tiles (a gate/up pair per
-// lane), chosen by plan_cost: 256x256 (M >= 512), 128x128 of eight 32x64
-// waves, 64x64 of two 32x64 waves (also every M <= 64).
+// GEGLU plans: chosen by plan_cost: 256x256 (M >= 512, gemm256_kernel),
+// 128x128 of eight 32x64 waves, 64x64 of two 32x64 waves (also every
+// M <= 64); a lane holds a gate column and its up column.
 hipError_t launch_gemm_geglu(const GemmArgs& a, hipStream_t st) {
   if (a.M > 64) {
     const int cus = device_cus();
     const int64_t c256 = a.M >= 512 ? plan_cost(a, 256, 256, cus) : INT64_MAX;
     const int64_t c128 = plan_cost(a, 128, 128, cus), c64 = plan_cost(a, 64, 64, cus);
     if (c256 < c128 && c256 < c64)
-      return a.K >= kDeepK ? launch_256<true, false>(a, st) : launch_tiles<256, 256, 128, 64, 2, 4, 1, 256, true>(a, st);
+      return launch_256<true, false>(a, st);
     if (c128 < c64) return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, true>(a, st);
   }
   return launch_tiles<64, 64, 32, 64, 4, 1, 1, 64, true>(a, st);

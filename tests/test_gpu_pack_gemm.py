@@ -270,13 +270,13 @@ def test_gemm_large_full_grid(K):
             assert np.array_equal(out, first), f"{M}x{N}x{K} rep {rep}"
 
 
-def test_gemm_large_staged_epilogue_matches_per_lane_stores():
+def test_gemm_large_vector_stores_match_per_element_stores():
     """The 256x256 plan (2000 x 5000 x 528 takes it: 160 tiles, one round)
-    stages bf16 results in LDS and stores whole 128-byte row segments when
-    every split width and row stride is a multiple of 8 elements; a padded
-    stride (ld = n + 6) takes the per-lane stores. Ragged M, N and K, a
-    bias, and a split boundary inside a tile: both layouts give the same
-    bits, match the oracle, and write nothing outside their outputs."""
+    stores bf16 results 16 bytes a lane when every split width and row
+    stride is a multiple of 8 elements; a padded stride (ld = n + 6) takes
+    the per-element stores. Ragged M, N and K, a bias, and a split boundary
+    inside a tile: both give the same bits, match the oracle, and write
+    nothing outside their outputs."""
     rng = np.random.default_rng(31)
     M, K, splits = 2000, 528, [3000, 2000]
     N = sum(splits)
@@ -285,16 +285,16 @@ def test_gemm_large_staged_epilogue_matches_per_lane_stores():
     bias = wl.to_bf16_bits(0.05 * rng.standard_normal(N).astype(np.float32))
     s_a, s_w = np.float32(0.003), np.float32(0.002)
     ref = gemm.packed_gemm_split(x8, w8, s_a, s_w, bias, splits)
-    staged = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
+    vec = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
     lane = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False, ld_pad=6)
-    for i, (a, b, r) in enumerate(zip(staged, lane, ref)):
-        assert np.array_equal(a, b), f"split {i}: staged and per-lane stores differ"
+    for i, (a, b, r) in enumerate(zip(vec, lane, ref)):
+        assert np.array_equal(a, b), f"split {i}: vector and per-element stores differ"
         assert_gemm_bf16(a, r, f"2000x5000x528 split {i}")
 
 
 @pytest.mark.parametrize("K", [2048, 3088, 6160])
 def test_gemm_deep_k_plan_full_grid(K):
-    """The 256x256 plan at K >= 2048 (four 128x128 waves, five-unit ring):
+    """The 256x256 plan (four 128x128 waves, five-unit ring) at deeper K:
     2000 x 5000 takes it (160 tiles, one round; ragged M and N), with a bias,
     three splits whose boundaries fall inside tiles and, at K = 3088 and
     6160, a K tail. Every fp32 output is checked against the oracle; the
@@ -312,10 +312,10 @@ def test_gemm_deep_k_plan_full_grid(K):
     f32 = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=True)
     for i, (g, r) in enumerate(zip(f32, ref)):
         assert_gemm_f32(g, r, f"2000x5000x{K} fp32 split {i}")
-    staged = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
+    vec = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
     lane = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False, ld_pad=6)
     again = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
-    for i, (a, b, c, r) in enumerate(zip(staged, lane, again, ref)):
+    for i, (a, b, c, r) in enumerate(zip(vec, lane, again, ref)):
         assert np.array_equal(a, b), f"split {i}: vector and per-element stores differ"
         assert np.array_equal(a, c), f"split {i}: repeated call differs"
         assert_gemm_bf16(a, r, f"2000x5000x{K} split {i}")
