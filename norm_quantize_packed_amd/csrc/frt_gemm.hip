@@ -584,32 +584,43 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
         bg[p][r] = ok ? bf16f(a.bias[gc]) : 0.0f;
         bu[p][r] = ok ? bf16f(a.bias[a.H + gc]) : 0.0f;
       }
+    // the wave's 64 gate columns and 128 rows all in range, 4-byte code
+    // stores: no per-value checks (a uniform branch)
+    const bool all_in = rows_in && vec4 && n0 + (wn0 >> 1) + 64 <= a.H;
+    auto body = [&](auto ALLC) {
+      constexpr bool ALL = decltype(ALLC)::value;
 #pragma unroll
-    for (int p = 0; p < NJ / 2; ++p) {
-      const int gc = n0 + (wn0 >> 1) + p * 16 + c4;
-      if (gc >= a.H) continue;
+      for (int p = 0; p < NJ / 2; ++p) {
+        const int gc = n0 + (wn0 >> 1) + p * 16 + c4;
+        if (!ALL && gc >= a.H) continue;
 #pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int m = mr + i * 16;
-        if (!rows_in && m >= a.M) continue;
-        uint32_t codes = 0;
+        for (int i = 0; i < MI; ++i) {
+          const int m = mr + i * 16;
+          if (!ALL && m >= a.M) continue;
+          float qv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float vg = alpha * acc[i][2 * p][r] + bg[p][r];
-          const float vu = alpha * acc[i][2 * p + 1][r] + bu[p][r];
-          const float y = gelu_tanh(__uint_as_float(f2bf(vg) << 16)) * __uint_as_float(f2bf(vu) << 16);
-          codes |= ((uint32_t)cvt2_fp8(clamp_fp8(div_rn(y, qs, qr)), 0.0f) & 0xFFu) << (8 * r);
-        }
-        uint8_t* q = a.q8 + (int64_t)m * a.ld_q8 + gc;
-        if (vec4 && gc + 4 <= a.H) {
-          *reinterpret_cast<uint32_t*>(q) = codes;
-        } else {
+          for (int r = 0; r < 4; ++r) {
+            // gate and up to bf16 in one conversion (pk_bf16 rounds as f2bf)
+            const uint32_t w = pk_bf16(alpha * acc[i][2 * p][r] + bg[p][r], alpha * acc[i][2 * p + 1][r] + bu[p][r]);
+            const float y = gelu_tanh(bf16lo(w)) * bf16hi(w);
+            qv[r] = clamp_fp8(div_rn(y, qs, qr));
+          }
+          const uint32_t codes = cvt4_fp8(qv[0], qv[1], qv[2], qv[3]);
+          uint8_t* q = a.q8 + (int64_t)m * a.ld_q8 + gc;
+          if (ALL || (vec4 && gc + 4 <= a.H)) {
+            *reinterpret_cast<uint32_t*>(q) = codes;
+          } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (gc + r < a.H) q[r] = (uint8_t)(codes >> (8 * r));
+            for (int r = 0; r < 4; ++r)
+              if (gc + r < a.H) q[r] = (uint8_t)(codes >> (8 * r));
+          }
         }
       }
-    }
+    };
+    if (all_in)
+      body(std::true_type{});
+    else
+      body(std::false_type{});
     return;
   }
   if (threadIdx.x < FRT_MAX_SPLITS) {
