@@ -471,7 +471,7 @@ struct LdsSplits {
   int64_t ld[FRT_MAX_SPLITS];
   int off[FRT_MAX_SPLITS];
   int n;
-  uint8_t grp[32];  // the split of each 8-column group of a 256-column tile
+  uint8_t grp[32];  // the split of each 8-column group of a (<= 256-column) tile
 };
 
 // Output pointer of column n (in its split) and its row stride, in bytes
@@ -510,10 +510,10 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 // a store, else one store per element; `tab` is the split table in LDS,
 // filled here after a block barrier. Rows past M exist only in the last row
 // of tiles.
-template <bool GLU, bool ROPE>
-__device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8][8], int m0, int n0, int wm0,
+template <bool GLU, bool ROPE, int NJ, int BN>
+__device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8][NJ], int m0, int n0, int wm0,
                                                  int wn0, int lane, LdsSplits* tab) {
-  constexpr int MI = 8, NJ = 8;
+  constexpr int MI = 8;
   const int c4 = (lane >> 4) * 4;            // GEGLU: first of the lane's columns in a fragment
   const int c8 = (lane >> 4) * 8;            // split, RoPE: first of its columns in a fragment pair
   const int mr = m0 + wm0 + (lane & 15);     // the lane's row in row block i = 0
@@ -628,7 +628,7 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
     tab->ld[threadIdx.x] = a.sp.ld[threadIdx.x];
     tab->off[threadIdx.x] = a.sp.off[threadIdx.x];
     if (threadIdx.x == 0) tab->n = a.sp.n;
-  } else if (threadIdx.x >= 64 && threadIdx.x < 96 && a.vec_out) {
+  } else if (threadIdx.x >= 64 && threadIdx.x < 64 + BN / 8 && a.vec_out) {
     // vec_out split widths are multiples of 8: an 8-column group lies in one
     // split, found once here for the whole block
     const int g = threadIdx.x - 64, n = n0 + 8 * g;
@@ -724,49 +724,52 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
     store_all(std::false_type{});
 }
 
-// Large-M FP8 kernel: a 256 x 256 block tile of four 128 x 128 wave tiles
-// (one wave per SIMD, accumulators in the matrix-core registers), on
-// v_mfma_f32_16x16x128_f8f6f4: each MFMA takes a whole 128-deep stage of a
-// 16-row A fragment and a 16-row B fragment. Under sustained load the board
-// holds an FP8 MFMA loop of this shape at a higher engine clock than one of
-// 32x32x64 MFMAs doing the same work (measured: 2.05 against 1.86 GHz), and
-// this kernel's time follows the clock.
+// Large-M FP8 kernel: a 256 x BN block tile (BN = 256 or 192) of four
+// 128 x BN/2 wave tiles (one wave per SIMD, accumulators in the
+// matrix-core registers), on v_mfma_f32_16x16x128_f8f6f4: each MFMA takes a
+// whole 128-deep stage of a 16-row A fragment and a 16-row B fragment.
+// Under sustained load the board holds an FP8 MFMA loop of this shape at a
+// higher engine clock than one of 32x32x64 MFMAs doing the same work
+// (measured: 2.05 against 1.86 GHz), and this kernel's time follows the
+// clock.
 //
-// The LDS is a ring of five 32 KB units; a unit holds the A rows or the B
-// rows of one 128-deep stage (256 rows x 128 bytes, the same swizzled row
-// layout as gemm_kernel). Stage kt reads units 2kt (A) and 2kt + 1 (B);
-// while it runs, unit 2kt + 2 is still in flight and units 2kt + 3 and
-// 2kt + 4 are issued into the slots of stage kt - 1, so up to three units
-// (96 KB) load behind the compute instead of one 64 KB stage (the load path
-// keeps more lines in flight this way; half-line row segments, the other way
-// to deepen a ring within 160 KB, fetch each line twice and are slower).
+// The LDS is a ring of five 32 KB units; a unit holds the A rows (256) or
+// the B rows (BN) of one 128-deep stage, 128 bytes a row in the swizzled
+// row layout of gemm_kernel. Unit u sits in slot u % 5; stage kt reads
+// units 2kt (A) and 2kt + 1 (B). During stage kt the wave issues the loads
+// of units 2kt + 4 and 2kt + 5 (the next-but-one stage), so a unit is in
+// flight for 1.5-1.75 stages before its first read.
 //
-// A wave's 128 x 128 tile is four 64 x 64 blocks over quarters of its
-// fragments (A lo / A hi: fragment rows 0-63 / 64-127; B lo / B hi likewise),
-// 16 MFMAs each, in the order (A lo, B lo), (A hi, B lo), (A lo, B hi),
-// (A hi, B hi), four register quarters (128 VGPRs) in all: during the first
-// block the wave issues the stage's 16 loads and reads the stage's A hi and
-// B hi; after the third it waits for the next stage's units and takes the
-// stage barrier, and during the last, which needs neither, it reads the next
-// stage's A lo and B lo. Work is issued in a fixed order (no compiler
-// reordering). Each accumulator takes one MFMA per stage, in K order. Past
-// the last stage the loads fetch zeros into free slots (branch-free); the
-// block drains them before the epilogue.
+// A wave's tile is four blocks over quarters of its fragments (A lo / A hi:
+// fragment rows 0-63 / 64-127; B lo / B hi: the first and second half of
+// its BN/2 rows), in the order (A lo, B lo), (A hi, B lo), (A lo, B hi),
+// (A hi, B hi), four register quarters (at most 128 VGPRs) in all. Block 0
+// issues the loads of unit 2kt + 4 (its slot, unit 2kt - 1's, freed at the
+// previous stage's first barrier) and reads the stage's A hi and B hi, which
+// ends the reads of units 2kt and 2kt + 1; a barrier frees their slots;
+// block 1 issues unit 2kt + 5 into unit 2kt's slot; after block 2 the wave
+// waits for units up to 2kt + 3 and takes a second barrier; block 3, which
+// needs neither, reads the next stage's A lo and B lo. Work is issued in a
+// fixed order (no compiler reordering). Each accumulator takes one MFMA per
+// stage, in K order. Past the last stage the loads fetch zeros into free
+// slots (branch-free); the block drains them before the epilogue.
 //
-// GLU and ROPE select the epilogue forms described at gemm_kernel; for GLU
-// the B tile interleaves 16 gate rows and the 16 matching up rows, so each
-// lane holds a gate column and its up column. KTAIL zero-fills the 16-byte
-// chunks past K.
-template <bool GLU, bool ROPE, bool KTAIL>
+// GLU and ROPE select the epilogue forms described at gemm_kernel (BN = 256
+// only); for GLU the B tile interleaves 16 gate rows and the 16 matching up
+// rows, so each lane holds a gate column and its up column. KTAIL
+// zero-fills the 16-byte chunks past K.
+template <bool GLU, bool ROPE, bool KTAIL, int BN = 256>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm256_kernel(GemmArgs a) {
-  constexpr int BM = 256, BN = 256, GM = 4, NW = 4, MI = 8, NJ = 8;
-  constexpr int UNIT = 256 * 128, RU = 5, LPU = 256 / 8 / NW;  // 8 loads a wave per unit
+  static_assert(BN == 256 || (BN == 192 && !GLU && !ROPE), "256 x 192 tiles: split form only");
+  constexpr int BM = 256, GM = 4, NW = 4, MI = 8, WN = BN / 2, NJ = WN / 16, NQ = NJ / 2;
+  constexpr int UNIT = 256 * 128, RU = 5;
+  constexpr int LPA = BM / 8 / NW, LPB = BN / 8 / NW;  // loads a wave per A / B unit
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RU * UNIT];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = (a.N + BN - 1) / BN;
-  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * 128;
+  const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * WN;
   const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + a.K);
   const uint32_t w_bytes = (uint32_t)((int64_t)a.N * a.K);
   const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, x_bytes);
@@ -789,6 +792,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // forms put W row 32j + 16 (wave % 2) + 8 (lrow / 4) + 4 (wave / 2) +
   // lrow % 4 into tile row 32j + 8 wave + lrow (load j), so that fragment
   // rows 4q..4q+3 of fragments 2p and 2p + 1 are columns 32p + 8q .. + 7
+  // (a wave's B rows start on a 32-row boundary)
   const uint32_t offB =
       GLU ? (uint32_t)(lrow * a.K + cch * 16)
           : (uint32_t)((int64_t)(n0 + 16 * (wave & 1) + 8 * (lrow >> 2) + 4 * (wave >> 1) + (lrow & 3)) * a.K) +
@@ -807,8 +811,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     return ks < KT ? o : kOOB;
   };
-  // load j (of LPU) of a unit whose ubase is `ob` into the ring slot at
-  // byte offset `so`
+  // load j of a unit whose ubase is `ob` into the ring slot at byte offset
+  // `so`
   auto ld = [&](int so, auto BC, uint32_t ob, int j) {
     constexpr bool B = decltype(BC)::value;
     uint8_t* dst = smem + so + (wave + j * NW) * 1024;
@@ -836,10 +840,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int lo = r16 * 128 + ((((lane >> 4) * 2) ^ sw) * 16);
   // the fragment's second chunk sits at position ^ 1, i.e. +16 or -16 bytes
   const int d1 = (sw & 1) ? -16 : 16;
-  v8i R[4][4];  // four quarters of four fragments
+  v8i R[4][4];  // four quarters of (up to) four fragments
   v4f acc[MI][NJ];
-  // 16-byte half h (0..7) of quarter Q: fragment h / 2 of the 64 rows from
-  // row0 of `unit` (which includes this lane's offset), part h % 2
+  // 16-byte half h of quarter Q: fragment h / 2 of the rows from row0 of
+  // `unit` (which includes this lane's offset), part h % 2
   auto rd = [&](auto QC, const uint8_t* unit, int row0, int h) {
     constexpr int Q = decltype(QC)::value;
     const int k = h >> 1;
@@ -857,10 +861,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     acc[i0 + i][j0 + j] =
         __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(R[QB][j], R[QA][i], acc[i0 + i][j0 + j], 0, 0, 0, 0, 0, 0);
   };
-  // MFMA order within a block: shells k = 0..3 ((k, 0..k) then (0..k-1, k)),
-  // so the first MFMAs need the fragments read first
-  constexpr int OI[16] = {0, 1, 1, 0, 2, 2, 2, 0, 1, 3, 3, 3, 3, 0, 1, 2};
-  constexpr int OJ[16] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2, 3, 3, 3, 3};
+  // MFMA order within a block (4 x NQ): shells k = 0..3 ((k, 0..k) then
+  // (0..k-1, k), columns < NQ), so the first MFMAs need the fragments read
+  // first
+  constexpr int NB = 4 * NQ;  // MFMAs a block
+  constexpr int OI4[16] = {0, 1, 1, 0, 2, 2, 2, 0, 1, 3, 3, 3, 3, 0, 1, 2};
+  constexpr int OJ4[16] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2, 3, 3, 3, 3};
+  constexpr int OI3[12] = {0, 1, 1, 0, 2, 2, 2, 0, 1, 3, 3, 3};
+  constexpr int OJ3[12] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2};
+  auto oi = [&](int q) { return NQ == 4 ? OI4[q] : OI3[q]; };
+  auto oj = [&](int q) { return NQ == 4 ? OJ4[q] : OJ3[q]; };
+  // the next stage's A lo / B lo half-reads in the order A0 B0 A1 B1 ...
+  // (B only for fragments < NQ): read n (0 .. 8 + 2 NQ - 1) is half h of
+  // quarter 0 (A) or 1 (B)
+  auto lo_read = [&](int n, const uint8_t* una, const uint8_t* unb) {
+    const int pair = n >> 1, part = n & 1;
+    // pairs alternate A, B while both remain, then A only
+    const int ab = pair < 2 * NQ ? (pair & 1) : 0;
+    const int k = pair < 2 * NQ ? (pair >> 1) : pair - NQ;
+    if (ab == 0)
+      rd(std::integral_constant<int, 0>{}, una, wm0, 2 * k + part);
+    else
+      rd(std::integral_constant<int, 1>{}, unb, wn0, 2 * k + part);
+  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -884,15 +907,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // was freed at the previous stage's first barrier); this stage's A hi
     // and B hi, which finish the reads of units 2kt and 2kt + 1
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      mf(I0{}, I1{}, 0, 0, OI[q], OJ[q]);
-      if ((q & 1) == 0) ld(s4, BA{}, oa2, q >> 1);
+    for (int q = 0; q < NB; ++q) {
+      mf(I0{}, I1{}, 0, 0, oi(q), oj(q));
+      if ((q & 1) == 0 && (q >> 1) < LPA) ld(s4, BA{}, oa2, q >> 1);
       if (q < 8)
         rd(I2{}, ua, wm0 + 64, q);
       else
-        rd(I3{}, ub, wn0 + 64, q - 8);
+        rd(I3{}, ub, wn0 + NQ * 16, q - 8);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int j = NB / 2; j < LPA; ++j) ld(s4, BA{}, oa2, j);
+#pragma unroll
+    for (int h = NB - 8; h < 2 * NQ; ++h) rd(I3{}, ub, wn0 + NQ * 16, h);
     // every wave done with units 2kt and 2kt + 1
     __builtin_amdgcn_s_waitcnt(lgkm_imm(0));
     __builtin_amdgcn_s_barrier();
@@ -900,33 +927,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // (A hi, B lo) with the loads of unit 2kt + 5 (into unit 2kt's slot),
     // then (A lo, B hi)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      mf(I2{}, I1{}, 4, 0, OI[q], OJ[q]);
-      if ((q & 1) == 0) ld(sa, BB{}, ob2, q >> 1);
+    for (int q = 0; q < NB; ++q) {
+      mf(I2{}, I1{}, 4, 0, oi(q), oj(q));
+      if ((q & 1) == 0 && (q >> 1) < LPB) ld(sa, BB{}, ob2, q >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      mf(I0{}, I3{}, 0, 4, OI[q], OJ[q]);
+    for (int j = NB / 2; j < LPB; ++j) ld(sa, BB{}, ob2, j);
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      mf(I0{}, I3{}, 0, NQ, oi(q), oj(q));
       __builtin_amdgcn_sched_barrier(0);
     }
-    // units up to 2kt + 3 landed (this wave's last 2 LPU loads are units
-    // 2kt + 4 and 2kt + 5)
-    __builtin_amdgcn_s_waitcnt(vm_imm(2 * LPU));
+    // units up to 2kt + 3 landed (this wave's last LPA + LPB loads are
+    // units 2kt + 4 and 2kt + 5)
+    __builtin_amdgcn_s_waitcnt(vm_imm(LPA + LPB));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    // (A hi, B hi); the next stage's A lo and B lo into their quarters, in
-    // the order A0 B0 A1 B1 ... the next first block needs
+    // (A hi, B hi); the next stage's A lo and B lo into their quarters
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      mf(I2{}, I3{}, 4, 4, OI[q], OJ[q]);
-      const int f = q >> 1, h = 2 * (f >> 1) + (q & 1);
-      if ((f & 1) == 0)
-        rd(I0{}, una, wm0, h);
-      else
-        rd(I1{}, unb, wn0, h);
+    for (int q = 0; q < NB; ++q) {
+      mf(I2{}, I3{}, 4, NQ, oi(q), oj(q));
+      lo_read(q, una, unb);
       __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int n = NB; n < 8 + 2 * NQ; ++n) lo_read(n, una, unb);
   };
 
 #pragma unroll
@@ -938,29 +964,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // prologue: units 0..3 in flight; once units 0 and 1 landed, stage 0's
   // A lo and B lo
 #pragma unroll
-  for (int j = 0; j < LPU; ++j) ld(0, BA{}, ubase(BA{}, 0), j);
+  for (int j = 0; j < LPA; ++j) ld(0, BA{}, ubase(BA{}, 0), j);
 #pragma unroll
-  for (int j = 0; j < LPU; ++j) ld(UNIT, BB{}, ubase(BB{}, 0), j);
+  for (int j = 0; j < LPB; ++j) ld(UNIT, BB{}, ubase(BB{}, 0), j);
 #pragma unroll
-  for (int j = 0; j < LPU; ++j) ld(2 * UNIT, BA{}, ubase(BA{}, 1), j);
+  for (int j = 0; j < LPA; ++j) ld(2 * UNIT, BA{}, ubase(BA{}, 1), j);
 #pragma unroll
-  for (int j = 0; j < LPU; ++j) ld(3 * UNIT, BB{}, ubase(BB{}, 1), j);
-  __builtin_amdgcn_s_waitcnt(vm_imm(2 * LPU));
+  for (int j = 0; j < LPB; ++j) ld(3 * UNIT, BB{}, ubase(BB{}, 1), j);
+  __builtin_amdgcn_s_waitcnt(vm_imm(LPA + LPB));
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int f = q >> 1, h = 2 * (f >> 1) + (q & 1);
-    if ((f & 1) == 0)
-      rd(I0{}, smem + lo, wm0, h);
-    else
-      rd(I1{}, smem + UNIT + lo, wn0, h);
-  }
+  for (int n = 0; n < 8 + 2 * NQ; ++n) lo_read(n, smem + lo, smem + UNIT + lo);
   for (int kt = 0, sa = 0; kt < KT; ++kt, sa = nx(nx(sa))) stage(kt, sa);
   // drain the zero-fill loads past the last stage; then every wave is done
   // with the ring and the epilogue may stage in any of it
   __builtin_amdgcn_s_waitcnt(vm_imm(0));
   __syncthreads();
-  gemm256_epilogue<GLU, ROPE>(a, acc, m0, n0, wm0, wn0, lane, reinterpret_cast<LdsSplits*>(smem));
+  gemm256_epilogue<GLU, ROPE, NJ, BN>(a, acc, m0, n0, wm0, wn0, lane, reinterpret_cast<LdsSplits*>(smem));
 }
 
 // The 256 x 256 plan runs on gemm256_kernel at every K the API admits: it
@@ -968,16 +988,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // direct-store improvements to its epilogue) down to K = 512 (rotated
 // operands, same box: 8192 x 9216 x 512 / 1024: 72.6 -> 67.6, 102.0 -> 94.0
 // us; 2048 x 32768 x 512 / 1024: 62.2 -> 55.8, 87.0 -> 78.0 us).
-template <bool GLU, bool ROPE>
+template <bool GLU, bool ROPE, int BN = 256>
 hipError_t launch_256(const GemmArgs& a, hipStream_t st) {
-  const int tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int tiles = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
   if (a.K % 128 == 0)
-    hipLaunchKernelGGL((gemm256_kernel<GLU, ROPE, false>), dim3(tiles), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm256_kernel<GLU, ROPE, false, BN>), dim3(tiles), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm256_kernel<GLU, ROPE, true>), dim3(tiles), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm256_kernel<GLU, ROPE, true, BN>), dim3(tiles), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
+// Rounds of 256 x BN tiles on `cus` CUs.
+int64_t rounds_256(const GemmArgs& a, int BN, int cus) {
+  const int64_t tiles = (int64_t)((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
+  return (tiles + cus - 1) / cus;
+}
 template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1, int AE = BM, bool GLU = false,
           bool ROPE = false, bool FP4 = false>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
@@ -1054,7 +1079,17 @@ hipError_t launch_planned(const GemmArgs& a, hipStream_t st) {
     for (int p = 0; p < 4; ++p)  // ordered large to small: ties go to the smaller tile
       if (cost[p] <= c) c = cost[p], best = p;
     switch (best) {
-      case 0: return launch_256<false, ROPE>(a, st);
+      case 0:
+        // split form: 256 x 192 tiles where they fill the same number of
+        // rounds (at least two) better (same box: 8192 x 3072 x 3072 77.0 ->
+        // 71.5 us, 2048 x 9216 x 4096 89.8 -> 77.3, 4096 x 6144 x 1024 39.3
+        // -> 37.3); with more rounds (8192 x 9216 x 3072: 5 against 6) or a
+        // single one (2000 x 5000 x 2048: 57.1 against 69.7 us) 256 x 256
+        if constexpr (!ROPE) {
+          const int64_t r256 = rounds_256(a, 256, cus);
+          if (r256 >= 2 && rounds_256(a, 192, cus) == r256) return launch_256<false, false, 192>(a, st);
+        }
+        return launch_256<false, ROPE>(a, st);
       case 1: return launch_tiles<128, 128, 32, 32, 3, 2, 1, 128, false, ROPE>(a, st);
       case 2: return launch_tiles<64, 64, 32, 32, 4, 1, 1, 64, false, ROPE>(a, st);
       default: return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, ROPE>(a, st);

@@ -293,32 +293,35 @@ def test_gemm_large_vector_stores_match_per_element_stores():
 
 
 @pytest.mark.parametrize("K", [2048, 3088, 6160])
-def test_gemm_deep_k_plan_full_grid(K):
-    """The 256x256 plan (four 128x128 waves, five-unit ring) at deeper K:
-    2000 x 5000 takes it (160 tiles, one round; ragged M and N), with a bias,
-    three splits whose boundaries fall inside tiles and, at K = 3088 and
-    6160, a K tail. Every fp32 output is checked against the oracle; the
-    8-byte row-segment bf16 stores and the per-element stores of a padded
-    stride give the same bits, match the oracle and write nothing outside
-    their outputs; a second call repeats the bits."""
+@pytest.mark.parametrize("splits", [[5000, 2400, 1600], [4000, 2400, 1600]])
+def test_gemm_deep_k_plan_full_grid(K, splits):
+    """The four-wave 256-row plans (five-unit ring) at deeper K: 2000 x 9000
+    takes 256 x 192 tiles (376 tiles against 288 of 256 x 256: two rounds
+    either way), 2000 x 8000 takes 256 x 256 tiles (256 tiles, one round;
+    256 x 192 would need two); ragged M and N, a
+    bias, three splits whose boundaries fall inside tiles and, at K = 3088
+    and 6160, a K tail. Every fp32 output is checked against the oracle; the
+    16-byte bf16 stores and the per-element stores of a padded stride give
+    the same bits, match the oracle and write nothing outside their outputs;
+    a second call repeats the bits."""
     rng = np.random.default_rng(K)
-    M, splits = 2000, [3000, 1200, 800]
+    M = 2000
     N = sum(splits)
     x8 = wl.random_codes(6101 + K, (M, K))
-    w8 = wl.random_codes(6102 + K, (N, K))
+    w8 = wl.random_codes(6102 + K + N, (N, K))
     bias = wl.to_bf16_bits(0.05 * rng.standard_normal(N).astype(np.float32))
     s_a, s_w = np.float32(0.003), np.float32(0.002)
     ref = gemm.packed_gemm_split(x8, w8, s_a, s_w, bias, splits)
     f32 = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=True)
     for i, (g, r) in enumerate(zip(f32, ref)):
-        assert_gemm_f32(g, r, f"2000x5000x{K} fp32 split {i}")
+        assert_gemm_f32(g, r, f"2000x{N}x{K} fp32 split {i}")
     vec = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
     lane = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False, ld_pad=6)
     again = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
     for i, (a, b, c, r) in enumerate(zip(vec, lane, again, ref)):
         assert np.array_equal(a, b), f"split {i}: vector and per-element stores differ"
         assert np.array_equal(a, c), f"split {i}: repeated call differs"
-        assert_gemm_bf16(a, r, f"2000x5000x{K} split {i}")
+        assert_gemm_bf16(a, r, f"2000x{N}x{K} split {i}")
 
 
 def test_gemm_deep_k_plan_row_capacity():
