@@ -724,7 +724,7 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
     store_all(std::false_type{});
 }
 
-// Large-M FP8 kernel: a 256 x BN block tile (BN = 256 or 192) of four
+// Large-M FP8 kernel: a 256 x BN block tile (BN = 256, 192 or 128) of four
 // 128 x BN/2 wave tiles (one wave per SIMD, accumulators in the
 // matrix-core registers), on v_mfma_f32_16x16x128_f8f6f4: each MFMA takes a
 // whole 128-deep stage of a 16-row A fragment and a 16-row B fragment.
@@ -760,7 +760,7 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
 // zero-fills the 16-byte chunks past K.
 template <bool GLU, bool ROPE, bool KTAIL, int BN = 256>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm256_kernel(GemmArgs a) {
-  static_assert(BN == 256 || (BN == 192 && !GLU && !ROPE), "256 x 192 tiles: split form only");
+  static_assert(BN == 256 || ((BN == 192 || BN == 128) && !GLU && !ROPE), "narrower tiles: split form only");
   constexpr int BM = 256, GM = 4, NW = 4, MI = 8, WN = BN / 2, NJ = WN / 16, NQ = NJ / 2;
   constexpr int UNIT = 256 * 128, RU = 5;
   constexpr int LPA = BM / 8 / NW, LPB = BN / 8 / NW;  // loads a wave per A / B unit
@@ -768,7 +768,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int tiles_m = (a.M + BM - 1) / BM;
-  const int tiles_n = (a.N + BN - 1) / BN;
+  const int tiles_n = (a.N - a.n_base + BN - 1) / BN;
   const int wm0 = (wave >> 1) * 128, wn0 = (wave & 1) * WN;
   const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + a.K);
   const uint32_t w_bytes = (uint32_t)((int64_t)a.N * a.K);
@@ -786,7 +786,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // have to wait for them: loads and stores share the wait counter).
   // m0, n0: the tile's first output row and column (GLU: first gate column)
   const TileXY t = tile_of(blockIdx.x, tiles_m, tiles_n, GM);
-  const int m0 = t.tm * BM, n0 = t.tn * (GLU ? BN / 2 : BN);
+  const int m0 = t.tm * BM, n0 = a.n_base + t.tn * (GLU ? BN / 2 : BN);
   const uint32_t offA = (uint32_t)((int64_t)(m0 + wave * 8 + lrow) * a.ld_x) + cch * 16;
   // B rows: GLU forms map each load's rows in ld below; the split and RoPE
   // forms put W row 32j + 16 (wave % 2) + 8 (lrow / 4) + 4 (wave / 2) +
@@ -869,8 +869,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int OJ4[16] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2, 3, 3, 3, 3};
   constexpr int OI3[12] = {0, 1, 1, 0, 2, 2, 2, 0, 1, 3, 3, 3};
   constexpr int OJ3[12] = {0, 0, 1, 1, 0, 1, 2, 2, 2, 0, 1, 2};
-  auto oi = [&](int q) { return NQ == 4 ? OI4[q] : OI3[q]; };
-  auto oj = [&](int q) { return NQ == 4 ? OJ4[q] : OJ3[q]; };
+  constexpr int OI2[8] = {0, 1, 1, 0, 2, 2, 3, 3};
+  constexpr int OJ2[8] = {0, 0, 1, 1, 0, 1, 0, 1};
+  auto oi = [&](int q) { return NQ == 4 ? OI4[q] : NQ == 3 ? OI3[q] : OI2[q]; };
+  auto oj = [&](int q) { return NQ == 4 ? OJ4[q] : NQ == 3 ? OJ3[q] : OJ2[q]; };
   // the next stage's A lo / B lo half-reads in the order A0 B0 A1 B1 ...
   // (B only for fragments < NQ): read n (0 .. 8 + 2 NQ - 1) is half h of
   // quarter 0 (A) or 1 (B)
@@ -990,7 +992,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // us; 2048 x 32768 x 512 / 1024: 62.2 -> 55.8, 87.0 -> 78.0 us).
 template <bool GLU, bool ROPE, int BN = 256>
 hipError_t launch_256(const GemmArgs& a, hipStream_t st) {
-  const int tiles = ((a.M + 255) / 256) * ((a.N + BN - 1) / BN);
+  const int tiles = ((a.M + 255) / 256) * ((a.N - a.n_base + BN - 1) / BN);
   if (a.K % 128 == 0)
     hipLaunchKernelGGL((gemm256_kernel<GLU, ROPE, false, BN>), dim3(tiles), dim3(256), 0, st, a);
   else
@@ -1088,6 +1090,25 @@ hipError_t launch_planned(const GemmArgs& a, hipStream_t st) {
         if constexpr (!ROPE) {
           const int64_t r256 = rounds_256(a, 256, cus);
           if (r256 >= 2 && rounds_256(a, 192, cus) == r256) return launch_256<false, false, 192>(a, st);
+          // else, with a partial last round, two launches: 256 x 256 tiles
+          // over the first columns, in whole rounds, then one round of
+          // 256 x 128 tiles over the rest (8192 x 9216 x 3072: 1024 + 256
+          // tiles instead of 1152 in 4.5 rounds)
+          const int tm = (a.M + 255) / 256, tn = (a.N + 255) / 256;
+          if (r256 >= 2 && ((int64_t)tm * tn) % cus != 0) {
+            int nm = tn - 1;
+            while (nm > 0 && ((int64_t)tm * nm) % cus != 0) --nm;
+            const int64_t rest = (int64_t)tm * ((a.N - nm * 256 + 127) / 128);
+            if (nm > 0 && rest <= cus && ((int64_t)tm * nm) / cus + 1 <= r256) {
+              GemmArgs head = a;
+              head.N = nm * 256;
+              hipError_t e = launch_256<false, false, 256>(head, st);
+              if (e != hipSuccess) return e;
+              GemmArgs tail = a;
+              tail.n_base = nm * 256;
+              return launch_256<false, false, 128>(tail, st);
+            }
+          }
         }
         return launch_256<false, ROPE>(a, st);
       case 1: return launch_tiles<128, 128, 32, 32, 3, 2, 1, 128, false, ROPE>(a, st);

@@ -73,8 +73,8 @@ struct GemmArgs {
   int out_f32;
   SplitTab sp;
   // bf16 outputs whose split widths and row strides are multiples of 8
-  // elements and whose pointers are 16-byte aligned: the 256x256 plan then
-  // stores whole 128-byte row segments (16 bytes a lane)
+  // elements and whose pointers are 16-byte aligned: the 256-row plans then
+  // store 16 bytes a lane
   int vec_out;
   // gate/up GEGLU epilogue (launch_gemm_geglu): W8 holds 2H rows, gate
   // first; codes of gelu_tanh(gate) * up go to q8 [M, ld_q8] at q_scale
@@ -98,6 +98,9 @@ struct GemmArgs {
   // stride ld_sc4; H % 256 == 0
   uint8_t* q4; int64_t ld_q4;
   uint8_t* sc4; int64_t ld_sc4;
+  // first output column of the tiles a launch covers (the 256-row split
+  // plan's second launch of narrower tiles over the last columns; else 0)
+  int n_base;
 };
 
 size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);

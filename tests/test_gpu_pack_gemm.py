@@ -324,6 +324,31 @@ def test_gemm_deep_k_plan_full_grid(K, splits):
         assert_gemm_bf16(a, r, f"2000x{N}x{K} split {i}")
 
 
+def test_gemm_256_plan_with_a_narrow_tail_launch():
+    """4000 x 17000 on the 256-row plan: 16 x 67 tiles of 256 x 256 would
+    leave a partial fifth round, so the columns below 16384 run as 1024
+    tiles of 256 x 256 (four whole rounds) and the last 616 columns as a
+    second launch of 256 x 128 tiles. Ragged M, N and K, a bias, splits whose
+    boundaries fall on both sides of the seam: every fp32 output matches the
+    oracle; 16-byte and per-element bf16 stores give the same bits."""
+    rng = np.random.default_rng(17)
+    M, K, splits = 4000, 1040, [9000, 5000, 3000]
+    N = sum(splits)
+    x8 = wl.random_codes(7101, (M, K))
+    w8 = wl.random_codes(7102, (N, K))
+    bias = wl.to_bf16_bits(0.05 * rng.standard_normal(N).astype(np.float32))
+    s_a, s_w = np.float32(0.003), np.float32(0.002)
+    ref = gemm.packed_gemm_split(x8, w8, s_a, s_w, bias, splits)
+    f32 = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=True)
+    for i, (g, r) in enumerate(zip(f32, ref)):
+        assert_gemm_f32(g, r, f"4000x17000x1040 fp32 split {i}")
+    vec = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False)
+    lane = _gpu_gemm(x8, w8, s_a, s_w, bias, splits, f32=False, ld_pad=6)
+    for i, (a, b, r) in enumerate(zip(vec, lane, ref)):
+        assert np.array_equal(a, b), f"split {i}: vector and per-element stores differ"
+        assert_gemm_bf16(a, r, f"4000x17000x1040 split {i}")
+
+
 def test_gemm_deep_k_plan_row_capacity():
     """M below the buffers' rows on the deep-K 256x256 plan (the last row of
     tiles is partial): rows past M are neither written nor read."""
