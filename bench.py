@@ -21,7 +21,10 @@ copy of the weights and activations, rotating through enough copies that the
 working set is at least 512 MiB, so the 256 MiB Infinity Cache cannot serve
 repeated weight streams (``--warm`` drops the rotation and labels the line:
 the cache-served figure). Per-kernel durations come from HIP events around
-graph replays of that kernel alone on the launch stream (same rotation).
+graph replays of that kernel alone on the launch stream, over a rotation
+extended until that table's smallest kernel moves at least 512 MiB of its
+own buffers per replay (each added set with its own outputs), so no
+per-kernel figure comes from the cache either.
 
 Output: one JSON line on stdout (metric, value, roofline of the dominant
 kernel, the CPU oracle's throughput on a bounded sample, per-kernel table).
@@ -84,6 +87,8 @@ FP8_PEAK_TFLOPS = 5000.0       # dense FP8 MFMA (datasheet 5.0 PFLOP/s)
 FP4_PEAK_TFLOPS = 10100.0      # dense FP4 MFMA (datasheet 10.1 PFLOP/s)
 RIDGE = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 ROTATE_BYTES = 512 << 20
+TABLE_MEM_BYTES = 16 << 30   # copies the per-kernel table may add
+TABLE_MAX_SETS = 256
 WARM_REPEATS = 16   # --warm: the one buffer set repeated this often per graph
 METRIC = "packed FP8 GEMM TFLOP/s (%MFMA peak) + norm-quant GB/s (%HBM peak)"
 
@@ -298,19 +303,22 @@ def build_ffn(w, rows, act, packs, frt, torch, mx=False, full=False):
             "scale": torch.tensor([float(s_h)], dtype=torch.float32, device="cuda")}
 
 
-def make_rotation(w, dev, packs, rows, torch, ffn=None, warm=False):
+def make_rotation(w, dev, packs, rows, torch, ffn=None, warm=False, n_sets=None, first=0):
     """Copies of activations and weights so one pass over the sets moves at
     least ROTATE_BYTES. Warm: one set, listed WARM_REPEATS times, so that a
     graph still holds many launches (the host's replay calls are slower than
-    one short launch)."""
+    one short launch). `n_sets` forces the count; `first` > 0 returns only
+    sets first .. n_sets - 1 (fresh copies, to extend an existing rotation)."""
     per = sum(t.numel() * t.element_size() for t in dev.values()
               if t.dim() > 1 and t.shape[0] == rows)
     per += sum(p["W8"].numel() for p in packs)
     if ffn is not None:
         per += ffn["W8"].numel()
     n = 1 if warm else max(1, math.ceil(ROTATE_BYTES / max(per, 1)))
+    if n_sets is not None:
+        n = n_sets
     sets = []
-    for i in range(n):
+    for i in range(first, n):
         s = {"dev": {}, "packs": []}
         for k, t in dev.items():
             rotate = t.dim() > 1 and t.shape[0] == rows
@@ -616,6 +624,13 @@ def kernel_work(w, kind, rows, packs, ffn=None, rope=None, oproj=None):
 
 # ------------------------------------------------------------------ timing
 
+def tensor_bytes(v):
+    """Bytes of the tensors in `v` (a tensor, or nested lists/tuples of them)."""
+    if isinstance(v, (list, tuple)):
+        return sum(tensor_bytes(x) for x in v)
+    return v.numel() * v.element_size()
+
+
 def capture(fn_list, torch):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
@@ -920,13 +935,10 @@ def main():
                              f"workloads {sorted(wl.FFN_HIDDEN)}")
         ffn = build_ffn(w, rows, act, packs, frt, torch, mx=a.mxfp4, full=a.fp4_full)
     sets, per_set = make_rotation(w, dev, packs, rows, torch, ffn, warm=a.warm)
-    outs = make_outputs(w, rows, packs, torch, ffn)
-    if a.mxfp4:
-        outs["x4"] = [(torch.empty(rows, w.D // 2, dtype=torch.uint8, device="cuda"),
-                       torch.empty(w.D // 256, rows, 8, dtype=torch.uint8, device="cuda")) for _ in packs]
     rp = make_rope(w, rows, torch) if a.rope else None
     op = make_oproj(w, rows, frt, torch, mx=a.mxfp4) if a.oproj else None
-    for i, st in enumerate(sets):
+
+    def attach(st, i):
         if rp is not None:
             st["rope"] = rp
         if op is not None:   # each rotation set streams its own W_o copy
@@ -934,10 +946,25 @@ def main():
             st["oproj"] = dict(op, W8=op["W8"].clone() if fresh else op["W8"])
             if a.mxfp4 and fresh:
                 st["oproj"]["ws"] = op["ws"].clone()
+
+    def new_outputs():
+        o = make_outputs(w, rows, packs, torch, ffn)
+        if a.mxfp4:
+            o["x4"] = [(torch.empty(rows, w.D // 2, dtype=torch.uint8, device="cuda"),
+                        torch.empty(w.D // 256, rows, 8, dtype=torch.uint8, device="cuda"))
+                       for _ in packs]
+        return o
+
+    def launches(s, o):
+        return (step_launches_mx(w, s, o, rows, frt, wl.EPS) if a.mxfp4 else
+                step_launches(w, s, act, o, rows, frt, wl.EPS))
+
+    outs = new_outputs()
+    for i, st in enumerate(sets):
+        attach(st, i)
     nset = len(sets)
 
-    steps_fns = [step_launches_mx(w, s, outs, rows, frt, wl.EPS) if a.mxfp4 else
-                 step_launches(w, s, act, outs, rows, frt, wl.EPS) for s in sets]
+    steps_fns = [launches(s, outs) for s in sets]
     if a.profile_kernel:
         # one kernel kind, eagerly, over the rotation sets (after one full
         # step so every input it reads is defined)
@@ -992,22 +1019,52 @@ def main():
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / a.steps
 
-    # per-kernel durations: graphs of one kernel kind over all sets
+    # per-kernel durations: graphs of one kernel kind over rotation sets.
+    # The step's rotation counts every byte of a set, most of which a small
+    # kernel of a large step never touches (workload 5's producer touches
+    # 235 MB of a ~1.1 GB set), so the table extends the rotation until the
+    # kernel with the fewest bytes moves ROTATE_BYTES over its launches
+    # (within TABLE_MEM_BYTES of copies and TABLE_MAX_SETS), each added set
+    # with its own outputs: no kernel's figure is served from the Infinity
+    # Cache by a repeat of its own buffers.
     kinds = [k for k, _ in steps_fns[0]]
-    timed = [[fn for _, fn in st] for st in steps_fns]
-    all_kinds = list(kinds)
-    if ffn is not None or rp is not None:
-        extra = [unfused_launches(w, s, act, outs, frt, mx=a.mxfp4) for s in sets]
-        all_kinds += [k for k, _ in extra[0]]
+    has_extra = ffn is not None or rp is not None
+    extra0 = unfused_launches(w, sets[0], act, outs, frt, mx=a.mxfp4) if has_extra else []
+    all_kinds = kinds + [k for k, _ in extra0]
+    work = {k: kernel_work(w, k, rows, packs, ffn, rp, op) for k in all_kinds}
+    tab_sets, tab_fns, tab_outs = sets, steps_fns, [outs] * nset
+    if not a.warm:
+        out_bytes = tensor_bytes(list(outs.values()))
+        least = min(b for b, _ in work.values())
+        need = math.ceil(ROTATE_BYTES / max(least, 1))
+        cap = max(nset, TABLE_MEM_BYTES // max(per_set + out_bytes, 1))
+        n_tab = max(nset, min(need, cap, TABLE_MAX_SETS))
+        if n_tab > nset:
+            more = make_rotation(w, dev, packs, rows, torch, ffn, n_sets=n_tab, first=nset)[0]
+            for i, st in enumerate(more):
+                attach(st, nset + i)
+            more_outs = [new_outputs() for _ in more]
+            tab_sets = sets + more
+            tab_outs = tab_outs + more_outs
+            tab_fns = steps_fns + [launches(st, o) for st, o in zip(more, more_outs)]
+    n_tab = len(tab_sets)
+    timed = [[fn for _, fn in st] for st in tab_fns]
+    if has_extra:
+        extra = [unfused_launches(w, st, act, o, frt, mx=a.mxfp4) for st, o in zip(tab_sets, tab_outs)]
         timed = [t + [fn for _, fn in e] for t, e in zip(timed, extra)]
+    for t in timed[nset:]:   # every added set's intermediate buffers defined once
+        for fn in t:
+            fn()
+    torch.cuda.synchronize()
     table = []
     for ki, kind in enumerate(all_kinds):
-        g = capture([timed[s][ki] for s in range(nset)], torch)
+        g = capture([timed[s][ki] for s in range(n_tab)], torch)
         prewarm(g, 0.3, torch)
-        us = time_graph(g, a.kernel_reps, torch) * 1e3 / nset
-        b, f = kernel_work(w, kind, rows, packs, ffn, rp, op)
+        us = time_graph(g, a.kernel_reps, torch) * 1e3 / n_tab
+        b, f = work[kind]
         row = {"kernel": kind, "us": round(us, 3), "bytes": int(b),
-               "GB/s": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+               "GB/s": round(b / us / 1e3, 1), "hbm_frac": round(b / us / 1e3 / HBM_PEAK_GBS, 4),
+               "rotated_mib": round(n_tab * b / 2**20, 1)}
         if f:
             peak = FP4_PEAK_TFLOPS if "_mx" in kind else FP8_PEAK_TFLOPS
             row["TFLOP/s"] = round(f / us / 1e6, 2)
@@ -1056,6 +1113,7 @@ def main():
                    "gemms": [list(p["splits"]) for p in packs], "bias": w.bias,
                    "rotation_sets": 1 if a.warm else nset,
                    "rotation_mib": round((1 if a.warm else nset) * per_set / 2**20, 1),
+                   "kernel_table_sets": 1 if a.warm else n_tab,
                    "cache": "warm: one buffer set, repeats may hit the Infinity Cache" if a.warm
                             else "rotated: each pass moves >= 512 MiB of distinct buffers",
                    "step_gemm_gflop": round(gemm_flops / 1e9, 3)},
