@@ -682,8 +682,14 @@ __device__ __forceinline__ void gemm256_epilogue(const GemmArgs& a, v4f (&acc)[8
                              pk_bf16(alpha * lo[2] + b[p][2], alpha * lo[3] + b[p][3]),
                              pk_bf16(alpha * hi[0] + b[p][4], alpha * hi[1] + b[p][5]),
                              pk_bf16(alpha * hi[2] + b[p][6], alpha * hi[3] + b[p][7])};
-          // a global (not flat) store: the split table holds generic pointers
-          *(__attribute__((address_space(1))) u32x4_t*)(uintptr_t)(colp[p] + (int64_t)(i * 16) * ldb[p]) = v;
+          // a global (not flat) store: the split table holds generic
+          // pointers. Non-temporal: the step's outputs are not read again
+          // by this launch, and streaming them past the caches keeps the
+          // end-of-round store bursts off the operand traffic (cold outputs,
+          // 8192 x 9216 x 3072 + bias: 205.8 -> 192.6 us; 2048 x 9216 x
+          // 4096: 83.7 -> 78.6 us)
+          __builtin_nontemporal_store(
+              v, (__attribute__((address_space(1))) u32x4_t*)(uintptr_t)(colp[p] + (int64_t)(i * 16) * ldb[p]));
         }
       }
     };
