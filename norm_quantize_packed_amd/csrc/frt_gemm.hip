@@ -152,7 +152,7 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // (block row and lane) is range-checked against it, so rows past M or N
 // fetch zeros, per lane; their results are never stored. alpha is 1.
 template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB, int AE = BM,
-          bool GLU = false, bool ROPE = false, bool FP4 = false>
+          bool GLU = false, bool ROPE = false, bool FP4 = false, bool WNT = false>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a) {
   constexpr int WAVES_N = BN / WN;
   constexpr int NW = (BM / WM) * WAVES_N;
@@ -270,10 +270,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
         if constexpr (KTAIL) {
           if (k0 + cch * 16 >= a.K) o = kOOB;
         }
+        // WNT (plans with one row of tiles, where each weight byte is read
+        // by one block): weight loads carry the non-temporal hint, so the
+        // stream allocates nothing in the caches (6144 x 4096 weights,
+        // rotated: M = 1 8.5 -> 7.9 us, M = 16 9.3 -> 8.5, M = 64 12.5 ->
+        // 11.6); with several rows of tiles sharing a weight tile through
+        // L2 it costs (256 x 2560 x 2048: 8.5 -> 10.7 us)
         if (A)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
         else
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)dst, 16, o, 0, 0, WNT ? 2 : 0);
       }
       if constexpr (FP4) {
         // the scales of run kt * NSUB + q: 32 rows (256 bytes) per load
@@ -1012,21 +1018,21 @@ int64_t rounds_256(const GemmArgs& a, int BN, int cus) {
   return (tiles + cus - 1) / cus;
 }
 template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1, int AE = BM, bool GLU = false,
-          bool ROPE = false, bool FP4 = false>
+          bool ROPE = false, bool FP4 = false, bool WNT = false>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   // (GLU: N = 2H, so this is also ceil(H / (BN / 2)) column tiles)
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int threads = (BM / WM) * (BN / WN) * 64;
   if constexpr (FP4) {  // whole stages (K a multiple of 256 * NSUB) is checked by the caller
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE, true>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE, true, WNT>), dim3(tiles),
                        dim3(threads), 0, st, a);
     return hipGetLastError();
   }
   if (a.K % (128 * NSUB) == 0)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE, false, WNT>), dim3(tiles),
                        dim3(threads), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, true, NSUB, AE, GLU, ROPE>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, true, NSUB, AE, GLU, ROPE, false, WNT>), dim3(tiles),
                        dim3(threads), 0, st, a);
   return hipGetLastError();
 }
@@ -1127,10 +1133,10 @@ hipError_t launch_planned(const GemmArgs& a, hipStream_t st) {
   // 9.8 -> 9.3 us for 6144 x 4096 weights. At M <= 16 a three-deep ring of
   // 512-deep stages keeps more of the weight stream in flight (M = 1
   // 8.75 -> 8.50 us, M = 16 9.23 -> 9.05 us; it loses at M = 32 and 64)
-  if (a.M <= 16 && a.K % 512 == 0) return launch_tiles<64, 32, 32, 32, 3, 1, 4, 16, false, ROPE>(a, st);
-  if (a.M <= 16) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 16, false, ROPE>(a, st);
-  if (a.M <= 32) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 32, false, ROPE>(a, st);
-  return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, ROPE>(a, st);
+  if (a.M <= 16 && a.K % 512 == 0) return launch_tiles<64, 32, 32, 32, 3, 1, 4, 16, false, ROPE, false, true>(a, st);
+  if (a.M <= 16) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 16, false, ROPE, false, true>(a, st);
+  if (a.M <= 32) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 32, false, ROPE, false, true>(a, st);
+  return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, ROPE, false, true>(a, st);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) { return launch_planned<false>(a, st); }
@@ -1146,11 +1152,11 @@ hipError_t launch_gemm_rope(const GemmArgs& a, hipStream_t st) { return launch_p
 // stage 1024 K-elements (four runs) in a three-deep ring when K allows it
 // (6144 x 4096 weights: M = 1 7.7 -> 6.9 us, M = 16 8.2 -> 7.3 us, M = 64
 // level), else 512 in a four-deep ring, else one run in a seven-deep ring.
-template <int AE, bool ROPE>
+template <int AE, bool ROPE, bool WNT>
 hipError_t launch_mx_narrow(const GemmArgs& a, hipStream_t st) {
-  if (a.K % 1024 == 0) return launch_tiles<64, 32, 32, 32, 3, 1, 4, AE, false, ROPE, true>(a, st);
-  if (a.K % 512 == 0) return launch_tiles<64, 32, 32, 32, 4, 1, 2, AE, false, ROPE, true>(a, st);
-  return launch_tiles<64, 32, 32, 32, 7, 1, 1, AE, false, ROPE, true>(a, st);
+  if (a.K % 1024 == 0) return launch_tiles<64, 32, 32, 32, 3, 1, 4, AE, false, ROPE, true, WNT>(a, st);
+  if (a.K % 512 == 0) return launch_tiles<64, 32, 32, 32, 4, 1, 2, AE, false, ROPE, true, WNT>(a, st);
+  return launch_tiles<64, 32, 32, 32, 7, 1, 1, AE, false, ROPE, true, WNT>(a, st);
 }
 
 // The split plans; the RoPE form (the QKV split + RoPE + KV-cache epilogue)
@@ -1164,11 +1170,12 @@ hipError_t launch_mx_planned(const GemmArgs& a, hipStream_t st) {
                   c32 = plan_cost(a, 64, 32, cus);
     if (c128 < c64 && c128 < c32) return launch_tiles<128, 128, 32, 64, 3, 2, 1, 128, false, ROPE, true>(a, st);
     if (c64 < c32) return launch_tiles<64, 64, 32, 32, 4, 1, 1, 64, false, ROPE, true>(a, st);
-    return launch_mx_narrow<64, ROPE>(a, st);
+    return launch_mx_narrow<64, ROPE, false>(a, st);
   }
-  if (a.M <= 16) return launch_mx_narrow<16, ROPE>(a, st);
-  if (a.M <= 32) return launch_mx_narrow<32, ROPE>(a, st);
-  return launch_mx_narrow<64, ROPE>(a, st);
+  // one row of tiles: the weight stream is read once, non-temporally
+  if (a.M <= 16) return launch_mx_narrow<16, ROPE, true>(a, st);
+  if (a.M <= 32) return launch_mx_narrow<32, ROPE, true>(a, st);
+  return launch_mx_narrow<64, ROPE, true>(a, st);
 }
 
 hipError_t launch_gemm_mxfp4(const GemmArgs& a, hipStream_t st) { return launch_mx_planned<false>(a, st); }

@@ -33,6 +33,13 @@ struct Vec<8> {
     uint4 t = *reinterpret_cast<const uint4*>(p);
     w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
   }
+  // non-temporal: for inputs this launch reads exactly once (a hit is still
+  // served from the caches; a miss allocates nothing there)
+  __device__ __forceinline__ void load_once(const uint16_t* p) {
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    w[0] = t.x; w[1] = t.y; w[2] = t.z; w[3] = t.w;
+  }
   __device__ __forceinline__ void store(uint16_t* p) const {
     *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
   }
@@ -42,6 +49,7 @@ template <>
 struct Vec<2> {
   uint32_t w[1];
   __device__ __forceinline__ void load(const uint16_t* p) { w[0] = *reinterpret_cast<const uint32_t*>(p); }
+  __device__ __forceinline__ void load_once(const uint16_t* p) { load(p); }
   __device__ __forceinline__ void store(uint16_t* p) const { *reinterpret_cast<uint32_t*>(p) = w[0]; }
   __device__ __forceinline__ float f(int e) const { return e ? bf16hi(w[0]) : bf16lo(w[0]); }
 };
@@ -260,9 +268,12 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ptok_norm_kernel(Pt
     const int v = sub * 64 + lane + i * 64 * WPR;
     if (row_ok && v < nvec) {
       const int64_t c = (int64_t)v * VEC;
-      xv[i].load(a.x + row * a.ld_x + c);
-      tsh[i].load(trow + (int64_t)a.shift_idx * a.D + c);
-      tsc[i].load(trow + (int64_t)a.scale_idx * a.D + c);
+      // x and the two temb chunks are read once (inputs rotated past the
+      // caches, 2048 x 16384: 53.3 -> 50.9 us; 8192 x 3072: 39.5 -> 38.2);
+      // the table rows, read by every row, keep the default policy
+      xv[i].load_once(a.x + row * a.ld_x + c);
+      tsh[i].load_once(trow + (int64_t)a.shift_idx * a.D + c);
+      tsc[i].load_once(trow + (int64_t)a.scale_idx * a.D + c);
       if constexpr (EARLY) {
         load_f32<VEC>(tab_s + c, ts[i]);
         load_f32<VEC>(tab_c + c, tc[i]);
