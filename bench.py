@@ -777,19 +777,41 @@ def copy_kernel(torch, launches):
     torch.cuda.synchronize()
 
 
-def _pmc_values(folder, counter, name_filter):
-    """Per-dispatch values of `counter` for kernels whose name passes
-    `name_filter`, from a rocprofv3 --pmc --output-format csv folder."""
+def _pmc_rows(folder, counter, name_filter):
+    """(kernel name, value) of `counter` per dispatch, in dispatch order, for
+    kernels whose name passes `name_filter`, from a rocprofv3 --pmc
+    --output-format csv folder."""
     import csv
-    vals = []
+    rows = []
     for dirpath, _, files in os.walk(folder):
         for f in files:
             if f.endswith("counter_collection.csv"):
                 with open(os.path.join(dirpath, f)) as fh:
                     for r in csv.DictReader(fh):
                         if r["Counter_Name"] == counter and name_filter(r["Kernel_Name"]):
-                            vals.append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
-    return [v for _, v in sorted(vals)]
+                            rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return [(k, v) for _, k, v in sorted(rows)]
+
+
+def _pmc_values(folder, counter, name_filter):
+    """Per-dispatch values of `counter` (see _pmc_rows)."""
+    return [v for _, v in _pmc_rows(folder, counter, name_filter)]
+
+
+def _pmc_per_call(folder, counter, name_filter, n):
+    """Values of `counter` per call over the last `n` calls of a kernel kind
+    whose call may be several dispatches of different kernels (a GEMM plan
+    of two launches): the dispatches of one call are the distinct kernel
+    names among the last `n` rows, in a repeating order, and are summed."""
+    rows = _pmc_rows(folder, counter, name_filter)
+    d = len({k for k, _ in rows[-n:]}) if rows else 1
+    rows = rows[-n * d:]
+    if len(rows) < n * d:
+        return []
+    calls = [rows[i * d:(i + 1) * d] for i in range(n)]
+    if any([k for k, _ in c] != [k for k, _ in calls[0]] for c in calls):
+        raise SystemExit(f"{counter}: the profiled calls do not repeat one dispatch sequence")
+    return [sum(v for _, v in c) for c in calls]
 
 
 def summarize_pmc(a):
@@ -801,11 +823,11 @@ def summarize_pmc(a):
     want = (lambda n: "gemm" in n and "frt::" in n) if is_gemm else \
         (lambda n: "norm_kernel" in n and "frt::" in n)
     is_copy = lambda n: "copyBuffer" in n  # noqa: E731
-    # the profiled launches are the last --launches dispatches of their kind
-    # (set-up launches of the same kernels come first)
+    # the profiled calls are the last --launches calls of their kind (set-up
+    # launches of the same kernels come first); a call's dispatches are summed
     n = a.launches
-    fk = _pmc_values(fetch_dir, "FETCH_SIZE", want)[-n:]
-    wk = _pmc_values(write_dir, "WRITE_SIZE", want)[-n:]
+    fk = _pmc_per_call(fetch_dir, "FETCH_SIZE", want, n)
+    wk = _pmc_per_call(write_dir, "WRITE_SIZE", want, n)
     fc = _pmc_values(cfetch_dir, "FETCH_SIZE", is_copy)[-n:]
     wc = _pmc_values(cwrite_dir, "WRITE_SIZE", is_copy)[-n:]
     if not (fk and wk and fc and wc):
@@ -816,7 +838,7 @@ def summarize_pmc(a):
     w_scale = COPY_BYTES / (med(wc) * 1024.0)
     fetch_b = med(fk) * 1024.0 * f_scale
     write_b = med(wk) * 1024.0 * w_scale
-    rec = {"workload": a.workload, "kernel": kind, "dispatches": [len(fk), len(wk)],
+    rec = {"workload": a.workload, "kernel": kind, "calls": [len(fk), len(wk)],
            "fetch_kib_median": med(fk), "write_kib_median": med(wk),
            "copy_fetch_kib_median": med(fc), "copy_write_kib_median": med(wc),
            "copy_bytes_each_way": COPY_BYTES,
