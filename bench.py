@@ -28,6 +28,10 @@ per-kernel figure comes from the cache either.
 
 Output: one JSON line on stdout (metric, value, roofline of the dominant
 kernel, the CPU oracle's throughput on a bounded sample, per-kernel table).
+The plain default run (workload 5) then measures workloads 3, 2, 4 and 1 the
+same way and appends their steps, rooflines and per-kernel tables to that
+line as ``other_workloads`` (``--no-other-workloads`` leaves them out);
+``wall_s_total`` is the whole run's wall time.
 
 ``--ffn`` (workloads 2 and 5) appends the FFN tail that follows the gate/up
 projection: the gate/up GEMM runs with the GEGLU quantiser as its epilogue
@@ -70,6 +74,7 @@ a step is the whole decoder layer around the attention core.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -87,6 +92,8 @@ FP8_PEAK_TFLOPS = 5000.0       # dense FP8 MFMA (datasheet 5.0 PFLOP/s)
 FP4_PEAK_TFLOPS = 10100.0      # dense FP4 MFMA (datasheet 10.1 PFLOP/s)
 RIDGE = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 ROTATE_BYTES = 512 << 20
+DEFAULT_WORKLOAD = 5
+OTHER_WORKLOADS = (3, 2, 4, 1)   # appended to the default line, in this order
 TABLE_MEM_BYTES = 16 << 30   # copies the per-kernel table may add
 TABLE_MAX_SETS = 256
 WARM_REPEATS = 16   # --warm: the one buffer set repeated this often per graph
@@ -98,10 +105,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", type=int, default=5, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--workload", type=int, default=DEFAULT_WORKLOAD, choices=[1, 2, 3, 4, 5])
     p.add_argument("--rows", type=int, default=None,
                    help="override the producer row count (e.g. the small-M sweep)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="the default line (workload 5, plain) also measures workloads "
+                        "3, 2, 4 and 1 and appends their steps and per-kernel tables as "
+                        "`other_workloads`; this leaves them out")
     p.add_argument("--ffn", action="store_true",
                    help="workloads 2 and 5: fuse GEGLU + FP8 into the gate/up "
                         "GEMM and append the down projection")
@@ -933,8 +944,39 @@ def main():
     import norm_quantize_packed_amd as frt
     import workloads as wl
 
+    t_start = time.perf_counter()
     torch.cuda.init()
     frt.load_library()
+    res = measure(a, torch, frt, wl)
+    if res is None:
+        return
+    # the default line also carries the other workloads' steps and per-kernel
+    # tables (same steps and warm-up, no CPU baseline), measured after it
+    plain = not (a.ffn or a.rope or a.oproj or a.mxfp4 or a.fp4_full or a.tp > 1
+                 or a.rows is not None or a.warm)
+    if a.workload == DEFAULT_WORKLOAD and plain and not a.no_other_workloads:
+        res["other_workloads"] = []
+        for wid in OTHER_WORKLOADS:
+            t0 = time.perf_counter()
+            b = argparse.Namespace(**vars(a))
+            b.workload, b.no_cpu_baseline = wid, True
+            r = measure(b, torch, frt, wl)
+            gc.collect()
+            torch.cuda.empty_cache()
+            res["other_workloads"].append({
+                "workload": r["config"]["workload"], "rows": r["config"]["rows"],
+                "D": r["config"]["D"], "gemms": r["config"]["gemms"],
+                "ms_per_step": r["ms_per_step"], "value": r["value"], "unit": r["unit"],
+                "rotation_sets": r["config"]["rotation_sets"],
+                "kernel_table_sets": r["config"]["kernel_table_sets"],
+                "roofline": r["roofline"], "kernels": r["kernels"],
+                "wall_s": round(time.perf_counter() - t0, 1)})
+    res["wall_s_total"] = round(time.perf_counter() - t_start, 1)
+    print(json.dumps(res), flush=True)
+
+
+def measure(a, torch, frt, wl):
+    """One workload's line (a dict), or None for a --profile-kernel run."""
     w0 = wl.WORKLOADS[a.workload]
     rows = a.rows if a.rows is not None else w0.rows
     if (a.rope or a.oproj) and a.workload not in wl.QKV_HEADS:
@@ -1001,7 +1043,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"profile_kernel": a.profile_kernel, "launches": a.launches,
                           "workload": w.name, "rotation_sets": nset}), flush=True)
-        return
+        return None
 
     # eager reference of one step, then graph replays must reproduce it
     for _, fn in steps_fns[0]:
@@ -1156,7 +1198,7 @@ def main():
     if (not a.no_cpu_baseline and ffn is None and rp is None and op is None and not a.mxfp4
             and a.tp == 1 and not a.warm):
         res["cpu_baseline"] = cpu_baseline(w, rows)
-    print(json.dumps(res), flush=True)
+    return res
 
 
 if __name__ == "__main__":

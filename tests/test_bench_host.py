@@ -96,6 +96,28 @@ def test_summarize_pmc_scales_by_the_copy(tmp_path, monkeypatch):
     assert rec["sources_sha256"] == bench.kernel_sources_sha("gemm2")
 
 
+def test_summarize_pmc_sums_the_launches_of_one_call(tmp_path, monkeypatch):
+    """A GEMM call made of two launches (a 256x256 head, then a 256x128 tail)
+    counts as one call: its two dispatches are summed, and the median runs
+    over calls, not over a mixture of head and tail dispatches."""
+    head = "void frt::gemm256_kernel<false, false, false, 256>(frt::GemmArgs)"
+    tail = "void frt::gemm256_kernel<false, false, false, 128>(frt::GemmArgs)"
+    copy = "__amd_rocclr_copyBuffer"
+    kib = bench.COPY_BYTES / 1024
+    f, wdir, cf, cw = (str(tmp_path / n) for n in ("f", "w", "cf", "cw"))
+    seq = [(head, 900.0), (tail, 100.0)] * 4   # a set-up call, then three profiled ones
+    _write_counter_csv(f, [(i, k, "FETCH_SIZE", v) for i, (k, v) in enumerate(seq)])
+    _write_counter_csv(wdir, [(i, k, "WRITE_SIZE", v / 2) for i, (k, v) in enumerate(seq)])
+    _write_counter_csv(cf, [(i, copy, "FETCH_SIZE", kib) for i in range(3)])
+    _write_counter_csv(cw, [(i, copy, "WRITE_SIZE", kib) for i in range(3)])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    a = SimpleNamespace(summarize_pmc=[f, wdir, cf, cw], profile_kernel="gemm1", launches=3, workload=3)
+    bench.summarize_pmc(a)
+    rec = json.load(open(tmp_path / "profiles" / "traffic_w3_gemm1.json"))
+    assert rec["calls"] == [3, 3]
+    assert rec["fetch_bytes"] == 1000 * 1024 and rec["write_bytes"] == 500 * 1024
+
+
 def test_traffic_record_needs_the_current_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     assert bench.load_traffic(2, "gemm2") is None            # no record
