@@ -1124,8 +1124,13 @@ hipError_t launch_planned(const GemmArgs& a, hipStream_t st) {
         }
         return launch_256<false, ROPE>(a, st);
       case 1: return launch_tiles<128, 128, 32, 32, 3, 2, 1, 128, false, ROPE>(a, st);
-      case 2: return launch_tiles<64, 64, 32, 32, 4, 1, 1, 64, false, ROPE>(a, st);
-      default: return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, ROPE>(a, st);
+      // tile rows rastered in pairs (GM = 2): an XCD's run of tiles covers
+      // two tile rows of each weight column it touches, so a weight tile
+      // reaches fewer XCD caches than with one tile row per run (same box,
+      // 256 x 2560 x 2048 + RoPE: 10.15 -> 9.85 us; 256 x 2048 x 8192:
+      // 18.08 -> 17.17 us; four rows a run measured 9.98 and 17.15)
+      case 2: return launch_tiles<64, 64, 32, 32, 4, 2, 1, 64, false, ROPE>(a, st);
+      default: return launch_tiles<64, 32, 32, 32, 4, 2, 2, 64, false, ROPE>(a, st);
     }
   }
   // rows past M are not loaded (at M <= 16, 8 of every 12 load
