@@ -45,6 +45,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr uint32_t kOOB = 0x80000000u;  // offset past any record count
 
+// a byte in global memory (so stores through it are global, not flat)
+typedef __attribute__((address_space(1))) uint8_t gbyte_t;
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   // flags: default data format for raw buffer loads on gfx9
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
@@ -189,6 +192,82 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   // n0: first output column (GLU: first gate column g0)
   const int m0 = t.tm * BM, n0 = t.tn * (GLU ? BN / 2 : BN);
   const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
+
+  // Epilogue operands of the FP8 split form. Tiles of at most 64 x 64 (few
+  // waves, short K loops: the epilogue is a visible tail) read them here,
+  // ahead of the main loop, so that their latency overlaps the weight
+  // stream; read in the epilogue they formed a chain behind the last stage:
+  // the two scale loads, the split table one scalar load and wait at a
+  // time, then the bias (same box: 6144 x 4096 at M = 1 7.53 -> 7.19 us,
+  // M = 16 8.49 -> 8.25; 16 x 768 x 512 4.10 -> 3.67; 256 x 2560 x 2048 bf16
+  // 9.27 -> 8.45; 256 x 2048 x 2048 7.36 -> 7.18; 256 x 2048 x 8192 17.17
+  // -> 16.96). These loads are older than every ring load, so the ring's
+  // vmcnt waits (in-order returns) stay exact. The others read them at the
+  // epilogue: 128 x 128 tiles (the registers held across the loop cost more
+  // than the tail: 15.6 -> 16.0 us at 256 x 16384 x 2048), the one-row
+  // weight-streaming plan with all 64 A rows (M = 64: 11.23 -> 11.31 us),
+  // and the GEGLU, RoPE and MXFP4 forms (no gain measured; MXFP4 at M = 1
+  // 6.07 -> 6.18 us). Read early: each lane's output column address, row
+  // stride (bytes) and bias bits; the other kernels find them in the
+  // epilogue itself.
+  constexpr bool SPLIT = !GLU && !ROPE;
+  constexpr bool EARLY = SPLIT && !FP4 && BM * BN <= 64 * 64 && !(WNT && AE == BM);
+  constexpr int NE = EARLY ? NJ : 1;
+  float alpha = 1.0f;
+  uint16_t ep_b[NE];
+  gbyte_t* ep_col[NE];
+  int64_t ep_ld[NE];
+  // the scales and the raw bias bits, loaded with no branch (from the
+  // weights when there is no bias: any readable address; the epilogue then
+  // ignores them) and converted only in the epilogue, so nothing waits for
+  // them early
+  auto ep_loads = [&]() {
+    alpha = FP4 ? 1.0f : (*a.act_scale) * (*a.w_scale);
+    if constexpr (EARLY) {
+      const uint16_t* bsrc = a.bias != nullptr ? a.bias : reinterpret_cast<const uint16_t*>(a.w);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) ep_b[j] = bsrc[min(n0 + wn0 + j * 32 + (lane & 31), a.N - 1)];
+    }
+  };
+  // split form: the split owning each of this lane's columns, by a
+  // run-time loop over the call's splits (one scalar load of each entry,
+  // selects per lane: a fully unrolled scan over the whole table held it
+  // in scalar registers and spilled them)
+  auto ep_splits = [&]() {
+    if constexpr (EARLY) {
+      const int esz = a.out_f32 ? 4 : 2;
+      int nv[NE];
+      uint64_t bv[NE];
+      int64_t lv[NE];
+      int ov[NE];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        nv[j] = n0 + wn0 + j * 32 + (lane & 31);
+        bv[j] = reinterpret_cast<uint64_t>(a.sp.ptr[0]);
+        lv[j] = a.sp.ld[0];
+        ov[j] = 0;
+      }
+#pragma unroll 1
+      for (int s = 1; s < a.sp.n; ++s) {
+        const int so = a.sp.off[s];
+        const uint64_t sp = reinterpret_cast<uint64_t>(a.sp.ptr[s]);
+        const int64_t sl = a.sp.ld[s];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const bool t = nv[j] >= so;
+          bv[j] = t ? sp : bv[j];
+          lv[j] = t ? sl : lv[j];
+          ov[j] = t ? so : ov[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        ep_col[j] = reinterpret_cast<gbyte_t*>(bv[j] + (uint64_t)((int64_t)(nv[j] - ov[j]) * esz));
+        ep_ld[j] = lv[j] * esz;
+      }
+    }
+  };
+  if constexpr (EARLY) ep_loads();
 
   const int Kb = FP4 ? a.K / 2 : a.K;  // operand bytes per row
   const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + Kb);
@@ -446,6 +525,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   [&]<int... I>(std::integer_sequence<int, I...>) {
     ((I < KT ? (issue(I, std::integral_constant<int, I>{}), 0) : 0), ...);
   }(std::make_integer_sequence<int, NS - 1>{});
+  if constexpr (EARLY) ep_splits();
   sync_stage(min(KT - 1, NS - 2));
   if constexpr (ALL) read_all(I0{});
   else read_frags(I0{}, I0{}, fa[0], fb[0]);
@@ -461,6 +541,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       for (int j = 0; j < NJ; ++j) acc[i][j] += acc2[i][j];
   }
 
+  if constexpr (!EARLY) ep_loads();
   {
     constexpr int SLOT = STAGE, TOTAL = NS * STAGE;
     uint8_t* slot = smem + (KT % NS) * STAGE;
