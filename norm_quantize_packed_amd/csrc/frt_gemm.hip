@@ -210,11 +210,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   // 6.07 -> 6.18 us). Read early: each lane's output column address, row
   // stride (bytes) and bias bits; the other kernels find them in the
   // epilogue itself.
+  // The RoPE form's 64 x 64 plan (one 32 x 32 accumulator a wave) reads
+  // its alpha, bias bits and the 16 (cos, sin) words of its rows early in
+  // the same way (256 x 2560 x 2048 + RoPE + cache).
   constexpr bool SPLIT = !GLU && !ROPE;
   constexpr bool EARLY = SPLIT && !FP4 && BM * BN <= 64 * 64 && !(WNT && AE == BM);
+  constexpr bool EARLY_R = ROPE && !FP4 && BM * BN <= 64 * 64 && MI * NJ == 1;
   constexpr int NE = EARLY ? NJ : 1;
   float alpha = 1.0f;
-  uint16_t ep_b[NE];
+  uint16_t ep_b[NE], ep_rb = 0;
+  uint32_t ep_cs[EARLY_R ? 16 : 1];
   gbyte_t* ep_col[NE];
   int64_t ep_ld[NE];
   // the scales and the raw bias bits, loaded with no branch (from the
@@ -227,6 +232,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       const uint16_t* bsrc = a.bias != nullptr ? a.bias : reinterpret_cast<const uint16_t*>(a.w);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) ep_b[j] = bsrc[min(n0 + wn0 + j * 32 + (lane & 31), a.N - 1)];
+    }
+    if constexpr (EARLY_R) {
+      // every lane reads its rope words (v columns too, whose values the
+      // epilogue ignores): rows clamped to M - 1, columns to an even d < hd
+      const uint16_t* bsrc = a.bias != nullptr ? a.bias : reinterpret_cast<const uint16_t*>(a.w);
+      const int n = n0 + wn0 + (lane & 31);
+      ep_rb = bsrc[min(n, a.N - 1)];
+      const uint16_t* rp = a.rope + ((n % a.hd) & ~1);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = min(m0 + wm0 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3), a.M - 1);
+        ep_cs[r] = *reinterpret_cast<const uint32_t*>(rp + (int64_t)m * a.hd);
+      }
     }
   };
   // split form: the split owning each of this lane's columns, by a
@@ -267,7 +285,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       }
     }
   };
-  if constexpr (EARLY) ep_loads();
+  if constexpr (EARLY || EARLY_R) ep_loads();
 
   const int Kb = FP4 ? a.K / 2 : a.K;  // operand bytes per row
   const uint32_t x_bytes = (uint32_t)((int64_t)(a.M - 1) * a.ld_x + Kb);
@@ -541,7 +559,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       for (int j = 0; j < NJ; ++j) acc[i][j] += acc2[i][j];
   }
 
-  if constexpr (!EARLY) ep_loads();
+  if constexpr (!EARLY && !EARLY_R) ep_loads();
   {
     constexpr int SLOT = STAGE, TOTAL = NS * STAGE;
     uint8_t* slot = smem + (KT % NS) * STAGE;
