@@ -137,7 +137,14 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ada_norm_kernel(Ada
   const uint16_t* mrow = a.mod + row * a.ld_mod;
 
   float h[NV][VEC];
-  Vec<VEC> msc[EARLY ? NV : 1], msh[EARLY ? NV : 1], mw[EARLY ? NV : 1];
+  Vec<VEC> msc[EARLY ? NV : 1], msh[EARLY ? NV : 1], mw[EARLY ? NV : 1], mg[EARLY ? NV : 1];
+  // the quantiser scale (and, with EARLY, the gate chunk echoed to gate_out)
+  // is read with the row's first loads: read after the reduction's barrier,
+  // its latency trailed the row (with one block per row and few rows, a
+  // visible tail: 16 x 512 2.65 -> 2.53 us; level at 64 x 4096 and 256 x
+  // 2048)
+  float s = 1.0f;
+  if (!MX && a.out != nullptr) s = *a.act_scale;
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -150,6 +157,7 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ada_norm_kernel(Ada
         msc[i].load(mrow + c);
         msh[i].load(mrow + a.D + c);
         if (a.weight != nullptr) mw[i].load(a.weight + c);
+        if (a.gout != nullptr) mg[i].load(mrow + 2 * a.D + c);
       }
       if (a.x != nullptr && a.gate != nullptr) {
         Vec<VEC> x, g;
@@ -177,11 +185,7 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ada_norm_kernel(Ada
   const float tot = row_sum<WPR>(ss, red, wave);
   const float rr = __builtin_amdgcn_rsqf(tot / (float)a.D + a.eps);
 
-  float s = 1.0f, rcp = 1.0f;
-  if (!MX && a.out != nullptr) {
-    s = *a.act_scale;
-    rcp = 1.0f / s;
-  }
+  const float rcp = 1.0f / s;
   float amax = 0.0f;
   if (row_ok) {
 #pragma unroll
@@ -230,7 +234,10 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ada_norm_kernel(Ada
         }
         if (a.gout != nullptr) {
           Vec<VEC> g;
-          g.load(mrow + 2 * a.D + c);
+          if constexpr (EARLY)
+            g = mg[i];
+          else
+            g.load(mrow + 2 * a.D + c);
           g.store(a.gout + row * a.ld_gout + c);
         }
       }
@@ -299,6 +306,8 @@ __global__ __launch_bounds__(WPR <= 4 ? 256 : 64 * WPR) void ptok_norm_kernel(Pt
   const float var = row_sum<WPR>(sq, red, wave) * inv_d;
   const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
 
+  // (the quantiser scale read here, after the reductions: read with the
+  // row's first loads it measured slower, 8192 x 3072: 35.9 -> 36.7 us)
   float s = 1.0f, rcp = 1.0f;
   if (a.out != nullptr) {
     s = *a.act_scale;
