@@ -198,6 +198,28 @@ def test_gemm_edges_k_tail_strides_unaligned_splits():
                     list(splits), f"M={M} K={K}", ld_pad=6)
 
 
+@pytest.mark.parametrize("M,K", [(1, 4096), (16, 1024), (17, 1040), (32, 2048),
+                                 (65, 1024), (256, 2048)])
+def test_gemm_small_tile_epilogue_operands(M, K):
+    """The small-tile plans (M = 1 and 16: 16 A rows; 17 and 32: 32 rows;
+    65 and 256: the 64x32 split plan) read their epilogue operands ahead of
+    the main loop: the scales, each lane's split address and row stride,
+    its bias. Sixteen splits whose widths cut the 32-column lane groups
+    anywhere, padded row strides, fp32 and bf16 outputs, with a bias and
+    without one (the kernel then reads, and ignores, weight bytes in the
+    bias's place)."""
+    rng = np.random.default_rng(M * 31 + K)
+    splits = [37, 5, 64, 1, 90, 33, 31, 128, 7, 9, 100, 3, 44, 20, 11, 29]
+    N = sum(splits)
+    w8 = wl.random_codes(int(rng.integers(1 << 30)), (N, K))
+    x8 = wl.random_codes(int(rng.integers(1 << 30)), (M, K))
+    bias = wl.to_bf16_bits(rng.standard_normal(N).astype(np.float32))
+    _check_gemm(x8, w8, np.float32(0.003), np.float32(0.002), bias, splits,
+                f"M={M} K={K} with bias", ld_pad=6)
+    _check_gemm(x8, w8, np.float32(0.003), np.float32(0.002), None, splits,
+                f"M={M} K={K} no bias", ld_pad=2)
+
+
 def test_gemm_joint_slots_share_one_buffer():
     """Two adjacent splits written into one [M, N0 + N1] region through
     offset pointers with a shared row stride (a joint q|k consumer)."""
