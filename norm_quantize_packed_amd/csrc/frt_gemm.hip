@@ -193,26 +193,27 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const int m0 = t.tm * BM, n0 = t.tn * (GLU ? BN / 2 : BN);
   const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
 
-  // Epilogue operands of the FP8 split form. Tiles of at most 64 x 64 (few
-  // waves, short K loops: the epilogue is a visible tail) read them here,
-  // ahead of the main loop, so that their latency overlaps the weight
-  // stream; read in the epilogue they formed a chain behind the last stage:
-  // the two scale loads, the split table one scalar load and wait at a
-  // time, then the bias (same box: 6144 x 4096 at M = 1 7.53 -> 7.19 us,
-  // M = 16 8.49 -> 8.25; 16 x 768 x 512 4.10 -> 3.67; 256 x 2560 x 2048 bf16
-  // 9.27 -> 8.45; 256 x 2048 x 2048 7.36 -> 7.18; 256 x 2048 x 8192 17.17
-  // -> 16.96). These loads are older than every ring load, so the ring's
-  // vmcnt waits (in-order returns) stay exact. The others read them at the
-  // epilogue: 128 x 128 tiles (the registers held across the loop cost more
-  // than the tail: 15.6 -> 16.0 us at 256 x 16384 x 2048), the one-row
-  // weight-streaming plan with all 64 A rows (M = 64: 11.23 -> 11.31 us),
-  // and the GEGLU, RoPE and MXFP4 forms (no gain measured; MXFP4 at M = 1
-  // 6.07 -> 6.18 us). Read early: each lane's output column address, row
-  // stride (bytes) and bias bits; the other kernels find them in the
-  // epilogue itself.
-  // The RoPE form's 64 x 64 plan (one 32 x 32 accumulator a wave) reads
-  // its alpha, bias bits and the 16 (cos, sin) words of its rows early in
-  // the same way (256 x 2560 x 2048 + RoPE + cache).
+  // Epilogue operands. Read in the epilogue, they formed a chain behind the
+  // last stage: the two scale loads, the split table one scalar load and
+  // wait at a time, then the bias (RoPE: and the rope words of the lane's
+  // rows). On small tiles (few waves, short K loops) that tail is visible,
+  // so these kernels read them ahead of the main loop, where their latency
+  // overlaps the weight stream. The loads are older than every ring load,
+  // so the ring's vmcnt waits (in-order returns) stay exact.
+  //  EARLY (FP8 split form, tiles of at most 64 x 64): alpha and each lane's
+  //    bias bits here, its output column address and row stride (bytes)
+  //    after the prologue's loads (same box: 6144 x 4096 at M = 1 7.53 ->
+  //    7.19 us, M = 16 8.49 -> 8.25; 16 x 768 x 512 4.10 -> 3.67; 256 x 2560
+  //    x 2048 bf16 9.27 -> 8.45; 256 x 2048 x 2048 7.36 -> 7.18; 256 x 2048
+  //    x 8192 17.17 -> 16.96).
+  //  EARLY_R (RoPE form, one 32 x 32 accumulator a wave: the 64 x 64 plan):
+  //    alpha, the bias bits and the 16 (cos, sin) words (256 x 2560 x 2048
+  //    + RoPE + cache: 9.83 -> 9.71 us).
+  // The rest read them in the epilogue: 128 x 128 tiles (the registers held
+  // across the loop cost more than the tail: 15.6 -> 16.0 us at 256 x 16384
+  // x 2048), the one-row weight-streaming plan with all 64 A rows (M = 64:
+  // 11.23 -> 11.31 us), the GEGLU form and the MXFP4 forms (no gain
+  // measured; MXFP4 at M = 1 6.07 -> 6.18 us).
   constexpr bool SPLIT = !GLU && !ROPE;
   constexpr bool EARLY = SPLIT && !FP4 && BM * BN <= 64 * 64 && !(WNT && AE == BM);
   constexpr bool EARLY_R = ROPE && !FP4 && BM * BN <= 64 * 64 && MI * NJ == 1;
