@@ -154,11 +154,21 @@ __device__ __forceinline__ TileXY tile_of(int b, int tiles_m, int tiles_n, int g
 // run has its own record count (rows x 8 bytes) and a lane's whole offset
 // (block row and lane) is range-checked against it, so rows past M or N
 // fetch zeros, per lane; their results are never stored. alpha is 1.
+//
+// KW = 2: the two waves of a one-wave-tile block split every stage's K, wave
+// k taking the 64-deep substeps of parity k, and the odd-substep partial
+// sums reach the even-substep wave through LDS at the end (the even wave
+// adds them and writes the tile). With one 32 x 32 tile of an M <= 32 call,
+// this replaces a 64-row tile whose second wave only computed rows past M
+// (same box, 6144 x 4096: M = 1 7.22 -> 7.15 us, M = 16 8.26 -> 8.15, M = 32
+// 9.45 -> 9.38; 16 x 768 x 512 3.67 -> 3.62).
 template <int BM, int BN, int WM, int WN, int NS, int GM, bool KTAIL, int NSUB, int AE = BM,
-          bool GLU = false, bool ROPE = false, bool FP4 = false, bool WNT = false>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmArgs a) {
+          bool GLU = false, bool ROPE = false, bool FP4 = false, bool WNT = false, int KW = 1>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * KW * 64) void gemm_kernel(GemmArgs a) {
   constexpr int WAVES_N = BN / WN;
-  constexpr int NW = (BM / WM) * WAVES_N;
+  constexpr int NQW = (BM / WM) * WAVES_N;  // waves with a tile of their own
+  constexpr int NW = NQW * KW;
+  static_assert(KW == 1 || (KW == 2 && NQW == 1 && !GLU && !FP4), "K split: one-wave tiles, split or RoPE form");
   constexpr int MI = WM / 32, NJ = WN / 32;
   constexpr int ROWS = AE + BN;  // LDS rows of a 128-deep sub-buffer: A, then B
   static_assert(AE <= BM && AE % 16 == 0, "A rows loaded");
@@ -191,7 +201,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const TileXY t = tile_of(blockIdx.x, tiles_m, tiles_n, GM);
   // n0: first output column (GLU: first gate column g0)
   const int m0 = t.tm * BM, n0 = t.tn * (GLU ? BN / 2 : BN);
-  const int wm0 = (wave / WAVES_N) * WM, wn0 = (wave % WAVES_N) * WN;
+  // the wave's tile (qw) and, with KW = 2, its substep parity (kslice)
+  const int qw = wave % NQW, kslice = wave / NQW;
+  const int wm0 = (qw / WAVES_N) * WM, wn0 = (qw % WAVES_N) * WN;
 
   // Epilogue operands. Read in the epilogue, they formed a chain behind the
   // last stage: the two scale loads, the split table one scalar load and
@@ -215,7 +227,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   // 11.23 -> 11.31 us), the GEGLU form and the MXFP4 forms (no gain
   // measured; MXFP4 at M = 1 6.07 -> 6.18 us).
   constexpr bool SPLIT = !GLU && !ROPE;
-  constexpr bool EARLY = SPLIT && !FP4 && BM * BN <= 64 * 64 && !(WNT && AE == BM);
+  constexpr bool EARLY = SPLIT && !FP4 && BM * BN <= 64 * 64 && !(WNT && AE == 64);
   constexpr bool EARLY_R = ROPE && !FP4 && BM * BN <= 64 * 64 && MI * NJ == 1;
   constexpr int NE = EARLY ? NJ : 1;
   float alpha = 1.0f;
@@ -399,6 +411,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   const int sw = (lrow32 >> 1) & 7;  // (row >> 1) & 7 for rows 32k + lrow32
   const uint8_t* lbase0 = smem + lrow32 * 128 + ((((lane >> 5) * 2) ^ sw) * 16);
   const uint8_t* lbase1 = smem + lrow32 * 128 + ((((lane >> 5) * 2 + 4) ^ sw) * 16);
+  const uint8_t* lbk = kslice ? lbase1 : lbase0;  // KW = 2: this wave's half of each 128-deep run
   // this lane's scale dword within a 32-row block: row lrow32, K half l / 32
   const uint8_t* sbase = smem + SCBASE + lane * 4;
   // first LDS row of A fragment i of this wave (row 0 past the loaded rows)
@@ -427,7 +440,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
       }
       return;
     } else {
-    const uint8_t* lb = ((SUB & 1) ? lbase1 : lbase0) + SL * STAGE + (SUB >> 1) * SUBB;
+    // KW = 2: SUB counts this wave's substeps (global substep 2 SUB + kslice)
+    const uint8_t* lb = (KW == 2 ? lbk : ((SUB & 1) ? lbase1 : lbase0)) + SL * STAGE +
+                        (KW == 2 ? SUB : (SUB >> 1)) * SUBB;
     // the second chunk sits at position ^ 1, i.e. +16 or -16 bytes
     const int d1 = (sw & 1) ? -16 : 16;
 #pragma unroll
@@ -471,8 +486,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
   // barrier (one LDS round trip per stage) and alternate between two
   // independent accumulator sets, so consecutive MFMAs do not wait on each
   // other; large wave tiles reuse one fragment set and one accumulator set.
-  constexpr int KSUB = (FP4 ? 4 : 2) * NSUB;
+  constexpr int KSUB = (FP4 ? 4 : 2) * NSUB / KW;  // 64-deep substeps a wave multiplies per stage
   constexpr bool ALL = MI * NJ * KSUB <= 8;
+  static_assert(KW == 1 || ALL, "K split: fragments of the whole stage read at once");
   constexpr int NACC = (ALL && KSUB >= 2) ? 2 : 1;
   constexpr int NF = ALL ? KSUB : 1;
   // (FP4 fragments use the low four dwords only; the MFMA reads four
@@ -558,6 +574,29 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_kernel(GemmAr
     for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] += acc2[i][j];
+  }
+  if constexpr (KW == 2) {
+    // the odd-substep wave's sums go through the ring slot that no load
+    // targets and no wave reads any more (that of stage KT, as the epilogue
+    // uses it); the even wave adds them to its own (a fixed order)
+    float* red = reinterpret_cast<float*>(smem + (KT % NS) * STAGE);
+    static_assert(MI * NJ * 16 * 64 * 4 <= STAGE, "partial sums fit one slot");
+    if (kslice == 1) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((i * NJ + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+    }
+    __syncthreads();
+    if (kslice == 1) return;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] += red[((i * NJ + j) * 16 + r) * 64 + lane];
   }
 
   if constexpr (!EARLY && !EARLY_R) ep_loads();
@@ -1118,21 +1157,21 @@ int64_t rounds_256(const GemmArgs& a, int BN, int cus) {
   return (tiles + cus - 1) / cus;
 }
 template <int BM, int BN, int WM, int WN, int NS, int GM, int NSUB = 1, int AE = BM, bool GLU = false,
-          bool ROPE = false, bool FP4 = false, bool WNT = false>
+          bool ROPE = false, bool FP4 = false, bool WNT = false, int KW = 1>
 hipError_t launch_tiles(const GemmArgs& a, hipStream_t st) {
   // (GLU: N = 2H, so this is also ceil(H / (BN / 2)) column tiles)
   const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  constexpr int threads = (BM / WM) * (BN / WN) * 64;
+  constexpr int threads = (BM / WM) * (BN / WN) * KW * 64;
   if constexpr (FP4) {  // whole stages (K a multiple of 256 * NSUB) is checked by the caller
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE, true, WNT>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE, true, WNT, KW>), dim3(tiles),
                        dim3(threads), 0, st, a);
     return hipGetLastError();
   }
   if (a.K % (128 * NSUB) == 0)
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE, false, WNT>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, false, NSUB, AE, GLU, ROPE, false, WNT, KW>), dim3(tiles),
                        dim3(threads), 0, st, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, true, NSUB, AE, GLU, ROPE, false, WNT>), dim3(tiles),
+    hipLaunchKernelGGL((gemm_kernel<BM, BN, WM, WN, NS, GM, true, NSUB, AE, GLU, ROPE, false, WNT, KW>), dim3(tiles),
                        dim3(threads), 0, st, a);
   return hipGetLastError();
 }
@@ -1237,10 +1276,11 @@ hipError_t launch_planned(const GemmArgs& a, hipStream_t st) {
   // instructions would only fetch zeros): M = 1 9.3 -> 8.8 us, M = 16
   // 9.8 -> 9.3 us for 6144 x 4096 weights. At M <= 16 a three-deep ring of
   // 512-deep stages keeps more of the weight stream in flight (M = 1
-  // 8.75 -> 8.50 us, M = 16 9.23 -> 9.05 us; it loses at M = 32 and 64)
-  if (a.M <= 16 && a.K % 512 == 0) return launch_tiles<64, 32, 32, 32, 3, 1, 4, 16, false, ROPE, false, true>(a, st);
-  if (a.M <= 16) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 16, false, ROPE, false, true>(a, st);
-  if (a.M <= 32) return launch_tiles<64, 32, 32, 32, 4, 1, 2, 32, false, ROPE, false, true>(a, st);
+  // 8.75 -> 8.50 us, M = 16 9.23 -> 9.05 us; it loses at M = 32 and 64).
+  // At M <= 32 one 32 x 32 tile of two K-splitting waves (KW = 2).
+  if (a.M <= 16 && a.K % 512 == 0) return launch_tiles<32, 32, 32, 32, 3, 1, 4, 16, false, ROPE, false, true, 2>(a, st);
+  if (a.M <= 16) return launch_tiles<32, 32, 32, 32, 4, 1, 2, 16, false, ROPE, false, true, 2>(a, st);
+  if (a.M <= 32) return launch_tiles<32, 32, 32, 32, 4, 1, 2, 32, false, ROPE, false, true, 2>(a, st);
   return launch_tiles<64, 32, 32, 32, 4, 1, 2, 64, false, ROPE, false, true>(a, st);
 }
 
