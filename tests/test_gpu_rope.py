@@ -88,6 +88,8 @@ def _qkv_operands(M, K, nh, kv, hd, seed, bias=False):
 @pytest.mark.parametrize("M,K,nh,kv,hd,P,bias", [
     (256, 2048, 8, 1, 256, 768, False),   # decoder layer (64x64 plan)
     (16, 2048, 8, 1, 256, 0, True),       # small M, rows past M not loaded
+    (3, 2048, 8, 1, 256, 11, True),       # M <= 8 in one round: five-deep ring
+    (1, 4096, 32, 8, 128, 0, False),      # one decode token, 6144 x 4096
     (40, 1040, 4, 2, 64, 5, False),       # K tail, two KV heads
     (600, 1024, 4, 2, 128, 100, False),   # ragged M > 512 (64x64 plan)
     (256, 512, 32, 8, 128, 7, False),     # 64x64 plan (ties with 128x128)
