@@ -112,6 +112,7 @@ def test_ada_norm_mxfp4_vs_oracle(M, D):
     (600, 1000, 1024, False),   # 64x64 plan
     (333, 1000, 512, True),     # 64x32 plan
     (5, 1000, 768, False),      # small-M plan
+    (3, 1000, 2048, True),      # M <= 8 in one round: five-deep ring
 ])
 def test_gemm_mxfp4_vs_oracle(M, N, K, bias):
     a = wl.random_bf16(1400 + M, (M, K), 1.0)
