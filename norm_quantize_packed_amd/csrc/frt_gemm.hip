@@ -1279,15 +1279,16 @@ hipError_t launch_planned(const GemmArgs& a, hipStream_t st) {
   // 8.75 -> 8.50 us, M = 16 9.23 -> 9.05 us; it loses at M = 32 and 64).
   // At M <= 32 one 32 x 32 tile of two K-splitting waves (KW = 2).
   // At M <= 8 (only the first 8-row A load of each stage fetches data) in
-  // one round (a block per CU, LDS to spare) a five-deep ring keeps more of
-  // the weight stream in flight (6144 x 4096 weights: M = 1 7.16 -> 6.77
-  // us, M = 4 7.87 -> 7.65, M = 8 7.86 -> 7.69; M = 9 and 16 keep the
-  // three-deep ring, which the deeper one did not beat). Deeper rings at
+  // one round (a block per CU, LDS to spare) a four-deep ring keeps more of
+  // the weight stream in flight (6144 x 4096 weights, ring depth 3 / 4 / 5
+  // / 6: M = 1 7.16 / 6.64 / 6.74 / 7.01 us, M = 8 7.86 / 7.58 / 7.69 /
+  // 7.83; M = 9 and 16 keep the three-deep ring, which a five-deep one did
+  // not beat). Deeper rings at
   // M = 16, 32 and 64 (five, seven and six deep) and for the one-round
   // 64x64 plan measured level or slower (8.15 -> 8.17, 9.40 -> 9.46,
   // 11.27 -> 11.64; 256 x 2560 x 2048 8.73 -> 9.24 us).
   if (a.M <= 8 && a.K % 512 == 0 && (a.N + 31) / 32 <= device_cus())
-    return launch_tiles<32, 32, 32, 32, 5, 1, 4, 16, false, ROPE, false, true, 2>(a, st);
+    return launch_tiles<32, 32, 32, 32, 4, 1, 4, 16, false, ROPE, false, true, 2>(a, st);
   if (a.M <= 16 && a.K % 512 == 0) return launch_tiles<32, 32, 32, 32, 3, 1, 4, 16, false, ROPE, false, true, 2>(a, st);
   if (a.M <= 16) return launch_tiles<32, 32, 32, 32, 4, 1, 2, 16, false, ROPE, false, true, 2>(a, st);
   if (a.M <= 32) return launch_tiles<32, 32, 32, 32, 4, 1, 2, 32, false, ROPE, false, true, 2>(a, st);
